@@ -1,0 +1,396 @@
+"""Pins for the CPU oracle: each check is independent of the oracle's own code.
+
+The pages print no worked example for any format or kernel, so the oracle is
+pinned by hand-built blocks (tests/golden), exact rational brute force, closed
+forms, textbook special cases and invariants.  A plausible slip anywhere in the
+oracle (nibble order, offset, sign, transposed operand, softmax over the wrong
+set, unstable sort, gate applied to the wrong pair) fails at least one test.
+"""
+import math
+import os
+from collections import Counter
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import scipy.special
+
+import oracle
+import synth
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _read_golden(name):
+    bytes_, values = None, []
+    with open(os.path.join(GOLDEN, name)) as f:
+        for line in f:
+            if line.startswith("bytes"):
+                bytes_ = bytes.fromhex("".join(line.split()[1:]))
+            elif line.startswith("values"):
+                values.append([float(v) for v in line.split()[1:]])
+    return np.frombuffer(bytes_, dtype=np.uint8), np.concatenate(values)
+
+
+def _f16(v):
+    return float(np.float16(v))
+
+
+def _f16_bytes(v):
+    return list(np.array([v], dtype=np.float16).view(np.uint8))
+
+
+# ----------------------------------------------------------------------------
+# Block decoding
+# ----------------------------------------------------------------------------
+def test_golden_q4_0():
+    raw, want = _read_golden("q4_0_blocks.txt")
+    got = oracle.dequant(oracle.Q4_0, raw, 1, 64)
+    assert got.shape == (1, 64)
+    assert np.array_equal(got[0], want)
+
+
+def test_golden_q8_0():
+    raw, want = _read_golden("q8_0_blocks.txt")
+    got = oracle.dequant(oracle.Q8_0, raw, 1, 32)
+    assert np.array_equal(got[0], want)
+
+
+@pytest.mark.parametrize("scale", [1.0, 2.0 ** -7, 0.002, 0.02, -0.5])
+def test_dequant_every_q4_code(scale):
+    """Every code 0..15 in every position: w == s*(q-8) exactly."""
+    s = _f16(scale)
+    rows = []
+    expect = []
+    for shift in range(16):
+        q = [(i + shift) % 16 for i in range(32)]
+        body = [q[i] | (q[i + 16] << 4) for i in range(16)]
+        rows.append(_f16_bytes(s) + body)
+        expect.append([s * (c - 8) for c in q])
+    raw = np.array(rows, dtype=np.uint8).reshape(-1)
+    got = oracle.dequant(oracle.Q4_0, raw, 16, 32)
+    assert np.array_equal(got, np.array(expect))
+
+
+@pytest.mark.parametrize("scale", [1.0, 2.0 ** -7, 0.0002, 0.002])
+def test_dequant_every_q8_code(scale):
+    """Every int8 code -128..127: w == s*q exactly."""
+    s = _f16(scale)
+    codes = np.arange(-128, 128, dtype=np.int64).reshape(8, 32)
+    rows = [_f16_bytes(s) + [int(c) & 0xFF for c in row] for row in codes]
+    raw = np.array(rows, dtype=np.uint8).reshape(-1)
+    got = oracle.dequant(oracle.Q8_0, raw, 8, 32)
+    assert np.array_equal(got, s * codes.astype(np.float64))
+
+
+@pytest.mark.parametrize("fmt", [synth.Q4_0, synth.Q8_0])
+def test_decode_returns_the_drawn_codes(fmt):
+    w = synth.q_weight(synth.rng_for(7, fmt), fmt, 5, 96)
+    s, q = oracle.decode(fmt, w.canon, 5, 96)
+    assert np.array_equal(s, w.scales.astype(np.float64))
+    assert np.array_equal(q, w.codes.astype(np.int64))
+
+
+def test_decode_rejects_bad_sizes():
+    with pytest.raises(ValueError):
+        oracle.decode(oracle.Q4_0, np.zeros(18, np.uint8), 1, 48)
+    with pytest.raises(ValueError):
+        oracle.decode(oracle.Q4_0, np.zeros(17, np.uint8), 1, 32)
+
+
+# ----------------------------------------------------------------------------
+# Products: exact rational brute force and closed forms
+# ----------------------------------------------------------------------------
+def _exact_gemv(fmt, w, x_values):
+    """Exact y and |w*x| bound from the logical draw, in Fractions."""
+    N, K = w.codes.shape
+    M = x_values.shape[0]
+    off = 8 if fmt == synth.Q4_0 else 0
+    y = [[Fraction(0)] * N for _ in range(M)]
+    b = [[Fraction(0)] * N for _ in range(M)]
+    for n in range(N):
+        for kk in range(K):
+            wv = Fraction(float(w.scales[n, kk // 32])) * (int(w.codes[n, kk]) - off)
+            for m in range(M):
+                t = wv * Fraction(float(x_values[m, kk]))
+                y[m][n] += t
+                b[m][n] += abs(t)
+    return y, b
+
+
+@pytest.mark.parametrize("fmt,xdt", [(synth.Q4_0, synth.F16), (synth.Q8_0, synth.BF16),
+                                     (synth.Q4_0, synth.BF16), (synth.Q8_0, synth.F16)])
+@pytest.mark.parametrize("K", [32, 64, 96])
+def test_gemv_matches_exact_rationals(fmt, xdt, K):
+    N, M = 4, 3
+    w = synth.q_weight(synth.rng_for(11, K + fmt), fmt, N, K)
+    x = synth.activation(synth.rng_for(12, K + xdt), (M, K), xdt)
+    y, b = oracle.qgemv(fmt, w.canon, N, K, x.values)
+    ye, be = _exact_gemv(fmt, w, x.values)
+    for m in range(M):
+        for n in range(N):
+            bound = float(be[m][n])
+            assert abs(y[m, n] - float(ye[m][n])) <= 1e-15 * bound + 1e-300
+            assert abs(b[m, n] - bound) <= 1e-15 * bound
+
+
+def test_gemv_one_hot_picks_a_column():
+    w = synth.q_weight(synth.rng_for(3, 0), synth.Q4_0, 8, 128)
+    W = w.scales.astype(np.float64).repeat(32, axis=1) * (w.codes.astype(np.float64) - 8)
+    for k in [0, 5, 31, 32, 127]:
+        x = np.zeros((1, 128))
+        x[0, k] = 1.0
+        y, _ = oracle.qgemv(synth.Q4_0, w.canon, 8, 128, x)
+        assert np.array_equal(y[0], W[:, k])
+
+
+def test_gemv_all_ones_closed_form():
+    """x = 1: y[n] = sum_b s[n,b] * (sum_i q[n,b,i] - 256) for Q4_0."""
+    w = synth.q_weight(synth.rng_for(4, 0), synth.Q4_0, 6, 256)
+    y, _ = oracle.qgemv(synth.Q4_0, w.canon, 6, 256, np.ones((1, 256)))
+    q = w.codes.astype(np.int64).reshape(6, 8, 32).sum(axis=2) - 256
+    want = (w.scales.astype(np.float64) * q).sum(axis=1)
+    assert np.allclose(y[0], want, rtol=1e-14, atol=0)
+    w8 = synth.q_weight(synth.rng_for(4, 1), synth.Q8_0, 6, 256)
+    y8, _ = oracle.qgemv(synth.Q8_0, w8.canon, 6, 256, np.ones((1, 256)))
+    q8 = w8.codes.astype(np.int64).reshape(6, 8, 32).sum(axis=2)
+    assert np.allclose(y8[0], (w8.scales.astype(np.float64) * q8).sum(axis=1), rtol=1e-14, atol=0)
+
+
+def test_gemv_zero_codes_give_zero():
+    scales = np.full((3, 4), np.float16(0.01))
+    codes = np.full((3, 128), 8, dtype=np.uint8)
+    raw = synth.pack_blocks(synth.Q4_0, scales, codes)
+    x = synth.activation(synth.rng_for(5, 0), (2, 128), synth.F16).values
+    y, b = oracle.qgemv(synth.Q4_0, raw, 3, 128, x)
+    assert np.all(y == 0) and np.all(b == 0)
+    raw8 = synth.pack_blocks(synth.Q8_0, scales, np.zeros((3, 128), np.int8))
+    y8, _ = oracle.qgemv(synth.Q8_0, raw8, 3, 128, x)
+    assert np.all(y8 == 0)
+
+
+def test_gemv_doubling_scales_doubles_y():
+    w = synth.q_weight(synth.rng_for(6, 0), synth.Q4_0, 5, 160)
+    x = synth.activation(synth.rng_for(6, 1), (2, 160), synth.F16).values
+    y1, _ = oracle.qgemv(synth.Q4_0, w.canon, 5, 160, x)
+    raw2 = synth.pack_blocks(synth.Q4_0, (w.scales.astype(np.float32) * 2).astype(np.float16), w.codes)
+    y2, _ = oracle.qgemv(synth.Q4_0, raw2, 5, 160, x)
+    assert np.array_equal(y2, 2 * y1)
+
+
+def test_gemv_linear_in_x():
+    w = synth.q_weight(synth.rng_for(8, 0), synth.Q8_0, 7, 96)
+    a = synth.activation(synth.rng_for(8, 1), (1, 96), synth.BF16).values
+    c = synth.activation(synth.rng_for(8, 2), (1, 96), synth.BF16).values
+    ya, ba = oracle.qgemv(synth.Q8_0, w.canon, 7, 96, a)
+    yc, bc = oracle.qgemv(synth.Q8_0, w.canon, 7, 96, c)
+    ys, _ = oracle.qgemv(synth.Q8_0, w.canon, 7, 96, 3 * a - c)
+    assert np.allclose(ys, 3 * ya - yc, rtol=0, atol=1e-13 * (3 * ba + bc).max())
+
+
+def test_gemm_rows_agree_with_full_product():
+    w = synth.q_weight(synth.rng_for(9, 0), synth.Q4_0, 40, 128)
+    X = synth.activation(synth.rng_for(9, 1), (17, 128), synth.BF16).values
+    Y, B = oracle.qgemm(synth.Q4_0, w.canon, 40, 128, X)
+    rows = [0, 3, 16, 16, 9]
+    cols = [39, 0, 7, 8, 20]
+    y, b = oracle.qgemm_rows(synth.Q4_0, w.canon, 40, 128, X, rows, cols)
+    assert np.allclose(y, Y[rows, cols], rtol=1e-14, atol=1e-14)
+    assert np.allclose(b, B[rows, cols], rtol=1e-14)
+
+
+# ----------------------------------------------------------------------------
+# Routing and sorting
+# ----------------------------------------------------------------------------
+def _brute_route(lg, k):
+    ids, gates = [], []
+    for row in lg:
+        order = sorted(range(len(row)), key=lambda e: (-float(row[e]), e))[:k]
+        sel = [float(row[e]) for e in order]
+        m = max(sel)
+        ex = [math.exp(v - m) for v in sel]
+        s = math.fsum(ex)
+        ids.append(order)
+        gates.append([v / s for v in ex])
+    return np.array(ids), np.array(gates)
+
+
+def test_route_matches_brute_force_with_ties():
+    rng = synth.rng_for(21, 0)
+    lg = synth.router_logits(rng, 40, 16)
+    lg[0, :] = 0.5                       # all tied: ids 0..k-1
+    lg[1, [3, 9, 12]] = 4.0              # three-way tie at the top
+    lg[2, [15, 0]] = 3.0                 # tie across the ends
+    lg[3, :] = -1.0
+    lg[3, 5] = np.float32(1.0) + np.float32(2.0 ** -23)
+    lg[3, 4] = 1.0                       # one ulp apart: 5 before 4
+    ids, gates = oracle.moe_route(lg, 4)
+    bi, bg = _brute_route(lg, 4)
+    assert np.array_equal(ids, bi)
+    assert np.allclose(gates, bg, rtol=1e-15, atol=0)
+    assert list(ids[0]) == [0, 1, 2, 3]
+    assert list(ids[1][:3]) == [3, 9, 12]
+    assert list(ids[2][:2]) == [0, 15]
+    assert list(ids[3][:2]) == [5, 4]
+
+
+def test_route_gates_are_a_softmax():
+    lg = synth.router_logits(synth.rng_for(22, 0), 64, 128)
+    ids, g = oracle.moe_route(lg, 8)
+    assert np.allclose(g.sum(axis=1), 1.0, rtol=0, atol=1e-15)
+    assert np.all(np.diff(g, axis=1) <= 0)
+    sel = np.take_along_axis(lg.astype(np.float64), ids.astype(np.int64), axis=1)
+    assert np.allclose(g, scipy.special.softmax(sel, axis=1), rtol=1e-14, atol=0)
+    # k = E: the gates are the softmax over all experts, in sorted order.
+    idsE, gE = oracle.moe_route(lg, 128)
+    full = scipy.special.softmax(lg.astype(np.float64), axis=1)
+    assert np.allclose(gE, np.take_along_axis(full, idsE.astype(np.int64), axis=1), rtol=1e-13, atol=0)
+    # k = 1: the arg-max with gate 1.
+    id1, g1 = oracle.moe_route(lg, 1)
+    assert np.array_equal(id1[:, 0], np.argmax(lg, axis=1))
+    assert np.all(g1 == 1.0)
+
+
+def test_route_rejects_bad_topk():
+    with pytest.raises(ValueError):
+        oracle.moe_route(np.zeros((2, 4), np.float32), 5)
+
+
+def test_sort_matches_brute_force():
+    rng = synth.rng_for(23, 0)
+    E, T, k = 16, 50, 4
+    ids, _ = oracle.moe_route(synth.router_logits(rng, T, E), k)
+    counts, offsets, sp = oracle.moe_sort(ids, E)
+    pairs = sorted((int(ids.reshape(-1)[p]), p) for p in range(T * k))
+    assert list(sp) == [p for _, p in pairs]
+    c = Counter(ids.reshape(-1).tolist())
+    assert list(counts) == [c.get(e, 0) for e in range(E)]
+    assert offsets[0] == 0 and offsets[-1] == T * k
+    assert np.all(np.diff(offsets) == counts)
+    assert sorted(sp.tolist()) == list(range(T * k))
+    e_sorted = ids.reshape(-1)[sp]
+    assert np.all(np.diff(e_sorted) >= 0)
+    for e in range(E):
+        seg = sp[offsets[e]:offsets[e + 1]]
+        assert np.all(np.diff(seg) > 0)          # stable: ascending pair id
+
+
+def test_sort_with_empty_experts():
+    ids = np.array([[3, 1], [3, 1], [1, 3]], dtype=np.int32)
+    counts, offsets, sp = oracle.moe_sort(ids, 6)
+    assert list(counts) == [0, 3, 0, 3, 0, 0]
+    assert list(offsets) == [0, 0, 3, 3, 6, 6, 6]
+    assert list(sp) == [1, 3, 4, 0, 2, 5]
+
+
+# ----------------------------------------------------------------------------
+# Expert SwiGLU and combine
+# ----------------------------------------------------------------------------
+def test_silu_textbook_values():
+    for z in [-40.0, -3.0, -1.0, 0.0, 0.5, 1.0, 3.0, 40.0, 800.0, -800.0]:
+        want = z / (1.0 + math.exp(-z)) if z > -700 else 0.0
+        assert abs(float(oracle.silu(z)) - want) <= 1e-15 * max(1.0, abs(z))
+    zs = np.linspace(-6, 6, 25)
+    h = 1e-6
+    fd = (oracle.silu(zs + h) - oracle.silu(zs - h)) / (2 * h)
+    assert np.allclose(oracle.silu_prime(zs), fd, rtol=0, atol=1e-8)
+
+
+def _small_moe(E=6, T=9, H=64, F=32, k=3, seed=31, same=False):
+    logits, x, wg, wu, wd = synth.moe(seed=seed, T=T, E=E, H=H, F=F)
+    if same:
+        wg = [wg[0]] * E
+        wu = [wu[0]] * E
+        wd = [wd[0]] * E
+    return logits, x, wg, wu, wd
+
+
+def _dense_ffn(w_g, w_u, w_d, xv):
+    """Dense SwiGLU from the logical draw (independent of the oracle decoder)."""
+    def deq(w):
+        return w.scales.astype(np.float64).repeat(32, axis=1) * (w.codes.astype(np.float64) - 8)
+    zg = xv @ deq(w_g).T
+    zu = xv @ deq(w_u).T
+    h = zg / (1.0 + np.exp(-zg)) * zu
+    return h @ deq(w_d).T
+
+
+def test_identical_experts_equal_a_dense_ffn():
+    E, T, H, F, k = 6, 9, 64, 32, 3
+    logits, x, wg, wu, wd = _small_moe(E, T, H, F, k, same=True)
+    r = oracle.moe(synth.Q4_0, [w.canon for w in wg], [w.canon for w in wu],
+                   [w.canon for w in wd], x.values, logits, k, H, F)
+    dense = _dense_ffn(wg[0], wu[0], wd[0], x.values)
+    assert np.allclose(r["out"], dense, rtol=1e-12, atol=1e-12)
+
+
+def test_top1_picks_the_argmax_expert():
+    E, T, H, F = 5, 7, 64, 32
+    logits, x, wg, wu, wd = _small_moe(E, T, H, F, seed=32)
+    r = oracle.moe(synth.Q4_0, [w.canon for w in wg], [w.canon for w in wu],
+                   [w.canon for w in wd], x.values, logits, 1, H, F)
+    for t in range(T):
+        e = int(np.argmax(logits[t]))
+        want = _dense_ffn(wg[e], wu[e], wd[e], x.values[t:t + 1])[0]
+        assert np.allclose(r["out"][t], want, rtol=1e-12, atol=1e-12)
+
+
+def test_one_hot_token_closed_form():
+    """x_t = e_c: z_g[f] = W_g[f, c] and z_u[f] = W_u[f, c] exactly."""
+    E, T, H, F, k = 4, 4, 64, 32, 2
+    logits, x, wg, wu, wd = _small_moe(E, T, H, F, k, seed=33)
+    xv = np.zeros((T, H))
+    cols = [0, 17, 33, 63]
+    for t, c in enumerate(cols):
+        xv[t, c] = 1.0
+    r = oracle.moe(synth.Q4_0, [w.canon for w in wg], [w.canon for w in wu],
+                   [w.canon for w in wd], xv, logits, k, H, F)
+    ids, gates = r["ids"], r["gates"]
+    for t, c in enumerate(cols):
+        acc = np.zeros(H)
+        for j in range(k):
+            e = int(ids[t, j])
+            g_col = wg[e].scales[:, c // 32].astype(np.float64) * (wg[e].codes[:, c].astype(np.float64) - 8)
+            u_col = wu[e].scales[:, c // 32].astype(np.float64) * (wu[e].codes[:, c].astype(np.float64) - 8)
+            h = [gv / (1.0 + math.exp(-gv)) * uv for gv, uv in zip(g_col, u_col)]
+            Wd = wd[e].scales.astype(np.float64).repeat(32, axis=1) * (wd[e].codes.astype(np.float64) - 8)
+            acc += gates[t, j] * (Wd @ np.array(h))
+        assert np.allclose(r["out"][t], acc, rtol=1e-12, atol=1e-13)
+
+
+def test_relabelling_experts_changes_nothing():
+    E, T, H, F, k = 6, 8, 64, 32, 3
+    logits, x, wg, wu, wd = _small_moe(E, T, H, F, k, seed=34)
+    perm = np.array([4, 2, 5, 0, 1, 3])          # new label i is old expert perm[i]
+    cg = [w.canon for w in wg]
+    cu = [w.canon for w in wu]
+    cd = [w.canon for w in wd]
+    r1 = oracle.moe(synth.Q4_0, cg, cu, cd, x.values, logits, k, H, F)
+    r2 = oracle.moe(synth.Q4_0, [cg[i] for i in perm], [cu[i] for i in perm], [cd[i] for i in perm],
+                    x.values, logits[:, perm], k, H, F)
+    assert np.allclose(r1["out"], r2["out"], rtol=1e-12, atol=1e-13)
+
+
+def test_moe_bounds_catch_a_planted_error():
+    """The propagated bound accepts the oracle and rejects plausible slips.
+
+    The acceptance rule scales sum|w*x|, which exceeds |y| by about sqrt(K) on
+    random data, so the slips planted here are the structural ones: silu on
+    the up projection instead of the gate, and gates applied to the wrong slot.
+    """
+    E, T, H, F, k = 6, 9, 64, 32, 3
+    logits, x, wg, wu, wd = _small_moe(E, T, H, F, k, seed=35)
+    cg, cu, cd = [w.canon for w in wg], [w.canon for w in wu], [w.canon for w in wd]
+    r = oracle.moe(synth.Q4_0, cg, cu, cd, x.values, logits, k, H, F)
+    hb = oracle.h_bound(r)
+    ob = oracle.moe_out_bound(synth.Q4_0, cd, r, r["ids"], r["gates"], r["sorted_pairs"], H, F, hb)
+    assert np.all(ob > 0)
+    assert np.all(np.abs(r["h"] - r["h"]) <= hb)
+    swapped = oracle.silu(r["zu"]) * r["zg"]
+    assert np.any(np.abs(swapped - r["h"]) > hb)
+    bad = oracle.moe_ffn(synth.Q4_0, cg, cu, cd, x.values, r["ids"], r["gates"], r["sorted_pairs"],
+                         H, F, h_override=swapped)
+    assert np.any(np.abs(bad["out"] - r["out"]) > ob)
+    g_bad = r["gates"][:, ::-1].copy()
+    bad2 = oracle.moe_ffn(synth.Q4_0, cg, cu, cd, x.values, r["ids"], g_bad, r["sorted_pairs"], H, F)
+    assert np.any(np.abs(bad2["out"] - r["out"]) > ob)
