@@ -1,0 +1,226 @@
+"""Python binding of libq4q8.so (ctypes), with torch tensors for memory and streams.
+
+Argument marshalling only: every computation runs in the library's HIP
+kernels.  Tensors are passed by data pointer together with the current HIP
+stream of their device.  If the library is not built the first call raises;
+there is no fallback path.
+
+Formats: Q4_0 = 1, Q8_0 = 2.  Activation dtypes: torch.float16 or
+torch.bfloat16.  Weights are uint8 tensors holding repacked blocks
+(see repack()).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+Q4_0 = 1
+Q8_0 = 2
+F16 = 1
+BF16 = 2
+F32 = 3
+MAX_GROUP = 8
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libq4q8.so")
+_lib = None
+
+_DT = {torch.float16: F16, torch.bfloat16: BF16, torch.float32: F32}
+
+
+class Q4Q8Error(RuntimeError):
+    def __init__(self, status: int, what: str):
+        super().__init__(f"{what}: status {status} ({status_string(status)}): {last_error()}")
+        self.status = status
+
+
+class GemvDesc(ctypes.Structure):
+    _fields_ = [("W", ctypes.c_void_p), ("x", ctypes.c_void_p), ("y", ctypes.c_void_p),
+                ("N", ctypes.c_int64), ("K", ctypes.c_int64),
+                ("ldx", ctypes.c_int64), ("ldy", ctypes.c_int64)]
+
+
+def _declare(lib):
+    i64, i32, vp, sz = ctypes.c_int64, ctypes.c_int, ctypes.c_void_p, ctypes.c_size_t
+    sig = {
+        "q4q8_abi_version": (i32, []),
+        "q4q8_status_string": (ctypes.c_char_p, [i32]),
+        "q4q8_last_error": (ctypes.c_char_p, []),
+        "q4q8_canonical_bytes": (sz, [i32, i64, i64]),
+        "q4q8_repacked_bytes": (sz, [i32, i64, i64]),
+        "q4q8_repack": (i32, [i32, vp, i64, i64, vp, sz, vp]),
+        "q4q8_repack_host": (i32, [i32, vp, i64, i64, vp, sz]),
+        "q4q8_qgemv": (i32, [i32, vp, i64, i64, vp, i32, i64, i32, vp, i64, vp]),
+        "q4q8_qgemv_grouped": (i32, [i32, ctypes.POINTER(GemvDesc), i32, i32, i32, vp]),
+        "q4q8_qgemm": (i32, [i32, vp, i64, i64, vp, i32, i64, i64, vp, i32, i64, vp]),
+        "q4q8_moe_route": (i32, [vp, i32, i32, i32, vp, vp, vp, vp, vp, vp]),
+        "q4q8_moe_workspace": (sz, [i32, i32, i32, i32, i32, i32]),
+        "q4q8_moe_qgemm": (i32, [i32, vp, vp, vp, i32, i32, i32, vp, i32, i32, i32,
+                                 vp, vp, vp, vp, vp, vp, sz, vp]),
+    }
+    for name, (res, args) in sig.items():
+        f = getattr(lib, name)
+        f.restype = res
+        f.argtypes = args
+    return lib
+
+
+def lib():
+    """The loaded library; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with __graft_entry__.build() "
+                               "(or python gemm_q4_q8_amd/build.py)")
+        _lib = _declare(ctypes.CDLL(LIB_PATH))
+    return _lib
+
+
+def status_string(s: int) -> str:
+    return lib().q4q8_status_string(s).decode()
+
+
+def last_error() -> str:
+    return lib().q4q8_last_error().decode()
+
+
+def _check(st: int, what: str):
+    if st != 0:
+        raise Q4Q8Error(st, what)
+
+
+def _stream(t: torch.Tensor):
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
+
+
+def _dev(t: torch.Tensor, name: str):
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+# ----------------------------------------------------------------------------
+# Layout
+# ----------------------------------------------------------------------------
+def canonical_bytes(fmt: int, N: int, K: int) -> int:
+    return int(lib().q4q8_canonical_bytes(fmt, N, K))
+
+
+def repacked_bytes(fmt: int, N: int, K: int) -> int:
+    return int(lib().q4q8_repacked_bytes(fmt, N, K))
+
+
+def repack(fmt: int, canon: torch.Tensor, N: int, K: int, out: torch.Tensor | None = None) -> torch.Tensor:
+    """Canonical blocks (uint8 GPU tensor) -> repacked weights (uint8 GPU tensor)."""
+    _dev(canon, "canon")
+    nb = repacked_bytes(fmt, N, K)
+    if out is None:
+        out = torch.empty(nb, dtype=torch.uint8, device=canon.device)
+    _dev(out, "out")
+    if canon.numel() * canon.element_size() != canonical_bytes(fmt, N, K):
+        raise ValueError("canonical tensor has the wrong size")
+    _check(lib().q4q8_repack(fmt, _ptr(canon), N, K, _ptr(out), out.numel() * out.element_size(),
+                             _stream(canon)), "repack")
+    return out
+
+
+def repack_host(fmt: int, canon, N: int, K: int):
+    """Host-side conversion (numpy uint8 in, numpy uint8 out); touches no GPU."""
+    import numpy as np
+    src = np.ascontiguousarray(canon, dtype=np.uint8)
+    if src.size != canonical_bytes(fmt, N, K):
+        raise ValueError("canonical buffer has the wrong size")
+    dst = np.empty(repacked_bytes(fmt, N, K), dtype=np.uint8)
+    _check(lib().q4q8_repack_host(fmt, src.ctypes.data_as(ctypes.c_void_p), N, K,
+                                  dst.ctypes.data_as(ctypes.c_void_p), dst.size), "repack_host")
+    return dst
+
+
+# ----------------------------------------------------------------------------
+# Products
+# ----------------------------------------------------------------------------
+def qgemv(fmt: int, W: torch.Tensor, N: int, K: int, x: torch.Tensor,
+          out: torch.Tensor | None = None) -> torch.Tensor:
+    """y[M, N] fp32 = x[M, K] (fp16/bf16) @ W^T, M = 1..8."""
+    _dev(W, "W")
+    if x.dim() != 2 or x.shape[1] != K:
+        raise ValueError("x must be [M, K]")
+    if x.stride(1) != 1:
+        raise ValueError("x rows must be contiguous")
+    M = x.shape[0]
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.float32, device=x.device)
+    _check(lib().q4q8_qgemv(fmt, _ptr(W), N, K, _ptr(x), _DT[x.dtype], x.stride(0), M,
+                            _ptr(out), out.stride(0), _stream(x)), "qgemv")
+    return out
+
+
+def qgemv_grouped(fmt: int, problems, M: int):
+    """problems: list of (W, N, K, x [M,K], y [M,N] fp32); one launch."""
+    n = len(problems)
+    arr = (GemvDesc * max(n, 1))()
+    xdt = None
+    for i, (W, N, K, x, y) in enumerate(problems):
+        _dev(W, "W")
+        arr[i] = GemvDesc(W.data_ptr(), x.data_ptr(), y.data_ptr(), N, K, x.stride(0), y.stride(0))
+        xdt = _DT[x.dtype]
+    st = lib().q4q8_qgemv_grouped(fmt, arr, n, xdt if xdt is not None else F16, M,
+                                  _stream(problems[0][3]) if n else ctypes.c_void_p(0))
+    _check(st, "qgemv_grouped")
+
+
+def qgemm(fmt: int, W: torch.Tensor, N: int, K: int, X: torch.Tensor,
+          out: torch.Tensor | None = None, out_dtype=torch.bfloat16) -> torch.Tensor:
+    """Y[M, N] = X[M, K] @ W^T, fp32 accumulation, output out_dtype."""
+    _dev(W, "W")
+    if X.dim() != 2 or X.shape[1] != K or X.stride(1) != 1:
+        raise ValueError("X must be [M, K] with contiguous rows")
+    M = X.shape[0]
+    if out is None:
+        out = torch.empty((M, N), dtype=out_dtype, device=X.device)
+    _check(lib().q4q8_qgemm(fmt, _ptr(W), N, K, _ptr(X), _DT[X.dtype], X.stride(0), M,
+                            _ptr(out), _DT[out.dtype], out.stride(0), _stream(X)), "qgemm")
+    return out
+
+
+def moe_route(logits: torch.Tensor, topk: int):
+    """-> ids [T,k] int32, gates [T,k] fp32, counts [E], offsets [E+1], sorted_pairs [T*k]."""
+    _dev(logits, "logits")
+    T, E = logits.shape
+    d = logits.device
+    ids = torch.empty((T, topk), dtype=torch.int32, device=d)
+    gates = torch.empty((T, topk), dtype=torch.float32, device=d)
+    counts = torch.empty(E, dtype=torch.int32, device=d)
+    offsets = torch.empty(E + 1, dtype=torch.int32, device=d)
+    sp = torch.empty(T * topk, dtype=torch.int32, device=d)
+    _check(lib().q4q8_moe_route(_ptr(logits), T, E, topk, _ptr(ids), _ptr(gates), _ptr(counts),
+                                _ptr(offsets), _ptr(sp), _stream(logits)), "moe_route")
+    return ids, gates, counts, offsets, sp
+
+
+def moe_workspace(fmt: int, T: int, E: int, topk: int, H: int, F: int) -> int:
+    return int(lib().q4q8_moe_workspace(fmt, T, E, topk, H, F))
+
+
+def moe_qgemm(fmt: int, Wg, Wu, Wd, E: int, H: int, F: int, X: torch.Tensor, topk: int,
+              gates, offsets, sorted_pairs, out=None, h_out=None, ws=None):
+    """Expert SwiGLU + weighted combine -> out [T, H] fp32."""
+    T = X.shape[0]
+    d = X.device
+    if out is None:
+        out = torch.empty((T, H), dtype=torch.float32, device=d)
+    nws = moe_workspace(fmt, T, E, topk, H, F)
+    if ws is None:
+        ws = torch.empty(nws, dtype=torch.uint8, device=d)
+    _check(lib().q4q8_moe_qgemm(fmt, _ptr(Wg), _ptr(Wu), _ptr(Wd), E, H, F, _ptr(X), _DT[X.dtype], T, topk,
+                                _ptr(gates), _ptr(offsets), _ptr(sorted_pairs), _ptr(out),
+                                _ptr(h_out), _ptr(ws), ws.numel() * ws.element_size(), _stream(X)),
+           "moe_qgemm")
+    return out

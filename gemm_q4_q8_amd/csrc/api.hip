@@ -1,0 +1,229 @@
+// C-ABI layer: argument validation (pure host code, before anything is
+// enqueued), error reporting and dispatch to the kernel launchers.
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "../../include/q4q8.h"
+#include "q4q8_internal.h"
+
+namespace {
+
+thread_local char g_last_error[512];
+
+int fail(int status, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+  va_end(ap);
+  return status;
+}
+
+int hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return Q4Q8_OK;
+  return fail(Q4Q8_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool fmt_ok(int fmt) { return fmt == Q4Q8_Q4_0 || fmt == Q4Q8_Q8_0; }
+bool act_ok(int dt) { return dt == Q4Q8_F16 || dt == Q4Q8_BF16; }
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+int64_t canon_block(int fmt) { return fmt == Q4Q8_Q4_0 ? 18 : 34; }
+int64_t rec_bytes(int fmt) { return fmt == Q4Q8_Q4_0 ? 1152 : 2176; }
+
+// Shape rules common to every weight matrix.
+int check_matrix(int fmt, int64_t N, int64_t K) {
+  if (!fmt_ok(fmt)) return fail(Q4Q8_ERR_UNSUPPORTED, "unknown weight format %d", fmt);
+  if (N < 1 || K < 32) return fail(Q4Q8_ERR_INVALID_ARG, "bad shape N=%lld K=%lld", (long long)N, (long long)K);
+  if (K % 32) return fail(Q4Q8_ERR_INVALID_ARG, "K=%lld is not a multiple of 32", (long long)K);
+  if (N > (1LL << 30) || K > (1LL << 30))
+    return fail(Q4Q8_ERR_UNSUPPORTED, "shape N=%lld K=%lld beyond 2^30", (long long)N, (long long)K);
+  return Q4Q8_OK;
+}
+
+int64_t repacked(int fmt, int64_t N, int64_t K) {
+  return ((N + 15) / 16) * ((K + 127) / 128) * rec_bytes(fmt);
+}
+
+void clear_hip_error() { (void)hipGetLastError(); }
+
+}  // namespace
+
+extern "C" {
+
+int q4q8_abi_version(void) { return Q4Q8_ABI_VERSION; }
+
+const char* q4q8_status_string(int s) {
+  switch (s) {
+    case Q4Q8_OK: return "ok";
+    case Q4Q8_ERR_INVALID_ARG: return "invalid argument";
+    case Q4Q8_ERR_UNSUPPORTED: return "unsupported";
+    case Q4Q8_ERR_WORKSPACE: return "workspace too small";
+    case Q4Q8_ERR_ALIGNMENT: return "misaligned pointer or leading dimension";
+    case Q4Q8_ERR_HIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+const char* q4q8_last_error(void) { return g_last_error; }
+
+size_t q4q8_canonical_bytes(int fmt, int64_t N, int64_t K) {
+  if (!fmt_ok(fmt) || N < 1 || K < 32 || K % 32) return 0;
+  return (size_t)(N * (K / 32) * canon_block(fmt));
+}
+
+size_t q4q8_repacked_bytes(int fmt, int64_t N, int64_t K) {
+  if (!fmt_ok(fmt) || N < 1 || K < 32 || K % 32) return 0;
+  return (size_t)repacked(fmt, N, K);
+}
+
+int q4q8_repack(int fmt, const void* canon, int64_t N, int64_t K, void* dst, size_t dst_bytes, void* stream) {
+  int st = check_matrix(fmt, N, K);
+  if (st) return st;
+  if (!canon || !dst) return fail(Q4Q8_ERR_INVALID_ARG, "repack: null pointer");
+  if (!aligned(dst, 16)) return fail(Q4Q8_ERR_ALIGNMENT, "repack: destination not 16-byte aligned");
+  if (dst_bytes < (size_t)repacked(fmt, N, K))
+    return fail(Q4Q8_ERR_INVALID_ARG, "repack: destination holds %zu bytes, needs %lld", dst_bytes,
+                (long long)repacked(fmt, N, K));
+  clear_hip_error();
+  return hip_status(q4q8::launch_repack(fmt, canon, N, K, dst, (hipStream_t)stream), "repack launch");
+}
+
+int q4q8_repack_host(int fmt, const void* canon, int64_t N, int64_t K, void* dst, size_t dst_bytes) {
+  int st = check_matrix(fmt, N, K);
+  if (st) return st;
+  if (!canon || !dst) return fail(Q4Q8_ERR_INVALID_ARG, "repack_host: null pointer");
+  if (dst_bytes < (size_t)repacked(fmt, N, K))
+    return fail(Q4Q8_ERR_INVALID_ARG, "repack_host: destination holds %zu bytes, needs %lld", dst_bytes,
+                (long long)repacked(fmt, N, K));
+  q4q8::repack_host(fmt, canon, N, K, dst);
+  return Q4Q8_OK;
+}
+
+static int check_gemv_desc(int fmt, const q4q8_gemv_desc& d, int xdt, int M, int idx) {
+  int st = check_matrix(fmt, d.N, d.K);
+  if (st) return st;
+  if (!d.W || !d.x || !d.y) return fail(Q4Q8_ERR_INVALID_ARG, "qgemv[%d]: null pointer", idx);
+  if (!aligned(d.W, 16)) return fail(Q4Q8_ERR_ALIGNMENT, "qgemv[%d]: weights not 16-byte aligned", idx);
+  if (!aligned(d.x, 16)) return fail(Q4Q8_ERR_ALIGNMENT, "qgemv[%d]: x not 16-byte aligned", idx);
+  if (!aligned(d.y, 4)) return fail(Q4Q8_ERR_ALIGNMENT, "qgemv[%d]: y not 4-byte aligned", idx);
+  if (M > 1) {
+    if (d.ldx < d.K || d.ldy < d.N)
+      return fail(Q4Q8_ERR_INVALID_ARG, "qgemv[%d]: ldx=%lld < K or ldy=%lld < N", idx, (long long)d.ldx,
+                  (long long)d.ldy);
+    if (d.ldx % 8) return fail(Q4Q8_ERR_ALIGNMENT, "qgemv[%d]: ldx=%lld not a multiple of 8", idx, (long long)d.ldx);
+  }
+  (void)xdt;
+  return Q4Q8_OK;
+}
+
+int q4q8_qgemv_grouped(int fmt, const q4q8_gemv_desc* descs, int count, int xdt, int M, void* stream) {
+  if (!fmt_ok(fmt)) return fail(Q4Q8_ERR_UNSUPPORTED, "unknown weight format %d", fmt);
+  if (!act_ok(xdt)) return fail(Q4Q8_ERR_UNSUPPORTED, "qgemv: activation dtype %d not F16/BF16", xdt);
+  if (M < 1 || M > 8) return fail(Q4Q8_ERR_INVALID_ARG, "qgemv: M=%d outside 1..8", M);
+  if (!descs || count < 1 || count > Q4Q8_MAX_GROUP)
+    return fail(Q4Q8_ERR_INVALID_ARG, "qgemv: %d problems (1..%d allowed)", count, Q4Q8_MAX_GROUP);
+  q4q8::GemvArgs args;
+  memset(&args, 0, sizeof(args));
+  int64_t tiles = 0;
+  int max_chunks = 0;
+  for (int i = 0; i < count; ++i) {
+    int st = check_gemv_desc(fmt, descs[i], xdt, M, i);
+    if (st) return st;
+    q4q8::GemvProb& p = args.p[i];
+    p.W = (const uint8_t*)descs[i].W;
+    p.x = (const uint16_t*)descs[i].x;
+    p.y = descs[i].y;
+    p.ldx = M > 1 ? descs[i].ldx : 0;
+    p.ldy = M > 1 ? descs[i].ldy : 0;
+    p.N = (int32_t)descs[i].N;
+    p.K = (int32_t)descs[i].K;
+    p.tile0 = (int32_t)tiles;
+    tiles += (descs[i].N + 15) / 16;
+    const int chunks = (int)((descs[i].K + 127) / 128);
+    if (chunks > max_chunks) max_chunks = chunks;
+  }
+  if (tiles > (1LL << 31) - 1) return fail(Q4Q8_ERR_UNSUPPORTED, "qgemv: too many row tiles");
+  args.count = count;
+  args.M = M;
+  args.total_tiles = (int32_t)tiles;
+  clear_hip_error();
+  return hip_status(q4q8::launch_qgemv(fmt, xdt, args, max_chunks, (hipStream_t)stream), "qgemv launch");
+}
+
+int q4q8_qgemv(int fmt, const void* W, int64_t N, int64_t K, const void* x, int xdt, int64_t ldx, int M, float* y,
+               int64_t ldy, void* stream) {
+  q4q8_gemv_desc d;
+  d.W = W;
+  d.x = x;
+  d.y = y;
+  d.N = N;
+  d.K = K;
+  d.ldx = ldx;
+  d.ldy = ldy;
+  return q4q8_qgemv_grouped(fmt, &d, 1, xdt, M, stream);
+}
+
+int q4q8_qgemm(int fmt, const void* W, int64_t N, int64_t K, const void* X, int xdt, int64_t ldx, int64_t M, void* Y,
+               int ydt, int64_t ldy, void* stream) {
+  int st = check_matrix(fmt, N, K);
+  if (st) return st;
+  if (!act_ok(xdt)) return fail(Q4Q8_ERR_UNSUPPORTED, "qgemm: activation dtype %d not F16/BF16", xdt);
+  if (ydt != Q4Q8_F16 && ydt != Q4Q8_BF16 && ydt != Q4Q8_F32)
+    return fail(Q4Q8_ERR_UNSUPPORTED, "qgemm: output dtype %d", ydt);
+  if (M < 1 || M > (1LL << 30)) return fail(Q4Q8_ERR_INVALID_ARG, "qgemm: M=%lld", (long long)M);
+  if (!W || !X || !Y) return fail(Q4Q8_ERR_INVALID_ARG, "qgemm: null pointer");
+  if (ldx < K || ldy < N) return fail(Q4Q8_ERR_INVALID_ARG, "qgemm: ldx < K or ldy < N");
+  if (!aligned(W, 16) || !aligned(X, 16) || !aligned(Y, 16) || ldx % 8 || ldy % 8)
+    return fail(Q4Q8_ERR_ALIGNMENT, "qgemm: pointers must be 16-byte aligned, ldx and ldy multiples of 8");
+  clear_hip_error();
+  return hip_status(q4q8::launch_qgemm(fmt, xdt, ydt, W, N, K, X, ldx, M, Y, ldy, (hipStream_t)stream),
+                    "qgemm launch");
+}
+
+int q4q8_moe_route(const float* logits, int T, int E, int topk, int32_t* ids, float* gates, int32_t* counts,
+                   int32_t* offsets, int32_t* sorted_pairs, void* stream) {
+  if (!logits || !ids || !gates || !counts || !offsets || !sorted_pairs)
+    return fail(Q4Q8_ERR_INVALID_ARG, "moe_route: null pointer");
+  if (T < 1 || E < 1 || topk < 1 || topk > E)
+    return fail(Q4Q8_ERR_INVALID_ARG, "moe_route: T=%d E=%d topk=%d", T, E, topk);
+  if (E > 1024 || topk > 16) return fail(Q4Q8_ERR_UNSUPPORTED, "moe_route: E=%d > 1024 or topk=%d > 16", E, topk);
+  if ((int64_t)T * topk > (1LL << 30)) return fail(Q4Q8_ERR_UNSUPPORTED, "moe_route: T*topk too large");
+  clear_hip_error();
+  return hip_status(q4q8::launch_moe_route(logits, T, E, topk, ids, gates, counts, offsets, sorted_pairs,
+                                           (hipStream_t)stream),
+                    "moe_route launch");
+}
+
+size_t q4q8_moe_workspace(int fmt, int T, int E, int topk, int H, int F) {
+  if (!fmt_ok(fmt) || T < 1 || E < 1 || topk < 1 || topk > E || H < 128 || F < 128) return 0;
+  return q4q8::moe_workspace_bytes(fmt, T, E, topk, H, F);
+}
+
+int q4q8_moe_qgemm(int fmt, const void* Wg, const void* Wu, const void* Wd, int E, int H, int F, const void* X,
+                   int xdt, int T, int topk, const float* gates, const int32_t* offsets,
+                   const int32_t* sorted_pairs, float* out, void* h_out, void* ws, size_t ws_bytes, void* stream) {
+  if (!fmt_ok(fmt)) return fail(Q4Q8_ERR_UNSUPPORTED, "unknown weight format %d", fmt);
+  if (!act_ok(xdt)) return fail(Q4Q8_ERR_UNSUPPORTED, "moe_qgemm: activation dtype %d not F16/BF16", xdt);
+  if (!Wg || !Wu || !Wd || !X || !gates || !offsets || !sorted_pairs || !out)
+    return fail(Q4Q8_ERR_INVALID_ARG, "moe_qgemm: null pointer");
+  if (T < 1 || E < 1 || topk < 1 || topk > E || topk > 16 || E > 1024)
+    return fail(Q4Q8_ERR_INVALID_ARG, "moe_qgemm: T=%d E=%d topk=%d", T, E, topk);
+  if (H < 128 || F < 128 || H % 128 || F % 128)
+    return fail(Q4Q8_ERR_INVALID_ARG, "moe_qgemm: H=%d and F=%d must be positive multiples of 128", H, F);
+  if ((int64_t)T * topk > (1LL << 30) || H > (1 << 20) || F > (1 << 20))
+    return fail(Q4Q8_ERR_UNSUPPORTED, "moe_qgemm: sizes beyond limits");
+  const size_t need = q4q8::moe_workspace_bytes(fmt, T, E, topk, H, F);
+  if (!ws || ws_bytes < need)
+    return fail(Q4Q8_ERR_WORKSPACE, "moe_qgemm: workspace holds %zu bytes, needs %zu", ws_bytes, need);
+  if (!aligned(ws, 256)) return fail(Q4Q8_ERR_ALIGNMENT, "moe_qgemm: workspace not 256-byte aligned");
+  if (!aligned(Wg, 16) || !aligned(Wu, 16) || !aligned(Wd, 16) || !aligned(X, 16) || !aligned(out, 16) ||
+      (h_out && !aligned(h_out, 16)))
+    return fail(Q4Q8_ERR_ALIGNMENT, "moe_qgemm: weights, X, out and h_out must be 16-byte aligned");
+  clear_hip_error();
+  return hip_status(q4q8::launch_moe_qgemm(fmt, xdt, Wg, Wu, Wd, E, H, F, X, T, topk, gates, offsets, sorted_pairs,
+                                           out, h_out, ws, (hipStream_t)stream),
+                    "moe_qgemm launch");
+}
+
+}  // extern "C"

@@ -1,0 +1,155 @@
+// Device-side building blocks shared by the gfx950 kernels: the repacked
+// weight layout, in-register dequantisation and the 16x16x32 MFMA wrappers.
+//
+// Repacked layout (one layout serves GEMV, GEMM and the MoE GEMMs):
+//   * rows in tiles of 16, K in chunks of 128 (4 blocks of 32);
+//   * record (tile t, chunk c) at byte (t * nchunks + c) * kRecBytes;
+//   * codes first: 64 lane slots; slot l = 16 g + r holds, for row r of the
+//     tile and each block j of the chunk, the 8 codes k = 32 j + 8 g + e
+//     (e = 0..7).  That is exactly the B operand lane l feeds to
+//     v_mfma_f32_16x16x32_{f16,bf16} when B = W^T restricted to one block:
+//     B[k][n] with n = l % 16 and k = 8 (l / 16) + e.
+//       Q4_0: 16 bytes per slot, one dword per block; code e sits at bit
+//             4 * ((e & 1) * 4 + (e >> 1)), so masking with 0x000F000F /
+//             0x00F000F0 (before and after an 8-bit shift) yields the fp16
+//             pairs (e0,e1) (e2,e3) (e4,e5) (e6,e7) directly.
+//       Q8_0: 32 bytes per slot in two 16-byte halves; half h (first or
+//             second kilobyte of the record) carries blocks 2h and 2h+1, 8
+//             bytes each, in natural order.
+//   * then 128 bytes of scales, fp16 [row r][block j].
+// Padding rows / blocks carry scale 0 and code 0.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace q4q8 {
+
+enum { kQ4_0 = 1, kQ8_0 = 2 };
+enum { kF16 = 1, kBF16 = 2, kF32 = 3 };
+
+constexpr int kTileRows = 16;
+constexpr int kChunkK = 128;
+constexpr int kBlocksPerChunk = 4;
+constexpr int kScaleBytes = 128;
+
+template <int FMT> struct Fmt;
+template <> struct Fmt<kQ4_0> {
+  static constexpr int kCanonBlock = 18;
+  static constexpr int kCodeBytes = 1024;
+  static constexpr int kRecBytes = 1024 + kScaleBytes;
+};
+template <> struct Fmt<kQ8_0> {
+  static constexpr int kCanonBlock = 34;
+  static constexpr int kCodeBytes = 2048;
+  static constexpr int kRecBytes = 2048 + kScaleBytes;
+};
+
+__host__ __device__ constexpr int q4_nibble_shift(int e) { return 4 * ((e & 1) * 4 + (e >> 1)); }
+
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float float4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+
+// ---------------------------------------------------------------------------
+// Operand types: XDT selects fp16 or bf16 matrix-core operands.
+// ---------------------------------------------------------------------------
+template <int XDT> struct Op;
+template <> struct Op<kF16> {
+  typedef half8_t vec;
+  static __device__ __forceinline__ float4_t mfma(vec a, vec b, float4_t c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ uint32_t pack(float lo, float hi) {
+    // Exact for the small integers and fp16-representable values packed here.
+    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(lo, hi));
+  }
+};
+template <> struct Op<kBF16> {
+  typedef bf16x8_t vec;
+  static __device__ __forceinline__ float4_t mfma(vec a, vec b, float4_t c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ uint32_t pack(float lo, float hi) {
+    __bf16 l = (__bf16)lo, h = (__bf16)hi;
+    return (uint32_t)__builtin_bit_cast(uint16_t, l) | ((uint32_t)__builtin_bit_cast(uint16_t, h) << 16);
+  }
+};
+
+// ---------------------------------------------------------------------------
+// Exact dequantisation of one lane's 8 codes of one block into an MFMA
+// operand (values q-8 or q, scale not applied).
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ u32x4_t deq_q4_f16(uint32_t w) {
+  // (nibble | 0x6400) is the fp16 1024 + n; (16n | 0x6400) is 1024 + 16n.
+  // Plain C on purpose: no inline asm next to MFMAs (the hazard recognizer
+  // does not see VALU writes made from inline asm).
+  const uint32_t kMagic = 0x64006400u;
+  uint32_t w2 = w >> 8;
+  half2_t h0 = __builtin_bit_cast(half2_t, (w & 0x000F000Fu) | kMagic);
+  half2_t h1 = __builtin_bit_cast(half2_t, (w & 0x00F000F0u) | kMagic);
+  half2_t h2 = __builtin_bit_cast(half2_t, (w2 & 0x000F000Fu) | kMagic);
+  half2_t h3 = __builtin_bit_cast(half2_t, (w2 & 0x00F000F0u) | kMagic);
+  const half2_t off = {(_Float16)1032.0f, (_Float16)1032.0f};
+  const half2_t sixteenth = {(_Float16)0.0625f, (_Float16)0.0625f};
+  const half2_t off16 = {(_Float16)-72.0f, (_Float16)-72.0f};
+  h0 = h0 - off;
+  h1 = h1 * sixteenth + off16;   // (1024 + 16n) / 16 - 72 = n - 8, exact
+  h2 = h2 - off;
+  h3 = h3 * sixteenth + off16;
+  u32x4_t r;
+  r[0] = __builtin_bit_cast(uint32_t, h0);
+  r[1] = __builtin_bit_cast(uint32_t, h1);
+  r[2] = __builtin_bit_cast(uint32_t, h2);
+  r[3] = __builtin_bit_cast(uint32_t, h3);
+  return r;
+}
+
+__device__ __forceinline__ u32x4_t deq_q4_bf16(uint32_t w) {
+  u32x4_t r;
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    int e0 = 2 * p, e1 = 2 * p + 1;
+    float lo = (float)(int)((w >> q4_nibble_shift(e0)) & 0xFu) - 8.0f;
+    float hi = (float)(int)((w >> q4_nibble_shift(e1)) & 0xFu) - 8.0f;
+    r[p] = Op<kBF16>::pack(lo, hi);
+  }
+  return r;
+}
+
+template <int XDT>
+__device__ __forceinline__ u32x4_t deq_q8(uint32_t d0, uint32_t d1) {
+  u32x4_t r;
+  r[0] = Op<XDT>::pack((float)(int)(int8_t)(d0), (float)(int)(int8_t)(d0 >> 8));
+  r[1] = Op<XDT>::pack((float)(int)(int8_t)(d0 >> 16), (float)(int)(int8_t)(d0 >> 24));
+  r[2] = Op<XDT>::pack((float)(int)(int8_t)(d1), (float)(int)(int8_t)(d1 >> 8));
+  r[3] = Op<XDT>::pack((float)(int)(int8_t)(d1 >> 16), (float)(int)(int8_t)(d1 >> 24));
+  return r;
+}
+
+template <int FMT, int XDT>
+__device__ __forceinline__ u32x4_t deq_block(const u32x4_t* codes, int j);
+
+// Q4_0: one 16-byte slot, dword j is block j.
+template <> __device__ __forceinline__ u32x4_t deq_block<kQ4_0, kF16>(const u32x4_t* c, int j) {
+  return deq_q4_f16(c[0][j]);
+}
+template <> __device__ __forceinline__ u32x4_t deq_block<kQ4_0, kBF16>(const u32x4_t* c, int j) {
+  return deq_q4_bf16(c[0][j]);
+}
+// Q8_0: two 16-byte halves; block j is dwords 2(j&1), 2(j&1)+1 of half j>>1.
+template <> __device__ __forceinline__ u32x4_t deq_block<kQ8_0, kF16>(const u32x4_t* c, int j) {
+  return deq_q8<kF16>(c[j >> 1][2 * (j & 1)], c[j >> 1][2 * (j & 1) + 1]);
+}
+template <> __device__ __forceinline__ u32x4_t deq_block<kQ8_0, kBF16>(const u32x4_t* c, int j) {
+  return deq_q8<kBF16>(c[j >> 1][2 * (j & 1)], c[j >> 1][2 * (j & 1) + 1]);
+}
+
+__device__ __forceinline__ float half_bits_to_float(uint32_t bits16) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)bits16);
+}
+
+}  // namespace q4q8

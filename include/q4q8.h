@@ -1,0 +1,225 @@
+/*
+ * q4q8.h -- C ABI of the block-quantised weight-product library for AMD MI355X
+ * (gfx950 / CDNA4).
+ *
+ * What the library computes.  "BaseRT: Best-in-Class LLM Inference on Apple
+ * Silicon via Native Metal" (gist.science technical summary, section
+ * "Methodologie", kernel specialisation) describes GEMV kernels for decode and
+ * GEMM kernels for prefill, one variant per quantisation format, that
+ * dequantise inside the inner loop so weights are never materialised in
+ * global memory.  Its follow-up, "BaseRT: Advancing Best-in-Class LLM
+ * Inference with Apple M5 Neural Accelerators" (review, section "Method"),
+ * adds grouped mixture-of-experts GEMMs with fused expert projections on the
+ * matrix units, with memory-bound decode kept on the GEMV path.  The same
+ * pages say weights are converted once to the runtime's own format (review,
+ * section "Comparison") and that the decode loop allocates nothing (technical
+ * summary, "Methodologie", zero-allocation decode loop).
+ *
+ * Formats (32 weights per block along K, one fp16 scale s per block):
+ *   Q4_0: 4-bit codes q in 0..15, weight = s * (q - 8)
+ *   Q8_0: int8 codes q,          weight = s * q
+ * Canonical (interchange) blocks: Q4_0 = 18 bytes [s][16 bytes, byte i =
+ * q[i] | q[i+16] << 4]; Q8_0 = 34 bytes [s][32 int8].  Blocks run along K,
+ * rows n = 0..N-1 follow one another.
+ *
+ * Conventions for every call below.
+ *   - Ownership: the caller allocates and frees everything (weights,
+ *     activations, outputs, workspace).  The library allocates no memory and
+ *     keeps no device state.
+ *   - Streams: `stream` is a hipStream_t passed as void* (NULL = the null
+ *     stream).  Calls enqueue work and return without synchronising; results
+ *     are ready once the stream reaches that point.
+ *   - Errors: arguments are validated on the host before anything is
+ *     enqueued.  On a validation failure the call returns a negative status,
+ *     enqueues nothing and leaves every output untouched.  A launch failure
+ *     returns Q4Q8_ERR_HIP.  A fault while a kernel runs surfaces at the
+ *     caller's next synchronisation.  q4q8_last_error() gives a one-line
+ *     description of the last failure on the calling thread.  No C++
+ *     exception crosses this interface.
+ *   - Threading: calls are re-entrant; calls on different streams may run
+ *     concurrently (they share no library state).
+ *   - Determinism: all outputs are bitwise reproducible run to run (no
+ *     floating-point atomics; every reduction has a fixed order).
+ *   - Shapes: K % 32 == 0, N >= 1, K >= 32.  Repacked weights and activation
+ *     rows must be 16-byte aligned (leading dimensions multiples of 8
+ *     elements).  Activation values are finite.
+ *   - Activations of dtype F16 are used as fp16.  BF16 activations are
+ *     exact in the GEMV; in the GEMM and the MoE path they are converted to
+ *     fp16 for the matrix cores, exactly for 2^-14 <= |x| < 65520 (smaller
+ *     magnitudes keep an absolute error below 2^-24, larger ones saturate).
+ */
+#ifndef Q4Q8_H
+#define Q4Q8_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define Q4Q8_ABI_VERSION 1
+
+typedef enum {
+  Q4Q8_OK = 0,
+  Q4Q8_ERR_INVALID_ARG = -1,   /* null pointer, bad shape or count          */
+  Q4Q8_ERR_UNSUPPORTED = -2,   /* unknown format / dtype, or size limit      */
+  Q4Q8_ERR_WORKSPACE = -3,     /* workspace missing or too small             */
+  Q4Q8_ERR_ALIGNMENT = -4,     /* pointer or leading dimension misaligned    */
+  Q4Q8_ERR_HIP = -5            /* the HIP runtime refused a launch or copy   */
+} q4q8_status;
+
+typedef enum { Q4Q8_Q4_0 = 1, Q4Q8_Q8_0 = 2 } q4q8_format;
+typedef enum { Q4Q8_F16 = 1, Q4Q8_BF16 = 2, Q4Q8_F32 = 3 } q4q8_dtype;
+
+/* Version of this interface (Q4Q8_ABI_VERSION of the built library). */
+int q4q8_abi_version(void);
+
+/* Human-readable name of a status code (static string). */
+const char* q4q8_status_string(int status);
+
+/* Detail of the last failing call on this thread ("" if none).  The string
+ * is thread-local and valid until the next failing call on this thread. */
+const char* q4q8_last_error(void);
+
+/* ------------------------------------------------------------------------ */
+/* Weight layout (load time)                                                */
+/* ------------------------------------------------------------------------ */
+
+/* Bytes of a canonical N x K matrix: N * (K/32) * (18 | 34).  0 on bad args. */
+size_t q4q8_canonical_bytes(int fmt, int64_t N, int64_t K);
+
+/* Bytes of the repacked N x K matrix.  Rows are padded to a multiple of 16
+ * and K to a multiple of 128; when N % 16 == 0 and K % 128 == 0 this equals
+ * the canonical size (no byte is added).  0 on bad args. */
+size_t q4q8_repacked_bytes(int fmt, int64_t N, int64_t K);
+
+/* Convert canonical blocks to the gfx950 layout every product call reads
+ * (the "native weight format" conversion, done once at load time).
+ * Layout: 16-row tiles; each tile holds K/128 records of 4 blocks; a record
+ * is 64 lane slots of codes (16 B per slot for Q4_0, 32 B for Q8_0, slot
+ * l = 16*g + r holds row r, codes 8g..8g+7 of each of the 4 blocks, nibbles
+ * pre-permuted for the in-register unpack) followed by the 16 x 4 fp16
+ * scales [row][block].  Padding rows and blocks get scale 0 and code 0.
+ *   canon:     device pointer, q4q8_canonical_bytes(fmt, N, K) bytes, any
+ *              alignment, read only.
+ *   dst:       device pointer, 16-byte aligned, dst_bytes >=
+ *              q4q8_repacked_bytes(fmt, N, K).  Written entirely.
+ * Asynchronous on `stream`. */
+int q4q8_repack(int fmt, const void* canon, int64_t N, int64_t K,
+                void* dst, size_t dst_bytes, void* stream);
+
+/* The same conversion on the host, for offline checkpoint conversion: both
+ * pointers are host memory; synchronous; touches no GPU.  Produces exactly
+ * the bytes q4q8_repack produces. */
+int q4q8_repack_host(int fmt, const void* canon, int64_t N, int64_t K,
+                     void* dst, size_t dst_bytes);
+
+/* ------------------------------------------------------------------------ */
+/* Decode: quantised GEMV, M = 1..8 activation rows                          */
+/* (technical summary, "Methodologie": a GEMV per quantisation format for   */
+/*  decode, dequantisation inside the inner loop)                           */
+/* ------------------------------------------------------------------------ */
+
+/* y[m, n] = sum_k W[n, k] * x[m, k]   for m < M, n < N.
+ *   W:   repacked weights (device), from q4q8_repack with the same fmt,N,K.
+ *   x:   device, M rows of K activations of dtype xdt (F16 or BF16),
+ *        row m at x + m*ldx elements; 16-byte aligned, ldx % 8 == 0,
+ *        ldx >= K when M > 1.
+ *   y:   device fp32, row m at y + m*ldy; ldy >= N when M > 1.  Written only
+ *        at [0, M) x [0, N).
+ * fp32 accumulation; the weights are exact in the matrix-core operand type
+ * and the block scales are applied in fp32. */
+int q4q8_qgemv(int fmt, const void* W, int64_t N, int64_t K,
+               const void* x, int xdt, int64_t ldx, int M,
+               float* y, int64_t ldy, void* stream);
+
+/* One GEMV problem of a grouped launch. */
+typedef struct {
+  const void* W;      /* repacked weights (device)             */
+  const void* x;      /* activations, M rows (device)           */
+  float* y;           /* fp32 output, M rows (device)           */
+  int64_t N, K;       /* matrix shape                           */
+  int64_t ldx, ldy;   /* leading dimensions (elements)          */
+} q4q8_gemv_desc;
+
+#define Q4Q8_MAX_GROUP 8
+
+/* Up to Q4Q8_MAX_GROUP independent GEMVs of one format, dtype and M in a
+ * single launch (e.g. the q/k/v projections of a layer, or gate and up).
+ * `descs` is host memory, read during the call only.  Each problem obeys
+ * the rules of q4q8_qgemv; outputs must not overlap. */
+int q4q8_qgemv_grouped(int fmt, const q4q8_gemv_desc* descs, int count,
+                       int xdt, int M, void* stream);
+
+/* ------------------------------------------------------------------------ */
+/* Prefill: quantised GEMM                                                   */
+/* (technical summary, "Methodologie", prefill optimisation: tiled GEMM on  */
+/*  matrix intrinsics; review, "Method": prefill GEMM on the matrix units)  */
+/* ------------------------------------------------------------------------ */
+
+/* Y[m, n] = sum_k X[m, k] * W[n, k]   for m < M, n < N.
+ *   X:   device, BF16 or F16 (xdt), row m at X + m*ldx; 16-byte aligned,
+ *        ldx % 8 == 0, ldx >= K.
+ *   Y:   device, ydt = BF16, F16 or F32, row m at Y + m*ldy, ldy >= N,
+ *        ldy % 8 == 0 and 16-byte aligned.
+ * fp32 accumulation on fp16 matrix-core operands (weights dequantised and
+ * scaled to fp16, relative rounding <= 2^-11); result rounded once to ydt.
+ * M >= 1 (any). */
+int q4q8_qgemm(int fmt, const void* W, int64_t N, int64_t K,
+               const void* X, int xdt, int64_t ldx, int64_t M,
+               void* Y, int ydt, int64_t ldy, void* stream);
+
+/* ------------------------------------------------------------------------ */
+/* Mixture of experts (review, "Method": MoE expert GEMM and fused expert    */
+/* projections on the matrix units; the routing rule is this library's)     */
+/* ------------------------------------------------------------------------ */
+
+/* Route T tokens over E experts and sort the (token, slot) pairs by expert.
+ *   logits:  device fp32 [T, E] row-major.
+ *   ids:     device int32 [T, topk]: per token the topk experts with the
+ *            largest logits, descending; equal logits -> lower id first.
+ *   gates:   device fp32 [T, topk]: softmax over the topk selected logits.
+ *   counts:  device int32 [E]: pairs routed to each expert.
+ *   offsets: device int32 [E+1]: exclusive scan of counts (offsets[E] =
+ *            T*topk).
+ *   sorted_pairs: device int32 [T*topk]: pair ids p = t*topk + j ordered by
+ *            (expert, p) -- a stable counting sort, bit-exact.
+ * Limits: 1 <= topk <= min(E, 16), 1 <= E <= 1024, T >= 1.  No workspace. */
+int q4q8_moe_route(const float* logits, int T, int E, int topk,
+                   int32_t* ids, float* gates, int32_t* counts,
+                   int32_t* offsets, int32_t* sorted_pairs, void* stream);
+
+/* Workspace bytes q4q8_moe_qgemm needs for these sizes. */
+size_t q4q8_moe_workspace(int fmt, int T, int E, int topk, int H, int F);
+
+/* Expert SwiGLU over every pair and the weighted combine:
+ *   h_p   = silu(x_t W_gate[e]^T) * (x_t W_up[e]^T)      (F values, fp32,
+ *           stored as bf16 in sorted-pair order)
+ *   y_p   = h_p W_down[e]^T                              (H values, fp32)
+ *   out_t = sum_j gates[t, j] * y_{t*topk + j}           (fp32)
+ *   Wg, Wu: device, E repacked [F, H] matrices, expert e at
+ *           e * q4q8_repacked_bytes(fmt, F, H).
+ *   Wd:     device, E repacked [H, F] matrices, expert e at
+ *           e * q4q8_repacked_bytes(fmt, H, F).
+ *   X:      device BF16 (or F16, xdt) [T, H] row-major, 16-byte aligned.
+ *   gates, offsets, sorted_pairs: as produced by q4q8_moe_route.
+ *   out:    device fp32 [T, H].
+ *   h_out:  optional (NULL to skip) device bf16 [T*topk, F]: the h rows in
+ *           sorted-pair order, for inspection.
+ *   ws:     device workspace of >= q4q8_moe_workspace(...) bytes, 256-byte
+ *           aligned; contents need no initialisation and are clobbered.
+ * H % 128 == 0 and F % 128 == 0.  Pairs of one expert are processed
+ * together, so each expert's weights are streamed once per call. */
+int q4q8_moe_qgemm(int fmt, const void* Wg, const void* Wu, const void* Wd,
+                   int E, int H, int F, const void* X, int xdt, int T,
+                   int topk, const float* gates,
+                   const int32_t* offsets, const int32_t* sorted_pairs,
+                   float* out, void* h_out, void* ws, size_t ws_bytes,
+                   void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* Q4Q8_H */

@@ -1,0 +1,184 @@
+"""Host-side checks of the C ABI: symbols, validation, host repack (no GPU)."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import synth
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "q4q8.h")
+
+
+@pytest.fixture(scope="module")
+def q():
+    import gemm_q4_q8_amd as q
+    q.lib()
+    return q
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(q4q8_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_declares_the_entry_points():
+    names = _declared_functions()
+    for need in ["q4q8_repack", "q4q8_repack_host", "q4q8_qgemv", "q4q8_qgemv_grouped", "q4q8_qgemm",
+                 "q4q8_moe_route", "q4q8_moe_qgemm", "q4q8_moe_workspace", "q4q8_last_error"]:
+        assert need in names
+
+
+def test_library_exports_every_declared_symbol(q):
+    raw = ctypes.CDLL(q.LIB_PATH)
+    missing = [n for n in _declared_functions() if not hasattr(raw, n)]
+    assert not missing, missing
+    assert q.lib().q4q8_abi_version() == 1
+
+
+def test_status_strings(q):
+    assert q.status_string(0) == "ok"
+    for s in (-1, -2, -3, -4, -5):
+        assert q.status_string(s) not in ("ok", "unknown status")
+
+
+@pytest.mark.parametrize("fmt,bb", [(synth.Q4_0, 18), (synth.Q8_0, 34)])
+def test_sizes(q, fmt, bb):
+    assert q.canonical_bytes(fmt, 4096, 4096) == 4096 * 128 * bb
+    assert q.repacked_bytes(fmt, 4096, 4096) == 4096 * 128 * bb      # aligned: no padding
+    assert q.repacked_bytes(fmt, 17, 160) == 2 * 2 * (64 * 16 * (bb - 2) // 16 + 128)
+    assert q.canonical_bytes(fmt, 4, 33) == 0
+    assert q.repacked_bytes(3, 4, 32) == 0
+
+
+def _unrepack(fmt, rep, N, K):
+    """Read scales/codes back out of the documented tile layout (test-side)."""
+    tiles, chunks = (N + 15) // 16, (K + 127) // 128
+    rb = 1152 if fmt == synth.Q4_0 else 2176
+    cb = rb - 128
+    recs = rep.reshape(tiles, chunks, rb)
+    codes = np.zeros((tiles * 16, chunks * 128), dtype=np.int64)
+    scales = np.zeros((tiles * 16, chunks * 4), dtype=np.float64)
+    for g in range(4):
+        for r in range(16):
+            slot = 16 * g + r
+            for j in range(4):
+                for e in range(8):
+                    k = 32 * j + 8 * g + e
+                    if fmt == synth.Q4_0:
+                        word = recs[:, :, slot * 16 + 4 * j: slot * 16 + 4 * j + 4].astype(np.uint32)
+                        word = word[..., 0] | (word[..., 1] << 8) | (word[..., 2] << 16) | (word[..., 3] << 24)
+                        sh = 4 * ((e & 1) * 4 + (e >> 1))
+                        codes[r::16, k::128][:tiles, :chunks] = ((word >> sh) & 0xF)
+                    else:
+                        off = (j >> 1) * 1024 + slot * 16 + (j & 1) * 8 + e
+                        codes[r::16, k::128][:tiles, :chunks] = recs[:, :, off].view(np.int8)
+    sc = recs[:, :, cb:].reshape(tiles, chunks, 16, 4, 2)
+    sbits = sc[..., 0].astype(np.uint16) | (sc[..., 1].astype(np.uint16) << 8)
+    scales = sbits.view(np.float16).astype(np.float64).transpose(0, 2, 1, 3).reshape(tiles * 16, chunks * 4)
+    return scales, codes
+
+
+@pytest.mark.parametrize("fmt", [synth.Q4_0, synth.Q8_0])
+@pytest.mark.parametrize("N,K", [(16, 128), (17, 160), (33, 256), (1, 32)])
+def test_host_repack_roundtrip(q, fmt, N, K):
+    w = synth.q_weight(synth.rng_for(41, N * K + fmt), fmt, N, K)
+    rep = q.repack_host(fmt, w.canon, N, K)
+    assert rep.size == q.repacked_bytes(fmt, N, K)
+    scales, codes = _unrepack(fmt, rep, N, K)
+    assert np.array_equal(scales[:N, :K // 32], w.scales.astype(np.float64))
+    assert np.array_equal(codes[:N, :K], w.codes.astype(np.int64))
+    # padding rows / blocks carry scale 0 and code 0
+    assert np.all(scales[N:] == 0) and np.all(scales[:, K // 32:] == 0)
+    assert np.all(codes[N:] == 0) and np.all(codes[:, K:] == 0)
+
+
+def test_host_repack_preserves_bytes(q):
+    w = synth.q_weight(synth.rng_for(42, 0), synth.Q8_0, 32, 256)
+    rep = q.repack_host(synth.Q8_0, w.canon, 32, 256)
+    assert rep.size == w.canon.size
+    assert np.array_equal(np.sort(rep), np.sort(w.canon))
+
+
+# --- validation: every bad call returns its status before touching the GPU ---
+def _vp(v=0x1000):
+    return ctypes.c_void_p(v)
+
+
+def test_qgemv_validation(q):
+    L = q.lib()
+    Q4, F16 = synth.Q4_0, synth.F16
+    cases = [
+        (dict(fmt=3), -2), (dict(N=0), -1), (dict(K=48), -1), (dict(K=0), -1), (dict(M=0), -1), (dict(M=9), -1),
+        (dict(xdt=3), -2), (dict(W=None), -1), (dict(x=None), -1), (dict(y=None), -1),
+        (dict(W=0x1008), -4), (dict(x=0x1004), -4), (dict(M=2, ldx=4100), -4), (dict(M=2, ldx=100), -1),
+        (dict(M=2, ldy=10), -1),
+    ]
+    for over, want in cases:
+        a = dict(fmt=Q4, W=0x1000, N=64, K=4096, x=0x2000, xdt=F16, ldx=4096, M=1, y=0x3000, ldy=64)
+        a.update(over)
+        st = L.q4q8_qgemv(a["fmt"], _vp(a["W"]) if a["W"] else None, a["N"], a["K"],
+                          _vp(a["x"]) if a["x"] else None, a["xdt"], a["ldx"], a["M"],
+                          _vp(a["y"]) if a["y"] else None, a["ldy"], None)
+        assert st == want, (over, st, q.last_error())
+        assert q.last_error()
+
+
+def test_grouped_validation(q):
+    L = q.lib()
+    arr = (q.GemvDesc * 9)()
+    for i in range(9):
+        arr[i] = q.GemvDesc(0x1000, 0x2000, 0x3000, 64, 256, 256, 64)
+    assert L.q4q8_qgemv_grouped(1, arr, 9, 1, 1, None) == -1
+    assert L.q4q8_qgemv_grouped(1, arr, 0, 1, 1, None) == -1
+    arr[3].K = 100
+    assert L.q4q8_qgemv_grouped(1, arr, 4, 1, 1, None) == -1
+    assert "qgemv" in q.last_error() or "K=" in q.last_error()
+
+
+def test_qgemm_validation(q):
+    L = q.lib()
+    ok = dict(fmt=1, W=0x1000, N=64, K=256, X=0x2000, xdt=2, ldx=256, M=17, Y=0x3000, ydt=2, ldy=64)
+    for over, want in [(dict(ydt=7), -2), (dict(xdt=3), -2), (dict(M=0), -1), (dict(ldx=128), -1),
+                       (dict(ldy=32), -1), (dict(Y=0x3008), -4), (dict(ldx=260), -4), (dict(K=100), -1)]:
+        a = dict(ok)
+        a.update(over)
+        st = L.q4q8_qgemm(a["fmt"], _vp(a["W"]), a["N"], a["K"], _vp(a["X"]), a["xdt"], a["ldx"], a["M"],
+                          _vp(a["Y"]), a["ydt"], a["ldy"], None)
+        assert st == want, (over, st, q.last_error())
+
+
+def test_moe_validation(q):
+    L = q.lib()
+    p = [_vp(0x1000 * (i + 1)) for i in range(6)]
+    assert L.q4q8_moe_route(p[0], 512, 128, 0, *p[1:], None) == -1
+    assert L.q4q8_moe_route(p[0], 512, 128, 129, *p[1:], None) == -1
+    assert L.q4q8_moe_route(p[0], 512, 2048, 8, *p[1:], None) == -2
+    assert L.q4q8_moe_route(None, 512, 128, 8, *p[1:], None) == -1
+    nws = q.moe_workspace(1, 512, 128, 8, 2048, 768)
+    assert nws > 0
+    args = [1, _vp(0x1000), _vp(0x2000), _vp(0x3000), 128, 2048, 768, _vp(0x4000), 2, 512, 8,
+            _vp(0x5000), _vp(0x6000), _vp(0x7000), _vp(0x8000), None, _vp(0x10000), nws, None]
+    a = list(args)
+    a[16] = None
+    assert L.q4q8_moe_qgemm(*a) == -3
+    a = list(args)
+    a[17] = nws - 1
+    assert L.q4q8_moe_qgemm(*a) == -3
+    a = list(args)
+    a[5] = 2000
+    assert L.q4q8_moe_qgemm(*a) == -1
+    a = list(args)
+    a[16] = _vp(0x10010)
+    assert L.q4q8_moe_qgemm(*a) == -4
+
+
+def test_repack_validation(q):
+    L = q.lib()
+    assert L.q4q8_repack(1, _vp(), 16, 128, _vp(0x2000), 10, None) == -1
+    assert L.q4q8_repack(1, _vp(), 16, 128, _vp(0x2008), 1 << 20, None) == -4
+    assert L.q4q8_repack(5, _vp(), 16, 128, _vp(0x2000), 1 << 20, None) == -2
+    assert L.q4q8_repack_host(1, None, 16, 128, _vp(0x2000), 1 << 20) == -1
