@@ -1,0 +1,398 @@
+#!/usr/bin/env python3
+"""Benchmark of the block-quantised weight products on one MI355X.
+
+Headline workload (one "step"): the decode step of one 8B-shaped transformer
+layer's projections over Q4_0 weights, M = 1 fp16 activation row -- q/k/v
+(4096x4096, 2x 1024x4096) in one grouped GEMV launch, o (4096x4096), gate
+and up (2x 12288x4096) in one grouped launch, down (4096x12288).  Four
+launches per step, in the dependency order of a real layer; consecutive
+steps use different copies of the layer's weights (8 copies, 868 MB, more
+than the 256 MB Infinity Cache), as consecutive layers of a model would, so
+the weights stream from HBM.  Launches are captured in HIP graphs.
+
+value = algorithmic bytes of K steps / wall time of K steps (GB/s), inputs
+resident in HBM.  Algorithmic bytes per step = repacked weight bytes (0.5625
+B per weight, exactly the canonical Q4_0 bytes) + activations read (fp16) +
+outputs written (fp32).
+
+roofline: the dominant kernel is the grouped gate+up GEMV (56.6 MB per
+launch); its duration comes from start/stop events recorded by its own
+dispatch (hipExtLaunchKernel), averaged over R launches on rotating weight
+copies.  traffic: HBM bytes per launch from rocprofv3 FETCH_SIZE/WRITE_SIZE
+counters (stored under profiles/ with the hash of the kernel sources they
+were taken on; null if the sources changed since).
+
+cpu_baseline: the fp64 NumPy oracle timed on the host on one decode step of
+the same layer (all seven matrices, M = 1).
+
+Other workloads (M = 2/4/8 layer steps, the single 2048x2048 GEMV, the Q8_0
+3B-shaped matrices, the prefill GEMM, the MoE layer) are reported under
+"workloads", each with its own algorithmic bytes / flops and time.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+F16_MFMA_PEAK_TFLOPS = 2500.0    # dense fp16/bf16 matrix-core peak
+LAYER_COPIES = 8
+
+
+def _kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for f in ("qgemv.hip", "q4q8_dev.h", "q4q8_internal.h"):
+        with open(os.path.join(ROOT, "gemm_q4_q8_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+class HipEvents:
+    """hipEvent_t pairs from the HIP runtime torch already loaded."""
+
+    def __init__(self):
+        self.hip = ctypes.CDLL("libamdhip64.so.7")
+        self.hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                                 ctypes.c_void_p]
+        self.hip.hipEventSynchronize.argtypes = [ctypes.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+
+    def create(self):
+        e = ctypes.c_void_p()
+        if self.hip.hipEventCreate(ctypes.byref(e)) != 0:
+            raise RuntimeError("hipEventCreate failed")
+        return e.value
+
+    def elapsed_ms(self, a, b) -> float:
+        self.hip.hipEventSynchronize(ctypes.c_void_p(b))
+        ms = ctypes.c_float()
+        if self.hip.hipEventElapsedTime(ctypes.byref(ms), ctypes.c_void_p(a), ctypes.c_void_p(b)) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return float(ms.value)
+
+    def destroy(self, e):
+        self.hip.hipEventDestroy(ctypes.c_void_p(e))
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+# ----------------------------------------------------------------------------
+# Decode layer (8B-shaped), the headline workload
+# ----------------------------------------------------------------------------
+class DecodeLayer:
+    GROUPS = [("qkv", ["wq", "wk", "wv"]), ("o", ["wo"]), ("gate_up", ["wg", "wu"]), ("down", ["wd"])]
+
+    def __init__(self, q, torch, synth, M: int, copies: int):
+        self.q, self.torch, self.M = q, torch, M
+        dev = torch.device("cuda:0")
+        ws, xs = synth.layer_8b(M)
+        self.shapes = {n: (w.N, w.K) for n, w in ws.items()}
+        self.input_of = dict(synth.LAYER_8B_INPUT)
+        base = {}
+        for n, w in ws.items():
+            canon = torch.from_numpy(w.canon).to(dev)
+            base[n] = q.repack(w.fmt, canon, w.N, w.K)
+            del canon
+        self.copies = [base] + [{n: t.clone() for n, t in base.items()} for _ in range(copies - 1)]
+        self.x = {}
+        for xn, a in xs.items():
+            t = torch.from_numpy(a.bits.view("int16")).view(torch.float16).to(dev)
+            self.x[xn] = t
+        self.y = {n: torch.empty((M, N), dtype=torch.float32, device=dev) for n, (N, K) in self.shapes.items()}
+        self.descs = []
+        for c in self.copies:
+            per = []
+            for g, names in self.GROUPS:
+                probs = [(c[n], self.shapes[n][0], self.shapes[n][1], self.x[synth.LAYER_8B_INPUT[n]],
+                          self.y[n]) for n in names]
+                per.append((g, probs, q.gemv_descs(probs)))
+            self.descs.append(per)
+        torch.cuda.synchronize()
+
+    def bytes_of(self, names) -> int:
+        """Algorithmic bytes of one launch over `names`: weights + outputs + each
+        distinct activation row block once."""
+        M = self.M
+        total = sum(self.q.repacked_bytes(1, *self.shapes[n]) + M * self.shapes[n][0] * 4 for n in names)
+        inputs = {self.input_of[n]: self.shapes[n][1] for n in names}
+        return total + sum(M * K * 2 for K in inputs.values())
+
+    def step_bytes(self) -> int:
+        return sum(self.bytes_of(names) for _, names in self.GROUPS)
+
+    def step(self, copy: int, timed_group=None, events=None):
+        for g, probs, descs in self.descs[copy]:
+            ev = events if g == timed_group else None
+            self.q.qgemv_grouped(1, probs, self.M, descs=descs, events=ev)
+
+
+def time_graph_steps(torch, layer: DecodeLayer, steps: int, warmup: int):
+    """Capture one graph over all weight copies (one step each) and replay."""
+    L = len(layer.copies)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        for c in range(L):               # eager warm-up on the capture stream
+            layer.step(c)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g_all = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g_all):
+        for c in range(L):
+            layer.step(c)
+    g_one = []
+    for c in range(L):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            layer.step(c)
+        g_one.append(g)
+    torch.cuda.synchronize()
+
+    def run(n):
+        for _ in range(n // L):
+            g_all.replay()
+        for c in range(n % L):
+            g_one[c].replay()
+
+    run(warmup)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    run(steps)
+    torch.cuda.synchronize()
+    return time.perf_counter() - t0
+
+
+def time_dominant_kernel(q, layer: DecodeLayer, ev: HipEvents, reps: int):
+    """Mean duration (s) of the grouped gate+up GEMV from dispatch-recorded events."""
+    pairs = [(ev.create(), ev.create()) for _ in range(reps)]
+    L = len(layer.copies)
+    for i in range(reps):
+        layer.step(i % L, timed_group="gate_up", events=pairs[i])
+    durs = [ev.elapsed_ms(a, b) * 1e-3 for a, b in pairs]
+    for a, b in pairs:
+        ev.destroy(a)
+        ev.destroy(b)
+    return sum(durs) / len(durs), durs
+
+
+def _profile_traffic(source_hash: str):
+    path = os.path.join(ROOT, "profiles", "qgemv_gate_up_8b_m1_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("kernel_source_hash") != source_hash:
+        return None
+    return rec.get("traffic_bytes_per_launch")
+
+
+# ----------------------------------------------------------------------------
+# CPU baseline: the oracle itself on one decode step of the layer
+# ----------------------------------------------------------------------------
+def cpu_baseline(synth, budget_s: float = 25.0):
+    import numpy as np
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        blas_threads = 1
+    ws, xs = synth.layer_8b(1)
+    total_bytes = 0
+    t0 = time.perf_counter()
+    steps = 0
+    while True:
+        for n, w in ws.items():
+            x = xs[synth.LAYER_8B_INPUT[n]]
+            oracle.qgemv(w.fmt, w.canon, w.N, w.K, x.values)
+            total_bytes += w.canon.size + 2 * w.K + 4 * w.N
+        steps += 1
+        if time.perf_counter() - t0 > budget_s / 3 or steps >= 3:
+            break
+    dt = time.perf_counter() - t0
+    del np
+    return {"value": total_bytes / dt / 1e9, "unit": "GB/s", "cores": blas_threads, "kind": "oracle",
+            "sample": f"{steps} decode step(s) of the 8B-shaped layer at M=1 (7 matrices, "
+                      f"{total_bytes // steps} algorithmic bytes each) through the fp64 NumPy oracle "
+                      f"(dequantise then matmul), {dt:.1f} s; elementwise NumPy is single-threaded, "
+                      f"BLAS used {blas_threads} thread(s)"}
+
+
+# ----------------------------------------------------------------------------
+# Other workloads
+# ----------------------------------------------------------------------------
+def _time_launches(torch, fn, reps: int, warmup: int = 3):
+    for i in range(warmup):
+        fn(i)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(reps):
+        fn(i)
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) * 1e-3 / reps
+
+
+def extra_workloads(q, torch, synth, ev: HipEvents, quick: bool):
+    out = []
+    dev = torch.device("cuda:0")
+    # Layer steps at other M (graph replays as for the headline).
+    for M in ([] if quick else [2, 4, 8]):
+        lay = DecodeLayer(q, torch, synth, M, LAYER_COPIES)
+        dt = time_graph_steps(torch, lay, 200, 16)
+        mean_k, _ = time_dominant_kernel(q, lay, ev, 32)
+        gu = lay.bytes_of(["wg", "wu"])
+        out.append({"workload": f"8B layer decode step M={M}", "GB/s": round(lay.step_bytes() * 200 / dt / 1e9, 1),
+                    "gate_up_kernel_us": round(mean_k * 1e6, 2),
+                    "gate_up_kernel_GB/s": round(gu / mean_k / 1e9, 1)})
+        del lay
+        torch.cuda.empty_cache()
+    # Single 2048x2048 GEMV (latency-bound: 2.37 MB).
+    w, x = synth.gemv_problem(1, 2048, 2048, 1, synth.F16, synth.GEMV_2048["seed"])
+    W0 = q.repack(1, torch.from_numpy(w.canon).to(dev), 2048, 2048)
+    Ws = [W0] + [W0.clone() for _ in range(127)]          # 302 MB: more than the Infinity Cache
+    xt = torch.from_numpy(x.bits.view("int16")).view(torch.float16).to(dev)
+    y = torch.empty((1, 2048), dtype=torch.float32, device=dev)
+    probs = [[(Wi, 2048, 2048, xt, y)] for Wi in Ws]
+    descs = [q.gemv_descs(p) for p in probs]
+    pairs = [(ev.create(), ev.create()) for _ in range(64)]
+    for i in range(64):
+        q.qgemv_grouped(1, probs[i], 1, descs=descs[i], events=pairs[i])
+    kd = sum(ev.elapsed_ms(a, b) for a, b in pairs) / 64 * 1e-3
+    nb = q.repacked_bytes(1, 2048, 2048) + 2048 * 2 + 2048 * 4
+    b2b = _time_launches(torch, lambda i: q.qgemv_grouped(1, probs[i % 128], 1, descs=descs[i % 128]), 256)
+    out.append({"workload": "q4_0 gemv 2048x2048 M=1", "kernel_us": round(kd * 1e6, 2),
+                "kernel_GB/s": round(nb / kd / 1e9, 1), "back_to_back_us": round(b2b * 1e6, 2),
+                "back_to_back_GB/s": round(nb / b2b / 1e9, 1)})
+    del Ws, probs, descs
+    torch.cuda.empty_cache()
+    # Q8_0 3B-shaped matrices, M = 1 and 8: sum of kernel times.
+    for M in ([1, 8] if not quick else [1]):
+        ws, xs = synth.q8_3b(M)
+        tot_b, tot_t = 0, 0.0
+        for name, w in ws.items():
+            W0 = q.repack(2, torch.from_numpy(w.canon).to(dev), w.N, w.K)
+            copies = [W0] + [W0.clone() for _ in range(max(1, 300_000_000 // W0.numel()))]
+            xt = torch.from_numpy(xs[name].bits.view("int16")).view(torch.bfloat16).to(dev)
+            yq = torch.empty((M, w.N), dtype=torch.float32, device=dev)
+            probs = [[(c, w.N, w.K, xt, yq)] for c in copies]
+            descs = [q.gemv_descs(p) for p in probs]
+            pairs = [(ev.create(), ev.create()) for _ in range(32)]
+            for i in range(32):
+                q.qgemv_grouped(2, probs[i % len(probs)], M, descs=descs[i % len(probs)], events=pairs[i])
+            kd = sum(ev.elapsed_ms(a, b) for a, b in pairs) / 32 * 1e-3
+            tot_t += kd
+            tot_b += q.repacked_bytes(2, w.N, w.K) + M * w.K * 2 + M * w.N * 4
+            del copies, probs, descs
+        torch.cuda.empty_cache()
+        out.append({"workload": f"q8_0 3B-shape 4 matrices M={M}", "sum_kernel_us": round(tot_t * 1e6, 2),
+                    "GB/s": round(tot_b / tot_t / 1e9, 1)})
+    return out
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=800)
+    ap.add_argument("--warmup", type=int, default=80)
+    ap.add_argument("--kernel-reps", type=int, default=64)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--no-extra", action="store_true", help="skip the other workloads")
+    ap.add_argument("--quick-extra", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="also run a 256 MiB device copy (known HBM bytes) for counter calibration")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(json.dumps({"error": "this benchmark runs on one GPU only: the quantised products are "
+                          "single-device kernels; --gpus must be 1"}))
+        sys.exit(2)
+
+    import torch
+    import gemm_q4_q8_amd as q
+    import synth
+
+    if not torch.cuda.is_available():
+        print(json.dumps({"error": "no GPU visible"}))
+        sys.exit(1)
+    q.lib()
+    ev = HipEvents()
+
+    log("building the 8B-shaped layer (8 weight copies)...")
+    layer = DecodeLayer(q, torch, synth, 1, LAYER_COPIES)
+    step_bytes = layer.step_bytes()
+    log(f"step bytes {step_bytes}; timing {args.steps} steps after {args.warmup} warm-up steps")
+    dt = time_graph_steps(torch, layer, args.steps, args.warmup)
+    value = step_bytes * args.steps / dt / 1e9
+    ms_per_step = dt / args.steps * 1e3
+    log(f"value {value:.1f} GB/s, {ms_per_step * 1e3:.2f} us/step")
+
+    mean_k, durs = time_dominant_kernel(q, layer, ev, args.kernel_reps)
+    gu_bytes = layer.bytes_of(["wg", "wu"])
+    achieved = gu_bytes / mean_k / 1e9
+    src_hash = _kernel_source_hash()
+    traffic = _profile_traffic(src_hash)
+    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+                "kernel": "qgemv grouped gate+up (2 x 12288x4096 Q4_0, M=1)",
+                "algorithmic_bytes_per_launch": gu_bytes, "mean_kernel_us": round(mean_k * 1e6, 3),
+                "kernel_us_min_median_max": [round(sorted(durs)[0] * 1e6, 2),
+                                             round(sorted(durs)[len(durs) // 2] * 1e6, 2),
+                                             round(sorted(durs)[-1] * 1e6, 2)],
+                "launches_timed": len(durs), "kernel_source_hash": src_hash}
+    sd = sorted(durs)
+    log(f"gate+up kernel mean {mean_k * 1e6:.2f} us (min {sd[0] * 1e6:.2f}, median {sd[len(sd) // 2] * 1e6:.2f}, "
+        f"max {sd[-1] * 1e6:.2f}) -> {achieved:.1f} GB/s")
+
+    if args.calibrate_copy:
+        a = torch.empty(1 << 28, dtype=torch.uint8, device="cuda:0")
+        b = torch.empty_like(a)
+        for _ in range(4):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        del a, b
+
+    del layer
+    torch.cuda.empty_cache()
+    workloads = []
+    if not args.no_extra:
+        workloads = extra_workloads(q, torch, synth, ev, args.quick_extra)
+        for w in workloads:
+            log(json.dumps(w))
+
+    cpu = None
+    if not args.no_cpu:
+        log("timing the CPU oracle...")
+        cpu = cpu_baseline(synth)
+        log(json.dumps(cpu))
+
+    line = {
+        "metric": "decode qGEMV GB/s (% HBM peak); prefill/MoE qGEMM TFLOP/s (% MFMA peak)",
+        "value": round(value, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f16", "data": "synthetic",
+        "config": {"workload": "decode step of one 8B-shaped layer's projections (q/k/v, o, gate+up, down; "
+                               "hidden 4096, ffn 12288), Q4_0 weights, M=1 fp16 activations",
+                   "M": 1, "weight_copies": LAYER_COPIES, "launches_per_step": 4, "step_bytes": step_bytes,
+                   "hbm_frac": round(value / HBM_PEAK_GBS, 4)},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "workloads": workloads,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

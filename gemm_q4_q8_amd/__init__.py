@@ -54,7 +54,9 @@ def _declare(lib):
         "q4q8_repack_host": (i32, [i32, vp, i64, i64, vp, sz]),
         "q4q8_qgemv": (i32, [i32, vp, i64, i64, vp, i32, i64, i32, vp, i64, vp]),
         "q4q8_qgemv_grouped": (i32, [i32, ctypes.POINTER(GemvDesc), i32, i32, i32, vp]),
+        "q4q8_qgemv_grouped_timed": (i32, [i32, ctypes.POINTER(GemvDesc), i32, i32, i32, vp, vp, vp]),
         "q4q8_qgemm": (i32, [i32, vp, i64, i64, vp, i32, i64, i64, vp, i32, i64, vp]),
+        "q4q8_qgemm_timed": (i32, [i32, vp, i64, i64, vp, i32, i64, i64, vp, i32, i64, vp, vp, vp]),
         "q4q8_moe_route": (i32, [vp, i32, i32, i32, vp, vp, vp, vp, vp, vp]),
         "q4q8_moe_workspace": (sz, [i32, i32, i32, i32, i32, i32]),
         "q4q8_moe_qgemm": (i32, [i32, vp, vp, vp, i32, i32, i32, vp, i32, i32, i32,
@@ -162,17 +164,31 @@ def qgemv(fmt: int, W: torch.Tensor, N: int, K: int, x: torch.Tensor,
     return out
 
 
-def qgemv_grouped(fmt: int, problems, M: int):
-    """problems: list of (W, N, K, x [M,K], y [M,N] fp32); one launch."""
-    n = len(problems)
-    arr = (GemvDesc * max(n, 1))()
-    xdt = None
+def gemv_descs(problems):
+    """ctypes descriptor array for problems [(W, N, K, x [M,K], y [M,N] fp32)]."""
+    arr = (GemvDesc * max(len(problems), 1))()
     for i, (W, N, K, x, y) in enumerate(problems):
         _dev(W, "W")
         arr[i] = GemvDesc(W.data_ptr(), x.data_ptr(), y.data_ptr(), N, K, x.stride(0), y.stride(0))
-        xdt = _DT[x.dtype]
-    st = lib().q4q8_qgemv_grouped(fmt, arr, n, xdt if xdt is not None else F16, M,
-                                  _stream(problems[0][3]) if n else ctypes.c_void_p(0))
+    return arr
+
+
+def qgemv_grouped(fmt: int, problems, M: int, descs=None, events=None):
+    """problems: list of (W, N, K, x [M,K], y [M,N] fp32); one launch.
+
+    descs: a prebuilt gemv_descs(problems) (saves rebuilding it per call).
+    events: optional (start, stop) raw hipEvent_t handles recorded by the
+    dispatch itself.
+    """
+    n = len(problems)
+    arr = descs if descs is not None else gemv_descs(problems)
+    xdt = _DT[problems[0][3].dtype]
+    stream = _stream(problems[0][3])
+    if events is None:
+        st = lib().q4q8_qgemv_grouped(fmt, arr, n, xdt, M, stream)
+    else:
+        st = lib().q4q8_qgemv_grouped_timed(fmt, arr, n, xdt, M, stream,
+                                            ctypes.c_void_p(events[0]), ctypes.c_void_p(events[1]))
     _check(st, "qgemv_grouped")
 
 

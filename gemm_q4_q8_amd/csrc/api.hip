@@ -36,8 +36,9 @@ int check_matrix(int fmt, int64_t N, int64_t K) {
   if (!fmt_ok(fmt)) return fail(Q4Q8_ERR_UNSUPPORTED, "unknown weight format %d", fmt);
   if (N < 1 || K < 32) return fail(Q4Q8_ERR_INVALID_ARG, "bad shape N=%lld K=%lld", (long long)N, (long long)K);
   if (K % 32) return fail(Q4Q8_ERR_INVALID_ARG, "K=%lld is not a multiple of 32", (long long)K);
-  if (N > (1LL << 30) || K > (1LL << 30))
-    return fail(Q4Q8_ERR_UNSUPPORTED, "shape N=%lld K=%lld beyond 2^30", (long long)N, (long long)K);
+  if (N > (1LL << 30) || K > (1LL << 24))
+    return fail(Q4Q8_ERR_UNSUPPORTED, "shape N=%lld K=%lld beyond N <= 2^30, K <= 2^24", (long long)N,
+                (long long)K);
   return Q4Q8_OK;
 }
 
@@ -117,7 +118,8 @@ static int check_gemv_desc(int fmt, const q4q8_gemv_desc& d, int xdt, int M, int
   return Q4Q8_OK;
 }
 
-int q4q8_qgemv_grouped(int fmt, const q4q8_gemv_desc* descs, int count, int xdt, int M, void* stream) {
+static int qgemv_grouped(int fmt, const q4q8_gemv_desc* descs, int count, int xdt, int M, void* stream,
+                         const q4q8::LaunchEvents& ev) {
   if (!fmt_ok(fmt)) return fail(Q4Q8_ERR_UNSUPPORTED, "unknown weight format %d", fmt);
   if (!act_ok(xdt)) return fail(Q4Q8_ERR_UNSUPPORTED, "qgemv: activation dtype %d not F16/BF16", xdt);
   if (M < 1 || M > 8) return fail(Q4Q8_ERR_INVALID_ARG, "qgemv: M=%d outside 1..8", M);
@@ -126,7 +128,7 @@ int q4q8_qgemv_grouped(int fmt, const q4q8_gemv_desc* descs, int count, int xdt,
   q4q8::GemvArgs args;
   memset(&args, 0, sizeof(args));
   int64_t tiles = 0;
-  int max_chunks = 0;
+  int max_chunks = 0, max_k = 0;
   for (int i = 0; i < count; ++i) {
     int st = check_gemv_desc(fmt, descs[i], xdt, M, i);
     if (st) return st;
@@ -138,17 +140,30 @@ int q4q8_qgemv_grouped(int fmt, const q4q8_gemv_desc* descs, int count, int xdt,
     p.ldy = M > 1 ? descs[i].ldy : 0;
     p.N = (int32_t)descs[i].N;
     p.K = (int32_t)descs[i].K;
-    p.tile0 = (int32_t)tiles;
     tiles += (descs[i].N + 15) / 16;
     const int chunks = (int)((descs[i].K + 127) / 128);
     if (chunks > max_chunks) max_chunks = chunks;
+    if (descs[i].K > max_k) max_k = (int)descs[i].K;
   }
   if (tiles > (1LL << 31) - 1) return fail(Q4Q8_ERR_UNSUPPORTED, "qgemv: too many row tiles");
   args.count = count;
   args.M = M;
   args.total_tiles = (int32_t)tiles;
   clear_hip_error();
-  return hip_status(q4q8::launch_qgemv(fmt, xdt, args, max_chunks, (hipStream_t)stream), "qgemv launch");
+  return hip_status(q4q8::launch_qgemv(fmt, xdt, args, max_chunks, max_k, (hipStream_t)stream, ev),
+                    "qgemv launch");
+}
+
+int q4q8_qgemv_grouped(int fmt, const q4q8_gemv_desc* descs, int count, int xdt, int M, void* stream) {
+  return qgemv_grouped(fmt, descs, count, xdt, M, stream, q4q8::LaunchEvents());
+}
+
+int q4q8_qgemv_grouped_timed(int fmt, const q4q8_gemv_desc* descs, int count, int xdt, int M, void* stream,
+                             void* ev_start, void* ev_stop) {
+  q4q8::LaunchEvents ev;
+  ev.start = (hipEvent_t)ev_start;
+  ev.stop = (hipEvent_t)ev_stop;
+  return qgemv_grouped(fmt, descs, count, xdt, M, stream, ev);
 }
 
 int q4q8_qgemv(int fmt, const void* W, int64_t N, int64_t K, const void* x, int xdt, int64_t ldx, int M, float* y,
@@ -164,8 +179,8 @@ int q4q8_qgemv(int fmt, const void* W, int64_t N, int64_t K, const void* x, int 
   return q4q8_qgemv_grouped(fmt, &d, 1, xdt, M, stream);
 }
 
-int q4q8_qgemm(int fmt, const void* W, int64_t N, int64_t K, const void* X, int xdt, int64_t ldx, int64_t M, void* Y,
-               int ydt, int64_t ldy, void* stream) {
+static int qgemm_impl(int fmt, const void* W, int64_t N, int64_t K, const void* X, int xdt, int64_t ldx, int64_t M,
+                      void* Y, int ydt, int64_t ldy, void* stream, const q4q8::LaunchEvents& ev) {
   int st = check_matrix(fmt, N, K);
   if (st) return st;
   if (!act_ok(xdt)) return fail(Q4Q8_ERR_UNSUPPORTED, "qgemm: activation dtype %d not F16/BF16", xdt);
@@ -177,8 +192,21 @@ int q4q8_qgemm(int fmt, const void* W, int64_t N, int64_t K, const void* X, int 
   if (!aligned(W, 16) || !aligned(X, 16) || !aligned(Y, 16) || ldx % 8 || ldy % 8)
     return fail(Q4Q8_ERR_ALIGNMENT, "qgemm: pointers must be 16-byte aligned, ldx and ldy multiples of 8");
   clear_hip_error();
-  return hip_status(q4q8::launch_qgemm(fmt, xdt, ydt, W, N, K, X, ldx, M, Y, ldy, (hipStream_t)stream),
+  return hip_status(q4q8::launch_qgemm(fmt, xdt, ydt, W, N, K, X, ldx, M, Y, ldy, (hipStream_t)stream, ev),
                     "qgemm launch");
+}
+
+int q4q8_qgemm(int fmt, const void* W, int64_t N, int64_t K, const void* X, int xdt, int64_t ldx, int64_t M, void* Y,
+               int ydt, int64_t ldy, void* stream) {
+  return qgemm_impl(fmt, W, N, K, X, xdt, ldx, M, Y, ydt, ldy, stream, q4q8::LaunchEvents());
+}
+
+int q4q8_qgemm_timed(int fmt, const void* W, int64_t N, int64_t K, const void* X, int xdt, int64_t ldx, int64_t M,
+                     void* Y, int ydt, int64_t ldy, void* stream, void* ev_start, void* ev_stop) {
+  q4q8::LaunchEvents ev;
+  ev.start = (hipEvent_t)ev_start;
+  ev.stop = (hipEvent_t)ev_stop;
+  return qgemm_impl(fmt, W, N, K, X, xdt, ldx, M, Y, ydt, ldy, stream, ev);
 }
 
 int q4q8_moe_route(const float* logits, int T, int E, int topk, int32_t* ids, float* gates, int32_t* counts,

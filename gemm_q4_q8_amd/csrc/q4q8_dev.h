@@ -85,14 +85,15 @@ template <> struct Op<kBF16> {
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ u32x4_t deq_q4_f16(uint32_t w) {
   // (nibble | 0x6400) is the fp16 1024 + n; (16n | 0x6400) is 1024 + 16n.
-  // Plain C on purpose: no inline asm next to MFMAs (the hazard recognizer
-  // does not see VALU writes made from inline asm).
+  // (w & mask) | magic is one v_bitop3_b32 (truth table 0xEA for
+  // (a & b) | c).  No inline asm here: the hazard recognizer does not see
+  // VALU writes made from inline asm next to in-flight MFMAs.
   const uint32_t kMagic = 0x64006400u;
-  uint32_t w2 = w >> 8;
-  half2_t h0 = __builtin_bit_cast(half2_t, (w & 0x000F000Fu) | kMagic);
-  half2_t h1 = __builtin_bit_cast(half2_t, (w & 0x00F000F0u) | kMagic);
-  half2_t h2 = __builtin_bit_cast(half2_t, (w2 & 0x000F000Fu) | kMagic);
-  half2_t h3 = __builtin_bit_cast(half2_t, (w2 & 0x00F000F0u) | kMagic);
+  const uint32_t w2 = w >> 8;
+  half2_t h0 = __builtin_bit_cast(half2_t, __builtin_amdgcn_bitop3_b32(w, 0x000F000Fu, kMagic, 0xEA));
+  half2_t h1 = __builtin_bit_cast(half2_t, __builtin_amdgcn_bitop3_b32(w, 0x00F000F0u, kMagic, 0xEA));
+  half2_t h2 = __builtin_bit_cast(half2_t, __builtin_amdgcn_bitop3_b32(w2, 0x000F000Fu, kMagic, 0xEA));
+  half2_t h3 = __builtin_bit_cast(half2_t, __builtin_amdgcn_bitop3_b32(w2, 0x00F000F0u, kMagic, 0xEA));
   const half2_t off = {(_Float16)1032.0f, (_Float16)1032.0f};
   const half2_t sixteenth = {(_Float16)0.0625f, (_Float16)0.0625f};
   const half2_t off16 = {(_Float16)-72.0f, (_Float16)-72.0f};

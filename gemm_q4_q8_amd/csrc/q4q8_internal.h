@@ -1,39 +1,56 @@
 // Host-side declarations shared by the C-ABI layer and the kernel launchers.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
 namespace q4q8 {
 
+// Optional start/stop events recorded by the dispatch itself
+// (hipExtLaunchKernel), so their elapsed time is the kernel's own duration.
+struct LaunchEvents {
+  hipEvent_t start = nullptr;
+  hipEvent_t stop = nullptr;
+};
+
+template <typename K, typename... A>
+inline void launch(K kernel, dim3 grid, dim3 block, uint32_t shmem, hipStream_t s, const LaunchEvents& ev,
+                   A... args) {
+  if (ev.start || ev.stop)
+    hipExtLaunchKernelGGL(kernel, grid, block, shmem, s, ev.start, ev.stop, 0, args...);
+  else
+    kernel<<<grid, block, shmem, s>>>(args...);
+}
+
 constexpr int kMaxGroup = 8;
 
-// One GEMV problem as the kernel sees it (tile0: first global tile index).
+// One GEMV problem as the kernel sees it.
 struct GemvProb {
   const uint8_t* W;
   const uint16_t* x;
   float* y;
   int64_t ldx, ldy;
   int32_t N, K;
-  int32_t tile0;
-  int32_t pad;
 };
 
 struct GemvArgs {
-  GemvProb p[kMaxGroup];
+  int32_t wg0[kMaxGroup];   // first workgroup of each problem (set by the launcher)
   int32_t count;
   int32_t M;
   int32_t total_tiles;
   int32_t pad;
+  GemvProb p[kMaxGroup];
 };
 
 hipError_t launch_repack(int fmt, const void* canon, int64_t N, int64_t K, void* dst, hipStream_t stream);
 void repack_host(int fmt, const void* canon, int64_t N, int64_t K, void* dst);
 
-hipError_t launch_qgemv(int fmt, int xdt, const GemvArgs& args, int max_chunks, hipStream_t stream);
+hipError_t launch_qgemv(int fmt, int xdt, GemvArgs args, int max_chunks, int max_k, hipStream_t stream,
+                        const LaunchEvents& ev);
 
 hipError_t launch_qgemm(int fmt, int xdt, int ydt, const void* W, int64_t N, int64_t K, const void* X, int64_t ldx,
-                        int64_t M, void* Y, int64_t ldy, hipStream_t stream);
+                        int64_t M, void* Y, int64_t ldy, hipStream_t stream, const LaunchEvents& ev);
 
 hipError_t launch_moe_route(const float* logits, int T, int E, int topk, int32_t* ids, float* gates,
                             int32_t* counts, int32_t* offsets, int32_t* sorted_pairs, hipStream_t stream);

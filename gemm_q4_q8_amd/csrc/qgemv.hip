@@ -3,193 +3,322 @@
 // The pages ("BaseRT: Best-in-Class LLM Inference on Apple Silicon via Native
 // Metal", gist.science technical summary, "Methodologie", kernel
 // specialisation) run decode on a GEMV per quantisation format that
-// dequantises inside its inner loop.  Here the inner product of each 32-weight
-// block is done by one v_mfma_f32_16x16x32 instruction instead of lane FMAs
+// dequantises inside its inner loop.  On gfx950 the inner product of each
+// 32-weight block is one v_mfma_f32_16x16x32 instruction instead of lane FMAs
 // plus a cross-lane reduction:
-//   * a wavefront owns a tile of 16 weight rows; the waves of a workgroup
-//     split K (chunk c goes to wave c % WAVES) and reduce through LDS in a
-//     fixed order at the end (split-K without atomics or workspace);
-//   * per chunk a lane loads 16 (Q4_0) or 32 (Q8_0) contiguous bytes of codes
-//     -- the wave reads 1 or 2 KB contiguous -- plus its row's 4 scales, and
-//     unpacks the codes in registers straight into the MFMA B operand;
-//   * the A operand holds the activation rows: row m sits in A row
-//     4 (m % 4) + m / 4, so the MFMA result for every m < 4 lands in the
-//     first accumulator register of each lane (m < 8: the first two) and the
-//     fp32 block scale costs one FMA per lane per block for M <= 4;
-//   * codes are exact in the operand type (fp16 or bf16) and the block scale
-//     is applied in fp32, so every product is exact and only the fp32
-//     accumulation rounds.
+//   * a wavefront owns a tile of 16 weight rows and a share of K; a workgroup
+//     holds TPW tiles x KS K-shares (TPW * KS waves); K-shares of one tile
+//     are reduced through LDS in a fixed order at the end (split-K without
+//     atomics or workspace);
+//   * the activation rows are staged once per workgroup in LDS; each lane
+//     reads its 16-byte A fragment from there;
+//   * weights stream through buffer loads: per chunk (4 blocks) a lane loads
+//     16 (Q4_0) or 32 (Q8_0) contiguous bytes of codes -- the wave reads 1 or
+//     2 KB contiguous -- plus its row's 4 fp16 scales, into a ring of P chunks
+//     in flight.  The buffer range is the tile itself, so loads past its end
+//     return zero (scale 0) and tails need no branches;
+//   * codes are unpacked in registers straight into the MFMA B operand; they
+//     are exact in the operand type (fp16 or bf16) and the block scale is
+//     applied in fp32, so every product is exact and only the fp32
+//     accumulation rounds;
+//   * activation row m sits in A row 4 (m % 4) + m / 4, so for every m < 4 the
+//     result lands in the first accumulator register of each lane (m < 8:
+//     the first two): one FMA per lane per block applies the scale for M <= 4.
 #include "q4q8_dev.h"
 #include "q4q8_internal.h"
 
 #include <stdlib.h>
 
+#include <mutex>
+
 namespace q4q8 {
 
-template <int FMT, int XDT, int NI, int WAVES>
-__global__ __launch_bounds__(WAVES * 64) void qgemv_kernel(const GemvArgs args) {
+constexpr int kBufFlags = 0x00020000;   // raw buffer, 32-bit data format (gfx9)
+#ifndef Q4Q8_WEIGHT_AUX
+#define Q4Q8_WEIGHT_AUX 0               // cache policy bits of the weight loads
+#endif
+constexpr int kXSlack = 512;            // zeroed LDS bytes after the activation rows
+constexpr int XP = 4;                   // x pieces per thread staged before the prefetch
+constexpr int64_t kLdsTotal = 160 * 1024;          // LDS per workgroup on gfx950
+constexpr int64_t kLdsCap = kLdsTotal - 8 * 1024;  // dynamic LDS for the activations
+
+template <int FMT, int XDT, int NI, int KS, int TPW, int P, bool XLDS>
+__global__ __launch_bounds__(KS* TPW * 64) void qgemv_kernel(const GemvArgs args) {
+  constexpr int WAVES = KS * TPW;
   constexpr int REC = Fmt<FMT>::kRecBytes;
   constexpr int CODE = Fmt<FMT>::kCodeBytes;
   constexpr int NV = FMT == kQ4_0 ? 1 : 2;
   typedef typename Op<XDT>::vec vec;
+  extern __shared__ __attribute__((aligned(16))) uint16_t xs[];
 
-  // Which problem of the group this workgroup serves (uniform selects).
+  // Problem of the group that owns this workgroup.  Problem 0's fields are
+  // loaded together with the boundaries; only later problems pay a second
+  // kernel-argument round trip.
   const int bid = blockIdx.x;
-  const uint8_t* Wp = args.p[0].W;
-  const uint16_t* xp = args.p[0].x;
-  float* yp = args.p[0].y;
-  int64_t ldx = args.p[0].ldx, ldy = args.p[0].ldy;
-  int N = args.p[0].N, K = args.p[0].K, tile0 = args.p[0].tile0;
+  int pi = 0;
 #pragma unroll
-  for (int i = 1; i < kMaxGroup; ++i) {
-    if (i < args.count && bid >= args.p[i].tile0) {
-      Wp = args.p[i].W; xp = args.p[i].x; yp = args.p[i].y;
-      ldx = args.p[i].ldx; ldy = args.p[i].ldy;
-      N = args.p[i].N; K = args.p[i].K; tile0 = args.p[i].tile0;
-    }
-  }
-  const int tile = bid - tile0;
+  for (int i = 1; i < kMaxGroup; ++i) pi += (i < args.count && bid >= args.wg0[i]) ? 1 : 0;
+  GemvProb prob = args.p[0];
+  if (pi != 0) prob = args.p[pi];
+  const int N = prob.N, K = prob.K;
   const int nchunks = (K + kChunkK - 1) / kChunkK;
   const int nblocks = K / 32;
-  const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int tiles = (N + kTileRows - 1) / kTileRows;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int slot = wave / KS, ks = wave % KS;
+  const int tile = (bid - args.wg0[pi]) * TPW + slot;
+  const bool tile_ok = tile < tiles;
   const int r = lane & 15, g = lane >> 4;
   const int m = 4 * (r & 3) + (r >> 2);          // activation row fed by this lane
   const bool mvalid = m < args.M;
-  // Lanes whose A row has no activation row (m >= M) read row 0: MFMA rows
-  // are independent and those result rows are never stored.  Blocks past K
-  // (padding, scale 0) read the last real block so every operand is finite.
-  const uint16_t* __restrict__ xrow = xp + (mvalid ? (int64_t)m * ldx : 0) + 8 * g;
-  const uint8_t* __restrict__ wt = Wp + (int64_t)tile * nchunks * REC;
+
+  // Buffer over this tile's records only: past the end reads return zero.
+  const uint8_t* tbase = prob.W + (int64_t)(tile_ok ? tile : 0) * nchunks * REC;
+  const __amdgpu_buffer_rsrc_t wres =
+      __builtin_amdgcn_make_buffer_rsrc((void*)tbase, (short)0, tile_ok ? nchunks * REC : 0, kBufFlags);
+
+  struct Stage {
+    u32x4_t codes[NV];
+    u32x2_t sc;
+  };
+  auto load = [&](Stage& st, int c) {
+    const int off = c * REC;
+#pragma unroll
+    for (int v = 0; v < NV; ++v)
+      st.codes[v] = __builtin_amdgcn_raw_buffer_load_b128(wres, off + v * 1024 + lane * 16, 0, Q4Q8_WEIGHT_AUX);
+    st.sc = __builtin_amdgcn_raw_buffer_load_b64(wres, off + CODE + r * 8, 0, Q4Q8_WEIGHT_AUX);
+  };
+
+  // Activations: LDS rows of K + 8 halfs (the pad staggers rows over banks),
+  // plus kXSlack zeroed bytes after the last row.  x is loaded first, then
+  // the weight prefetch is issued, so the wait before the LDS writes covers
+  // only the x loads.  Reads of blocks past K (chunk tails, scale 0) land in
+  // the zeroed pad, the next row or the slack: always finite.
+  const int ldsx = K + 8;
+  const int M = args.M;
+  const uint16_t* __restrict__ xg = prob.x;
+  Stage st[P];
+  if constexpr (XLDS) {
+    const int per_row = K / 8 + 1;                 // 16-byte pieces incl. the pad
+    const int pieces = M * per_row + kXSlack / 16;
+    u32x4_t xv[XP];
+#pragma unroll
+    for (int u = 0; u < XP; ++u) {
+      const int i = tid + u * WAVES * 64;
+      const int mm = i / per_row, k8 = i - mm * per_row;
+      xv[u] = (mm < M && k8 < K / 8) ? *(const u32x4_t*)(xg + (int64_t)mm * prob.ldx + k8 * 8) : u32x4_t{0, 0, 0, 0};
+    }
+#pragma unroll
+    for (int p = 0; p < P; ++p) load(st[p], ks + p * KS);   // past the tile: zero, no memory traffic
+#pragma unroll
+    for (int u = 0; u < XP; ++u) {
+      const int i = tid + u * WAVES * 64;
+      if (i < pieces) *(u32x4_t*)(xs + i * 8) = xv[u];
+    }
+    for (int i = tid + XP * WAVES * 64; i < pieces; i += WAVES * 64) {
+      const int mm = i / per_row, k8 = i - mm * per_row;
+      const u32x4_t v =
+          (mm < M && k8 < K / 8) ? *(const u32x4_t*)(xg + (int64_t)mm * prob.ldx + k8 * 8) : u32x4_t{0, 0, 0, 0};
+      *(u32x4_t*)(xs + i * 8) = v;
+    }
+    __syncthreads();
+  } else {
+#pragma unroll
+    for (int p = 0; p < P; ++p) load(st[p], ks + p * KS);
+  }
+  const int xrow_lds = (mvalid ? m : 0) * ldsx + 8 * g;
+  const uint16_t* __restrict__ xrow_g = xg + (mvalid ? (int64_t)m * prob.ldx : 0) + 8 * g;
 
   float acc[NI];
 #pragma unroll
   for (int i = 0; i < NI; ++i) acc[i] = 0.0f;
 
-  struct Stage {
-    u32x4_t codes[NV];
-    u32x2_t sc;
+  auto compute = [&](const Stage& s, int c) {
     vec a[kBlocksPerChunk];
-  };
-  auto load = [&](Stage& st, int c) {
-    c = c < nchunks ? c : nchunks - 1;
-    const uint8_t* __restrict__ rec = wt + (int64_t)c * REC;
+    if constexpr (XLDS) {
+      const int cx = c < nchunks ? c : nchunks - 1;   // chunks past the tile are all zero-scale
+      const uint16_t* xa = xs + xrow_lds + cx * kChunkK;
 #pragma unroll
-    for (int v = 0; v < NV; ++v) st.codes[v] = *(const u32x4_t*)(rec + v * 1024 + lane * 16);
-    st.sc = *(const u32x2_t*)(rec + CODE + r * 8);
+      for (int j = 0; j < kBlocksPerChunk; ++j) a[j] = *(const vec*)(xa + j * 32);
+    } else {
 #pragma unroll
-    for (int j = 0; j < kBlocksPerChunk; ++j) {
-      int blk = c * kBlocksPerChunk + j;
-      blk = blk < nblocks ? blk : nblocks - 1;
-      st.a[j] = *(const vec*)(xrow + blk * 32);
+      for (int j = 0; j < kBlocksPerChunk; ++j) {
+        int blk = c * kBlocksPerChunk + j;
+        blk = blk < nblocks ? blk : nblocks - 1;     // past-K blocks have scale 0
+        a[j] = *(const vec*)(xrow_g + blk * 32);
+      }
     }
-  };
-  auto compute = [&](const Stage& st) {
-    // All four block products first (independent MFMAs), then the scales.
     float4_t d[kBlocksPerChunk];
 #pragma unroll
     for (int j = 0; j < kBlocksPerChunk; ++j) {
-      const u32x4_t b = deq_block<FMT, XDT>(st.codes, j);
-      d[j] = Op<XDT>::mfma(st.a[j], __builtin_bit_cast(vec, b), float4_t{0.0f, 0.0f, 0.0f, 0.0f});
+      const u32x4_t b = deq_block<FMT, XDT>(s.codes, j);
+      d[j] = Op<XDT>::mfma(a[j], __builtin_bit_cast(vec, b), float4_t{0.0f, 0.0f, 0.0f, 0.0f});
     }
 #pragma unroll
     for (int j = 0; j < kBlocksPerChunk; ++j) {
-      const uint32_t sbits = (j & 1) ? (st.sc[j >> 1] >> 16) : (st.sc[j >> 1] & 0xFFFFu);
-      const float s = half_bits_to_float(sbits);
+      const uint32_t sbits = (j & 1) ? (s.sc[j >> 1] >> 16) : (s.sc[j >> 1] & 0xFFFFu);
+      const float sf = half_bits_to_float(sbits);
 #pragma unroll
-      for (int i = 0; i < NI; ++i) acc[i] = __builtin_fmaf(s, d[j][i], acc[i]);
+      for (int i = 0; i < NI; ++i) acc[i] = __builtin_fmaf(sf, d[j][i], acc[i]);
     }
   };
 
-  // Two-stage pipeline: the next chunk of this wave is in flight while the
-  // current one is unpacked and multiplied.
-  Stage s0, s1;
-  int c = wave;
-  if (c < nchunks) {
-    load(s0, c);
-    // The scheduling barriers keep the compiler from sinking the prefetch
-    // next to its use, which would serialise memory latency per chunk.
-    while (true) {
-      load(s1, c + WAVES);
+  // Chunks of this wave: ks + i KS for i < nw.  Stage p holds chunk i with
+  // i % P == p; full groups of P prefetch the next group, the last group
+  // (possibly partial) issues no loads, so no load runs past the wave's share.
+  const int nw = (nchunks - ks + KS - 1) / KS;
+  int i0 = 0;
+  for (; i0 + P < nw; i0 += P) {
+#pragma unroll
+    for (int p = 0; p < P; ++p) {
+      const int c = ks + (i0 + p) * KS;
+      compute(st[p], c);
       __builtin_amdgcn_sched_barrier(0);
-      compute(s0);
-      c += WAVES;
-      if (c >= nchunks) break;
-      load(s0, c + WAVES);
-      __builtin_amdgcn_sched_barrier(0);
-      compute(s1);
-      c += WAVES;
-      if (c >= nchunks) break;
+      load(st[p], c + P * KS);
     }
   }
+#pragma unroll
+  for (int p = 0; p < P; ++p)
+    if (i0 + p < nw) compute(st[p], ks + (i0 + p) * KS);
 
-  if constexpr (WAVES > 1) {
+  if constexpr (KS > 1) {
     __shared__ float red[WAVES][NI][64];
 #pragma unroll
     for (int i = 0; i < NI; ++i) red[wave][i][lane] = acc[i];
     __syncthreads();
-    if (wave != 0) return;
+    if (ks != 0) return;
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
-      float v = red[0][i][lane];
+      float v = red[wave][i][lane];
 #pragma unroll
-      for (int w = 1; w < WAVES; ++w) v += red[w][i][lane];
+      for (int w = 1; w < KS; ++w) v += red[wave + w][i][lane];
       acc[i] = v;
     }
   }
+  if (!tile_ok) return;
   // Lane (r, g), register i holds y[m = 4 i + g][n = 16 tile + r].
   const int n = tile * kTileRows + r;
 #pragma unroll
   for (int i = 0; i < NI; ++i) {
     const int mo = 4 * i + g;
-    if (mo < args.M && n < N) yp[(int64_t)mo * ldy + n] = acc[i];
+    if (mo < args.M && n < N) prob.y[(int64_t)mo * prob.ldy + n] = acc[i];
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Launch configuration
+// ---------------------------------------------------------------------------
+struct GemvShape {
+  int ks, tpw, p;
+  bool xlds;
+};
+
+template <int FMT, int XDT, int NI, int KS, int TPW, int P>
+static void launch_cfg(bool xlds, const GemvArgs& args, int wgs, size_t lds, hipStream_t s, const LaunchEvents& ev) {
+  const dim3 grid((unsigned)wgs), block(KS * TPW * 64);
+  if (xlds) {
+    auto k = qgemv_kernel<FMT, XDT, NI, KS, TPW, P, true>;
+    if (lds > 64 * 1024) {
+      // Opt in once to dynamic LDS beyond 64 KB: the device's 160 KB per
+      // workgroup minus this kernel's static LDS (the split-K buffer).
+      static std::once_flag once;
+      static size_t dyn_max = 64 * 1024;
+      std::call_once(once, [&] {
+        hipFuncAttributes fa;
+        if (hipFuncGetAttributes(&fa, (const void*)k) == hipSuccess) {
+          const size_t avail = kLdsTotal - fa.sharedSizeBytes;
+          if (hipFuncSetAttribute((const void*)k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)avail) ==
+              hipSuccess)
+            dyn_max = avail;
+        }
+      });
+      if (lds > dyn_max) {   // does not fit: read x from global memory instead
+        launch(qgemv_kernel<FMT, XDT, NI, KS, TPW, P, false>, grid, block, 0, s, ev, args);
+        return;
+      }
+    }
+    launch(k, grid, block, (uint32_t)lds, s, ev, args);
+  } else
+    launch(qgemv_kernel<FMT, XDT, NI, KS, TPW, P, false>, grid, block, 0, s, ev, args);
+}
+
+template <int FMT, int XDT, int NI, int P>
+static void launch_p(const GemvShape& c, const GemvArgs& args, int wgs, size_t lds, hipStream_t s,
+                     const LaunchEvents& ev) {
+  switch (c.ks) {
+    case 1: launch_cfg<FMT, XDT, NI, 1, 4, P>(c.xlds, args, wgs, lds, s, ev); break;
+    case 2: launch_cfg<FMT, XDT, NI, 2, 2, P>(c.xlds, args, wgs, lds, s, ev); break;
+    case 4: launch_cfg<FMT, XDT, NI, 4, 1, P>(c.xlds, args, wgs, lds, s, ev); break;
+    case 8: launch_cfg<FMT, XDT, NI, 8, 1, P>(c.xlds, args, wgs, lds, s, ev); break;
+    default: launch_cfg<FMT, XDT, NI, 16, 1, P>(c.xlds, args, wgs, lds, s, ev); break;
   }
 }
 
 template <int FMT, int XDT, int NI>
-static void launch_waves(int waves, const GemvArgs& args, hipStream_t s) {
-  const dim3 grid((unsigned)args.total_tiles);
-  switch (waves) {
-    case 4: qgemv_kernel<FMT, XDT, NI, 4><<<grid, dim3(256), 0, s>>>(args); break;
-    case 8: qgemv_kernel<FMT, XDT, NI, 8><<<grid, dim3(512), 0, s>>>(args); break;
-    default: qgemv_kernel<FMT, XDT, NI, 16><<<grid, dim3(1024), 0, s>>>(args); break;
-  }
-}
-
-template <int FMT, int XDT>
-static void launch_ni(int waves, const GemvArgs& args, hipStream_t s) {
-  if (args.M > 4)
-    launch_waves<FMT, XDT, 2>(waves, args, s);
+static void launch_ni(const GemvShape& c, const GemvArgs& args, int wgs, size_t lds, hipStream_t s,
+                      const LaunchEvents& ev) {
+  if (c.p == 8)
+    launch_p<FMT, XDT, NI, 8>(c, args, wgs, lds, s, ev);
   else
-    launch_waves<FMT, XDT, 1>(waves, args, s);
+    launch_p<FMT, XDT, NI, 4>(c, args, wgs, lds, s, ev);
 }
 
-// Waves per workgroup: enough workgroups x waves to fill 256 CUs with a few
-// waves each, but at least two chunks per wave.
-static int pick_waves(int tiles, int max_chunks) {
-  int waves = 4;
-  while (waves < 16 && tiles * waves < 4096 && max_chunks >= 4 * waves) waves *= 2;
-  return waves;
+// K-shares per tile: about 2048 waves over the chip (8 per CU) with at least
+// 8 chunks each; a ring of 4 chunks in flight per wave.  (Measured on MI355X:
+// more waves or a deeper ring both lose, as does a split below 8 chunks.)
+// The activation block goes to LDS when it fits in 160 KB; above 80 KB a
+// workgroup gets at least 8 waves since few workgroups then share a CU.
+static GemvShape pick_shape(int tiles, int max_chunks, int M, int max_k) {
+  GemvShape c;
+  const int64_t lds = (int64_t)M * (max_k + 8) * 2 + kXSlack;
+  int ks = 1;
+  while (ks < 16 && tiles * ks < 2048 && max_chunks >= 16 * ks) ks *= 2;
+  if (lds > 80 * 1024 && ks < 8) ks = 8;
+  if (const char* e = getenv("Q4Q8_GEMV_KS")) {   // tuning experiments only
+    const int v = atoi(e);
+    if (v == 1 || v == 2 || v == 4 || v == 8 || v == 16) ks = v;
+  }
+  c.ks = ks;
+  c.tpw = ks >= 4 ? 1 : 4 / ks;
+  c.p = 4;
+  if (const char* e = getenv("Q4Q8_GEMV_P")) {    // tuning experiments only
+    const int v = atoi(e);
+    if (v == 4 || v == 8) c.p = v;
+  }
+  c.xlds = lds <= kLdsCap;
+  return c;
 }
 
-// Q4Q8_GEMV_WAVES=4|8|16 overrides the choice (tuning experiments only).
-static int waves_override() {
-  static const int v = [] {
-    const char* e = getenv("Q4Q8_GEMV_WAVES");
-    const int w = e ? atoi(e) : 0;
-    return (w == 4 || w == 8 || w == 16) ? w : 0;
-  }();
-  return v;
-}
-
-hipError_t launch_qgemv(int fmt, int xdt, const GemvArgs& args, int max_chunks, hipStream_t s) {
-  const int waves = waves_override() ? waves_override() : pick_waves(args.total_tiles, max_chunks);
+hipError_t launch_qgemv(int fmt, int xdt, GemvArgs args, int max_chunks, int max_k, hipStream_t s,
+                        const LaunchEvents& ev) {
+  const GemvShape c = pick_shape(args.total_tiles, max_chunks, args.M, max_k);
+  // Workgroup ranges per problem.
+  int wgs = 0;
+  for (int i = 0; i < args.count; ++i) {
+    args.wg0[i] = wgs;
+    wgs += (args.p[i].N + kTileRows * c.tpw - 1) / (kTileRows * c.tpw);
+  }
+  for (int i = args.count; i < kMaxGroup; ++i) args.wg0[i] = wgs;
+  const size_t lds = c.xlds ? (size_t)args.M * (max_k + 8) * 2 + kXSlack : 0;
   if (fmt == kQ4_0) {
-    if (xdt == kF16) launch_ni<kQ4_0, kF16>(waves, args, s);
-    else launch_ni<kQ4_0, kBF16>(waves, args, s);
+    if (xdt == kF16) {
+      if (args.M > 4) launch_ni<kQ4_0, kF16, 2>(c, args, wgs, lds, s, ev);
+      else launch_ni<kQ4_0, kF16, 1>(c, args, wgs, lds, s, ev);
+    } else {
+      if (args.M > 4) launch_ni<kQ4_0, kBF16, 2>(c, args, wgs, lds, s, ev);
+      else launch_ni<kQ4_0, kBF16, 1>(c, args, wgs, lds, s, ev);
+    }
   } else {
-    if (xdt == kF16) launch_ni<kQ8_0, kF16>(waves, args, s);
-    else launch_ni<kQ8_0, kBF16>(waves, args, s);
+    if (xdt == kF16) {
+      if (args.M > 4) launch_ni<kQ8_0, kF16, 2>(c, args, wgs, lds, s, ev);
+      else launch_ni<kQ8_0, kF16, 1>(c, args, wgs, lds, s, ev);
+    } else {
+      if (args.M > 4) launch_ni<kQ8_0, kBF16, 2>(c, args, wgs, lds, s, ev);
+      else launch_ni<kQ8_0, kBF16, 1>(c, args, wgs, lds, s, ev);
+    }
   }
   return hipGetLastError();
 }

@@ -152,6 +152,14 @@ typedef struct {
 int q4q8_qgemv_grouped(int fmt, const q4q8_gemv_desc* descs, int count,
                        int xdt, int M, void* stream);
 
+/* As q4q8_qgemv_grouped, and the dispatch itself records ev_start when the
+ * kernel starts and ev_stop when it ends (hipEvent_t handles, either may be
+ * NULL), so hipEventElapsedTime gives the kernel's own duration.  For
+ * measurement; the result is identical. */
+int q4q8_qgemv_grouped_timed(int fmt, const q4q8_gemv_desc* descs, int count,
+                             int xdt, int M, void* stream,
+                             void* ev_start, void* ev_stop);
+
 /* ------------------------------------------------------------------------ */
 /* Prefill: quantised GEMM                                                   */
 /* (technical summary, "Methodologie", prefill optimisation: tiled GEMM on  */
@@ -169,6 +177,13 @@ int q4q8_qgemv_grouped(int fmt, const q4q8_gemv_desc* descs, int count,
 int q4q8_qgemm(int fmt, const void* W, int64_t N, int64_t K,
                const void* X, int xdt, int64_t ldx, int64_t M,
                void* Y, int ydt, int64_t ldy, void* stream);
+
+/* As q4q8_qgemm, with dispatch-recorded start/stop events (see
+ * q4q8_qgemv_grouped_timed).  For measurement; the result is identical. */
+int q4q8_qgemm_timed(int fmt, const void* W, int64_t N, int64_t K,
+                     const void* X, int xdt, int64_t ldx, int64_t M,
+                     void* Y, int ydt, int64_t ldy, void* stream,
+                     void* ev_start, void* ev_stop);
 
 /* ------------------------------------------------------------------------ */
 /* Mixture of experts (review, "Method": MoE expert GEMM and fused expert    */
