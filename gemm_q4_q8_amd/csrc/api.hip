@@ -189,6 +189,7 @@ static int qgemm_impl(int fmt, const void* W, int64_t N, int64_t K, const void* 
   if (M < 1 || M > (1LL << 30)) return fail(Q4Q8_ERR_INVALID_ARG, "qgemm: M=%lld", (long long)M);
   if (!W || !X || !Y) return fail(Q4Q8_ERR_INVALID_ARG, "qgemm: null pointer");
   if (ldx < K || ldy < N) return fail(Q4Q8_ERR_INVALID_ARG, "qgemm: ldx < K or ldy < N");
+  if (ldx > (1LL << 22)) return fail(Q4Q8_ERR_UNSUPPORTED, "qgemm: ldx=%lld beyond 2^22", (long long)ldx);
   if (!aligned(W, 16) || !aligned(X, 16) || !aligned(Y, 16) || ldx % 8 || ldy % 8)
     return fail(Q4Q8_ERR_ALIGNMENT, "qgemm: pointers must be 16-byte aligned, ldx and ldy multiples of 8");
   clear_hip_error();

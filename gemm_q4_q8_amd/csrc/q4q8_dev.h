@@ -149,6 +149,20 @@ template <> __device__ __forceinline__ u32x4_t deq_block<kQ8_0, kBF16>(const u32
   return deq_q8<kBF16>(c[j >> 1][2 * (j & 1)], c[j >> 1][2 * (j & 1) + 1]);
 }
 
+// Multiply 8 fp16 values (4 packed pairs) by the scale pair s2.  Each element
+// is copied into a scalar first: hipcc (clang 22) miscompiles
+// __builtin_bit_cast applied directly to an ext_vector element inside an
+// unrolled read-modify-write loop (every element came out as element 0).
+__device__ __forceinline__ u32x4_t scale_f16x8(const u32x4_t q, const half2_t s2) {
+  const uint32_t q0 = q[0], q1 = q[1], q2 = q[2], q3 = q[3];
+  u32x4_t o;
+  o[0] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(half2_t, q0) * s2);
+  o[1] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(half2_t, q1) * s2);
+  o[2] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(half2_t, q2) * s2);
+  o[3] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(half2_t, q3) * s2);
+  return o;
+}
+
 __device__ __forceinline__ float half_bits_to_float(uint32_t bits16) {
   return (float)__builtin_bit_cast(_Float16, (uint16_t)bits16);
 }

@@ -1,0 +1,97 @@
+"""GPU parity of the prefill GEMM against the CPU oracle."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from util import act_tensor, bytes_tensor, check, check_rounded, dev, values
+
+pytestmark = pytest.mark.gpu
+
+OUT = {"bf16": torch.bfloat16, "f16": torch.float16, "f32": torch.float32}
+
+
+@pytest.fixture(scope="module")
+def q():
+    import gemm_q4_q8_amd as q
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    q.lib()
+    return q
+
+
+def _compare(got, ref, bound, ydt, what):
+    if ydt == "f32":
+        return check(got, ref, bound, what)
+    return check_rounded(got, ref, bound, what, dtype=ydt)
+
+
+SMALL = [(1, 16, 128), (17, 48, 160), (64, 256, 256), (100, 200, 1056), (128, 192, 4096),
+         (300, 400, 512), (257, 1000, 384), (129, 64, 32)]
+
+
+@pytest.mark.parametrize("fmt,xdt,ydt", [(synth.Q4_0, synth.BF16, "bf16"), (synth.Q4_0, synth.F16, "f32"),
+                                         (synth.Q8_0, synth.BF16, "bf16"), (synth.Q8_0, synth.F16, "f16")])
+@pytest.mark.parametrize("M,N,K", SMALL)
+def test_qgemm_parity_small(q, fmt, xdt, ydt, M, N, K):
+    w = synth.q_weight(synth.rng_for(61, M + N + K + fmt), fmt, N, K)
+    x = synth.activation(synth.rng_for(62, M * 3 + K + xdt), (M, K), xdt)
+    Wd = q.repack(fmt, bytes_tensor(w.canon), N, K)
+    y = q.qgemm(fmt, Wd, N, K, act_tensor(x), out_dtype=OUT[ydt])
+    torch.cuda.synchronize()
+    ref, bound = oracle.qgemm(fmt, w.canon, N, K, x.values)
+    _compare(values(y), ref, bound, ydt, f"gemm fmt{fmt} M{M} N{N} K{K} {ydt}")
+
+
+def test_qgemm_strided_and_deterministic(q):
+    M, N, K = 70, 96, 256
+    w = synth.q_weight(synth.rng_for(63, 0), synth.Q4_0, N, K)
+    x = synth.activation(synth.rng_for(63, 1), (M, K), synth.BF16)
+    X = torch.zeros((M, K + 24), dtype=torch.bfloat16, device=dev())
+    X[:, :K] = act_tensor(x)
+    Y = torch.full((M, N + 8), 3.0, dtype=torch.float32, device=dev())
+    Wd = q.repack(synth.Q4_0, bytes_tensor(w.canon), N, K)
+    L = q.lib()
+    for _ in range(2):
+        st = L.q4q8_qgemm(1, q._ptr(Wd), N, K, q._ptr(X), 2, K + 24, M, q._ptr(Y), 3, N + 8, q._stream(X))
+        assert st == 0, q.last_error()
+        first = Y.clone() if _ == 0 else first
+    torch.cuda.synchronize()
+    assert torch.equal(first, Y)
+    ref, bound = oracle.qgemm(synth.Q4_0, w.canon, N, K, x.values)
+    yh = Y.cpu().numpy()
+    check(yh[:, :N], ref, bound)
+    assert np.all(yh[:, N:] == 3.0)
+
+
+def test_qgemm_zero_weights(q):
+    N, K, M = 64, 512, 40
+    scales = np.full((N, K // 32), np.float16(0.02))
+    codes = np.full((N, K), 8, dtype=np.uint8)
+    w = synth.QWeight(synth.Q4_0, N, K, synth.pack_blocks(synth.Q4_0, scales, codes), scales, codes)
+    x = synth.activation(synth.rng_for(64, 0), (M, K), synth.BF16)
+    y = q.qgemm(synth.Q4_0, q.repack(1, bytes_tensor(w.canon), N, K), N, K, act_tensor(x), out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    assert torch.all(y.abs() <= 1e-5)
+
+
+@pytest.mark.parametrize("M", [512, 2048])
+def test_qgemm_prefill_full_size_sampled(q, M):
+    """The prefill shapes (K 4096, N 12288) in the benchmark's launch shape;
+    4096 sampled outputs plus every output of the first and last 16-row
+    block against the oracle, and NaN/Inf-free everywhere."""
+    w, x = synth.prefill(M)
+    N, K = w.N, w.K
+    Wd = q.repack(synth.Q4_0, bytes_tensor(w.canon), N, K)
+    y = q.qgemm(synth.Q4_0, Wd, N, K, act_tensor(x), out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    yv = values(y)
+    assert np.all(np.isfinite(yv))
+    rng = np.random.default_rng(65 + M)
+    rows = np.concatenate([rng.integers(0, M, 4096), np.zeros(64, int), np.full(64, M - 1)])
+    cols = np.concatenate([rng.integers(0, N, 4096), np.arange(64), N - 1 - np.arange(64)])
+    ref, bound = oracle.qgemm_rows(synth.Q4_0, w.canon, N, K, x.values, rows, cols)
+    check_rounded(yv[rows, cols], ref, bound, f"prefill M{M} sampled")
+    for r0 in (0, M - 16):
+        ref, bound = oracle.qgemm(synth.Q4_0, w.canon, N, K, x.values[r0:r0 + 16])
+        check_rounded(yv[r0:r0 + 16], ref, bound, f"prefill M{M} rows {r0}..")

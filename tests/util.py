@@ -51,19 +51,36 @@ def bf16_values(t: torch.Tensor) -> np.ndarray:
     return synth.bits_to_values(synth.BF16, bits)
 
 
-def check_rounded(got_bf16: np.ndarray, ref, bound, what=""):
-    """A bf16 output passes if it is the nearest-even bf16 of some value v with
-    |v - ref| <= 2e-3 * sum|w*x| + 1e-5 (the output format's own rounding is
-    allowed on top of the tolerance)."""
+def values(t: torch.Tensor) -> np.ndarray:
+    """Exact fp64 values of a bf16 / fp16 / fp32 GPU tensor."""
+    if t.dtype == torch.bfloat16:
+        return bf16_values(t)
+    return t.detach().cpu().to(torch.float64).numpy()
+
+
+def _round_to(dtype, v64):
+    """Nearest-even rounding of fp64 values to bf16 / fp16 (via fp32 for bf16)."""
+    if dtype == "bf16":
+        v32 = v64.astype(np.float32)
+        return synth.bits_to_values(synth.BF16, synth.f32_to_bf16_bits(v32))
+    return v64.astype(np.float16).astype(np.float64)
+
+
+def check_rounded(got_bf16: np.ndarray, ref, bound, what="", dtype="bf16"):
+    """A bf16 (or fp16) output passes if it is the nearest-even rounding of some
+    value v with |v - ref| <= 2e-3 * sum|w*x| + 1e-5: the output format's own
+    rounding is allowed on top of the tolerance.  Rounding is monotone, so
+    that is: got in [round(ref - tol), round(ref + tol)]."""
     ref = np.asarray(ref, dtype=np.float64)
     tol = tolerance(bound)
-    lo = synth.bits_to_values(synth.BF16, synth.f32_to_bf16_bits((ref - tol).astype(np.float32)))
-    hi = synth.bits_to_values(synth.BF16, synth.f32_to_bf16_bits((ref + tol).astype(np.float32)))
-    # fp32 rounding of ref +- tol may move the ends by one fp32 ulp; widen by it.
-    lo = np.minimum(lo, synth.bits_to_values(synth.BF16, synth.f32_to_bf16_bits(
-        np.nextafter((ref - tol).astype(np.float32), np.float32(-np.inf)))))
-    hi = np.maximum(hi, synth.bits_to_values(synth.BF16, synth.f32_to_bf16_bits(
-        np.nextafter((ref + tol).astype(np.float32), np.float32(np.inf)))))
+    lo = _round_to(dtype, ref - tol)
+    hi = _round_to(dtype, ref + tol)
+    if dtype == "bf16":
+        # the fp32 step before bf16 may move the ends by one fp32 ulp; widen by it
+        lo = np.minimum(lo, _round_to(dtype, np.nextafter((ref - tol).astype(np.float32), np.float32(-np.inf))
+                                      .astype(np.float64)))
+        hi = np.maximum(hi, _round_to(dtype, np.nextafter((ref + tol).astype(np.float32), np.float32(np.inf))
+                                      .astype(np.float64)))
     got = np.asarray(got_bf16, dtype=np.float64)
     assert np.all(np.isfinite(got)), f"{what}: non-finite output"
     ok = (got >= lo) & (got <= hi)
