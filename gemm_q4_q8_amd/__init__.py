@@ -55,8 +55,9 @@ def _declare(lib):
         "q4q8_qgemv": (i32, [i32, vp, i64, i64, vp, i32, i64, i32, vp, i64, vp]),
         "q4q8_qgemv_grouped": (i32, [i32, ctypes.POINTER(GemvDesc), i32, i32, i32, vp]),
         "q4q8_qgemv_grouped_timed": (i32, [i32, ctypes.POINTER(GemvDesc), i32, i32, i32, vp, vp, vp]),
-        "q4q8_qgemm": (i32, [i32, vp, i64, i64, vp, i32, i64, i64, vp, i32, i64, vp]),
-        "q4q8_qgemm_timed": (i32, [i32, vp, i64, i64, vp, i32, i64, i64, vp, i32, i64, vp, vp, vp]),
+        "q4q8_qgemm_workspace": (sz, [i32, i64, i64]),
+        "q4q8_qgemm": (i32, [i32, vp, i64, i64, vp, i32, i64, i64, vp, i32, i64, vp, sz, vp]),
+        "q4q8_qgemm_timed": (i32, [i32, vp, i64, i64, vp, i32, i64, i64, vp, i32, i64, vp, sz, vp, vp, vp]),
         "q4q8_moe_route": (i32, [vp, i32, i32, i32, vp, vp, vp, vp, vp, vp]),
         "q4q8_moe_workspace": (sz, [i32, i32, i32, i32, i32, i32]),
         "q4q8_moe_qgemm": (i32, [i32, vp, vp, vp, i32, i32, i32, vp, i32, i32, i32,
@@ -192,17 +193,36 @@ def qgemv_grouped(fmt: int, problems, M: int, descs=None, events=None):
     _check(st, "qgemv_grouped")
 
 
+def qgemm_workspace(xdt: int, M: int, K: int) -> int:
+    return int(lib().q4q8_qgemm_workspace(xdt, M, K))
+
+
 def qgemm(fmt: int, W: torch.Tensor, N: int, K: int, X: torch.Tensor,
-          out: torch.Tensor | None = None, out_dtype=torch.bfloat16) -> torch.Tensor:
-    """Y[M, N] = X[M, K] @ W^T, fp32 accumulation, output out_dtype."""
+          out: torch.Tensor | None = None, out_dtype=torch.bfloat16, ws: torch.Tensor | None = None,
+          events=None) -> torch.Tensor:
+    """Y[M, N] = X[M, K] @ W^T, fp32 accumulation, output out_dtype.
+
+    ws: optional uint8 workspace of >= qgemm_workspace() bytes (allocated per
+    call if omitted).  events: optional (start, stop) raw hipEvent_t handles.
+    """
     _dev(W, "W")
     if X.dim() != 2 or X.shape[1] != K or X.stride(1) != 1:
         raise ValueError("X must be [M, K] with contiguous rows")
     M = X.shape[0]
     if out is None:
         out = torch.empty((M, N), dtype=out_dtype, device=X.device)
-    _check(lib().q4q8_qgemm(fmt, _ptr(W), N, K, _ptr(X), _DT[X.dtype], X.stride(0), M,
-                            _ptr(out), _DT[out.dtype], out.stride(0), _stream(X)), "qgemm")
+    xdt = _DT[X.dtype]
+    nws = qgemm_workspace(xdt, M, K)
+    if ws is None and nws:
+        ws = torch.empty(nws, dtype=torch.uint8, device=X.device)
+    nbytes = ws.numel() * ws.element_size() if ws is not None else 0
+    args = (fmt, _ptr(W), N, K, _ptr(X), xdt, X.stride(0), M, _ptr(out), _DT[out.dtype], out.stride(0),
+            _ptr(ws), nbytes, _stream(X))
+    if events is None:
+        st = lib().q4q8_qgemm(*args)
+    else:
+        st = lib().q4q8_qgemm_timed(*args, ctypes.c_void_p(events[0]), ctypes.c_void_p(events[1]))
+    _check(st, "qgemm")
     return out
 
 

@@ -180,7 +180,8 @@ int q4q8_qgemv(int fmt, const void* W, int64_t N, int64_t K, const void* x, int 
 }
 
 static int qgemm_impl(int fmt, const void* W, int64_t N, int64_t K, const void* X, int xdt, int64_t ldx, int64_t M,
-                      void* Y, int ydt, int64_t ldy, void* stream, const q4q8::LaunchEvents& ev) {
+                      void* Y, int ydt, int64_t ldy, void* ws, size_t ws_bytes, void* stream,
+                      const q4q8::LaunchEvents& ev) {
   int st = check_matrix(fmt, N, K);
   if (st) return st;
   if (!act_ok(xdt)) return fail(Q4Q8_ERR_UNSUPPORTED, "qgemm: activation dtype %d not F16/BF16", xdt);
@@ -192,22 +193,32 @@ static int qgemm_impl(int fmt, const void* W, int64_t N, int64_t K, const void* 
   if (ldx > (1LL << 22)) return fail(Q4Q8_ERR_UNSUPPORTED, "qgemm: ldx=%lld beyond 2^22", (long long)ldx);
   if (!aligned(W, 16) || !aligned(X, 16) || !aligned(Y, 16) || ldx % 8 || ldy % 8)
     return fail(Q4Q8_ERR_ALIGNMENT, "qgemm: pointers must be 16-byte aligned, ldx and ldy multiples of 8");
+  const size_t need = q4q8::qgemm_workspace_bytes(xdt, M, K);
+  if (need && (!ws || ws_bytes < need))
+    return fail(Q4Q8_ERR_WORKSPACE, "qgemm: workspace holds %zu bytes, needs %zu", ws ? ws_bytes : 0, need);
+  if (need && !aligned(ws, 256)) return fail(Q4Q8_ERR_ALIGNMENT, "qgemm: workspace not 256-byte aligned");
   clear_hip_error();
-  return hip_status(q4q8::launch_qgemm(fmt, xdt, ydt, W, N, K, X, ldx, M, Y, ldy, (hipStream_t)stream, ev),
+  return hip_status(q4q8::launch_qgemm(fmt, xdt, ydt, W, N, K, X, ldx, M, Y, ldy, ws, (hipStream_t)stream, ev),
                     "qgemm launch");
 }
 
+size_t q4q8_qgemm_workspace(int xdt, int64_t M, int64_t K) {
+  if (!act_ok(xdt) || M < 1 || K < 1) return 0;
+  return q4q8::qgemm_workspace_bytes(xdt, M, K);
+}
+
 int q4q8_qgemm(int fmt, const void* W, int64_t N, int64_t K, const void* X, int xdt, int64_t ldx, int64_t M, void* Y,
-               int ydt, int64_t ldy, void* stream) {
-  return qgemm_impl(fmt, W, N, K, X, xdt, ldx, M, Y, ydt, ldy, stream, q4q8::LaunchEvents());
+               int ydt, int64_t ldy, void* ws, size_t ws_bytes, void* stream) {
+  return qgemm_impl(fmt, W, N, K, X, xdt, ldx, M, Y, ydt, ldy, ws, ws_bytes, stream, q4q8::LaunchEvents());
 }
 
 int q4q8_qgemm_timed(int fmt, const void* W, int64_t N, int64_t K, const void* X, int xdt, int64_t ldx, int64_t M,
-                     void* Y, int ydt, int64_t ldy, void* stream, void* ev_start, void* ev_stop) {
+                     void* Y, int ydt, int64_t ldy, void* ws, size_t ws_bytes, void* stream, void* ev_start,
+                     void* ev_stop) {
   q4q8::LaunchEvents ev;
   ev.start = (hipEvent_t)ev_start;
   ev.stop = (hipEvent_t)ev_stop;
-  return qgemm_impl(fmt, W, N, K, X, xdt, ldx, M, Y, ydt, ldy, stream, ev);
+  return qgemm_impl(fmt, W, N, K, X, xdt, ldx, M, Y, ydt, ldy, ws, ws_bytes, stream, ev);
 }
 
 int q4q8_moe_route(const float* logits, int T, int E, int topk, int32_t* ids, float* gates, int32_t* counts,

@@ -163,6 +163,17 @@ __device__ __forceinline__ u32x4_t scale_f16x8(const u32x4_t q, const half2_t s2
   return o;
 }
 
+// A raw buffer resource whose base and size are provably wave-uniform (built
+// from readfirstlane'd values), so loads through it take the descriptor from
+// SGPRs instead of a per-lane waterfall loop.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t uniform_rsrc(const void* base, int bytes) {
+  const uint64_t b = (uint64_t)base;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)b);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(b >> 32));
+  const int n = __builtin_amdgcn_readfirstlane(bytes);
+  return __builtin_amdgcn_make_buffer_rsrc((void*)(((uint64_t)hi << 32) | lo), (short)0, n, 0x00020000);
+}
+
 __device__ __forceinline__ float half_bits_to_float(uint32_t bits16) {
   return (float)__builtin_bit_cast(_Float16, (uint16_t)bits16);
 }

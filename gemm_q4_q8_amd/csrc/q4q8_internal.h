@@ -49,8 +49,9 @@ void repack_host(int fmt, const void* canon, int64_t N, int64_t K, void* dst);
 hipError_t launch_qgemv(int fmt, int xdt, GemvArgs args, int max_chunks, int max_k, hipStream_t stream,
                         const LaunchEvents& ev);
 
+size_t qgemm_workspace_bytes(int xdt, int64_t M, int64_t K);
 hipError_t launch_qgemm(int fmt, int xdt, int ydt, const void* W, int64_t N, int64_t K, const void* X, int64_t ldx,
-                        int64_t M, void* Y, int64_t ldy, hipStream_t stream, const LaunchEvents& ev);
+                        int64_t M, void* Y, int64_t ldy, void* ws, hipStream_t stream, const LaunchEvents& ev);
 
 hipError_t launch_moe_route(const float* logits, int T, int E, int topk, int32_t* ids, float* gates,
                             int32_t* counts, int32_t* offsets, int32_t* sorted_pairs, hipStream_t stream);

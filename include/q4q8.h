@@ -166,23 +166,35 @@ int q4q8_qgemv_grouped_timed(int fmt, const q4q8_gemv_desc* descs, int count,
 /*  matrix intrinsics; review, "Method": prefill GEMM on the matrix units)  */
 /* ------------------------------------------------------------------------ */
 
+/* Workspace bytes q4q8_qgemm needs: for BF16 activations their fp16 copy,
+ * M * Kp * 2 with Kp = K rounded up to 128, rounded up to 256 bytes; 0 for
+ * F16.  0 also for invalid xdt/M/K. */
+size_t q4q8_qgemm_workspace(int xdt, int64_t M, int64_t K);
+
 /* Y[m, n] = sum_k X[m, k] * W[n, k]   for m < M, n < N.
  *   X:   device, BF16 or F16 (xdt), row m at X + m*ldx; 16-byte aligned,
- *        ldx % 8 == 0, ldx >= K.
+ *        ldx % 8 == 0, K <= ldx <= 2^22.
  *   Y:   device, ydt = BF16, F16 or F32, row m at Y + m*ldy, ldy >= N,
  *        ldy % 8 == 0 and 16-byte aligned.
+ *   ws:  device workspace of >= q4q8_qgemm_workspace(xdt, M, K) bytes,
+ *        256-byte aligned (may be NULL when that is 0); clobbered.
  * fp32 accumulation on fp16 matrix-core operands (weights dequantised and
- * scaled to fp16, relative rounding <= 2^-11); result rounded once to ydt.
- * M >= 1 (any). */
+ * scaled to fp16, relative rounding <= 2^-11; BF16 activations converted to
+ * fp16, exact for 2^-14 <= |x| < 65520); result rounded once to ydt.
+ * M >= 1 (any).  Errors: Q4Q8_ERR_WORKSPACE if ws is missing or short. */
 int q4q8_qgemm(int fmt, const void* W, int64_t N, int64_t K,
                const void* X, int xdt, int64_t ldx, int64_t M,
-               void* Y, int ydt, int64_t ldy, void* stream);
+               void* Y, int ydt, int64_t ldy, void* ws, size_t ws_bytes,
+               void* stream);
 
-/* As q4q8_qgemm, with dispatch-recorded start/stop events (see
- * q4q8_qgemv_grouped_timed).  For measurement; the result is identical. */
+/* As q4q8_qgemm, with dispatch-recorded events (see
+ * q4q8_qgemv_grouped_timed): ev_start when the first kernel of the call
+ * starts, ev_stop when the last ends.  For measurement; the result is
+ * identical. */
 int q4q8_qgemm_timed(int fmt, const void* W, int64_t N, int64_t K,
                      const void* X, int xdt, int64_t ldx, int64_t M,
-                     void* Y, int ydt, int64_t ldy, void* stream,
+                     void* Y, int ydt, int64_t ldy, void* ws,
+                     size_t ws_bytes, void* stream,
                      void* ev_start, void* ev_stop);
 
 /* ------------------------------------------------------------------------ */

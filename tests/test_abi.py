@@ -142,12 +142,16 @@ def test_grouped_validation(q):
 def test_qgemm_validation(q):
     L = q.lib()
     ok = dict(fmt=1, W=0x1000, N=64, K=256, X=0x2000, xdt=2, ldx=256, M=17, Y=0x3000, ydt=2, ldy=64)
+    ok["ws"], ok["nws"] = 0x100000, q.qgemm_workspace(2, 17, 256)
+    assert ok["nws"] == 17 * 256 * 2 // 256 * 256 + 256 * (17 * 256 * 2 % 256 != 0)
+    assert q.qgemm_workspace(1, 17, 256) == 0 and q.qgemm_workspace(5, 17, 256) == 0
     for over, want in [(dict(ydt=7), -2), (dict(xdt=3), -2), (dict(M=0), -1), (dict(ldx=128), -1),
-                       (dict(ldy=32), -1), (dict(Y=0x3008), -4), (dict(ldx=260), -4), (dict(K=100), -1)]:
+                       (dict(ldy=32), -1), (dict(Y=0x3008), -4), (dict(ldx=260), -4), (dict(K=100), -1),
+                       (dict(ws=0), -3), (dict(nws=ok["nws"] - 1), -3), (dict(ws=0x100010), -4)]:
         a = dict(ok)
         a.update(over)
         st = L.q4q8_qgemm(a["fmt"], _vp(a["W"]), a["N"], a["K"], _vp(a["X"]), a["xdt"], a["ldx"], a["M"],
-                          _vp(a["Y"]), a["ydt"], a["ldy"], None)
+                          _vp(a["Y"]), a["ydt"], a["ldy"], _vp(a["ws"]), a["nws"], None)
         assert st == want, (over, st, q.last_error())
 
 

@@ -27,7 +27,7 @@ def _compare(got, ref, bound, ydt, what):
 
 
 SMALL = [(1, 16, 128), (17, 48, 160), (64, 256, 256), (100, 200, 1056), (128, 192, 4096),
-         (300, 400, 512), (257, 1000, 384), (129, 64, 32)]
+         (300, 400, 512), (257, 1000, 384), (129, 64, 32), (300, 1536, 256), (70, 3072, 160)]
 
 
 @pytest.mark.parametrize("fmt,xdt,ydt", [(synth.Q4_0, synth.BF16, "bf16"), (synth.Q4_0, synth.F16, "f32"),
@@ -52,8 +52,11 @@ def test_qgemm_strided_and_deterministic(q):
     Y = torch.full((M, N + 8), 3.0, dtype=torch.float32, device=dev())
     Wd = q.repack(synth.Q4_0, bytes_tensor(w.canon), N, K)
     L = q.lib()
+    nws = q.qgemm_workspace(2, M, K)
+    ws = torch.empty(nws, dtype=torch.uint8, device=dev())
     for _ in range(2):
-        st = L.q4q8_qgemm(1, q._ptr(Wd), N, K, q._ptr(X), 2, K + 24, M, q._ptr(Y), 3, N + 8, q._stream(X))
+        st = L.q4q8_qgemm(1, q._ptr(Wd), N, K, q._ptr(X), 2, K + 24, M, q._ptr(Y), 3, N + 8, q._ptr(ws), nws,
+                          q._stream(X))
         assert st == 0, q.last_error()
         first = Y.clone() if _ == 0 else first
     torch.cuda.synchronize()
