@@ -188,6 +188,8 @@ static int qgemm_impl(int fmt, const void* W, int64_t N, int64_t K, const void* 
   if (ydt != Q4Q8_F16 && ydt != Q4Q8_BF16 && ydt != Q4Q8_F32)
     return fail(Q4Q8_ERR_UNSUPPORTED, "qgemm: output dtype %d", ydt);
   if (M < 1 || M > (1LL << 30)) return fail(Q4Q8_ERR_INVALID_ARG, "qgemm: M=%lld", (long long)M);
+  if (((M + 63) / 64) * ((N + 63) / 64) >= (1LL << 23))
+    return fail(Q4Q8_ERR_UNSUPPORTED, "qgemm: M x N too large for one launch (split it)");
   if (!W || !X || !Y) return fail(Q4Q8_ERR_INVALID_ARG, "qgemm: null pointer");
   if (ldx < K || ldy < N) return fail(Q4Q8_ERR_INVALID_ARG, "qgemm: ldx < K or ldy < N");
   if (ldx > (1LL << 22)) return fail(Q4Q8_ERR_UNSUPPORTED, "qgemm: ldx=%lld beyond 2^22", (long long)ldx);
@@ -228,7 +230,8 @@ int q4q8_moe_route(const float* logits, int T, int E, int topk, int32_t* ids, fl
   if (T < 1 || E < 1 || topk < 1 || topk > E)
     return fail(Q4Q8_ERR_INVALID_ARG, "moe_route: T=%d E=%d topk=%d", T, E, topk);
   if (E > 1024 || topk > 16) return fail(Q4Q8_ERR_UNSUPPORTED, "moe_route: E=%d > 1024 or topk=%d > 16", E, topk);
-  if ((int64_t)T * topk > (1LL << 30)) return fail(Q4Q8_ERR_UNSUPPORTED, "moe_route: T*topk too large");
+  if ((int64_t)T * topk > (1LL << 22))
+    return fail(Q4Q8_ERR_UNSUPPORTED, "moe_route: T*topk=%lld beyond 2^22", (long long)T * topk);
   clear_hip_error();
   return hip_status(q4q8::launch_moe_route(logits, T, E, topk, ids, gates, counts, offsets, sorted_pairs,
                                            (hipStream_t)stream),
@@ -251,8 +254,11 @@ int q4q8_moe_qgemm(int fmt, const void* Wg, const void* Wu, const void* Wd, int 
     return fail(Q4Q8_ERR_INVALID_ARG, "moe_qgemm: T=%d E=%d topk=%d", T, E, topk);
   if (H < 128 || F < 128 || H % 128 || F % 128)
     return fail(Q4Q8_ERR_INVALID_ARG, "moe_qgemm: H=%d and F=%d must be positive multiples of 128", H, F);
-  if ((int64_t)T * topk > (1LL << 30) || H > (1 << 20) || F > (1 << 20))
-    return fail(Q4Q8_ERR_UNSUPPORTED, "moe_qgemm: sizes beyond limits");
+  const int64_t P = (int64_t)T * topk;
+  if (P > (1LL << 22) || H > (1 << 20) || F > (1 << 20) || (int64_t)T * H * 2 >= (1LL << 31) ||
+      P * F * 2 >= (1LL << 31) || P * H * 2 >= (1LL << 31))
+    return fail(Q4Q8_ERR_UNSUPPORTED, "moe_qgemm: sizes beyond limits (T*topk <= 2^22, T*H, T*topk*F and "
+                                      "T*topk*H below 2^30 elements)");
   const size_t need = q4q8::moe_workspace_bytes(fmt, T, E, topk, H, F);
   if (!ws || ws_bytes < need)
     return fail(Q4Q8_ERR_WORKSPACE, "moe_qgemm: workspace holds %zu bytes, needs %zu", ws_bytes, need);

@@ -50,6 +50,10 @@ hipError_t launch_qgemv(int fmt, int xdt, GemvArgs args, int max_chunks, int max
                         const LaunchEvents& ev);
 
 size_t qgemm_workspace_bytes(int xdt, int64_t M, int64_t K);
+// bf16 [rows, cols] (row stride lds_) -> fp16 [rows, colsp] (row stride ldd),
+// columns cols .. colsp - 1 zero.  cols and colsp multiples of 8.
+hipError_t launch_bf16_to_f16(const void* src, int64_t lds_, void* dst, int64_t ldd, int64_t rows, int64_t cols,
+                              int64_t colsp, hipStream_t s, const LaunchEvents& ev);
 hipError_t launch_qgemm(int fmt, int xdt, int ydt, const void* W, int64_t N, int64_t K, const void* X, int64_t ldx,
                         int64_t M, void* Y, int64_t ldy, void* ws, hipStream_t stream, const LaunchEvents& ev);
 

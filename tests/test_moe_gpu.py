@@ -1,0 +1,191 @@
+"""GPU parity of the MoE path against the CPU oracle.
+
+Routing and the permutation (ids, counts, offsets, sorted_pairs) must match
+bit for bit; gates within 2e-3 relative; h (the bf16 SwiGLU output, read back
+through h_out) within the first-order bound propagated from the per-dot-
+product tolerance; out within the bound propagated through the whole chain,
+and again, tighter, against the oracle fed the GPU's own h (down projection
+and combine checked on their own).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from util import act_tensor, bytes_tensor, dev, values
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def q():
+    import gemm_q4_q8_amd as q
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    q.lib()
+    return q
+
+
+def _route(q, logits, k):
+    L = torch.from_numpy(np.ascontiguousarray(logits, dtype=np.float32)).to(dev())
+    got = q.moe_route(L, k)
+    torch.cuda.synchronize()
+    return [a.cpu().numpy() for a in got]
+
+
+def _check_route(logits, k, got):
+    ids, gates, counts, offsets, sp = got
+    rid, rg = oracle.moe_route(logits, k)
+    rc, ro, rsp = oracle.moe_sort(rid, logits.shape[1])
+    assert np.array_equal(ids, rid), "ids differ"
+    assert np.array_equal(counts, rc), "counts differ"
+    assert np.array_equal(offsets, ro), "offsets differ"
+    assert np.array_equal(sp, rsp), "sorted_pairs differ"
+    assert np.all(np.abs(gates - rg) <= 2e-3 * rg + 1e-5), np.abs(gates - rg).max()
+
+
+ROUTE_CASES = [(512, 128, 8), (37, 10, 3), (1, 1, 1), (5, 16, 16), (64, 65, 4), (300, 1024, 16),
+               (1000, 64, 1), (3, 200, 7)]
+
+
+@pytest.mark.parametrize("T,E,k", ROUTE_CASES)
+def test_route_parity(q, T, E, k):
+    logits = synth.router_logits(synth.rng_for(70, T * 7 + E * 3 + k), T, E)
+    _check_route(logits, k, _route(q, logits, k))
+
+
+def test_route_ties_and_infinities(q):
+    """Many exact ties (integer logits), a row of equal values, -inf entries
+    (a row keeps two finite logits: with every selected logit -inf the
+    softmax is undefined)."""
+    rng = synth.rng_for(71, 0)
+    logits = rng.integers(-2, 3, size=(200, 40)).astype(np.float32)
+    logits[5] = 0.0
+    logits[6, ::3] = -np.inf
+    logits[7] = -np.inf
+    logits[7, [3, 30]] = [1.0, -5.0]
+    _check_route(logits, 6, _route(q, logits, 6))
+
+
+def test_route_many_pairs(q):
+    """65536 pairs: every wave of the sort handles several rounds of 64."""
+    logits = synth.router_logits(synth.rng_for(72, 0), 8192, 128)
+    _check_route(logits, 8, _route(q, logits, 8))
+
+
+def _stack(q, fmt, ws, n, k):
+    return torch.cat([q.repack(fmt, bytes_tensor(w.canon), n, k) for w in ws])
+
+
+def _run_moe(q, fmt, logits, x, wg, wu, wd, k, H, F):
+    E = len(wg)
+    Wg, Wu, Wd = _stack(q, fmt, wg, F, H), _stack(q, fmt, wu, F, H), _stack(q, fmt, wd, H, F)
+    L = torch.from_numpy(logits).to(dev())
+    ids, gates, counts, offsets, sp = q.moe_route(L, k)
+    T = logits.shape[0]
+    h = torch.full((T * k, F), float("nan"), dtype=torch.bfloat16, device=dev())
+    out = q.moe_qgemm(fmt, Wg, Wu, Wd, E, H, F, act_tensor(x), k, gates, offsets, sp, h_out=h)
+    torch.cuda.synchronize()
+    return dict(ids=ids.cpu().numpy(), gates=gates.cpu().numpy(), offsets=offsets.cpu().numpy(),
+                sp=sp.cpu().numpy(), h=values(h), out=out.cpu().numpy().astype(np.float64))
+
+
+def _check_moe(fmt, logits, x, wg, wu, wd, k, H, F, got, what):
+    cg, cu, cd = [w.canon for w in wg], [w.canon for w in wu], [w.canon for w in wd]
+    r = oracle.moe(fmt, cg, cu, cd, x.values, logits, k, H, F)
+    assert np.array_equal(got["ids"], r["ids"]) and np.array_equal(got["sp"], r["sorted_pairs"])
+    hb = oracle.h_bound(r)
+    herr = np.abs(got["h"] - r["h"])
+    assert np.all(np.isfinite(got["h"])), f"{what}: h not finite"
+    assert np.all(herr <= hb), f"{what}: h err/bound {(herr / hb).max():.3g}"
+    ob = oracle.moe_out_bound(fmt, cd, r, r["ids"], r["gates"], r["sorted_pairs"], H, F, hb)
+    oerr = np.abs(got["out"] - r["out"])
+    assert np.all(oerr <= ob), f"{what}: out err/bound {(oerr / ob).max():.3g}"
+    # Down projection + combine on their own: the oracle takes the GPU's h.
+    r2 = oracle.moe_ffn(fmt, cg, cu, cd, x.values, r["ids"], r["gates"], r["sorted_pairs"], H, F,
+                        h_override=got["h"])
+    ob2 = oracle.moe_out_bound(fmt, cd, r2, r["ids"], r["gates"], r["sorted_pairs"], H, F,
+                               np.zeros_like(got["h"]))
+    oerr2 = np.abs(got["out"] - r2["out"])
+    assert np.all(oerr2 <= ob2), f"{what}: isolated out err/bound {(oerr2 / ob2).max():.3g}"
+
+
+MOE_CASES = [
+    # fmt, xdt, T, E, k, H, F
+    (synth.Q4_0, synth.BF16, 40, 8, 2, 256, 128),
+    (synth.Q8_0, synth.F16, 33, 5, 3, 384, 256),
+    (synth.Q4_0, synth.BF16, 100, 16, 4, 256, 384),
+    (synth.Q4_0, synth.F16, 200, 4, 2, 128, 256),    # ~100 pairs per expert: two row tiles
+    (synth.Q8_0, synth.BF16, 10, 16, 1, 128, 128),   # most experts empty
+    (synth.Q4_0, synth.BF16, 1, 3, 3, 128, 128),     # one token
+]
+
+
+@pytest.mark.parametrize("fmt,xdt,T,E,k,H,F", MOE_CASES)
+def test_moe_parity(q, fmt, xdt, T, E, k, H, F):
+    seed = 80 + T + E
+    logits = synth.router_logits(synth.rng_for(seed, 0), T, E)
+    x = synth.activation(synth.rng_for(seed, 1), (T, H), xdt)
+    wg = [synth.q_weight(synth.rng_for(seed, 1000 + e), fmt, F, H) for e in range(E)]
+    wu = [synth.q_weight(synth.rng_for(seed, 2000 + e), fmt, F, H) for e in range(E)]
+    wd = [synth.q_weight(synth.rng_for(seed, 3000 + e), fmt, H, F) for e in range(E)]
+    got = _run_moe(q, fmt, logits, x, wg, wu, wd, k, H, F)
+    _check_moe(fmt, logits, x, wg, wu, wd, k, H, F, got, f"moe fmt{fmt} T{T} E{E} k{k} H{H} F{F}")
+
+
+def test_moe_deterministic(q):
+    T, E, k, H, F = 64, 8, 2, 256, 128
+    logits = synth.router_logits(synth.rng_for(90, 0), T, E)
+    x = synth.activation(synth.rng_for(90, 1), (T, H), synth.BF16)
+    wg = [synth.q_weight(synth.rng_for(90, 1000 + e), synth.Q4_0, F, H) for e in range(E)]
+    wu = [synth.q_weight(synth.rng_for(90, 2000 + e), synth.Q4_0, F, H) for e in range(E)]
+    wd = [synth.q_weight(synth.rng_for(90, 3000 + e), synth.Q4_0, H, F) for e in range(E)]
+    a = _run_moe(q, synth.Q4_0, logits, x, wg, wu, wd, k, H, F)
+    b = _run_moe(q, synth.Q4_0, logits, x, wg, wu, wd, k, H, F)
+    assert np.array_equal(a["out"], b["out"]) and np.array_equal(a["h"], b["h"])
+
+
+def test_moe_full_size_sampled(q):
+    """The MoE workload (T 512, E 128, top-8, H 2048, F 768, Q4_0, bf16 X) in
+    the benchmark's launch shape: routing bit-exact; h of every pair of four
+    sampled experts against the oracle; out of six sampled tokens against
+    the oracle's down projection and combine fed the GPU's h."""
+    cfg = synth.MOE
+    T, E, k, H, F = cfg["T"], cfg["E"], cfg["topk"], cfg["H"], cfg["F"]
+    logits, x, wg, wu, wd = synth.moe()
+    got = _run_moe(q, synth.Q4_0, logits, x, wg, wu, wd, k, H, F)
+    rid, rg = oracle.moe_route(logits, k)
+    rc, ro, rsp = oracle.moe_sort(rid, E)
+    assert np.array_equal(got["ids"], rid) and np.array_equal(got["sp"], rsp)
+    assert np.array_equal(got["offsets"], ro)
+    assert np.all(np.abs(got["gates"] - rg) <= 2e-3 * rg + 1e-5)
+    assert np.all(np.isfinite(got["out"]))
+
+    flat = rid.reshape(-1)
+    rng = np.random.default_rng(91)
+    for e in rng.choice(np.nonzero(rc)[0], 4, replace=False):
+        rows = np.arange(ro[e], ro[e + 1])            # sorted-order positions of expert e
+        toks = rsp[rows] // k
+        xe = x.values[toks]
+        Wg = oracle.dequant(synth.Q4_0, wg[e].canon, F, H)
+        Wu = oracle.dequant(synth.Q4_0, wu[e].canon, F, H)
+        r = dict(zg=xe @ Wg.T, zu=xe @ Wu.T, bg=np.abs(xe) @ np.abs(Wg).T, bu=np.abs(xe) @ np.abs(Wu).T)
+        r["h"] = oracle.silu(r["zg"]) * r["zu"]
+        hb = oracle.h_bound(r)
+        assert np.all(np.abs(got["h"][rows] - r["h"]) <= hb), f"expert {e}: h"
+
+    inv = np.empty(T * k, dtype=np.int64)
+    inv[rsp] = np.arange(T * k)
+    for t in rng.choice(T, 6, replace=False):
+        ref = np.zeros(H)
+        bound = np.full(H, 1e-5)
+        for j in range(k):
+            p = t * k + j
+            e = flat[p]
+            hrow = got["h"][inv[p]]
+            Wd = oracle.dequant(synth.Q4_0, wd[e].canon, H, F)
+            y = Wd @ hrow
+            by = np.abs(Wd) @ np.abs(hrow)
+            ref += rg[t, j] * y
+            bound += rg[t, j] * (2e-3 * by + 1e-5) + (2e-3 * rg[t, j] + 1e-5) * np.abs(y)
+        assert np.all(np.abs(got["out"][t] - ref) <= bound), f"token {t}: out"
