@@ -26,8 +26,9 @@ cpu_baseline: the fp64 NumPy oracle timed on the host on one decode step of
 the same layer (all seven matrices, M = 1).
 
 Other workloads (M = 2/4/8 layer steps, the single 2048x2048 GEMV, the Q8_0
-3B-shaped matrices, the prefill GEMM, the MoE layer) are reported under
-"workloads", each with its own algorithmic bytes / flops and time.
+3B-shaped matrices, the prefill GEMM at M = 512 and 2048, the MoE layer) are
+reported under "workloads", each with its own algorithmic bytes / flops and
+time.
 """
 from __future__ import annotations
 
@@ -299,7 +300,74 @@ def extra_workloads(q, torch, synth, ev: HipEvents, quick: bool):
         torch.cuda.empty_cache()
         out.append({"workload": f"q8_0 3B-shape 4 matrices M={M}", "sum_kernel_us": round(tot_t * 1e6, 2),
                     "GB/s": round(tot_b / tot_t / 1e9, 1)})
+    out += prefill_workloads(q, torch, synth, ev, quick)
+    out.append(moe_workload(q, torch, synth))
     return out
+
+
+def prefill_workloads(q, torch, synth, ev: HipEvents, quick: bool):
+    """Prefill GEMM Y[M, 12288] = X[M, 4096] W^T, Q4_0, bf16 in and out.  The
+    timed span of one call covers both of its kernels (bf16 -> fp16 pre-pass
+    and the GEMM), from the first dispatch's start to the last one's end."""
+    out = []
+    dev = torch.device("cuda:0")
+    for M in ([512] if quick else [512, 2048]):
+        w, x = synth.prefill(M)
+        W0 = q.repack(1, torch.from_numpy(w.canon).to(dev), w.N, w.K)
+        Ws = [W0] + [W0.clone() for _ in range(3)]
+        X = torch.from_numpy(x.bits.view("int16")).view(torch.bfloat16).to(dev)
+        Y = torch.empty((M, w.N), dtype=torch.bfloat16, device=dev)
+        wsp = torch.empty(q.qgemm_workspace(synth.BF16, M, w.K), dtype=torch.uint8, device=dev)
+        reps = 24
+        pairs = [(ev.create(), ev.create()) for _ in range(reps + 4)]
+        for i in range(reps + 4):
+            q.qgemm(1, Ws[i % 4], w.N, w.K, X, out=Y, ws=wsp, events=pairs[i])
+        d = sorted(ev.elapsed_ms(a, b) * 1e-3 for a, b in pairs[4:])
+        mean = sum(d) / len(d)
+        fl = 2.0 * M * w.N * w.K
+        out.append({"workload": f"q4_0 prefill gemm M={M} K={w.K} N={w.N} (bf16 in/out)",
+                    "call_us_mean": round(mean * 1e6, 2), "call_us_min": round(d[0] * 1e6, 2),
+                    "TFLOP/s": round(fl / mean / 1e12, 1),
+                    "mfma_frac": round(fl / mean / 1e12 / F16_MFMA_PEAK_TFLOPS, 4)})
+        del Ws, W0, X, Y, wsp
+        torch.cuda.empty_cache()
+    return out
+
+
+def moe_workload(q, torch, synth):
+    """MoE layer: 512 bf16 tokens, 128 Q4_0 experts (gate/up 768x2048, down
+    2048x768), top-8.  One step = route + sort + expert GEMMs + combine,
+    timed with stream events (launch gaps included).  Expert weights are
+    340 MB (more than the Infinity Cache): the layer is HBM-bound, so the
+    roofline is max(weight bytes / 8 TB/s, flops / 2.5 PFLOP/s)."""
+    dev = torch.device("cuda:0")
+    cfg = synth.MOE
+    T, E, k, H, F = cfg["T"], cfg["E"], cfg["topk"], cfg["H"], cfg["F"]
+    logits, x, wg, wu, wd = synth.moe()
+
+    def stack(ws, n, kk):
+        return torch.cat([q.repack(1, torch.from_numpy(w.canon).to(dev), n, kk) for w in ws])
+
+    Wg, Wu, Wd = stack(wg, F, H), stack(wu, F, H), stack(wd, H, F)
+    L = torch.from_numpy(logits).to(dev)
+    X = torch.from_numpy(x.bits.view("int16")).view(torch.bfloat16).to(dev)
+    out = torch.empty((T, H), dtype=torch.float32, device=dev)
+    wsp = torch.empty(q.moe_workspace(1, T, E, k, H, F), dtype=torch.uint8, device=dev)
+
+    def step(_):
+        ids, gates, counts, offsets, sp = q.moe_route(L, k)
+        q.moe_qgemm(1, Wg, Wu, Wd, E, H, F, X, k, gates, offsets, sp, out=out, ws=wsp)
+
+    dt = _time_launches(torch, step, 30)
+    fl = 2.0 * T * k * 3 * F * H
+    wbytes = 3 * E * q.repacked_bytes(1, F, H)
+    roof = max(wbytes / (HBM_PEAK_GBS * 1e9), fl / (F16_MFMA_PEAK_TFLOPS * 1e12))
+    del Wg, Wu, Wd, wsp
+    torch.cuda.empty_cache()
+    return {"workload": f"q4_0 moe T={T} E={E} top{k} H={H} F={F} (bf16 tokens)", "step_us": round(dt * 1e6, 2),
+            "TFLOP/s": round(fl / dt / 1e12, 1), "mfma_frac": round(fl / dt / 1e12 / F16_MFMA_PEAK_TFLOPS, 4),
+            "weight_GB/s": round(wbytes / dt / 1e9, 1), "roofline_us": round(roof * 1e6, 2),
+            "roofline_frac": round(roof / dt, 4)}
 
 
 def main():

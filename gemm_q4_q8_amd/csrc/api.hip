@@ -193,8 +193,10 @@ static int qgemm_impl(int fmt, const void* W, int64_t N, int64_t K, const void* 
   if (!W || !X || !Y) return fail(Q4Q8_ERR_INVALID_ARG, "qgemm: null pointer");
   if (ldx < K || ldy < N) return fail(Q4Q8_ERR_INVALID_ARG, "qgemm: ldx < K or ldy < N");
   if (ldx > (1LL << 22)) return fail(Q4Q8_ERR_UNSUPPORTED, "qgemm: ldx=%lld beyond 2^22", (long long)ldx);
-  if (!aligned(W, 16) || !aligned(X, 16) || !aligned(Y, 16) || ldx % 8 || ldy % 8)
-    return fail(Q4Q8_ERR_ALIGNMENT, "qgemm: pointers must be 16-byte aligned, ldx and ldy multiples of 8");
+  const int ysz = ydt == Q4Q8_F32 ? 4 : 2;
+  if (!aligned(W, 16) || !aligned(X, 16) || !aligned(Y, ysz) || ldx % 8)
+    return fail(Q4Q8_ERR_ALIGNMENT,
+                "qgemm: W and X must be 16-byte aligned, ldx a multiple of 8, Y aligned to its element size");
   const size_t need = q4q8::qgemm_workspace_bytes(xdt, M, K);
   if (need && (!ws || ws_bytes < need))
     return fail(Q4Q8_ERR_WORKSPACE, "qgemm: workspace holds %zu bytes, needs %zu", ws ? ws_bytes : 0, need);

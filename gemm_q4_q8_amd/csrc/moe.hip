@@ -41,48 +41,49 @@ __device__ __forceinline__ bool route_before(float v, int i, float bv, int bi) {
   return v > bv || (v == bv && i < bi);
 }
 
+// NS: 64-expert slots per lane (E <= 64 NS).  Branch-free: out-of-range and
+// taken experts compare as never better.
+template <int NS>
 __global__ __launch_bounds__(256) void moe_topk_kernel(const float* __restrict__ logits, int T, int E, int topk,
                                                        int32_t* __restrict__ ids, float* __restrict__ gates) {
   const int lane = threadIdx.x & 63;
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= T) return;   // whole wave
-  const float* row = logits + (int64_t)t * E;
   // Lane holds experts lane + 64 i.  NaN ranks as -inf.
-  float v[kRouteMaxE / 64];
+  const __amdgpu_buffer_rsrc_t rs = uniform_rsrc(logits + (int64_t)t * E, E * 4);
+  float v[NS];
 #pragma unroll
-  for (int i = 0; i < kRouteMaxE / 64; ++i) {
-    const int e = lane + 64 * i;
-    const float x = e < E ? row[e] : -INFINITY;
-    v[i] = x != x ? -INFINITY : x;
+  for (int i = 0; i < NS; ++i) {
+    const float x = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, (lane + 64 * i) * 4, 0, 0));
+    v[i] = (lane + 64 * i < E && x == x) ? x : -INFINITY;
   }
-  uint32_t taken = 0;
+  uint32_t live = 0;   // bit i: expert lane + 64 i exists and is not taken yet
+#pragma unroll
+  for (int i = 0; i < NS; ++i) live |= (lane + 64 * i < E ? 1u : 0u) << i;
   float v0 = 0.0f, my_exp = 0.0f, sum = 0.0f;
   for (int j = 0; j < topk; ++j) {
     float bv = -INFINITY;
     int bi = 0x7fffffff;
 #pragma unroll
-    for (int i = 0; i < kRouteMaxE / 64; ++i) {
-      const int e = lane + 64 * i;
-      if (e < E && !((taken >> i) & 1u) && route_before(v[i], e, bv, bi)) {
-        bv = v[i];
-        bi = e;
-      }
+    for (int i = 0; i < NS; ++i) {
+      const bool better = ((live >> i) & 1u) && route_before(v[i], lane + 64 * i, bv, bi);
+      bv = better ? v[i] : bv;
+      bi = better ? lane + 64 * i : bi;
     }
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) {
       const float ov = __shfl_xor(bv, off);
       const int oi = __shfl_xor(bi, off);
-      if (route_before(ov, oi, bv, bi)) {
-        bv = ov;
-        bi = oi;
-      }
+      const bool better = route_before(ov, oi, bv, bi);
+      bv = better ? ov : bv;
+      bi = better ? oi : bi;
     }
     // Every lane now holds the winner; its owner marks it taken.
-    if ((bi & 63) == lane) taken |= 1u << (bi >> 6);
-    if (j == 0) v0 = bv;
+    live &= ~(((bi & 63) == lane ? 1u : 0u) << (bi >> 6));
+    v0 = j == 0 ? bv : v0;
     const float ex = expf(bv - v0);
     sum += ex;
-    if (lane == j) my_exp = ex;
+    my_exp = lane == j ? ex : my_exp;
     if (lane == 0) ids[(int64_t)t * topk + j] = bi;
   }
   if (lane < topk) gates[(int64_t)t * topk + lane] = my_exp / sum;
@@ -95,24 +96,25 @@ __global__ __launch_bounds__(256) void moe_topk_kernel(const float* __restrict__
 __global__ __launch_bounds__(1024) void moe_sort_kernel(const int32_t* __restrict__ ids, int P, int E,
                                                         int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
                                                         int32_t* __restrict__ sorted_pairs) {
-  __shared__ int hist[kSortWaves][kRouteMaxE];   // per-wave counts, then per-wave bases
+  __shared__ int hist_s[kSortWaves * kRouteMaxE];   // [wave][expert]: counts, then bases
+  int* hist = hist_s;
   __shared__ int wave_sum[kSortWaves];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int chunk = ((P + kSortWaves - 1) / kSortWaves + 63) / 64 * 64;
   const int p0 = w * chunk, p1 = min(P, p0 + chunk);
 
-  for (int i = tid; i < kSortWaves * kRouteMaxE; i += 1024) (&hist[0][0])[i] = 0;
+  for (int i = tid; i < kSortWaves * E; i += 1024) hist[i] = 0;
   __syncthreads();
   for (int p = p0 + lane; p < p1; p += 64) {
     const int e = min(max(ids[p], 0), E - 1);
-    atomicAdd(&hist[w][e], 1);
+    atomicAdd(&hist[w * E + e], 1);
   }
   __syncthreads();
 
   // Thread e: total count, exclusive scan over experts, per-wave bases.
   int tot = 0;
   if (tid < E)
-    for (int k = 0; k < kSortWaves; ++k) tot += hist[k][tid];
+    for (int k = 0; k < kSortWaves; ++k) tot += hist[k * E + tid];
   int incl = tot;
 #pragma unroll
   for (int off = 1; off < 64; off <<= 1) {
@@ -129,8 +131,8 @@ __global__ __launch_bounds__(1024) void moe_sort_kernel(const int32_t* __restric
     offsets[tid] = excl;
     int run = excl;
     for (int k = 0; k < kSortWaves; ++k) {
-      const int c = hist[k][tid];
-      hist[k][tid] = run;
+      const int c = hist[k * E + tid];
+      hist[k * E + tid] = run;
       run += c;
     }
   }
@@ -151,16 +153,21 @@ __global__ __launch_bounds__(1024) void moe_sort_kernel(const int32_t* __restric
       match &= ((e >> b) & 1) ? ones : ~ones;
     }
     const int rank = __popcll(match & below);
-    const int pos = hist[w][e] + rank;
+    const int pos = hist[w * E + e] + rank;
     if (active) sorted_pairs[pos] = p;
     const int last = 63 - __clzll(match);
-    if (active && lane == last) hist[w][e] = pos + 1;
+    if (active && lane == last) hist[w * E + e] = pos + 1;
   }
 }
 
 hipError_t launch_moe_route(const float* logits, int T, int E, int topk, int32_t* ids, float* gates,
                             int32_t* counts, int32_t* offsets, int32_t* sorted_pairs, hipStream_t stream) {
-  moe_topk_kernel<<<dim3((unsigned)((T + 3) / 4)), dim3(256), 0, stream>>>(logits, T, E, topk, ids, gates);
+  const dim3 grid((unsigned)((T + 3) / 4)), block(256);
+  if (E <= 64) moe_topk_kernel<1><<<grid, block, 0, stream>>>(logits, T, E, topk, ids, gates);
+  else if (E <= 128) moe_topk_kernel<2><<<grid, block, 0, stream>>>(logits, T, E, topk, ids, gates);
+  else if (E <= 256) moe_topk_kernel<4><<<grid, block, 0, stream>>>(logits, T, E, topk, ids, gates);
+  else if (E <= 512) moe_topk_kernel<8><<<grid, block, 0, stream>>>(logits, T, E, topk, ids, gates);
+  else moe_topk_kernel<16><<<grid, block, 0, stream>>>(logits, T, E, topk, ids, gates);
   moe_sort_kernel<<<dim3(1), dim3(1024), 0, stream>>>(ids, T * topk, E, counts, offsets, sorted_pairs);
   return hipGetLastError();
 }

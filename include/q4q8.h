@@ -175,7 +175,7 @@ size_t q4q8_qgemm_workspace(int xdt, int64_t M, int64_t K);
  *   X:   device, BF16 or F16 (xdt), row m at X + m*ldx; 16-byte aligned,
  *        ldx % 8 == 0, K <= ldx <= 2^22.
  *   Y:   device, ydt = BF16, F16 or F32, row m at Y + m*ldy, ldy >= N,
- *        ldy % 8 == 0 and 16-byte aligned.
+ *        aligned to its element size.
  *   ws:  device workspace of >= q4q8_qgemm_workspace(xdt, M, K) bytes,
  *        256-byte aligned (may be NULL when that is 0); clobbered.
  * fp32 accumulation on fp16 matrix-core operands (weights dequantised and

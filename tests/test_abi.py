@@ -146,7 +146,7 @@ def test_qgemm_validation(q):
     assert ok["nws"] == 17 * 256 * 2 // 256 * 256 + 256 * (17 * 256 * 2 % 256 != 0)
     assert q.qgemm_workspace(1, 17, 256) == 0 and q.qgemm_workspace(5, 17, 256) == 0
     for over, want in [(dict(ydt=7), -2), (dict(xdt=3), -2), (dict(M=0), -1), (dict(ldx=128), -1),
-                       (dict(ldy=32), -1), (dict(Y=0x3008), -4), (dict(ldx=260), -4), (dict(K=100), -1),
+                       (dict(ldy=32), -1), (dict(Y=0x3001), -4), (dict(ydt=3, Y=0x3002), -4), (dict(ldx=260), -4), (dict(K=100), -1),
                        (dict(ws=0), -3), (dict(nws=ok["nws"] - 1), -3), (dict(ws=0x100010), -4)]:
         a = dict(ok)
         a.update(over)

@@ -27,7 +27,7 @@ def _compare(got, ref, bound, ydt, what):
 
 
 SMALL = [(1, 16, 128), (17, 48, 160), (64, 256, 256), (100, 200, 1056), (128, 192, 4096),
-         (300, 400, 512), (257, 1000, 384), (129, 64, 32), (300, 1536, 256), (70, 3072, 160)]
+         (300, 400, 512), (257, 1000, 384), (129, 64, 32), (300, 1536, 256), (70, 3072, 160), (70, 100, 352)]
 
 
 @pytest.mark.parametrize("fmt,xdt,ydt", [(synth.Q4_0, synth.BF16, "bf16"), (synth.Q4_0, synth.F16, "f32"),
