@@ -12,19 +12,21 @@
 //   moe_sort_kernel   one workgroup: per-wave histograms, scan, then each
 //                     wave places its pairs in order (ranks from ballots), so
 //                     the order is stable and bit-exact.
-//   moe_gateup_kernel tile engine with two weight matrices (gate, up) over
-//                     the expert's rows gathered from X by token; epilogue
-//                     h = silu(z_gate) * z_up, rounded to bf16 (h's storage
-//                     precision) and kept as fp16 for the down GEMM (exact).
-//   moe_down_kernel   tile engine over the contiguous h rows of the expert;
+//   moe_stream_kernel gate+up: the expert's rows gathered from X by token
+//                     into LDS, gate and up weights streamed per wave;
+//                     epilogue h = silu(z_gate) * z_up, rounded to bf16 (h's
+//                     storage precision) and kept as fp16 for the down GEMM
+//                     (exact).  down: the expert's contiguous h rows in LDS,
 //                     y_p stored as fp16 at its pair index p.
 //   moe_combine_kernel out[t] = sum_j g[t, j] y_{t k + j} in fp32, j in order:
 //                     deterministic (no atomics).
 #include "q4q8_dev.h"
 #include "q4q8_internal.h"
-#include "qgemm_core.h"
+#include "qgemm_core.h"   // static_for, x_slot, kOOB
 
 #include <math.h>
+
+#include <algorithm>
 
 namespace q4q8 {
 
@@ -172,169 +174,236 @@ hipError_t launch_moe_route(const float* logits, int T, int E, int topk, int32_t
   return hipGetLastError();
 }
 
-// ---------------------------------------------------------------------------
-// Expert GEMMs
-// ---------------------------------------------------------------------------
-
-// Workgroup row index idx -> (expert e, first row r0 of the expert's segment)
-// over the experts' ceil(count / BM) row tiles in expert order.  Every wave
-// computes it (no barrier).  False when idx is past the last tile.
-__device__ __forceinline__ bool find_row_tile(const int32_t* __restrict__ offsets, int E, int BM, int idx, int& e_out,
-                                              int& r0_out) {
-  const int lane = threadIdx.x & 63;
-  int cum = 0;
-  for (int base = 0; base < E; base += 64) {
-    const int e = base + lane;
-    const int c = e < E ? offsets[e + 1] - offsets[e] : 0;
-    const int nt = (max(c, 0) + BM - 1) / BM;
-    int incl = nt;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-      const int o = __shfl_up(incl, off);
-      if (lane >= off) incl += o;
-    }
-    const int lo = cum + incl - nt;
-    const uint64_t hit = __ballot(nt > 0 && idx >= lo && idx < cum + incl);
-    if (hit) {
-      const int src = __ffsll((unsigned long long)hit) - 1;
-      e_out = __shfl(e, src);
-      r0_out = (idx - __shfl(lo, src)) * BM;
-      return true;
-    }
-    cum += __shfl(incl, 63);
-  }
-  return false;
-}
-
 // silu(z) = z / (1 + exp(-z)), fp32.
 __device__ __forceinline__ float silu_f32(float z) { return z / (1.0f + expf(-z)); }
 
-// Gate+up for one row tile of one expert and 64 NT h columns (per wave
-// 16 NT).  x16: fp16 [T, H]; h16: fp16 [P, F] and h_out: bf16 [P, F] (may be
-// null), both in sorted-pair order.
-template <int FMT, int MT, int NT, int S>
-__global__ __launch_bounds__(512) void moe_gateup_kernel(const uint8_t* __restrict__ Wg, const uint8_t* __restrict__ Wu,
-                                                         int64_t wstride, int E, int H, int F,
-                                                         const uint16_t* __restrict__ x16, int T, int topk,
-                                                         const int32_t* __restrict__ offsets,
-                                                         const int32_t* __restrict__ sorted_pairs,
-                                                         uint16_t* __restrict__ h16, uint16_t* __restrict__ h_out) {
-  using C = TileCfg<FMT, MT, NT, 2, S>;
-  __shared__ __attribute__((aligned(1024))) uint16_t xs[C::LDS_HALFS];
-  int e, r0;
-  if (!find_row_tile(offsets, E, C::BM, blockIdx.y, e, r0)) return;   // uniform over the workgroup
+// ---------------------------------------------------------------------------
+// Expert GEMMs, streaming form (few rows per expert)
+//
+// At a few dozen rows per expert the expert GEMMs are weight streams, and a
+// barrier per 128-wide chunk leaves them latency-bound.  Here a workgroup
+// takes one expert and a range of its output tiles:
+//   * the expert's rows (64 at a time) are copied once into LDS through the
+//     buffer loads' LDS path -- all of K when it fits in 128 KB, else in
+//     phases of 1024 columns -- in the same XOR-swizzled chunk layout as the
+//     tile engine;
+//   * each wave then streams its own weight tiles (NT at a time, both gate
+//     and up for the gate+up pass) through a P-stage register ring that runs
+//     across tile groups, K phases and row tiles, with no barrier except
+//     around the LDS reloads;
+//   * at the end of each tile group the epilogue stores h = silu(g) * u
+//     (gate+up) or y at its pair row (down).
+// Every step issues the same weight loads (the ring runs past the end on
+// harmless re-reads), so the compiler's wait counts stay exact.
+// ---------------------------------------------------------------------------
+enum { kGateUp = 0, kDown = 1 };
+constexpr int kStreamBM = 64;
+constexpr int kStreamKP = 1024;   // LDS phase: 64 rows x 1024 fp16 = 128 KB
 
+template <int FMT, int MODE, int NT, int P>
+__global__ __launch_bounds__(512) void moe_stream_kernel(
+    const uint8_t* __restrict__ W0, const uint8_t* __restrict__ W1, int64_t wstride, int N, int K,
+    const uint16_t* __restrict__ src, int src_rows, int T, int topk, int Ptot,
+    const int32_t* __restrict__ offsets, const int32_t* __restrict__ sorted_pairs, uint16_t* __restrict__ out16,
+    uint16_t* __restrict__ h_out, int tiles_per_wave, int groups) {
+  constexpr int NW = MODE == kGateUp ? 2 : 1;
+  constexpr int MT = 4, BM = kStreamBM;
+  constexpr int REC = Fmt<FMT>::kRecBytes;
+  constexpr int CODE = Fmt<FMT>::kCodeBytes;
+  constexpr int NV = FMT == kQ4_0 ? 1 : 2;
+  __shared__ __attribute__((aligned(1024))) uint16_t xs[BM * kStreamKP];
+
+  const int e = blockIdx.y;
+  const int seg = offsets[e];
+  const int cnt = offsets[e + 1] - seg;
+  if (cnt <= 0) return;   // uniform over the workgroup
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int nw = wave & 3;
   const int r = lane & 15, g = lane >> 4;
-  const int seg = offsets[e];
-  const int valid = min(C::BM, offsets[e + 1] - seg - r0);
-  const int nchunks = H / kChunkK;
-  const int tiles = F / kTileRows;
+  const int nchunks = K / kChunkK;
+  const int tiles = N / kTileRows;
+  const int kpc = K < kStreamKP ? K : kStreamKP;     // columns per LDS phase
+  const int cpp = kpc / kChunkK;                      // chunks per phase
+  const int n_rt = (cnt + BM - 1) / BM;
+  const int total = n_rt * groups * nchunks;
 
-  const int t0 = (blockIdx.x * 4 + nw) * NT;
-  const int tv = tiles - t0 < NT ? (tiles - t0 > 0 ? tiles - t0 : 0) : NT;
-  const int64_t woff = e * wstride + (int64_t)(t0 < tiles ? t0 : 0) * nchunks * C::REC;
-  const __amdgpu_buffer_rsrc_t wres[2] = {uniform_rsrc(Wg + woff, tv * nchunks * C::REC),
-                                          uniform_rsrc(Wu + woff, tv * nchunks * C::REC)};
-  // Rows gathered by token: row i of the tile is pair sorted_pairs[seg + r0 + i].
-  const __amdgpu_buffer_rsrc_t xres = uniform_rsrc(x16, (int)((int64_t)T * H * 2));
-  uint32_t xv[C::XLOADS];
-#pragma unroll
-  for (int p = 0; p < C::XLOADS; ++p) {
-    int row, cg;
-    x_slot(p, tid, row, cg);
-    uint32_t v = kOOB;
-    if (row < valid) {
-      const int tok = min(sorted_pairs[seg + r0 + row] / topk, T - 1);
-      v = (uint32_t)(((int64_t)tok * H + cg * 8) * 2);
-    }
-    xv[p] = v;
-  }
+  // This wave's tiles: t_w0 .. t_w0 + tv - 1 of the expert's matrix.
+  const int t_w0 = (blockIdx.x * 8 + wave) * tiles_per_wave;
+  const int tv = min(max(tiles - t_w0, 0), tiles_per_wave);
+  const int64_t woff = e * wstride + (int64_t)(tv > 0 ? t_w0 : 0) * nchunks * REC;
+  __amdgpu_buffer_rsrc_t wres[NW];
+  wres[0] = uniform_rsrc(W0 + woff, tv * nchunks * REC);
+  if constexpr (NW == 2) wres[1] = uniform_rsrc(W1 + woff, tv * nchunks * REC);
 
-  float4_t acc[2 * MT * NT];
-  tile_mainloop<FMT, MT, NT, 2, S, false>(wres, tv, H, nchunks, xres, xv, xs, acc);
-  float4_t kept[2 * (MT / 2) * NT];
-  khalf_reduce<MT, NT, 2>(acc, (float4_t*)xs, kept);
-
-  const int rk = (wave >> 2) * (MT / 2) * 16 + 4 * g;
+  struct WStage {
+    u32x4_t codes[NW][NT][NV];
+    u32x2_t sc[NW][NT];
+  };
+  // Load cursor: (group lg, chunk lc); it advances one chunk per step and
+  // wraps over groups (and, implicitly, row tiles: the weights do not depend
+  // on the row tile).
+  int lg = 0, lc = 0;
+  auto load_next = [&](WStage& s) __attribute__((always_inline)) {
 #pragma unroll
-  for (int t = 0; t < NT; ++t) {
-    const int n = (t0 + t) * kTileRows + r;
-    if (n < F) {
+    for (int t = 0; t < NT; ++t) {
+      const int lt = lg * NT + t;
+      const int so = (lt * nchunks + lc) * REC;
+      const bool ok = lt < tv;
 #pragma unroll
-      for (int i = 0; i < MT / 2; ++i)
+      for (int w = 0; w < NW; ++w) {
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          const int row = rk + i * 16 + k;
-          if (row < valid) {
-            const float zg = kept[i * NT + t][k], zu = kept[((MT / 2) + i) * NT + t][k];
-            const __bf16 hb = (__bf16)(silu_f32(zg) * zu);
-            const int64_t idx = (int64_t)(seg + r0 + row) * F + n;
-            h16[idx] = __builtin_bit_cast(uint16_t, (_Float16)(float)hb);
-            if (h_out) h_out[idx] = __builtin_bit_cast(uint16_t, hb);
-          }
-        }
-    }
-  }
-}
-
-// Down projection for one row tile of one expert and 64 NT output columns:
-// y16[p] (fp16 [P, H], pair order) = h16 rows (contiguous per expert) W_d^T.
-template <int FMT, int MT, int NT, int S>
-__global__ __launch_bounds__(512) void moe_down_kernel(const uint8_t* __restrict__ Wd, int64_t wstride, int E, int H,
-                                                       int F, const uint16_t* __restrict__ h16, int P,
-                                                       const int32_t* __restrict__ offsets,
-                                                       const int32_t* __restrict__ sorted_pairs,
-                                                       uint16_t* __restrict__ y16) {
-  using C = TileCfg<FMT, MT, NT, 1, S>;
-  __shared__ __attribute__((aligned(1024))) uint16_t xs[C::LDS_HALFS];
-  int e, r0;
-  if (!find_row_tile(offsets, E, C::BM, blockIdx.y, e, r0)) return;
-
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int nw = wave & 3;
-  const int r = lane & 15, g = lane >> 4;
-  const int seg = offsets[e];
-  const int valid = min(C::BM, offsets[e + 1] - seg - r0);
-  const int nchunks = F / kChunkK;
-  const int tiles = H / kTileRows;
-
-  const int t0 = (blockIdx.x * 4 + nw) * NT;
-  const int tv = tiles - t0 < NT ? (tiles - t0 > 0 ? tiles - t0 : 0) : NT;
-  const __amdgpu_buffer_rsrc_t wres[1] = {
-      uniform_rsrc(Wd + e * wstride + (int64_t)(t0 < tiles ? t0 : 0) * nchunks * C::REC, tv * nchunks * C::REC)};
-  const __amdgpu_buffer_rsrc_t xres = uniform_rsrc(h16, (int)((int64_t)P * F * 2));
-  uint32_t xv[C::XLOADS];
-#pragma unroll
-  for (int p = 0; p < C::XLOADS; ++p) {
-    int row, cg;
-    x_slot(p, tid, row, cg);
-    xv[p] = row < valid ? (uint32_t)(((int64_t)(seg + r0 + row) * F + cg * 8) * 2) : kOOB;
-  }
-
-  float4_t acc[MT * NT];
-  tile_mainloop<FMT, MT, NT, 1, S, false>(wres, tv, F, nchunks, xres, xv, xs, acc);
-  float4_t kept[(MT / 2) * NT];
-  khalf_reduce<MT, NT, 1>(acc, (float4_t*)xs, kept);
-
-  const int rk = (wave >> 2) * (MT / 2) * 16 + 4 * g;
-#pragma unroll
-  for (int i = 0; i < MT / 2; ++i)
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const int row = rk + i * 16 + k;
-      if (row < valid) {
-        const int64_t pair = min(max(sorted_pairs[seg + r0 + row], 0), P - 1);
-#pragma unroll
-        for (int t = 0; t < NT; ++t) {
-          const int n = (t0 + t) * kTileRows + r;
-          if (n < H) y16[pair * H + n] = __builtin_bit_cast(uint16_t, (_Float16)kept[i * NT + t][k]);
-        }
+        for (int v = 0; v < NV; ++v)
+          s.codes[w][t][v] =
+              __builtin_amdgcn_raw_buffer_load_b128(wres[w], ok ? (uint32_t)(v * 1024 + lane * 16) : kOOB, so, 0);
+        s.sc[w][t] = __builtin_amdgcn_raw_buffer_load_b64(wres[w], ok ? (uint32_t)(CODE + r * 8) : kOOB, so, 0);
       }
     }
+    if (++lc == nchunks) {
+      lc = 0;
+      if (++lg == groups) lg = 0;
+    }
+  };
+
+  // Activation rows of row tile rt, LDS phase kph -> xs.  Copy p of this
+  // thread fills slot 512 p + tid of the phase: chunk slot / (BM 16), then
+  // row / column group as in the tile engine.
+  const __amdgpu_buffer_rsrc_t xres = uniform_rsrc(src, (int)((int64_t)src_rows * K * 2));
+  auto load_x = [&](int rt, int kph) __attribute__((always_inline)) {
+    const int col0 = kph * kpc;
+    const int ncols = min(kpc, K - col0);
+    const int nslots = BM * ncols / 8;
+    int rowoff[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {   // slot % (BM 16) takes two values per thread: rows (h 512 + tid) / 16
+      const int row = (h * 512 + tid) >> 4;
+      const int i = rt * BM + row;
+      int base = -1;
+      if (i < cnt) {
+        if constexpr (MODE == kGateUp)
+          base = min(sorted_pairs[seg + i] / topk, T - 1);
+        else
+          base = seg + i;
+      }
+      rowoff[h] = base;
+    }
+    for (int p = 0; p * 512 < nslots; ++p) {
+      const int slot = p * 512 + tid;
+      const int cc = slot / (BM * 16), q = slot % (BM * 16);
+      const int row = q >> 4, cg = (q & 15) ^ (row & 15);
+      const int base = rowoff[p & 1];
+      const uint32_t v =
+          (base >= 0 && slot < nslots) ? (uint32_t)(((int64_t)base * K + col0 + cc * kChunkK + cg * 8) * 2) : kOOB;
+      uint16_t* dst = xs + (p * 512 + wave * 64) * 8;   // wave-uniform
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(xres, (__attribute__((address_space(3))) void*)dst, 16, v, 0, 0, 0);
+    }
+  };
+
+  float4_t acc[NW * NT * MT];
+#pragma unroll
+  for (int i = 0; i < NW * NT * MT; ++i) acc[i] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
+
+  // Products of chunk lcl of the loaded phase with one weight stage.
+  auto compute = [&](const WStage& s, int lcl) __attribute__((always_inline)) {
+    const uint16_t* xb = xs + lcl * BM * kChunkK;
+#pragma unroll
+    for (int j = 0; j < kBlocksPerChunk; ++j) {
+      half8_t b[NW][NT];
+#pragma unroll
+      for (int w = 0; w < NW; ++w)
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+          u32x4_t q;
+          if constexpr (FMT == kQ4_0) {
+            const uint32_t wd = s.codes[w][t][0][j];
+            q = deq_q4_f16(wd);
+          } else {
+            const uint32_t d0 = s.codes[w][t][j >> 1][2 * (j & 1)], d1 = s.codes[w][t][j >> 1][2 * (j & 1) + 1];
+            q = deq_q8<kF16>(d0, d1);
+          }
+          const uint32_t sbits = (j & 1) ? (s.sc[w][t][j >> 1] >> 16) : (s.sc[w][t][j >> 1] & 0xFFFFu);
+          const _Float16 sh = __builtin_bit_cast(_Float16, (uint16_t)sbits);
+          const half2_t s2 = {sh, sh};
+          b[w][t] = __builtin_bit_cast(half8_t, scale_f16x8(q, s2));
+        }
+#pragma unroll
+      for (int i = 0; i < MT; ++i) {
+        const int row = i * 16 + r;
+        const half8_t a = *(const half8_t*)(xb + (row * 16 + ((4 * j + g) ^ r)) * 8);
+#pragma unroll
+        for (int w = 0; w < NW; ++w)
+#pragma unroll
+          for (int t = 0; t < NT; ++t)
+            acc[(w * NT + t) * MT + i] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b[w][t], acc[(w * NT + t) * MT + i], 0, 0, 0);
+      }
+    }
+  };
+
+  // Lane (r, g), register k of tile (w, t, i): row 16 i + 4 g + k, column 16 (t_w0 + gi NT + t) + r.
+  auto epilogue = [&](int rt, int gi) __attribute__((always_inline)) {
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      const int lt = gi * NT + t;
+      const int n = (t_w0 + lt) * kTileRows + r;
+      if (lt < tv) {
+#pragma unroll
+        for (int i = 0; i < MT; ++i)
+#pragma unroll
+          for (int k = 0; k < 4; ++k) {
+            const int row = rt * BM + i * 16 + 4 * g + k;
+            if (row < cnt) {
+              if constexpr (MODE == kGateUp) {
+                const float zg = acc[(0 * NT + t) * MT + i][k], zu = acc[(1 * NT + t) * MT + i][k];
+                const __bf16 hb = (__bf16)(silu_f32(zg) * zu);
+                const int64_t idx = (int64_t)(seg + row) * N + n;
+                out16[idx] = __builtin_bit_cast(uint16_t, (_Float16)(float)hb);
+                if (h_out) h_out[idx] = __builtin_bit_cast(uint16_t, hb);
+              } else {
+                const int64_t pair = min(max(sorted_pairs[seg + row], 0), Ptot - 1);
+                out16[pair * N + n] = __builtin_bit_cast(uint16_t, (_Float16)acc[t * MT + i][k]);
+              }
+            }
+          }
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < NW * NT * MT; ++i) acc[i] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
+  };
+
+  // Prologue: the first phase of X, then P steps of weights in flight; the
+  // barrier's fence waits for the X copies only (they were issued first).
+  WStage ws[P];
+  load_x(0, 0);
+  static_for<0, P>([&](auto jc) __attribute__((always_inline)) { load_next(ws[decltype(jc)::value]); });
+  __syncthreads();
+  int cur_rt = 0, cur_kph = 0;
+
+  // Compute cursor: row tile rt, group gi, chunk c.
+  int rt = 0, gi = 0, c = 0;
+  for (int s0 = 0; s0 < total; s0 += P) {
+    static_for<0, P>([&](auto jc) __attribute__((always_inline)) {
+      constexpr int J = decltype(jc)::value;
+      if (s0 + J < total) {
+        const int kph = c / cpp;
+        if (kph != cur_kph || rt != cur_rt) {   // uniform: reload the LDS phase
+          __syncthreads();
+          load_x(rt, kph);
+          __syncthreads();
+          cur_rt = rt;
+          cur_kph = kph;
+        }
+        compute(ws[J], c - kph * cpp);
+        if (c == nchunks - 1) epilogue(rt, gi);
+        if (++c == nchunks) {
+          c = 0;
+          if (++gi == groups) {
+            gi = 0;
+            ++rt;
+          }
+        }
+      }
+      load_next(ws[J]);
+    });
+  }
 }
 
 // out[t, n] = sum_j gates[t, j] y16[t k + j, n]; 8 columns per thread.
@@ -366,10 +435,6 @@ __global__ __launch_bounds__(256) void moe_combine_kernel(const uint16_t* __rest
 // ---------------------------------------------------------------------------
 
 namespace {
-constexpr int kMoeMT = 4;   // 64-row tiles: about one per expert at 32 pairs per expert
-constexpr int kMoeNT = 2;   // 128 columns per workgroup
-constexpr int kMoeS = 4;
-constexpr int kMoeBM = 16 * kMoeMT;
 
 size_t round256(size_t b) { return (b + 255) / 256 * 256; }
 
@@ -396,16 +461,27 @@ void launch_experts(const void* Wg, const void* Wu, const void* Wd, int E, int H
                     int topk, const float* gates, const int32_t* offsets, const int32_t* sorted_pairs, float* out,
                     void* h_out, const MoeWs& w, hipStream_t s) {
   const int P = T * topk;
-  const int max_rtiles = (P + kMoeBM - 1) / kMoeBM + E;
   const int64_t sg = (int64_t)(F / kTileRows) * (H / kChunkK) * Fmt<FMT>::kRecBytes;   // repacked [F, H]
   const int64_t sd = (int64_t)(H / kTileRows) * (F / kChunkK) * Fmt<FMT>::kRecBytes;   // repacked [H, F]
-  moe_gateup_kernel<FMT, kMoeMT, kMoeNT, kMoeS>
-      <<<dim3((unsigned)((F + 64 * kMoeNT - 1) / (64 * kMoeNT)), (unsigned)max_rtiles), dim3(512), 0, s>>>(
-          (const uint8_t*)Wg, (const uint8_t*)Wu, sg, E, H, F, x16, T, topk, offsets, sorted_pairs, w.h16,
-          (uint16_t*)h_out);
-  moe_down_kernel<FMT, kMoeMT, kMoeNT, kMoeS>
-      <<<dim3((unsigned)((H + 64 * kMoeNT - 1) / (64 * kMoeNT)), (unsigned)max_rtiles), dim3(512), 0, s>>>(
-          (const uint8_t*)Wd, sd, E, H, F, w.h16, P, offsets, sorted_pairs, w.y16);
+  // Workgroups per expert: about one per CU over all experts.
+  auto split = [&](int tiles, int nt, int& nwe, int& tpw, int& groups) {
+    nwe = std::max(1, std::min(tiles, 256 / std::max(E, 1)));
+    const int per_wg = (tiles + nwe - 1) / nwe;
+    tpw = (per_wg + 7) / 8;
+    nwe = (tiles + 8 * tpw - 1) / (8 * tpw);
+    groups = (tpw + nt - 1) / nt;
+  };
+  constexpr int NTG = FMT == kQ4_0 ? 3 : 2, PG = 2;   // gate+up: tile pairs per group (Q8_0 codes are twice as large)
+  constexpr int NTD = 4, PD = 3;   // down: 4 tiles per group, 3 stages
+  int nwe, tpw, groups;
+  split(F / kTileRows, NTG, nwe, tpw, groups);
+  moe_stream_kernel<FMT, kGateUp, NTG, PG><<<dim3((unsigned)nwe, (unsigned)E), dim3(512), 0, s>>>(
+      (const uint8_t*)Wg, (const uint8_t*)Wu, sg, F, H, x16, T, T, topk, P, offsets, sorted_pairs, w.h16,
+      (uint16_t*)h_out, tpw, groups);
+  split(H / kTileRows, NTD, nwe, tpw, groups);
+  moe_stream_kernel<FMT, kDown, NTD, PD><<<dim3((unsigned)nwe, (unsigned)E), dim3(512), 0, s>>>(
+      (const uint8_t*)Wd, nullptr, sd, H, F, w.h16, P, T, topk, P, offsets, sorted_pairs, w.y16, nullptr, tpw,
+      groups);
   moe_combine_kernel<<<dim3((unsigned)((H / 8 + 255) / 256), (unsigned)T), dim3(256), 0, s>>>(w.y16, gates, T, topk,
                                                                                               H, out);
 }
