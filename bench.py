@@ -2,33 +2,38 @@
 """Benchmark of the block-quantised weight products on one MI355X.
 
 Headline workload (one "step"): the decode step of one 8B-shaped transformer
-layer's projections over Q4_0 weights, M = 1 fp16 activation row -- q/k/v
-(4096x4096, 2x 1024x4096) in one grouped GEMV launch, o (4096x4096), gate
-and up (2x 12288x4096) in one grouped launch, down (4096x12288).  Four
-launches per step, in the dependency order of a real layer; consecutive
-steps use different copies of the layer's weights (8 copies, 868 MB, more
-than the 256 MB Infinity Cache), as consecutive layers of a model would, so
-the weights stream from HBM.  Launches are captured in HIP graphs.
+layer's projections over Q4_0 weights, M = 1 fp16 activation row: q/k/v
+(4096x4096, 2x 1024x4096), o (4096x4096), gate and up (2x 12288x4096), down
+(4096x12288).  The workload gives the seven products four independent
+activation inputs (x_attn for q/k/v, x_o, x_ffn for gate/up, x_dn), so a
+step computes them in one grouped launch, each matrix with its own split of
+K so that every wave streams about the same number of chunks.  The same step
+in the dependency order of a real layer (q/k/v, then o, then gate+up, then
+down: four launches, since attention, norms and SwiGLU would sit between
+them) is reported under "workloads".  Consecutive steps use different copies
+of the layer's weights (8 copies, 868 MB, more than the 256 MB Infinity
+Cache), as consecutive layers of a model would, so the weights stream from
+HBM.  Launches are captured in HIP graphs.
 
 value = algorithmic bytes of K steps / wall time of K steps (GB/s), inputs
 resident in HBM.  Algorithmic bytes per step = repacked weight bytes (0.5625
 B per weight, exactly the canonical Q4_0 bytes) + activations read (fp16) +
 outputs written (fp32).
 
-roofline: the dominant kernel is the grouped gate+up GEMV (56.6 MB per
-launch); its duration comes from start/stop events recorded by its own
-dispatch (hipExtLaunchKernel), averaged over R launches on rotating weight
-copies.  traffic: HBM bytes per launch from rocprofv3 FETCH_SIZE/WRITE_SIZE
-counters (stored under profiles/ with the hash of the kernel sources they
-were taken on; null if the sources changed since).
+roofline: the dominant kernel is the step's single grouped launch (108.7 MB);
+its duration comes from start/stop events recorded by its own dispatch
+(hipExtLaunchKernel), averaged over R launches on rotating weight copies.
+traffic: HBM bytes per launch from rocprofv3 FETCH_SIZE/WRITE_SIZE counters
+(stored under profiles/ with the hash of the kernel sources they were taken
+on; null if the sources changed since).
 
 cpu_baseline: the fp64 NumPy oracle timed on the host on one decode step of
 the same layer (all seven matrices, M = 1).
 
-Other workloads (M = 2/4/8 layer steps, the single 2048x2048 GEMV, the Q8_0
-3B-shaped matrices, the prefill GEMM at M = 512 and 2048, the MoE layer) are
-reported under "workloads", each with its own algorithmic bytes / flops and
-time.
+Other workloads (the dependency-order step at M = 1, one-launch steps at
+M = 2/4/8, the single 2048x2048 GEMV, the Q8_0 3B-shaped matrices, the
+prefill GEMM at M = 512 and 2048, the MoE layer) are reported under
+"workloads", each with its own algorithmic bytes / flops and time.
 """
 from __future__ import annotations
 
@@ -92,7 +97,8 @@ def log(*a):
 # Decode layer (8B-shaped), the headline workload
 # ----------------------------------------------------------------------------
 class DecodeLayer:
-    GROUPS = [("qkv", ["wq", "wk", "wv"]), ("o", ["wo"]), ("gate_up", ["wg", "wu"]), ("down", ["wd"])]
+    CHAIN = [("qkv", ["wq", "wk", "wv"]), ("o", ["wo"]), ("gate_up", ["wg", "wu"]), ("down", ["wd"])]
+    ONE = [("all", ["wq", "wk", "wv", "wo", "wg", "wu", "wd"])]
 
     def __init__(self, q, torch, synth, M: int, copies: int):
         self.q, self.torch, self.M = q, torch, M
@@ -111,14 +117,18 @@ class DecodeLayer:
             t = torch.from_numpy(a.bits.view("int16")).view(torch.float16).to(dev)
             self.x[xn] = t
         self.y = {n: torch.empty((M, N), dtype=torch.float32, device=dev) for n, (N, K) in self.shapes.items()}
-        self.descs = []
-        for c in self.copies:
-            per = []
-            for g, names in self.GROUPS:
-                probs = [(c[n], self.shapes[n][0], self.shapes[n][1], self.x[synth.LAYER_8B_INPUT[n]],
-                          self.y[n]) for n in names]
-                per.append((g, probs, q.gemv_descs(probs)))
-            self.descs.append(per)
+        self.descs = {}
+        for mode, groups in (("one", self.ONE), ("chain", self.CHAIN)):
+            per_copy = []
+            for c in self.copies:
+                per = []
+                for g, names in groups:
+                    probs = [(c[n], self.shapes[n][0], self.shapes[n][1], self.x[synth.LAYER_8B_INPUT[n]],
+                              self.y[n]) for n in names]
+                    per.append((g, probs, q.gemv_descs(probs)))
+                per_copy.append(per)
+            self.descs[mode] = per_copy
+        self.mode = "one"
         torch.cuda.synchronize()
 
     def bytes_of(self, names) -> int:
@@ -130,10 +140,11 @@ class DecodeLayer:
         return total + sum(M * K * 2 for K in inputs.values())
 
     def step_bytes(self) -> int:
-        return sum(self.bytes_of(names) for _, names in self.GROUPS)
+        groups = self.ONE if self.mode == "one" else self.CHAIN
+        return sum(self.bytes_of(names) for _, names in groups)
 
     def step(self, copy: int, timed_group=None, events=None):
-        for g, probs, descs in self.descs[copy]:
+        for g, probs, descs in self.descs[self.mode][copy]:
             ev = events if g == timed_group else None
             self.q.qgemv_grouped(1, probs, self.M, descs=descs, events=ev)
 
@@ -174,12 +185,12 @@ def time_graph_steps(torch, layer: DecodeLayer, steps: int, warmup: int):
     return time.perf_counter() - t0
 
 
-def time_dominant_kernel(q, layer: DecodeLayer, ev: HipEvents, reps: int):
-    """Mean duration (s) of the grouped gate+up GEMV from dispatch-recorded events."""
+def time_dominant_kernel(q, layer: DecodeLayer, ev: HipEvents, reps: int, group: str):
+    """Mean duration (s) of one launch group, from dispatch-recorded events."""
     pairs = [(ev.create(), ev.create()) for _ in range(reps)]
     L = len(layer.copies)
     for i in range(reps):
-        layer.step(i % L, timed_group="gate_up", events=pairs[i])
+        layer.step(i % L, timed_group=group, events=pairs[i])
     durs = [ev.elapsed_ms(a, b) * 1e-3 for a, b in pairs]
     for a, b in pairs:
         ev.destroy(a)
@@ -188,7 +199,7 @@ def time_dominant_kernel(q, layer: DecodeLayer, ev: HipEvents, reps: int):
 
 
 def _profile_traffic(source_hash: str):
-    path = os.path.join(ROOT, "profiles", "qgemv_gate_up_8b_m1_traffic.json")
+    path = os.path.join(ROOT, "profiles", "qgemv_layer_8b_m1_one_launch_traffic.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
@@ -249,15 +260,20 @@ def _time_launches(torch, fn, reps: int, warmup: int = 3):
 def extra_workloads(q, torch, synth, ev: HipEvents, quick: bool):
     out = []
     dev = torch.device("cuda:0")
-    # Layer steps at other M (graph replays as for the headline).
-    for M in ([] if quick else [2, 4, 8]):
+    # The M = 1 step in dependency order, and both forms at other M (graph replays as for the headline).
+    for M in ([1] if quick else [1, 2, 4, 8]):
         lay = DecodeLayer(q, torch, synth, M, LAYER_COPIES)
-        dt = time_graph_steps(torch, lay, 200, 16)
-        mean_k, _ = time_dominant_kernel(q, lay, ev, 32)
-        gu = lay.bytes_of(["wg", "wu"])
-        out.append({"workload": f"8B layer decode step M={M}", "GB/s": round(lay.step_bytes() * 200 / dt / 1e9, 1),
-                    "gate_up_kernel_us": round(mean_k * 1e6, 2),
-                    "gate_up_kernel_GB/s": round(gu / mean_k / 1e9, 1)})
+        for mode in (["chain"] if M == 1 else ["one", "chain"]):
+            lay.mode = mode
+            dt = time_graph_steps(torch, lay, 200, 16)
+            rec = {"workload": f"8B layer decode step M={M}, " + (
+                "one grouped launch" if mode == "one" else "dependency order (4 launches)"),
+                "GB/s": round(lay.step_bytes() * 200 / dt / 1e9, 1), "us_per_step": round(dt / 200 * 1e6, 2)}
+            if mode == "chain":
+                mean_k, _ = time_dominant_kernel(q, lay, ev, 32, "gate_up")
+                rec["gate_up_kernel_us"] = round(mean_k * 1e6, 2)
+                rec["gate_up_kernel_GB/s"] = round(lay.bytes_of(["wg", "wu"]) / mean_k / 1e9, 1)
+            out.append(rec)
         del lay
         torch.cuda.empty_cache()
     # Single 2048x2048 GEMV (latency-bound: 2.37 MB).
@@ -298,8 +314,24 @@ def extra_workloads(q, torch, synth, ev: HipEvents, quick: bool):
             tot_b += q.repacked_bytes(2, w.N, w.K) + M * w.K * 2 + M * w.N * 4
             del copies, probs, descs
         torch.cuda.empty_cache()
-        out.append({"workload": f"q8_0 3B-shape 4 matrices M={M}", "sum_kernel_us": round(tot_t * 1e6, 2),
+        out.append({"workload": f"q8_0 3B-shape 4 matrices M={M}, one launch each", "sum_kernel_us": round(tot_t * 1e6, 2),
                     "GB/s": round(tot_b / tot_t / 1e9, 1)})
+        # The four matrices in one grouped launch (independent inputs).
+        names = list(ws)
+        Ws = {n: q.repack(2, torch.from_numpy(ws[n].canon).to(dev), ws[n].N, ws[n].K) for n in names}
+        copies = [Ws] + [{n: t.clone() for n, t in Ws.items()} for _ in range(4)]   # 334 MB
+        xts = {n: torch.from_numpy(xs[n].bits.view("int16")).view(torch.bfloat16).to(dev) for n in names}
+        yq = {n: torch.empty((M, ws[n].N), dtype=torch.float32, device=dev) for n in names}
+        probs = [[(c[n], ws[n].N, ws[n].K, xts[n], yq[n]) for n in names] for c in copies]
+        descs = [q.gemv_descs(p) for p in probs]
+        pairs = [(ev.create(), ev.create()) for _ in range(32)]
+        for i in range(32):
+            q.qgemv_grouped(2, probs[i % 5], M, descs=descs[i % 5], events=pairs[i])
+        kd = sum(ev.elapsed_ms(a, b) for a, b in pairs[4:]) / 28 * 1e-3
+        out.append({"workload": f"q8_0 3B-shape 4 matrices M={M}, one grouped launch", "kernel_us": round(kd * 1e6, 2),
+                    "GB/s": round(tot_b / kd / 1e9, 1)})
+        del Ws, copies, probs, descs
+        torch.cuda.empty_cache()
     out += prefill_workloads(q, torch, synth, ev, quick)
     out.append(moe_workload(q, torch, synth))
     return out
@@ -407,21 +439,20 @@ def main():
     ms_per_step = dt / args.steps * 1e3
     log(f"value {value:.1f} GB/s, {ms_per_step * 1e3:.2f} us/step")
 
-    mean_k, durs = time_dominant_kernel(q, layer, ev, args.kernel_reps)
-    gu_bytes = layer.bytes_of(["wg", "wu"])
-    achieved = gu_bytes / mean_k / 1e9
+    mean_k, durs = time_dominant_kernel(q, layer, ev, args.kernel_reps, "all")
+    k_bytes = step_bytes
+    achieved = k_bytes / mean_k / 1e9
     src_hash = _kernel_source_hash()
     traffic = _profile_traffic(src_hash)
+    sd = sorted(durs)
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
-                "kernel": "qgemv grouped gate+up (2 x 12288x4096 Q4_0, M=1)",
-                "algorithmic_bytes_per_launch": gu_bytes, "mean_kernel_us": round(mean_k * 1e6, 3),
-                "kernel_us_min_median_max": [round(sorted(durs)[0] * 1e6, 2),
-                                             round(sorted(durs)[len(durs) // 2] * 1e6, 2),
-                                             round(sorted(durs)[-1] * 1e6, 2)],
+                "kernel": "qgemv grouped launch of the 8B layer's seven Q4_0 projections, M=1",
+                "algorithmic_bytes_per_launch": k_bytes, "mean_kernel_us": round(mean_k * 1e6, 3),
+                "kernel_us_min_median_max": [round(sd[0] * 1e6, 2), round(sd[len(sd) // 2] * 1e6, 2),
+                                             round(sd[-1] * 1e6, 2)],
                 "launches_timed": len(durs), "kernel_source_hash": src_hash}
-    sd = sorted(durs)
-    log(f"gate+up kernel mean {mean_k * 1e6:.2f} us (min {sd[0] * 1e6:.2f}, median {sd[len(sd) // 2] * 1e6:.2f}, "
+    log(f"step kernel mean {mean_k * 1e6:.2f} us (min {sd[0] * 1e6:.2f}, median {sd[len(sd) // 2] * 1e6:.2f}, "
         f"max {sd[-1] * 1e6:.2f}) -> {achieved:.1f} GB/s")
 
     if args.calibrate_copy:
@@ -451,9 +482,10 @@ def main():
         "value": round(value, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": round(ms_per_step, 5), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "f16", "data": "synthetic",
-        "config": {"workload": "decode step of one 8B-shaped layer's projections (q/k/v, o, gate+up, down; "
-                               "hidden 4096, ffn 12288), Q4_0 weights, M=1 fp16 activations",
-                   "M": 1, "weight_copies": LAYER_COPIES, "launches_per_step": 4, "step_bytes": step_bytes,
+        "config": {"workload": "decode step of one 8B-shaped layer's seven projections (q, k, v, o, gate, up, "
+                               "down; hidden 4096, ffn 12288), Q4_0 weights, M=1 fp16 activations (four "
+                               "independent inputs), one grouped launch",
+                   "M": 1, "weight_copies": LAYER_COPIES, "launches_per_step": 1, "step_bytes": step_bytes,
                    "hbm_frac": round(value / HBM_PEAK_GBS, 4)},
         "roofline": roofline,
         "cpu_baseline": cpu,

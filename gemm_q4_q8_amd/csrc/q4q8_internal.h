@@ -36,6 +36,7 @@ struct GemvProb {
 
 struct GemvArgs {
   int32_t wg0[kMaxGroup];   // first workgroup of each problem (set by the launcher)
+  int32_t ks[kMaxGroup];    // K-shares per tile of each problem, a power of 2 dividing the waves per workgroup
   int32_t count;
   int32_t M;
   int32_t total_tiles;

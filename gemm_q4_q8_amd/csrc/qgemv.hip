@@ -7,9 +7,10 @@
 // 32-weight block is one v_mfma_f32_16x16x32 instruction instead of lane FMAs
 // plus a cross-lane reduction:
 //   * a wavefront owns a tile of 16 weight rows and a share of K; a workgroup
-//     holds TPW tiles x KS K-shares (TPW * KS waves); K-shares of one tile
-//     are reduced through LDS in a fixed order at the end (split-K without
-//     atomics or workspace);
+//     of WAVES waves holds WAVES / KS tiles x KS K-shares, KS chosen per
+//     problem of a grouped launch so that every wave streams about as many
+//     chunks; K-shares of one tile are reduced through LDS in a fixed order
+//     at the end (split-K without atomics or workspace);
 //   * the activation rows are staged once per workgroup in LDS; each lane
 //     reads its 16-byte A fragment from there;
 //   * weights stream through buffer loads: per chunk (4 blocks) a lane loads
@@ -42,9 +43,8 @@ constexpr int XP = 4;                   // x pieces per thread staged before the
 constexpr int64_t kLdsTotal = 160 * 1024;          // LDS per workgroup on gfx950
 constexpr int64_t kLdsCap = kLdsTotal - 8 * 1024;  // dynamic LDS for the activations
 
-template <int FMT, int XDT, int NI, int KS, int TPW, int P, bool XLDS>
-__global__ __launch_bounds__(KS* TPW * 64) void qgemv_kernel(const GemvArgs args) {
-  constexpr int WAVES = KS * TPW;
+template <int FMT, int XDT, int NI, int WAVES, int P, bool XLDS>
+__global__ __launch_bounds__(WAVES * 64) void qgemv_kernel(const GemvArgs args) {
   constexpr int REC = Fmt<FMT>::kRecBytes;
   constexpr int CODE = Fmt<FMT>::kCodeBytes;
   constexpr int NV = FMT == kQ4_0 ? 1 : 2;
@@ -68,7 +68,9 @@ __global__ __launch_bounds__(KS* TPW * 64) void qgemv_kernel(const GemvArgs args
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int slot = wave / KS, ks = wave % KS;
+  const int KS = __builtin_amdgcn_readfirstlane(args.ks[pi]);   // power of 2 dividing WAVES
+  const int TPW = WAVES / KS;
+  const int slot = wave / KS, ks = wave & (KS - 1);
   const int tile = (bid - args.wg0[pi]) * TPW + slot;
   const bool tile_ok = tile < tiles;
   const int r = lane & 15, g = lane >> 4;
@@ -184,7 +186,7 @@ __global__ __launch_bounds__(KS* TPW * 64) void qgemv_kernel(const GemvArgs args
   for (int p = 0; p < P; ++p)
     if (i0 + p < nw) compute(st[p], ks + (i0 + p) * KS);
 
-  if constexpr (KS > 1) {
+  if (KS > 1) {   // uniform over the workgroup
     __shared__ float red[WAVES][NI][64];
 #pragma unroll
     for (int i = 0; i < NI; ++i) red[wave][i][lane] = acc[i];
@@ -193,7 +195,6 @@ __global__ __launch_bounds__(KS* TPW * 64) void qgemv_kernel(const GemvArgs args
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
       float v = red[wave][i][lane];
-#pragma unroll
       for (int w = 1; w < KS; ++w) v += red[wave + w][i][lane];
       acc[i] = v;
     }
@@ -216,11 +217,11 @@ struct GemvShape {
   bool xlds;
 };
 
-template <int FMT, int XDT, int NI, int KS, int TPW, int P>
+template <int FMT, int XDT, int NI, int WAVES, int P>
 static void launch_cfg(bool xlds, const GemvArgs& args, int wgs, size_t lds, hipStream_t s, const LaunchEvents& ev) {
-  const dim3 grid((unsigned)wgs), block(KS * TPW * 64);
+  const dim3 grid((unsigned)wgs), block(WAVES * 64);
   if (xlds) {
-    auto k = qgemv_kernel<FMT, XDT, NI, KS, TPW, P, true>;
+    auto k = qgemv_kernel<FMT, XDT, NI, WAVES, P, true>;
     if (lds > 64 * 1024) {
       // Opt in once to dynamic LDS beyond 64 KB: the device's 160 KB per
       // workgroup minus this kernel's static LDS (the split-K buffer).
@@ -236,34 +237,32 @@ static void launch_cfg(bool xlds, const GemvArgs& args, int wgs, size_t lds, hip
         }
       });
       if (lds > dyn_max) {   // does not fit: read x from global memory instead
-        launch(qgemv_kernel<FMT, XDT, NI, KS, TPW, P, false>, grid, block, 0, s, ev, args);
+        launch(qgemv_kernel<FMT, XDT, NI, WAVES, P, false>, grid, block, 0, s, ev, args);
         return;
       }
     }
     launch(k, grid, block, (uint32_t)lds, s, ev, args);
   } else
-    launch(qgemv_kernel<FMT, XDT, NI, KS, TPW, P, false>, grid, block, 0, s, ev, args);
+    launch(qgemv_kernel<FMT, XDT, NI, WAVES, P, false>, grid, block, 0, s, ev, args);
 }
 
 template <int FMT, int XDT, int NI, int P>
-static void launch_p(const GemvShape& c, const GemvArgs& args, int wgs, size_t lds, hipStream_t s,
+static void launch_p(int waves, bool xlds, const GemvArgs& args, int wgs, size_t lds, hipStream_t s,
                      const LaunchEvents& ev) {
-  switch (c.ks) {
-    case 1: launch_cfg<FMT, XDT, NI, 1, 4, P>(c.xlds, args, wgs, lds, s, ev); break;
-    case 2: launch_cfg<FMT, XDT, NI, 2, 2, P>(c.xlds, args, wgs, lds, s, ev); break;
-    case 4: launch_cfg<FMT, XDT, NI, 4, 1, P>(c.xlds, args, wgs, lds, s, ev); break;
-    case 8: launch_cfg<FMT, XDT, NI, 8, 1, P>(c.xlds, args, wgs, lds, s, ev); break;
-    default: launch_cfg<FMT, XDT, NI, 16, 1, P>(c.xlds, args, wgs, lds, s, ev); break;
+  switch (waves) {
+    case 4: launch_cfg<FMT, XDT, NI, 4, P>(xlds, args, wgs, lds, s, ev); break;
+    case 8: launch_cfg<FMT, XDT, NI, 8, P>(xlds, args, wgs, lds, s, ev); break;
+    default: launch_cfg<FMT, XDT, NI, 16, P>(xlds, args, wgs, lds, s, ev); break;
   }
 }
 
 template <int FMT, int XDT, int NI>
-static void launch_ni(const GemvShape& c, const GemvArgs& args, int wgs, size_t lds, hipStream_t s,
+static void launch_ni(int waves, const GemvShape& c, const GemvArgs& args, int wgs, size_t lds, hipStream_t s,
                       const LaunchEvents& ev) {
   if (c.p == 8)
-    launch_p<FMT, XDT, NI, 8>(c, args, wgs, lds, s, ev);
+    launch_p<FMT, XDT, NI, 8>(waves, c.xlds, args, wgs, lds, s, ev);
   else
-    launch_p<FMT, XDT, NI, 4>(c, args, wgs, lds, s, ev);
+    launch_p<FMT, XDT, NI, 4>(waves, c.xlds, args, wgs, lds, s, ev);
 }
 
 // K-shares per tile: about 2048 waves over the chip (8 per CU) with at least
@@ -295,29 +294,50 @@ static GemvShape pick_shape(int tiles, int max_chunks, int M, int max_k) {
 hipError_t launch_qgemv(int fmt, int xdt, GemvArgs args, int max_chunks, int max_k, hipStream_t s,
                         const LaunchEvents& ev) {
   const GemvShape c = pick_shape(args.total_tiles, max_chunks, args.M, max_k);
+  // Problems of one K share the launch-wide split.  When K differs, the
+  // workgroup is 8 waves and each problem takes the power-of-2 split closest
+  // to 16 chunks per wave, so the long-K problems do not trail the launch.
+  bool mixed = false;
+  for (int i = 1; i < args.count; ++i) mixed |= args.p[i].K != args.p[0].K;
+  int waves = c.ks * c.tpw;
+  if (mixed && !getenv("Q4Q8_GEMV_KS")) {
+    waves = c.ks > 8 ? c.ks : 8;
+    for (int i = 0; i < args.count; ++i) {
+      const int nch = (args.p[i].K + kChunkK - 1) / kChunkK;
+      int ks = 1;
+      while (ks < waves && nch >= 24 * ks) ks *= 2;   // nch / ks nearest 16 among powers of 2
+      args.ks[i] = ks;
+    }
+  } else {
+    for (int i = 0; i < args.count; ++i) args.ks[i] = c.ks;
+  }
   // Workgroup ranges per problem.
   int wgs = 0;
   for (int i = 0; i < args.count; ++i) {
+    const int tpw = waves / args.ks[i];
     args.wg0[i] = wgs;
-    wgs += (args.p[i].N + kTileRows * c.tpw - 1) / (kTileRows * c.tpw);
+    wgs += (args.p[i].N + kTileRows * tpw - 1) / (kTileRows * tpw);
   }
-  for (int i = args.count; i < kMaxGroup; ++i) args.wg0[i] = wgs;
+  for (int i = args.count; i < kMaxGroup; ++i) {
+    args.wg0[i] = wgs;
+    args.ks[i] = 1;
+  }
   const size_t lds = c.xlds ? (size_t)args.M * (max_k + 8) * 2 + kXSlack : 0;
   if (fmt == kQ4_0) {
     if (xdt == kF16) {
-      if (args.M > 4) launch_ni<kQ4_0, kF16, 2>(c, args, wgs, lds, s, ev);
-      else launch_ni<kQ4_0, kF16, 1>(c, args, wgs, lds, s, ev);
+      if (args.M > 4) launch_ni<kQ4_0, kF16, 2>(waves, c, args, wgs, lds, s, ev);
+      else launch_ni<kQ4_0, kF16, 1>(waves, c, args, wgs, lds, s, ev);
     } else {
-      if (args.M > 4) launch_ni<kQ4_0, kBF16, 2>(c, args, wgs, lds, s, ev);
-      else launch_ni<kQ4_0, kBF16, 1>(c, args, wgs, lds, s, ev);
+      if (args.M > 4) launch_ni<kQ4_0, kBF16, 2>(waves, c, args, wgs, lds, s, ev);
+      else launch_ni<kQ4_0, kBF16, 1>(waves, c, args, wgs, lds, s, ev);
     }
   } else {
     if (xdt == kF16) {
-      if (args.M > 4) launch_ni<kQ8_0, kF16, 2>(c, args, wgs, lds, s, ev);
-      else launch_ni<kQ8_0, kF16, 1>(c, args, wgs, lds, s, ev);
+      if (args.M > 4) launch_ni<kQ8_0, kF16, 2>(waves, c, args, wgs, lds, s, ev);
+      else launch_ni<kQ8_0, kF16, 1>(waves, c, args, wgs, lds, s, ev);
     } else {
-      if (args.M > 4) launch_ni<kQ8_0, kBF16, 2>(c, args, wgs, lds, s, ev);
-      else launch_ni<kQ8_0, kBF16, 1>(c, args, wgs, lds, s, ev);
+      if (args.M > 4) launch_ni<kQ8_0, kBF16, 2>(waves, c, args, wgs, lds, s, ev);
+      else launch_ni<kQ8_0, kBF16, 1>(waves, c, args, wgs, lds, s, ev);
     }
   }
   return hipGetLastError();

@@ -144,3 +144,41 @@ def test_qgemv_q8_3b_full(q, M):
         y = _run(q, w, xs[name])
         ref, bound = oracle.qgemv(synth.Q8_0, w.canon, w.N, w.K, xs[name].values)
         check(y, ref, bound, f"q8 3B {name} M{M}")
+
+
+def _grouped_check(q, fmt, ws, xs, M, what):
+    """One grouped launch over problems of different K, every output against
+    the oracle (each problem takes its own K split inside the launch)."""
+    Wds = [q.repack(fmt, bytes_tensor(w.canon), w.N, w.K) for w in ws]
+    xts = [act_tensor(x) for x in xs]
+    ys = [torch.full((M, w.N), float("nan"), dtype=torch.float32, device=dev()) for w in ws]
+    q.qgemv_grouped(fmt, [(Wd, w.N, w.K, xt, y) for Wd, w, xt, y in zip(Wds, ws, xts, ys)], M)
+    torch.cuda.synchronize()
+    for w, x, y, i in zip(ws, xs, ys, range(len(ws))):
+        ref, bound = oracle.qgemv(fmt, w.canon, w.N, w.K, x.values)
+        check(y.cpu().numpy(), ref, bound, f"{what} problem {i}")
+
+
+@pytest.mark.parametrize("M", [1, 3, 8])
+def test_qgemv_grouped_mixed_k_ragged(q, M):
+    shapes = [(200, 1056), (48, 160), (1000, 4096), (64, 12288), (17, 32)]
+    ws = [synth.q_weight(synth.rng_for(58, i), synth.Q4_0, N, K) for i, (N, K) in enumerate(shapes)]
+    xs = [synth.activation(synth.rng_for(58, 10 + i), (M, K), synth.F16) for i, (N, K) in enumerate(shapes)]
+    _grouped_check(q, synth.Q4_0, ws, xs, M, f"mixed-K group M{M}")
+
+
+@pytest.mark.parametrize("M", [1, 8])
+def test_qgemv_layer_8b_one_launch(q, M):
+    """The 8B-shaped layer's seven projections in one grouped launch (the
+    benchmark's headline launch shape), every output."""
+    names = ["wq", "wk", "wv", "wo", "wg", "wu", "wd"]
+    ws, xs = synth.layer_8b(M, mats=names)
+    _grouped_check(q, synth.Q4_0, [ws[n] for n in names], [xs[synth.LAYER_8B_INPUT[n]] for n in names], M,
+                   f"8B layer one launch M{M}")
+
+
+@pytest.mark.parametrize("M", [1, 8])
+def test_qgemv_q8_3b_one_launch(q, M):
+    ws, xs = synth.q8_3b(M)
+    names = list(ws)
+    _grouped_check(q, synth.Q8_0, [ws[n] for n in names], [xs[n] for n in names], M, f"q8 3B one launch M{M}")
