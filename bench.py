@@ -32,8 +32,10 @@ the same layer (all seven matrices, M = 1).
 
 Other workloads (the dependency-order step at M = 1, one-launch steps at
 M = 2/4/8, the single 2048x2048 GEMV, the Q8_0 3B-shaped matrices, the
-prefill GEMM at M = 512 and 2048, the MoE layer) are reported under
-"workloads", each with its own algorithmic bytes / flops and time.
+layer's fused decode FFN at M = 1 and 8, the prefill GEMM at M = 512 and
+2048, the MoE layer at 512 tokens and its decode at 1 and 8 tokens) are
+reported under "workloads", each with its own algorithmic bytes / flops and
+time.
 """
 from __future__ import annotations
 
@@ -332,8 +334,72 @@ def extra_workloads(q, torch, synth, ev: HipEvents, quick: bool):
                     "GB/s": round(tot_b / kd / 1e9, 1)})
         del Ws, copies, probs, descs
         torch.cuda.empty_cache()
+    out += ffn_workloads(q, torch, synth, ev, quick)
     out += prefill_workloads(q, torch, synth, ev, quick)
     out.append(moe_workload(q, torch, synth))
+    out += moe_decode_workloads(q, torch, synth, quick)
+    return out
+
+
+def ffn_workloads(q, torch, synth, ev: HipEvents, quick: bool):
+    """Decode FFN of the 8B-shaped layer (H 4096, F 12288, Q4_0): the fused
+    gate/up SwiGLU GEMV (h as bf16, never zg/zu) then the down GEMV.
+    Algorithmic bytes = the three matrices + x + h written and read back +
+    y.  Timed as graph replays over 8 weight copies (step time) and with
+    dispatch events around the two kernels of one call."""
+    out = []
+    dev = torch.device("cuda:0")
+    H, F = 4096, 12288
+    for M in ([1] if quick else [1, 8]):
+        ws, xs = synth.layer_8b(M, mats=["wg", "wu", "wd"])
+        base = {n: q.repack(1, torch.from_numpy(ws[n].canon).to(dev), ws[n].N, ws[n].K) for n in ws}
+        copies = [base] + [{n: t.clone() for n, t in base.items()} for _ in range(LAYER_COPIES - 1)]
+        x = torch.from_numpy(xs["x_ffn"].bits.view("int16")).view(torch.float16).to(dev)
+        y = torch.empty((M, H), dtype=torch.float32, device=dev)
+        h = torch.empty((M, F), dtype=torch.bfloat16, device=dev)
+        wsp = torch.empty(q.ffn_decode_workspace(M, F), dtype=torch.uint8, device=dev)
+        wbytes = 3 * q.repacked_bytes(1, F, H)
+        nb = wbytes + M * H * 2 + 2 * M * F * 2 + M * H * 4
+        nb_gu = 2 * q.repacked_bytes(1, F, H) + M * H * 2 + M * F * 2
+
+        def step(i):
+            c = copies[i % LAYER_COPIES]
+            q.ffn_decode(1, c["wg"], c["wu"], c["wd"], H, F, x, out=y, ws=wsp)
+
+        for i in range(LAYER_COPIES):
+            step(i)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for i in range(LAYER_COPIES):
+                step(i)
+        for _ in range(4):
+            g.replay()
+        torch.cuda.synchronize()
+        reps = 25
+        t0 = time.perf_counter()
+        for _ in range(reps):
+            g.replay()
+        torch.cuda.synchronize()
+        dt = (time.perf_counter() - t0) / (reps * LAYER_COPIES)
+        pairs = [(ev.create(), ev.create()) for _ in range(36)]
+        for i, pr in enumerate(pairs):
+            c = copies[i % LAYER_COPIES]
+            q.ffn_decode(1, c["wg"], c["wu"], c["wd"], H, F, x, out=y, ws=wsp, events=pr)
+        kd = sum(ev.elapsed_ms(a, b) for a, b in pairs[4:]) / 32 * 1e-3
+        for i, pr in enumerate(pairs):
+            c = copies[i % LAYER_COPIES]
+            q.qgemv_swiglu(1, c["wg"], c["wu"], F, H, x, out=h, events=pr)
+        kg = sum(ev.elapsed_ms(a, b) for a, b in pairs[4:]) / 32 * 1e-3
+        for a, b in pairs:
+            ev.destroy(a)
+            ev.destroy(b)
+        out.append({"workload": f"8B-shape decode FFN M={M}: fused gate/up SwiGLU GEMV + down GEMV (2 launches)",
+                    "step_us": round(dt * 1e6, 2), "GB/s": round(nb / dt / 1e9, 1),
+                    "call_kernels_us": round(kd * 1e6, 2), "call_kernels_GB/s": round(nb / kd / 1e9, 1),
+                    "swiglu_kernel_us": round(kg * 1e6, 2), "swiglu_kernel_GB/s": round(nb_gu / kg / 1e9, 1)})
+        del base, copies, g
+        torch.cuda.empty_cache()
     return out
 
 
@@ -400,6 +466,70 @@ def moe_workload(q, torch, synth):
             "TFLOP/s": round(fl / dt / 1e12, 1), "mfma_frac": round(fl / dt / 1e12 / F16_MFMA_PEAK_TFLOPS, 4),
             "weight_GB/s": round(wbytes / dt / 1e9, 1), "roofline_us": round(roof * 1e6, 2),
             "roofline_frac": round(roof / dt, 4)}
+
+
+def moe_decode_workloads(q, torch, synth, quick: bool):
+    """MoE decode: T = 1 and 8 tokens over the MoE layer's experts (E 128,
+    top-8, H 2048, F 768, Q4_0).  One step = route + expert GEMVs (gate/up
+    SwiGLU, down) + combine, captured in a HIP graph.  Steps cycle through 16
+    token sets and two copies of the expert weights (680 MB, more than the
+    Infinity Cache).  Algorithmic bytes = the distinct selected experts'
+    three matrices + x + out."""
+    out = []
+    dev = torch.device("cuda:0")
+    cfg = synth.MOE
+    E, k, H, F = cfg["E"], cfg["topk"], cfg["H"], cfg["F"]
+    _, _, wg, wu, wd = synth.moe(T=1)
+
+    def stack(ws, n, kk):
+        return torch.cat([q.repack(1, torch.from_numpy(w.canon).to(dev), n, kk) for w in ws])
+
+    base = (stack(wg, F, H), stack(wu, F, H), stack(wd, H, F))
+    copies = [base, tuple(t.clone() for t in base)]
+    mat = q.repacked_bytes(1, F, H)
+    for T in ([1] if quick else [1, 8]):
+        sets = 16
+        Ls = [torch.from_numpy(synth.router_logits(synth.rng_for(140, 100 * T + i), T, E)).to(dev)
+              for i in range(sets)]
+        X = torch.from_numpy(synth.activation(synth.rng_for(141, T), (T, H), synth.BF16).bits.view("int16")
+                             ).view(torch.bfloat16).to(dev)
+        o = torch.empty((T, H), dtype=torch.float32, device=dev)
+        rt = (torch.empty((T, k), dtype=torch.int32, device=dev), torch.empty((T, k), dtype=torch.float32, device=dev),
+              torch.empty(E, dtype=torch.int32, device=dev), torch.empty(E + 1, dtype=torch.int32, device=dev),
+              torch.empty(T * k, dtype=torch.int32, device=dev))
+        wsp = torch.empty(q.moe_workspace(1, T, E, k, H, F), dtype=torch.uint8, device=dev)
+
+        def step(i):
+            Wg, Wu, Wd = copies[i % 2]
+            ids, gates, counts, offsets, sp = q.moe_route(Ls[i % sets], k, out=rt)
+            q.moe_qgemm(1, Wg, Wu, Wd, E, H, F, X, k, gates, offsets, sp, out=o, ws=wsp)
+
+        nbytes = 0
+        for i in range(sets):
+            step(i)
+            torch.cuda.synchronize()
+            nbytes += int((rt[2] > 0).sum().item()) * 3 * mat + T * H * 2 + T * H * 4
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for i in range(sets):
+                step(i)
+        for _ in range(3):
+            g.replay()
+        torch.cuda.synchronize()
+        reps = 20
+        t0 = time.perf_counter()
+        for _ in range(reps):
+            g.replay()
+        torch.cuda.synchronize()
+        dt = (time.perf_counter() - t0) / (reps * sets)
+        per = nbytes / sets
+        out.append({"workload": f"q4_0 moe decode T={T} E={E} top{k} H={H} F={F} (route + GEMV path + combine)",
+                    "step_us": round(dt * 1e6, 2), "bytes_per_step": int(per), "GB/s": round(per / dt / 1e9, 1),
+                    "hbm_frac": round(per / dt / 1e9 / HBM_PEAK_GBS, 4)})
+        del g
+    del base, copies
+    torch.cuda.empty_cache()
+    return out
 
 
 def main():

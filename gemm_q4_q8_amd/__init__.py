@@ -55,6 +55,12 @@ def _declare(lib):
         "q4q8_qgemv": (i32, [i32, vp, i64, i64, vp, i32, i64, i32, vp, i64, vp]),
         "q4q8_qgemv_grouped": (i32, [i32, ctypes.POINTER(GemvDesc), i32, i32, i32, vp]),
         "q4q8_qgemv_grouped_timed": (i32, [i32, ctypes.POINTER(GemvDesc), i32, i32, i32, vp, vp, vp]),
+        "q4q8_qgemv_swiglu": (i32, [i32, vp, vp, i64, i64, vp, i32, i64, i32, vp, i32, i64, vp]),
+        "q4q8_qgemv_swiglu_timed": (i32, [i32, vp, vp, i64, i64, vp, i32, i64, i32, vp, i32, i64, vp, vp, vp]),
+        "q4q8_ffn_decode_workspace": (sz, [i32, i64]),
+        "q4q8_ffn_decode": (i32, [i32, vp, vp, vp, i64, i64, vp, i32, i64, i32, vp, i64, vp, sz, vp]),
+        "q4q8_ffn_decode_timed": (i32, [i32, vp, vp, vp, i64, i64, vp, i32, i64, i32, vp, i64, vp, sz, vp,
+                                        vp, vp]),
         "q4q8_qgemm_workspace": (sz, [i32, i64, i64]),
         "q4q8_qgemm": (i32, [i32, vp, i64, i64, vp, i32, i64, i64, vp, i32, i64, vp, sz, vp]),
         "q4q8_qgemm_timed": (i32, [i32, vp, i64, i64, vp, i32, i64, i64, vp, i32, i64, vp, sz, vp, vp, vp]),
@@ -193,6 +199,56 @@ def qgemv_grouped(fmt: int, problems, M: int, descs=None, events=None):
     _check(st, "qgemv_grouped")
 
 
+def qgemv_swiglu(fmt: int, Wg: torch.Tensor, Wu: torch.Tensor, F: int, K: int, x: torch.Tensor,
+                 out: torch.Tensor | None = None, out_dtype=torch.bfloat16, events=None) -> torch.Tensor:
+    """h[M, F] = silu(x @ Wg^T) * (x @ Wu^T), one launch, output out_dtype."""
+    _dev(Wg, "Wg")
+    _dev(Wu, "Wu")
+    if x.dim() != 2 or x.shape[1] != K or x.stride(1) != 1:
+        raise ValueError("x must be [M, K] with contiguous rows")
+    M = x.shape[0]
+    if out is None:
+        out = torch.empty((M, F), dtype=out_dtype, device=x.device)
+    args = (fmt, _ptr(Wg), _ptr(Wu), F, K, _ptr(x), _DT[x.dtype], x.stride(0), M, _ptr(out), _DT[out.dtype],
+            out.stride(0), _stream(x))
+    if events is None:
+        st = lib().q4q8_qgemv_swiglu(*args)
+    else:
+        st = lib().q4q8_qgemv_swiglu_timed(*args, ctypes.c_void_p(events[0]), ctypes.c_void_p(events[1]))
+    _check(st, "qgemv_swiglu")
+    return out
+
+
+def ffn_decode_workspace(M: int, F: int) -> int:
+    return int(lib().q4q8_ffn_decode_workspace(M, F))
+
+
+def ffn_decode(fmt: int, Wg: torch.Tensor, Wu: torch.Tensor, Wd: torch.Tensor, H: int, F: int, x: torch.Tensor,
+               out: torch.Tensor | None = None, ws: torch.Tensor | None = None, events=None) -> torch.Tensor:
+    """y[M, H] fp32 = (silu(x Wg^T) * (x Wu^T)) Wd^T, h held as bf16; two launches.
+
+    ws: optional uint8 workspace of >= ffn_decode_workspace(M, F) bytes (the
+    bf16 h rows; allocated per call if omitted).
+    """
+    for t, n in ((Wg, "Wg"), (Wu, "Wu"), (Wd, "Wd")):
+        _dev(t, n)
+    if x.dim() != 2 or x.shape[1] != H or x.stride(1) != 1:
+        raise ValueError("x must be [M, H] with contiguous rows")
+    M = x.shape[0]
+    if out is None:
+        out = torch.empty((M, H), dtype=torch.float32, device=x.device)
+    if ws is None:
+        ws = torch.empty(max(ffn_decode_workspace(M, F), 1), dtype=torch.uint8, device=x.device)
+    args = (fmt, _ptr(Wg), _ptr(Wu), _ptr(Wd), H, F, _ptr(x), _DT[x.dtype], x.stride(0), M, _ptr(out),
+            out.stride(0), _ptr(ws), ws.numel() * ws.element_size(), _stream(x))
+    if events is None:
+        st = lib().q4q8_ffn_decode(*args)
+    else:
+        st = lib().q4q8_ffn_decode_timed(*args, ctypes.c_void_p(events[0]), ctypes.c_void_p(events[1]))
+    _check(st, "ffn_decode")
+    return out
+
+
 def qgemm_workspace(xdt: int, M: int, K: int) -> int:
     return int(lib().q4q8_qgemm_workspace(xdt, M, K))
 
@@ -226,16 +282,22 @@ def qgemm(fmt: int, W: torch.Tensor, N: int, K: int, X: torch.Tensor,
     return out
 
 
-def moe_route(logits: torch.Tensor, topk: int):
-    """-> ids [T,k] int32, gates [T,k] fp32, counts [E], offsets [E+1], sorted_pairs [T*k]."""
+def moe_route(logits: torch.Tensor, topk: int, out=None):
+    """-> ids [T,k] int32, gates [T,k] fp32, counts [E], offsets [E+1], sorted_pairs [T*k].
+
+    out: optional preallocated (ids, gates, counts, offsets, sorted_pairs).
+    """
     _dev(logits, "logits")
     T, E = logits.shape
     d = logits.device
-    ids = torch.empty((T, topk), dtype=torch.int32, device=d)
-    gates = torch.empty((T, topk), dtype=torch.float32, device=d)
-    counts = torch.empty(E, dtype=torch.int32, device=d)
-    offsets = torch.empty(E + 1, dtype=torch.int32, device=d)
-    sp = torch.empty(T * topk, dtype=torch.int32, device=d)
+    if out is not None:
+        ids, gates, counts, offsets, sp = out
+    else:
+        ids = torch.empty((T, topk), dtype=torch.int32, device=d)
+        gates = torch.empty((T, topk), dtype=torch.float32, device=d)
+        counts = torch.empty(E, dtype=torch.int32, device=d)
+        offsets = torch.empty(E + 1, dtype=torch.int32, device=d)
+        sp = torch.empty(T * topk, dtype=torch.int32, device=d)
     _check(lib().q4q8_moe_route(_ptr(logits), T, E, topk, _ptr(ids), _ptr(gates), _ptr(counts),
                                 _ptr(offsets), _ptr(sp), _stream(logits)), "moe_route")
     return ids, gates, counts, offsets, sp

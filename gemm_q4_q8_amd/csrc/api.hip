@@ -101,49 +101,73 @@ int q4q8_repack_host(int fmt, const void* canon, int64_t N, int64_t K, void* dst
   return Q4Q8_OK;
 }
 
-static int check_gemv_desc(int fmt, const q4q8_gemv_desc& d, int xdt, int M, int idx) {
+}  // extern "C"
+
+// One GEMV problem as the entry points hand it over: plain (W2 null, fp32 y)
+// or a SwiGLU pair (W gate, W2 up, y of dtype ydt).
+struct GemvIn {
+  const void* W;
+  const void* W2;
+  const void* x;
+  void* y;
+  int64_t N, K, ldx, ldy;
+  int ydt;
+};
+
+static int check_gemv_prob(int fmt, const GemvIn& d, int M, int idx) {
   int st = check_matrix(fmt, d.N, d.K);
   if (st) return st;
   if (!d.W || !d.x || !d.y) return fail(Q4Q8_ERR_INVALID_ARG, "qgemv[%d]: null pointer", idx);
-  if (!aligned(d.W, 16)) return fail(Q4Q8_ERR_ALIGNMENT, "qgemv[%d]: weights not 16-byte aligned", idx);
+  if (!aligned(d.W, 16) || (d.W2 && !aligned(d.W2, 16)))
+    return fail(Q4Q8_ERR_ALIGNMENT, "qgemv[%d]: weights not 16-byte aligned", idx);
   if (!aligned(d.x, 16)) return fail(Q4Q8_ERR_ALIGNMENT, "qgemv[%d]: x not 16-byte aligned", idx);
-  if (!aligned(d.y, 4)) return fail(Q4Q8_ERR_ALIGNMENT, "qgemv[%d]: y not 4-byte aligned", idx);
+  if (d.ydt != Q4Q8_F16 && d.ydt != Q4Q8_BF16 && d.ydt != Q4Q8_F32)
+    return fail(Q4Q8_ERR_UNSUPPORTED, "qgemv[%d]: output dtype %d", idx, d.ydt);
+  const size_t ysz = d.ydt == Q4Q8_F32 ? 4 : 2;
+  if (!aligned(d.y, ysz))
+    return fail(Q4Q8_ERR_ALIGNMENT, "qgemv[%d]: y not aligned to its %zu-byte element", idx, ysz);
   if (M > 1) {
     if (d.ldx < d.K || d.ldy < d.N)
       return fail(Q4Q8_ERR_INVALID_ARG, "qgemv[%d]: ldx=%lld < K or ldy=%lld < N", idx, (long long)d.ldx,
                   (long long)d.ldy);
     if (d.ldx % 8) return fail(Q4Q8_ERR_ALIGNMENT, "qgemv[%d]: ldx=%lld not a multiple of 8", idx, (long long)d.ldx);
+    if (d.ldx > (1LL << 40) || d.ldy > (1LL << 40))
+      return fail(Q4Q8_ERR_UNSUPPORTED, "qgemv[%d]: leading dimension beyond 2^40", idx);
   }
-  (void)xdt;
   return Q4Q8_OK;
 }
 
-static int qgemv_grouped(int fmt, const q4q8_gemv_desc* descs, int count, int xdt, int M, void* stream,
-                         const q4q8::LaunchEvents& ev) {
+static int check_gemv_common(int fmt, int xdt, int M, int count) {
   if (!fmt_ok(fmt)) return fail(Q4Q8_ERR_UNSUPPORTED, "unknown weight format %d", fmt);
   if (!act_ok(xdt)) return fail(Q4Q8_ERR_UNSUPPORTED, "qgemv: activation dtype %d not F16/BF16", xdt);
   if (M < 1 || M > 8) return fail(Q4Q8_ERR_INVALID_ARG, "qgemv: M=%d outside 1..8", M);
-  if (!descs || count < 1 || count > Q4Q8_MAX_GROUP)
+  if (count < 1 || count > Q4Q8_MAX_GROUP)
     return fail(Q4Q8_ERR_INVALID_ARG, "qgemv: %d problems (1..%d allowed)", count, Q4Q8_MAX_GROUP);
+  return Q4Q8_OK;
+}
+
+// Enqueues one launch over already validated problems.
+static int run_gemv(int fmt, const GemvIn* in, int count, int xdt, int M, void* stream,
+                    const q4q8::LaunchEvents& ev) {
   q4q8::GemvArgs args;
   memset(&args, 0, sizeof(args));
   int64_t tiles = 0;
   int max_chunks = 0, max_k = 0;
   for (int i = 0; i < count; ++i) {
-    int st = check_gemv_desc(fmt, descs[i], xdt, M, i);
-    if (st) return st;
     q4q8::GemvProb& p = args.p[i];
-    p.W = (const uint8_t*)descs[i].W;
-    p.x = (const uint16_t*)descs[i].x;
-    p.y = descs[i].y;
-    p.ldx = M > 1 ? descs[i].ldx : 0;
-    p.ldy = M > 1 ? descs[i].ldy : 0;
-    p.N = (int32_t)descs[i].N;
-    p.K = (int32_t)descs[i].K;
-    tiles += (descs[i].N + 15) / 16;
-    const int chunks = (int)((descs[i].K + 127) / 128);
+    p.W = (const uint8_t*)in[i].W;
+    p.W2 = (const uint8_t*)in[i].W2;
+    p.x = (const uint16_t*)in[i].x;
+    p.y = in[i].y;
+    p.ldx = M > 1 ? in[i].ldx : 0;
+    p.ldy = M > 1 ? in[i].ldy : 0;
+    p.N = (int32_t)in[i].N;
+    p.K = (int32_t)in[i].K;
+    p.ydt = in[i].ydt;
+    tiles += (in[i].W2 ? 2 : 1) * ((in[i].N + 15) / 16);
+    const int chunks = (int)((in[i].K + 127) / 128);
     if (chunks > max_chunks) max_chunks = chunks;
-    if (descs[i].K > max_k) max_k = (int)descs[i].K;
+    if (in[i].K > max_k) max_k = (int)in[i].K;
   }
   if (tiles > (1LL << 31) - 1) return fail(Q4Q8_ERR_UNSUPPORTED, "qgemv: too many row tiles");
   args.count = count;
@@ -153,6 +177,23 @@ static int qgemv_grouped(int fmt, const q4q8_gemv_desc* descs, int count, int xd
   return hip_status(q4q8::launch_qgemv(fmt, xdt, args, max_chunks, max_k, (hipStream_t)stream, ev),
                     "qgemv launch");
 }
+
+static int qgemv_grouped(int fmt, const q4q8_gemv_desc* descs, int count, int xdt, int M, void* stream,
+                         const q4q8::LaunchEvents& ev) {
+  if (!descs) return fail(Q4Q8_ERR_INVALID_ARG, "qgemv: null descriptor array");
+  int st = check_gemv_common(fmt, xdt, M, count);
+  if (st) return st;
+  GemvIn in[Q4Q8_MAX_GROUP];
+  for (int i = 0; i < count; ++i) {
+    in[i] = GemvIn{descs[i].W, nullptr, descs[i].x, descs[i].y, descs[i].N, descs[i].K, descs[i].ldx,
+                   descs[i].ldy, Q4Q8_F32};
+    st = check_gemv_prob(fmt, in[i], M, i);
+    if (st) return st;
+  }
+  return run_gemv(fmt, in, count, xdt, M, stream, ev);
+}
+
+extern "C" {
 
 int q4q8_qgemv_grouped(int fmt, const q4q8_gemv_desc* descs, int count, int xdt, int M, void* stream) {
   return qgemv_grouped(fmt, descs, count, xdt, M, stream, q4q8::LaunchEvents());
@@ -178,6 +219,86 @@ int q4q8_qgemv(int fmt, const void* W, int64_t N, int64_t K, const void* x, int 
   d.ldy = ldy;
   return q4q8_qgemv_grouped(fmt, &d, 1, xdt, M, stream);
 }
+
+}  // extern "C"
+
+static int swiglu_impl(int fmt, const void* Wg, const void* Wu, int64_t F, int64_t K, const void* x, int xdt,
+                       int64_t ldx, int M, void* h, int hdt, int64_t ldh, void* stream,
+                       const q4q8::LaunchEvents& ev) {
+  int st = check_gemv_common(fmt, xdt, M, 1);
+  if (st) return st;
+  if (!Wu) return fail(Q4Q8_ERR_INVALID_ARG, "qgemv_swiglu: null pointer");
+  const GemvIn in{Wg, Wu, x, h, F, K, ldx, ldh, hdt};
+  st = check_gemv_prob(fmt, in, M, 0);
+  if (st) return st;
+  return run_gemv(fmt, &in, 1, xdt, M, stream, ev);
+}
+
+static size_t ffn_ws(int M, int64_t F) { return (size_t)(((int64_t)M * F * 2 + 255) / 256 * 256); }
+
+static int ffn_impl(int fmt, const void* Wg, const void* Wu, const void* Wd, int64_t H, int64_t F, const void* x,
+                    int xdt, int64_t ldx, int M, float* y, int64_t ldy, void* ws, size_t ws_bytes, void* stream,
+                    const q4q8::LaunchEvents& ev) {
+  int st = check_gemv_common(fmt, xdt, M, 1);
+  if (st) return st;
+  if (!Wg || !Wu || !Wd) return fail(Q4Q8_ERR_INVALID_ARG, "ffn_decode: null pointer");
+  // Validate both launches before enqueuing either.
+  const GemvIn gu{Wg, Wu, x, ws ? ws : (void*)Wg, F, H, ldx, F, Q4Q8_BF16};
+  st = check_gemv_prob(fmt, gu, M, 0);
+  if (st) return st;
+  const GemvIn dn{Wd, nullptr, ws ? ws : (void*)Wd, y, H, F, F, ldy, Q4Q8_F32};
+  st = check_gemv_prob(fmt, dn, M, 1);
+  if (st) return st;
+  const size_t need = ffn_ws(M, F);
+  if (!ws || ws_bytes < need)
+    return fail(Q4Q8_ERR_WORKSPACE, "ffn_decode: workspace holds %zu bytes, needs %zu", ws ? ws_bytes : 0, need);
+  if (!aligned(ws, 256)) return fail(Q4Q8_ERR_ALIGNMENT, "ffn_decode: workspace not 256-byte aligned");
+  q4q8::LaunchEvents e1, e2;
+  e1.start = ev.start;
+  e2.stop = ev.stop;
+  st = run_gemv(fmt, &gu, 1, xdt, M, stream, e1);
+  if (st) return st;
+  return run_gemv(fmt, &dn, 1, Q4Q8_BF16, M, stream, e2);
+}
+
+extern "C" {
+
+int q4q8_qgemv_swiglu(int fmt, const void* Wg, const void* Wu, int64_t F, int64_t K, const void* x, int xdt,
+                      int64_t ldx, int M, void* h, int hdt, int64_t ldh, void* stream) {
+  return swiglu_impl(fmt, Wg, Wu, F, K, x, xdt, ldx, M, h, hdt, ldh, stream, q4q8::LaunchEvents());
+}
+
+int q4q8_qgemv_swiglu_timed(int fmt, const void* Wg, const void* Wu, int64_t F, int64_t K, const void* x, int xdt,
+                            int64_t ldx, int M, void* h, int hdt, int64_t ldh, void* stream, void* ev_start,
+                            void* ev_stop) {
+  q4q8::LaunchEvents ev;
+  ev.start = (hipEvent_t)ev_start;
+  ev.stop = (hipEvent_t)ev_stop;
+  return swiglu_impl(fmt, Wg, Wu, F, K, x, xdt, ldx, M, h, hdt, ldh, stream, ev);
+}
+
+size_t q4q8_ffn_decode_workspace(int M, int64_t F) {
+  if (M < 1 || M > 8 || F < 32 || F % 32 || F > (1LL << 24)) return 0;
+  return ffn_ws(M, F);
+}
+
+int q4q8_ffn_decode(int fmt, const void* Wg, const void* Wu, const void* Wd, int64_t H, int64_t F, const void* x,
+                    int xdt, int64_t ldx, int M, float* y, int64_t ldy, void* ws, size_t ws_bytes, void* stream) {
+  return ffn_impl(fmt, Wg, Wu, Wd, H, F, x, xdt, ldx, M, y, ldy, ws, ws_bytes, stream, q4q8::LaunchEvents());
+}
+
+int q4q8_ffn_decode_timed(int fmt, const void* Wg, const void* Wu, const void* Wd, int64_t H, int64_t F,
+                          const void* x, int xdt, int64_t ldx, int M, float* y, int64_t ldy, void* ws,
+                          size_t ws_bytes, void* stream, void* ev_start, void* ev_stop) {
+  q4q8::LaunchEvents ev;
+  ev.start = (hipEvent_t)ev_start;
+  ev.stop = (hipEvent_t)ev_stop;
+  return ffn_impl(fmt, Wg, Wu, Wd, H, F, x, xdt, ldx, M, y, ldy, ws, ws_bytes, stream, ev);
+}
+
+}  // extern "C"
+
+extern "C" {
 
 static int qgemm_impl(int fmt, const void* W, int64_t N, int64_t K, const void* X, int xdt, int64_t ldx, int64_t M,
                       void* Y, int ydt, int64_t ldy, void* ws, size_t ws_bytes, void* stream,

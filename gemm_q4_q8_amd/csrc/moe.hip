@@ -12,6 +12,7 @@
 //   moe_sort_kernel   one workgroup: per-wave histograms, scan, then each
 //                     wave places its pairs in order (ranks from ballots), so
 //                     the order is stable and bit-exact.
+//   moe_route_small_kernel  both in one workgroup for up to 16 tokens.
 //   moe_stream_kernel gate+up: the expert's rows gathered from X by token
 //                     into LDS, gate and up weights streamed per wave;
 //                     epilogue h = silu(z_gate) * z_up, rounded to bf16 (h's
@@ -43,14 +44,11 @@ __device__ __forceinline__ bool route_before(float v, int i, float bv, int bi) {
   return v > bv || (v == bv && i < bi);
 }
 
-// NS: 64-expert slots per lane (E <= 64 NS).  Branch-free: out-of-range and
-// taken experts compare as never better.
+// Top-k of token t by one wave.  NS: 64-expert slots per lane (E <= 64 NS).
+// Branch-free: out-of-range and taken experts compare as never better.
 template <int NS>
-__global__ __launch_bounds__(256) void moe_topk_kernel(const float* __restrict__ logits, int T, int E, int topk,
-                                                       int32_t* __restrict__ ids, float* __restrict__ gates) {
-  const int lane = threadIdx.x & 63;
-  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (t >= T) return;   // whole wave
+__device__ __forceinline__ void topk_token(const float* __restrict__ logits, int t, int E, int topk, int lane,
+                                           int32_t* __restrict__ ids, float* __restrict__ gates) {
   // Lane holds experts lane + 64 i.  NaN ranks as -inf.
   const __amdgpu_buffer_rsrc_t rs = uniform_rsrc(logits + (int64_t)t * E, E * 4);
   float v[NS];
@@ -91,13 +89,21 @@ __global__ __launch_bounds__(256) void moe_topk_kernel(const float* __restrict__
   if (lane < topk) gates[(int64_t)t * topk + lane] = my_exp / sum;
 }
 
+template <int NS>
+__global__ __launch_bounds__(256) void moe_topk_kernel(const float* __restrict__ logits, int T, int E, int topk,
+                                                       int32_t* __restrict__ ids, float* __restrict__ gates) {
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t < T) topk_token<NS>(logits, t, E, topk, threadIdx.x & 63, ids, gates);   // whole wave
+}
+
 // ---------------------------------------------------------------------------
 // Sort: counts, offsets, sorted_pairs (stable counting sort, one workgroup)
 // ---------------------------------------------------------------------------
 
-__global__ __launch_bounds__(1024) void moe_sort_kernel(const int32_t* __restrict__ ids, int P, int E,
-                                                        int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
-                                                        int32_t* __restrict__ sorted_pairs) {
+// The sort body, run by one workgroup of kSortWaves waves.
+__device__ __forceinline__ void sort_pairs(const int32_t* __restrict__ ids, int P, int E,
+                                           int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
+                                           int32_t* __restrict__ sorted_pairs) {
   __shared__ int hist_s[kSortWaves * kRouteMaxE];   // [wave][expert]: counts, then bases
   int* hist = hist_s;
   __shared__ int wave_sum[kSortWaves];
@@ -162,8 +168,44 @@ __global__ __launch_bounds__(1024) void moe_sort_kernel(const int32_t* __restric
   }
 }
 
+__global__ __launch_bounds__(1024) void moe_sort_kernel(const int32_t* __restrict__ ids, int P, int E,
+                                                        int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
+                                                        int32_t* __restrict__ sorted_pairs) {
+  sort_pairs(ids, P, E, counts, offsets, sorted_pairs);
+}
+
+// A few tokens (T <= kSortWaves): top-k and sort in one workgroup, one
+// launch.  Wave t takes token t; the sort reads ids once every wave's writes
+// are visible to the workgroup.
+template <int NS>
+__global__ __launch_bounds__(1024) void moe_route_small_kernel(const float* __restrict__ logits, int T, int E,
+                                                               int topk, int32_t* __restrict__ ids,
+                                                               float* __restrict__ gates, int32_t* __restrict__ counts,
+                                                               int32_t* __restrict__ offsets,
+                                                               int32_t* __restrict__ sorted_pairs) {
+  const int w = threadIdx.x >> 6;
+  if (w < T) topk_token<NS>(logits, w, E, topk, threadIdx.x & 63, ids, gates);
+  __threadfence();
+  __syncthreads();
+  sort_pairs(ids, T * topk, E, counts, offsets, sorted_pairs);
+}
+
 hipError_t launch_moe_route(const float* logits, int T, int E, int topk, int32_t* ids, float* gates,
                             int32_t* counts, int32_t* offsets, int32_t* sorted_pairs, hipStream_t stream) {
+  if (T <= kSortWaves) {
+    const dim3 g1(1), b1(1024);
+    if (E <= 64) moe_route_small_kernel<1><<<g1, b1, 0, stream>>>(logits, T, E, topk, ids, gates, counts, offsets,
+                                                                  sorted_pairs);
+    else if (E <= 128) moe_route_small_kernel<2><<<g1, b1, 0, stream>>>(logits, T, E, topk, ids, gates, counts,
+                                                                        offsets, sorted_pairs);
+    else if (E <= 256) moe_route_small_kernel<4><<<g1, b1, 0, stream>>>(logits, T, E, topk, ids, gates, counts,
+                                                                        offsets, sorted_pairs);
+    else if (E <= 512) moe_route_small_kernel<8><<<g1, b1, 0, stream>>>(logits, T, E, topk, ids, gates, counts,
+                                                                        offsets, sorted_pairs);
+    else moe_route_small_kernel<16><<<g1, b1, 0, stream>>>(logits, T, E, topk, ids, gates, counts, offsets,
+                                                           sorted_pairs);
+    return hipGetLastError();
+  }
   const dim3 grid((unsigned)((T + 3) / 4)), block(256);
   if (E <= 64) moe_topk_kernel<1><<<grid, block, 0, stream>>>(logits, T, E, topk, ids, gates);
   else if (E <= 128) moe_topk_kernel<2><<<grid, block, 0, stream>>>(logits, T, E, topk, ids, gates);
@@ -174,8 +216,6 @@ hipError_t launch_moe_route(const float* logits, int T, int E, int topk, int32_t
   return hipGetLastError();
 }
 
-// silu(z) = z / (1 + exp(-z)), fp32.
-__device__ __forceinline__ float silu_f32(float z) { return z / (1.0f + expf(-z)); }
 
 // ---------------------------------------------------------------------------
 // Expert GEMMs, streaming form (few rows per expert)
@@ -498,6 +538,14 @@ hipError_t launch_moe_qgemm(int fmt, int xdt, const void* Wg, const void* Wu, co
                             const void* X, int T, int topk, const float* gates, const int32_t* offsets,
                             const int32_t* sorted_pairs, float* out, void* h_out, void* ws, hipStream_t stream) {
   const MoeWs w = moe_ws_layout(ws, T, topk, H, F);
+  if (moe_decode_fits(T, H, F)) {
+    // A few tokens: every expert product is a GEMV over the expert's weights.
+    uint16_t* h = h_out ? (uint16_t*)h_out : w.h16;
+    launch_moe_decode(fmt, xdt, Wg, Wu, Wd, E, H, F, X, T, topk, offsets, sorted_pairs, h, w.y16, stream);
+    moe_combine_kernel<<<dim3((unsigned)((H / 8 + 255) / 256), (unsigned)T), dim3(256), 0, stream>>>(
+        w.y16, gates, T, topk, H, out);
+    return hipGetLastError();
+  }
   const uint16_t* x16 = (const uint16_t*)X;
   if (xdt == kBF16) {
     const hipError_t e = launch_bf16_to_f16(X, H, w.x16, H, T, H, H, stream, LaunchEvents());

@@ -1,0 +1,266 @@
+// Mixture-of-experts decode: T <= 8 tokens, each routed to its top-k experts.
+//
+// "BaseRT: Advancing Best-in-Class LLM Inference with Apple M5 Neural
+// Accelerators" (review, "Method") keeps memory-bound decode on the GEMV
+// kernels and sends only compute-bound work (prefill GEMM, MoE expert GEMM)
+// to the matrix-unit tile path.  With a handful of tokens an expert sees at
+// most T rows, so its products are GEMVs over its weights: this path runs
+// them on the GEMV machinery (gemv_core.h) instead of 64-row MFMA tiles.
+//
+// Work split.  Pairs (token t, slot j) arrive sorted by expert (offsets,
+// sorted_pairs from the routing step).  Workgroup (position p, group g) loads
+// offsets into LDS and finds the expert e that owns sorted position p (binary
+// search there: one memory round trip instead of a chain of them); only
+// the expert's first position works, with the expert's M = offsets[e+1] -
+// offsets[e] <= T rows as the GEMV's activation rows, so each selected
+// expert's weights stream exactly once per call.  The other positions' groups
+// exit at once.
+//   * gate/up: a SwiGLU pair per 16-row tile (half of the tile's waves on
+//     the gate rows, half on the up rows, K split in ksh shares each), x rows
+//     gathered from the tokens into LDS; h = silu(gate) * up rounded to bf16,
+//     stored in sorted-pair order;
+//   * down: x = the expert's h rows (contiguous in sorted order, bf16
+//     operands, exact), y rounded to fp16 per pair id, then the weighted
+//     combine kernel of the prefill path.
+// K-shares are reduced in a fixed order through LDS: results are bitwise
+// reproducible.
+#include "gemv_core.h"
+#include "q4q8_internal.h"
+
+#include <algorithm>
+
+namespace q4q8 {
+
+enum { kDecGateUp = 0, kDecDown = 1 };
+
+struct MoeDecArgs {
+  const uint8_t* W;          // gate (gate/up pass) or down weights of expert 0
+  const uint8_t* W2;         // up weights of expert 0 (gate/up pass)
+  int64_t mat_bytes;         // repacked bytes of one expert's matrix
+  const uint16_t* X;         // gate/up: tokens [T, ldx]; down: h [positions, ldx], sorted
+  int64_t ldx;
+  uint16_t* out;             // gate/up: h bf16 [positions, N], sorted; down: y fp16 [pair id, N]
+  const int32_t* offsets;    // [E + 1]
+  const int32_t* sorted_pairs;
+  int32_t N, K;              // output rows per expert, reduction length (multiples of 128)
+  int32_t topk, E, npos;     // npos = T * topk sorted positions
+  int32_t groups;            // workgroups per sorted position
+  int32_t ksh;               // K-shares per matrix, a power of 2
+};
+
+constexpr int kDecXSlack = 512;
+constexpr int kDecMaxExperts = 1024;
+
+template <int FMT, int XDT, int MODE, int NI, int WAVES, int P>
+__global__ __launch_bounds__(WAVES * 64) void moe_gemv_kernel(const MoeDecArgs a) {
+  typedef typename Op<XDT>::vec vec;
+  typedef GemvStage<FMT> Stage;
+  constexpr int REC = Fmt<FMT>::kRecBytes;
+  extern __shared__ __attribute__((aligned(16))) uint16_t xs[];
+
+  const int pos = blockIdx.x / a.groups;
+  const int grp = blockIdx.x - pos * a.groups;
+  const int tid = threadIdx.x;
+  // One round trip for the routing data: offsets into LDS, and the pair ids
+  // of positions pos .. pos + 7 (this workgroup's rows if it leads).
+  __shared__ int32_t s_off[kDecMaxExperts + 1];
+  __shared__ int32_t s_pair[kMoeDecodeMaxTokens];
+  for (int i = tid; i <= a.E; i += WAVES * 64) s_off[i] = a.offsets[i];
+  if (tid < kMoeDecodeMaxTokens && pos + tid < a.npos) s_pair[tid] = a.sorted_pairs[pos + tid];
+  __syncthreads();
+  // Expert owning sorted position pos: the largest e with offsets[e] <= pos.
+  int lo = 0, hi = a.E;
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (s_off[mid] <= pos) lo = mid;
+    else hi = mid;
+  }
+  const int e = lo;
+  const int r0 = s_off[e];
+  if (r0 != pos) return;                      // not the expert's first position
+  const int M = s_off[e + 1] - r0;            // the expert's rows, 1..T
+
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  constexpr int MATS = MODE == kDecGateUp ? 2 : 1;
+  const int KSH = a.ksh;
+  const int KS = KSH * MATS;                  // waves per tile
+  const int TPW = WAVES / KS;
+  const int slot = wave / KS, kw = wave & (KS - 1);
+  const bool up = MODE == kDecGateUp && kw >= KSH;
+  const int ks = up ? kw - KSH : kw;
+  const int N = a.N, K = a.K;
+  const int nchunks = K / kChunkK;
+  const int tiles = N / kTileRows;
+  const int tile = grp * TPW + slot;
+  const bool tile_ok = tile < tiles;
+  const int r = lane & 15, g = lane >> 4;
+  const int m = 4 * (r & 3) + (r >> 2);       // activation row fed by this lane
+  const bool mvalid = m < M;
+
+  const uint8_t* wbase = (up ? a.W2 : a.W) + (int64_t)e * a.mat_bytes;
+  const __amdgpu_buffer_rsrc_t wres = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(wbase + (int64_t)(tile_ok ? tile : 0) * nchunks * REC), (short)0, tile_ok ? nchunks * REC : 0,
+      kGemvBufFlags);
+
+  // Weight prefetch first (it does not depend on x), then the x rows into
+  // LDS: rows of K + 8 halfs, then kDecXSlack zero bytes.
+  Stage st[P];
+#pragma unroll
+  for (int p = 0; p < P; ++p) gemv_load<FMT>(st[p], wres, ks + p * KSH, lane, r);
+  const int per_row = K / 8 + 1;
+  const int pieces = M * per_row + kDecXSlack / 16;
+  for (int i = tid; i < pieces; i += WAVES * 64) {
+    const int mm = i / per_row, k8 = i - mm * per_row;
+    u32x4_t v = u32x4_t{0, 0, 0, 0};
+    if (mm < M && k8 < K / 8) {
+      const int64_t row = MODE == kDecGateUp ? s_pair[mm] / a.topk : r0 + mm;
+      v = *(const u32x4_t*)(a.X + row * a.ldx + k8 * 8);
+    }
+    *(u32x4_t*)(xs + i * 8) = v;
+  }
+  __syncthreads();
+  const uint16_t* xrow = xs + (mvalid ? m : 0) * (K + 8) + 8 * g;
+
+  float acc[NI];
+#pragma unroll
+  for (int i = 0; i < NI; ++i) acc[i] = 0.0f;
+  auto compute = [&](const Stage& s, int c) {
+    vec av[kBlocksPerChunk];
+#pragma unroll
+    for (int j = 0; j < kBlocksPerChunk; ++j) av[j] = *(const vec*)(xrow + c * kChunkK + j * 32);
+    gemv_mma<FMT, XDT, NI>(s, av, acc);
+  };
+  // Chunks of this wave: ks + i KSH, i < nw; full groups of P prefetch the
+  // next group, the last (possibly partial) group issues no loads.
+  const int nw = (nchunks - ks + KSH - 1) / KSH;
+  int i0 = 0;
+  for (; i0 + P < nw; i0 += P) {
+#pragma unroll
+    for (int p = 0; p < P; ++p) {
+      const int c = ks + (i0 + p) * KSH;
+      compute(st[p], c);
+      __builtin_amdgcn_sched_barrier(0);
+      gemv_load<FMT>(st[p], wres, c + P * KSH, lane, r);
+    }
+  }
+#pragma unroll
+  for (int p = 0; p < P; ++p)
+    if (i0 + p < nw) compute(st[p], ks + (i0 + p) * KSH);
+
+  __shared__ float red[WAVES][NI][64];
+  if (KS > 1) {   // uniform over the workgroup
+#pragma unroll
+    for (int i = 0; i < NI; ++i) red[wave][i][lane] = acc[i];
+    __syncthreads();
+    if (kw != 0) return;
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      float v = red[wave][i][lane];
+      for (int w = 1; w < KSH; ++w) v += red[wave + w][i][lane];
+      if (MODE == kDecGateUp) {
+        float u = red[wave + KSH][i][lane];
+        for (int w = 1; w < KSH; ++w) u += red[wave + KSH + w][i][lane];
+        v = silu_f32(v) * u;
+      }
+      acc[i] = v;
+    }
+  }
+  if (!tile_ok) return;
+  // Lane (r, g), register i holds row m = 4 i + g, output n = 16 tile + r.
+  const int n = tile * kTileRows + r;
+#pragma unroll
+  for (int i = 0; i < NI; ++i) {
+    const int mo = 4 * i + g;
+    if (mo < M) {
+      if (MODE == kDecGateUp) {
+        a.out[(int64_t)(r0 + mo) * N + n] = __builtin_bit_cast(uint16_t, (__bf16)acc[i]);
+      } else {
+        const int pair = s_pair[mo];
+        a.out[(int64_t)pair * N + n] = __builtin_bit_cast(uint16_t, (_Float16)acc[i]);
+      }
+    }
+  }
+}
+
+namespace {
+
+constexpr int kDecWaves = 8;
+constexpr int kDecRing = 4;
+
+// K-shares per matrix: split K while the busiest case (every pair on its
+// own expert) stays below about 4096 waves, each wave keeps >= 3 chunks and
+// the tile's waves fit the workgroup.
+int dec_ksh(int nchunks, int mats, int64_t tile_waves) {
+  int ksh = 1;
+  while (ksh * 2 * mats <= kDecWaves && nchunks >= 3 * ksh * 2 && tile_waves * ksh * 2 <= 4096) ksh *= 2;
+  return ksh;
+}
+
+template <int FMT, int XDT, int MODE>
+void launch_dec(MoeDecArgs a, int T, int npos, hipStream_t s) {
+  const int mats = MODE == kDecGateUp ? 2 : 1;
+  const int64_t experts = std::min(npos, a.E);
+  a.ksh = dec_ksh(a.K / kChunkK, mats, experts * (a.N / kTileRows) * mats);
+  const int tpw = kDecWaves / (a.ksh * mats);
+  a.groups = (a.N / kTileRows + tpw - 1) / tpw;
+  const dim3 grid((unsigned)(npos * a.groups)), block(kDecWaves * 64);
+  const size_t lds = (size_t)T * (a.K + 8) * 2 + kDecXSlack;
+  if (T > 4)
+    moe_gemv_kernel<FMT, XDT, MODE, 2, kDecWaves, kDecRing><<<grid, block, lds, s>>>(a);
+  else
+    moe_gemv_kernel<FMT, XDT, MODE, 1, kDecWaves, kDecRing><<<grid, block, lds, s>>>(a);
+}
+
+template <int FMT>
+void launch_dec_fmt(int xdt, const void* Wg, const void* Wu, const void* Wd, int E, int H, int F, const void* X,
+                    int T, int topk, const int32_t* offsets, const int32_t* sorted_pairs, uint16_t* h,
+                    uint16_t* y16, hipStream_t s) {
+  const int npos = T * topk;
+  MoeDecArgs a;
+  a.offsets = offsets;
+  a.sorted_pairs = sorted_pairs;
+  a.topk = topk;
+  a.E = E;
+  a.npos = npos;
+  // gate/up: [F, H] per expert, x = the tokens.
+  a.W = (const uint8_t*)Wg;
+  a.W2 = (const uint8_t*)Wu;
+  a.mat_bytes = (int64_t)(F / kTileRows) * (H / kChunkK) * Fmt<FMT>::kRecBytes;
+  a.X = (const uint16_t*)X;
+  a.ldx = H;
+  a.out = h;
+  a.N = F;
+  a.K = H;
+  if (xdt == kF16) launch_dec<FMT, kF16, kDecGateUp>(a, T, npos, s);
+  else launch_dec<FMT, kBF16, kDecGateUp>(a, T, npos, s);
+  // down: [H, F] per expert, x = the h rows.
+  a.W = (const uint8_t*)Wd;
+  a.W2 = nullptr;
+  a.mat_bytes = (int64_t)(H / kTileRows) * (F / kChunkK) * Fmt<FMT>::kRecBytes;
+  a.X = h;
+  a.ldx = F;
+  a.out = y16;
+  a.N = H;
+  a.K = F;
+  launch_dec<FMT, kBF16, kDecDown>(a, T, npos, s);
+}
+
+}  // namespace
+
+bool moe_decode_fits(int T, int H, int F) {
+  const int64_t k = H > F ? H : F;
+  // Dynamic LDS plus the static buffers (reduction, offsets) stay within 64 KB.
+  return T >= 1 && T <= kMoeDecodeMaxTokens && (int64_t)T * (k + 8) * 2 + kDecXSlack <= 52 * 1024;
+}
+
+void launch_moe_decode(int fmt, int xdt, const void* Wg, const void* Wu, const void* Wd, int E, int H, int F,
+                       const void* X, int T, int topk, const int32_t* offsets, const int32_t* sorted_pairs,
+                       uint16_t* h, uint16_t* y16, hipStream_t s) {
+  if (fmt == kQ4_0)
+    launch_dec_fmt<kQ4_0>(xdt, Wg, Wu, Wd, E, H, F, X, T, topk, offsets, sorted_pairs, h, y16, s);
+  else
+    launch_dec_fmt<kQ8_0>(xdt, Wg, Wu, Wd, E, H, F, X, T, topk, offsets, sorted_pairs, h, y16, s);
+}
+
+}  // namespace q4q8

@@ -174,6 +174,9 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t uniform_rsrc(const void* base,
   return __builtin_amdgcn_make_buffer_rsrc((void*)(((uint64_t)hi << 32) | lo), (short)0, n, 0x00020000);
 }
 
+// silu(z) = z / (1 + exp(-z)), fp32 (the SwiGLU gate activation).
+__device__ __forceinline__ float silu_f32(float z) { return z / (1.0f + expf(-z)); }
+
 __device__ __forceinline__ float half_bits_to_float(uint32_t bits16) {
   return (float)__builtin_bit_cast(_Float16, (uint16_t)bits16);
 }

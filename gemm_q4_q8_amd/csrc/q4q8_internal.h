@@ -25,18 +25,24 @@ inline void launch(K kernel, dim3 grid, dim3 block, uint32_t shmem, hipStream_t 
 
 constexpr int kMaxGroup = 8;
 
-// One GEMV problem as the kernel sees it.
+// One GEMV problem as the kernel sees it.  A SwiGLU pair has W = gate and
+// W2 = up weights (same shape, same x) and stores h = silu(W x) * (W2 x) as
+// ydt; a plain problem has W2 = null and stores fp32 dot products.
 struct GemvProb {
   const uint8_t* W;
+  const uint8_t* W2;
   const uint16_t* x;
-  float* y;
+  void* y;
   int64_t ldx, ldy;
   int32_t N, K;
+  int32_t ydt;   // output dtype of a pair (kF16, kBF16, kF32); unused otherwise
+  int32_t pad;
 };
 
 struct GemvArgs {
   int32_t wg0[kMaxGroup];   // first workgroup of each problem (set by the launcher)
-  int32_t ks[kMaxGroup];    // K-shares per tile of each problem, a power of 2 dividing the waves per workgroup
+  int32_t ks[kMaxGroup];    // waves per tile of each problem (a pair: 2 x its K-shares), a power of 2
+                            // dividing the waves per workgroup
   int32_t count;
   int32_t M;
   int32_t total_tiles;
@@ -62,6 +68,15 @@ hipError_t launch_moe_route(const float* logits, int T, int E, int topk, int32_t
                             int32_t* counts, int32_t* offsets, int32_t* sorted_pairs, hipStream_t stream);
 
 size_t moe_workspace_bytes(int fmt, int T, int E, int topk, int H, int F);
+
+// Decode path of the expert products (GEMV kernels), used for T <= 8 tokens
+// when the token rows fit the workgroup's activation buffer.  h: bf16
+// [T*topk, F] in sorted-pair order; y16: fp16 [T*topk, H] by pair id.
+constexpr int kMoeDecodeMaxTokens = 8;
+bool moe_decode_fits(int T, int H, int F);
+void launch_moe_decode(int fmt, int xdt, const void* Wg, const void* Wu, const void* Wd, int E, int H, int F,
+                       const void* X, int T, int topk, const int32_t* offsets, const int32_t* sorted_pairs,
+                       uint16_t* h, uint16_t* y16, hipStream_t s);
 
 hipError_t launch_moe_qgemm(int fmt, int xdt, const void* Wg, const void* Wu, const void* Wd, int E, int H, int F,
                             const void* X, int T, int topk, const float* gates, const int32_t* offsets,

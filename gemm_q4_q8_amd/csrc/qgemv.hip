@@ -5,7 +5,7 @@
 // specialisation) run decode on a GEMV per quantisation format that
 // dequantises inside its inner loop.  On gfx950 the inner product of each
 // 32-weight block is one v_mfma_f32_16x16x32 instruction instead of lane FMAs
-// plus a cross-lane reduction:
+// plus a cross-lane reduction (gemv_core.h):
 //   * a wavefront owns a tile of 16 weight rows and a share of K; a workgroup
 //     of WAVES waves holds WAVES / KS tiles x KS K-shares, KS chosen per
 //     problem of a grouped launch so that every wave streams about as many
@@ -13,19 +13,14 @@
 //     at the end (split-K without atomics or workspace);
 //   * the activation rows are staged once per workgroup in LDS; each lane
 //     reads its 16-byte A fragment from there;
-//   * weights stream through buffer loads: per chunk (4 blocks) a lane loads
-//     16 (Q4_0) or 32 (Q8_0) contiguous bytes of codes -- the wave reads 1 or
-//     2 KB contiguous -- plus its row's 4 fp16 scales, into a ring of P chunks
-//     in flight.  The buffer range is the tile itself, so loads past its end
-//     return zero (scale 0) and tails need no branches;
-//   * codes are unpacked in registers straight into the MFMA B operand; they
-//     are exact in the operand type (fp16 or bf16) and the block scale is
-//     applied in fp32, so every product is exact and only the fp32
-//     accumulation rounds;
-//   * activation row m sits in A row 4 (m % 4) + m / 4, so for every m < 4 the
-//     result lands in the first accumulator register of each lane (m < 8:
-//     the first two): one FMA per lane per block applies the scale for M <= 4.
-#include "q4q8_dev.h"
+//   * weights stream through buffer loads into a ring of P chunks in flight.
+//     The buffer range is the tile itself, so loads past its end return zero
+//     (scale 0) and tails need no branches;
+//   * a SwiGLU pair (gate and up rows of one FFN, same x) spends half of a
+//     tile's waves on each matrix and forms h = silu(gate) * up in the
+//     reduction, so neither product reaches memory (technical summary,
+//     "Methodologie", fusion of feed-forward operator sequences).
+#include "gemv_core.h"
 #include "q4q8_internal.h"
 
 #include <stdlib.h>
@@ -34,10 +29,6 @@
 
 namespace q4q8 {
 
-constexpr int kBufFlags = 0x00020000;   // raw buffer, 32-bit data format (gfx9)
-#ifndef Q4Q8_WEIGHT_AUX
-#define Q4Q8_WEIGHT_AUX 0               // cache policy bits of the weight loads
-#endif
 constexpr int kXSlack = 512;            // zeroed LDS bytes after the activation rows
 constexpr int XP = 4;                   // x pieces per thread staged before the prefetch
 constexpr int64_t kLdsTotal = 160 * 1024;          // LDS per workgroup on gfx950
@@ -46,9 +37,8 @@ constexpr int64_t kLdsCap = kLdsTotal - 8 * 1024;  // dynamic LDS for the activa
 template <int FMT, int XDT, int NI, int WAVES, int P, bool XLDS>
 __global__ __launch_bounds__(WAVES * 64) void qgemv_kernel(const GemvArgs args) {
   constexpr int REC = Fmt<FMT>::kRecBytes;
-  constexpr int CODE = Fmt<FMT>::kCodeBytes;
-  constexpr int NV = FMT == kQ4_0 ? 1 : 2;
   typedef typename Op<XDT>::vec vec;
+  typedef GemvStage<FMT> Stage;
   extern __shared__ __attribute__((aligned(16))) uint16_t xs[];
 
   // Problem of the group that owns this workgroup.  Problem 0's fields are
@@ -68,9 +58,15 @@ __global__ __launch_bounds__(WAVES * 64) void qgemv_kernel(const GemvArgs args) 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int KS = __builtin_amdgcn_readfirstlane(args.ks[pi]);   // power of 2 dividing WAVES
+  const int KS = __builtin_amdgcn_readfirstlane(args.ks[pi]);   // waves per tile, a power of 2 dividing WAVES
   const int TPW = WAVES / KS;
-  const int slot = wave / KS, ks = wave & (KS - 1);
+  const int slot = wave / KS, kw = wave & (KS - 1);
+  // A SwiGLU pair spends the first half of a tile's waves on the gate rows
+  // and the second half on the same rows of the up matrix.
+  const bool pair = prob.W2 != nullptr;
+  const int KSH = pair ? KS >> 1 : KS;           // K-shares per matrix
+  const bool up = pair && kw >= KSH;
+  const int ks = up ? kw - KSH : kw;             // this wave's K-share
   const int tile = (bid - args.wg0[pi]) * TPW + slot;
   const bool tile_ok = tile < tiles;
   const int r = lane & 15, g = lane >> 4;
@@ -78,21 +74,10 @@ __global__ __launch_bounds__(WAVES * 64) void qgemv_kernel(const GemvArgs args) 
   const bool mvalid = m < args.M;
 
   // Buffer over this tile's records only: past the end reads return zero.
-  const uint8_t* tbase = prob.W + (int64_t)(tile_ok ? tile : 0) * nchunks * REC;
+  const uint8_t* tbase = (up ? prob.W2 : prob.W) + (int64_t)(tile_ok ? tile : 0) * nchunks * REC;
   const __amdgpu_buffer_rsrc_t wres =
-      __builtin_amdgcn_make_buffer_rsrc((void*)tbase, (short)0, tile_ok ? nchunks * REC : 0, kBufFlags);
-
-  struct Stage {
-    u32x4_t codes[NV];
-    u32x2_t sc;
-  };
-  auto load = [&](Stage& st, int c) {
-    const int off = c * REC;
-#pragma unroll
-    for (int v = 0; v < NV; ++v)
-      st.codes[v] = __builtin_amdgcn_raw_buffer_load_b128(wres, off + v * 1024 + lane * 16, 0, Q4Q8_WEIGHT_AUX);
-    st.sc = __builtin_amdgcn_raw_buffer_load_b64(wres, off + CODE + r * 8, 0, Q4Q8_WEIGHT_AUX);
-  };
+      __builtin_amdgcn_make_buffer_rsrc((void*)tbase, (short)0, tile_ok ? nchunks * REC : 0, kGemvBufFlags);
+  auto load = [&](Stage& st, int c) { gemv_load<FMT>(st, wres, c, lane, r); };
 
   // Activations: LDS rows of K + 8 halfs (the pad staggers rows over banks),
   // plus kXSlack zeroed bytes after the last row.  x is loaded first, then
@@ -114,7 +99,7 @@ __global__ __launch_bounds__(WAVES * 64) void qgemv_kernel(const GemvArgs args) 
       xv[u] = (mm < M && k8 < K / 8) ? *(const u32x4_t*)(xg + (int64_t)mm * prob.ldx + k8 * 8) : u32x4_t{0, 0, 0, 0};
     }
 #pragma unroll
-    for (int p = 0; p < P; ++p) load(st[p], ks + p * KS);   // past the tile: zero, no memory traffic
+    for (int p = 0; p < P; ++p) load(st[p], ks + p * KSH);   // past the tile: zero, no memory traffic
 #pragma unroll
     for (int u = 0; u < XP; ++u) {
       const int i = tid + u * WAVES * 64;
@@ -129,7 +114,7 @@ __global__ __launch_bounds__(WAVES * 64) void qgemv_kernel(const GemvArgs args) 
     __syncthreads();
   } else {
 #pragma unroll
-    for (int p = 0; p < P; ++p) load(st[p], ks + p * KS);
+    for (int p = 0; p < P; ++p) load(st[p], ks + p * KSH);
   }
   const int xrow_lds = (mvalid ? m : 0) * ldsx + 8 * g;
   const uint16_t* __restrict__ xrow_g = xg + (mvalid ? (int64_t)m * prob.ldx : 0) + 8 * g;
@@ -153,49 +138,44 @@ __global__ __launch_bounds__(WAVES * 64) void qgemv_kernel(const GemvArgs args) 
         a[j] = *(const vec*)(xrow_g + blk * 32);
       }
     }
-    float4_t d[kBlocksPerChunk];
-#pragma unroll
-    for (int j = 0; j < kBlocksPerChunk; ++j) {
-      const u32x4_t b = deq_block<FMT, XDT>(s.codes, j);
-      d[j] = Op<XDT>::mfma(a[j], __builtin_bit_cast(vec, b), float4_t{0.0f, 0.0f, 0.0f, 0.0f});
-    }
-#pragma unroll
-    for (int j = 0; j < kBlocksPerChunk; ++j) {
-      const uint32_t sbits = (j & 1) ? (s.sc[j >> 1] >> 16) : (s.sc[j >> 1] & 0xFFFFu);
-      const float sf = half_bits_to_float(sbits);
-#pragma unroll
-      for (int i = 0; i < NI; ++i) acc[i] = __builtin_fmaf(sf, d[j][i], acc[i]);
-    }
+    gemv_mma<FMT, XDT, NI>(s, a, acc);
   };
 
-  // Chunks of this wave: ks + i KS for i < nw.  Stage p holds chunk i with
+  // Chunks of this wave: ks + i KSH for i < nw.  Stage p holds chunk i with
   // i % P == p; full groups of P prefetch the next group, the last group
   // (possibly partial) issues no loads, so no load runs past the wave's share.
-  const int nw = (nchunks - ks + KS - 1) / KS;
+  const int nw = (nchunks - ks + KSH - 1) / KSH;
   int i0 = 0;
   for (; i0 + P < nw; i0 += P) {
 #pragma unroll
     for (int p = 0; p < P; ++p) {
-      const int c = ks + (i0 + p) * KS;
+      const int c = ks + (i0 + p) * KSH;
       compute(st[p], c);
       __builtin_amdgcn_sched_barrier(0);
-      load(st[p], c + P * KS);
+      load(st[p], c + P * KSH);
     }
   }
 #pragma unroll
   for (int p = 0; p < P; ++p)
-    if (i0 + p < nw) compute(st[p], ks + (i0 + p) * KS);
+    if (i0 + p < nw) compute(st[p], ks + (i0 + p) * KSH);
 
   if (KS > 1) {   // uniform over the workgroup
     __shared__ float red[WAVES][NI][64];
 #pragma unroll
     for (int i = 0; i < NI; ++i) red[wave][i][lane] = acc[i];
     __syncthreads();
-    if (ks != 0) return;
+    if (kw != 0) return;
+    // Fixed order: K-shares 0..KSH-1 of the gate (or plain) rows, then of the
+    // up rows; SwiGLU in fp32.
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
       float v = red[wave][i][lane];
-      for (int w = 1; w < KS; ++w) v += red[wave + w][i][lane];
+      for (int w = 1; w < KSH; ++w) v += red[wave + w][i][lane];
+      if (pair) {
+        float u = red[wave + KSH][i][lane];
+        for (int w = 1; w < KSH; ++w) u += red[wave + KSH + w][i][lane];
+        v = silu_f32(v) * u;
+      }
       acc[i] = v;
     }
   }
@@ -205,7 +185,15 @@ __global__ __launch_bounds__(WAVES * 64) void qgemv_kernel(const GemvArgs args) 
 #pragma unroll
   for (int i = 0; i < NI; ++i) {
     const int mo = 4 * i + g;
-    if (mo < args.M && n < N) prob.y[(int64_t)mo * prob.ldy + n] = acc[i];
+    if (mo < args.M && n < N) {
+      const int64_t o = (int64_t)mo * prob.ldy + n;
+      if (!pair || prob.ydt == kF32)
+        ((float*)prob.y)[o] = acc[i];
+      else if (prob.ydt == kBF16)
+        ((__bf16*)prob.y)[o] = (__bf16)acc[i];
+      else
+        ((_Float16*)prob.y)[o] = (_Float16)acc[i];
+    }
   }
 }
 
@@ -297,19 +285,26 @@ hipError_t launch_qgemv(int fmt, int xdt, GemvArgs args, int max_chunks, int max
   // Problems of one K share the launch-wide split.  When K differs, the
   // workgroup is 8 waves and each problem takes the power-of-2 split closest
   // to 16 chunks per wave, so the long-K problems do not trail the launch.
-  bool mixed = false;
+  // A SwiGLU pair takes twice its K-shares in waves (gate and up halves).
+  bool mixed = false, pairs = false;
   for (int i = 1; i < args.count; ++i) mixed |= args.p[i].K != args.p[0].K;
+  for (int i = 0; i < args.count; ++i) pairs |= args.p[i].W2 != nullptr;
   int waves = c.ks * c.tpw;
   if (mixed && !getenv("Q4Q8_GEMV_KS")) {
     waves = c.ks > 8 ? c.ks : 8;
     for (int i = 0; i < args.count; ++i) {
       const int nch = (args.p[i].K + kChunkK - 1) / kChunkK;
+      const int mats = args.p[i].W2 ? 2 : 1;
       int ks = 1;
-      while (ks < waves && nch >= 24 * ks) ks *= 2;   // nch / ks nearest 16 among powers of 2
-      args.ks[i] = ks;
+      while (ks * mats < waves && nch >= 24 * ks) ks *= 2;   // nch / ks nearest 16 among powers of 2
+      args.ks[i] = ks * mats;
     }
   } else {
-    for (int i = 0; i < args.count; ++i) args.ks[i] = c.ks;
+    if (pairs && waves < 2 * c.ks) waves = 2 * c.ks > 16 ? 16 : 2 * c.ks;
+    for (int i = 0; i < args.count; ++i) {
+      const int ks = args.p[i].W2 ? (2 * c.ks > waves ? waves : 2 * c.ks) : c.ks;
+      args.ks[i] = ks;
+    }
   }
   // Workgroup ranges per problem.
   int wgs = 0;

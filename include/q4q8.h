@@ -161,6 +161,64 @@ int q4q8_qgemv_grouped_timed(int fmt, const q4q8_gemv_desc* descs, int count,
                              void* ev_start, void* ev_stop);
 
 /* ------------------------------------------------------------------------ */
+/* Decode FFN: fused gate/up GEMV with a SwiGLU epilogue, then down          */
+/* (technical summary, "Methodologie": kernel fusion of FFN blocks, which    */
+/*  matters in decode where kernels are short; the SwiGLU expert form is    */
+/*  this library's reading, as for the mixture-of-experts path below)       */
+/* ------------------------------------------------------------------------ */
+
+/* h[m, f] = silu(zg) * zu  with  zg = sum_k Wg[f, k] x[m, k],
+ *                               zu = sum_k Wu[f, k] x[m, k],
+ * silu(z) = z / (1 + exp(-z)), for m < M <= 8, f < F, in one launch: both
+ * matrices stream in the same workgroups and h is formed in registers, so
+ * neither zg nor zu reaches memory.
+ *   Wg, Wu: repacked [F, K] weights of one format (device, 16-byte aligned).
+ *   x:      as for q4q8_qgemv (shared by both products).
+ *   h:      device, dtype hdt (F16, BF16 or F32), row m at h + m*ldh,
+ *           ldh >= F when M > 1, aligned to its element size.  Rounded once
+ *           from the fp32 value.
+ * Rules and errors as for q4q8_qgemv. */
+int q4q8_qgemv_swiglu(int fmt, const void* Wg, const void* Wu, int64_t F,
+                      int64_t K, const void* x, int xdt, int64_t ldx, int M,
+                      void* h, int hdt, int64_t ldh, void* stream);
+
+/* As q4q8_qgemv_swiglu, with dispatch-recorded events (see
+ * q4q8_qgemv_grouped_timed).  For measurement; the result is identical. */
+int q4q8_qgemv_swiglu_timed(int fmt, const void* Wg, const void* Wu,
+                            int64_t F, int64_t K, const void* x, int xdt,
+                            int64_t ldx, int M, void* h, int hdt,
+                            int64_t ldh, void* stream, void* ev_start,
+                            void* ev_stop);
+
+/* Workspace bytes of q4q8_ffn_decode: the bf16 h rows, M * F * 2 rounded up
+ * to 256.  0 for M outside 1..8 or F not a positive multiple of 32. */
+size_t q4q8_ffn_decode_workspace(int M, int64_t F);
+
+/* The decode FFN of a layer, two launches on `stream`:
+ *   h = silu(x Wg^T) * (x Wu^T)   (q4q8_qgemv_swiglu, h as bf16 in ws)
+ *   y = h Wd^T                    (q4q8_qgemv, fp32)
+ *   Wg, Wu: repacked [F, H]; Wd: repacked [H, F]; one format.
+ *   x:      M rows of H activations (F16/BF16), as for q4q8_qgemv.
+ *   y:      device fp32, row m at y + m*ldy, ldy >= H when M > 1.
+ *   ws:     device, >= q4q8_ffn_decode_workspace(M, F) bytes, 256-byte
+ *           aligned; overwritten.  Once the stream has run the call it
+ *           holds h, bf16 [M, F] row-major (row stride F).
+ * Every argument of both launches is validated before the first is
+ * enqueued.  Errors: as q4q8_qgemv, plus Q4Q8_ERR_WORKSPACE. */
+int q4q8_ffn_decode(int fmt, const void* Wg, const void* Wu, const void* Wd,
+                    int64_t H, int64_t F, const void* x, int xdt,
+                    int64_t ldx, int M, float* y, int64_t ldy, void* ws,
+                    size_t ws_bytes, void* stream);
+
+/* As q4q8_ffn_decode, with ev_start recorded when the first kernel starts
+ * and ev_stop when the second ends.  For measurement. */
+int q4q8_ffn_decode_timed(int fmt, const void* Wg, const void* Wu,
+                          const void* Wd, int64_t H, int64_t F,
+                          const void* x, int xdt, int64_t ldx, int M,
+                          float* y, int64_t ldy, void* ws, size_t ws_bytes,
+                          void* stream, void* ev_start, void* ev_stop);
+
+/* ------------------------------------------------------------------------ */
 /* Prefill: quantised GEMM                                                   */
 /* (technical summary, "Methodologie", prefill optimisation: tiled GEMM on  */
 /*  matrix intrinsics; review, "Method": prefill GEMM on the matrix units)  */
@@ -237,7 +295,13 @@ size_t q4q8_moe_workspace(int fmt, int T, int E, int topk, int H, int F);
  *   ws:     device workspace of >= q4q8_moe_workspace(...) bytes, 256-byte
  *           aligned; contents need no initialisation and are clobbered.
  * H % 128 == 0 and F % 128 == 0.  Pairs of one expert are processed
- * together, so each expert's weights are streamed once per call. */
+ * together, so each expert's weights are streamed once per call.
+ * Kernel choice (review, "Method": memory-bound decode stays on the GEMV
+ * kernels, compute-bound prefill goes to the matrix-unit tiles): up to 8
+ * tokens whose rows fit 52 KB of LDS (8 x max(H, F) halfs) run on GEMV
+ * kernels, each expert's routed tokens as its activation rows; larger T on
+ * 64-row matrix-core tiles.  Both paths round h to bf16 and y to fp16 and
+ * combine in the same fixed order. */
 int q4q8_moe_qgemm(int fmt, const void* Wg, const void* Wu, const void* Wd,
                    int E, int H, int F, const void* X, int xdt, int T,
                    int topk, const float* gates,

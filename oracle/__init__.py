@@ -29,7 +29,10 @@ the pages; the oracle takes these readings:
 * Sorting: pairs p = t*k + j are ordered by (expert, p); counts and offsets are
   the histogram and its exclusive scan.
 * Expert: h = silu(x W_gate^T) * (x W_up^T), y = h W_down^T,
-  out[t] = sum_j gate[t, j] * y[pair(t, j)].
+  out[t] = sum_j gate[t, j] * y[pair(t, j)].  The decode FFN (ffn) is the
+  same SwiGLU block on a dense layer; the pages credit fusing such
+  feed-forward operator sequences for decode (technical summary,
+  "Methodologie", fusion).
 
 Every function returns float64 (or exact integers).  Error bounds returned
 next to the values are the sums of |w*x| that the acceptance rule scales.
@@ -244,6 +247,35 @@ def moe_ffn(fmt: int, wg, wu, wd, x: np.ndarray, ids: np.ndarray, gates: np.ndar
         out[t] += g[p] * y[r]
         bout[t] += g[p] * by[r]
     return dict(zg=zg, zu=zu, bg=bg, bu=bu, h=h, y=y, by=by, out=out, bout=bout)
+
+
+def ffn(fmt: int, wg, wu, wd, x: np.ndarray, H: int, F: int, h_override=None):
+    """Dense SwiGLU FFN of a decode step (the fused gate/up GEMV, then down).
+
+    wg, wu: canonical [F, H]; wd: canonical [H, F]; x: [M, H] fp64.
+    Returns zg, zu, bg, bu, h = silu(zg) * zu  [M, F]; y = h W_down^T and its
+    bound by = |h| |W_down|^T  [M, H] (omitted when wd is None: the gate/up
+    stage alone).  h_override replaces h as the input of the down projection
+    (to check that stage on its own).
+    """
+    x = np.asarray(x, dtype=np.float64)
+    Wg, Wu = dequant(fmt, wg, F, H), dequant(fmt, wu, F, H)
+    zg, zu = x @ Wg.T, x @ Wu.T
+    h = silu(zg) * zu
+    r = dict(zg=zg, zu=zu, bg=np.abs(x) @ np.abs(Wg).T, bu=np.abs(x) @ np.abs(Wu).T, h=h)
+    if wd is not None:
+        Wd = dequant(fmt, wd, H, F)
+        hin = h if h_override is None else np.asarray(h_override, dtype=np.float64)
+        r.update(y=hin @ Wd.T, by=np.abs(hin) @ np.abs(Wd).T)
+    return r
+
+
+def ffn_out_bound(fmt: int, wd, r: dict, hb: np.ndarray, H: int, F: int, rel: float = 2e-3,
+                  abs_tol: float = 1e-5) -> np.ndarray:
+    """First-order bound on |y_gpu - y| of the FFN: the down dot products'
+    own tolerance plus the input error hb carried through |W_down|."""
+    Wd = dequant(fmt, wd, H, F)
+    return rel * r["by"] + hb @ np.abs(Wd).T + abs_tol
 
 
 def moe(fmt: int, wg, wu, wd, x, logits, topk: int, H: int, F: int):

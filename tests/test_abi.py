@@ -139,6 +139,38 @@ def test_grouped_validation(q):
     assert "qgemv" in q.last_error() or "K=" in q.last_error()
 
 
+def test_swiglu_validation(q):
+    L = q.lib()
+    ok = dict(fmt=1, Wg=0x1000, Wu=0x5000, F=64, K=256, x=0x2000, xdt=2, ldx=256, M=3, h=0x3000, hdt=2, ldh=64)
+    for over, want in [(dict(Wu=None), -1), (dict(Wu=0x5008), -4), (dict(hdt=0), -2),
+                       (dict(hdt=3, h=0x3002), -4), (dict(h=0x3001), -4), (dict(ldh=32), -1), (dict(M=9), -1),
+                       (dict(K=100), -1), (dict(xdt=3), -2)]:
+        a = dict(ok)
+        a.update(over)
+        st = L.q4q8_qgemv_swiglu(a["fmt"], _vp(a["Wg"]), _vp(a["Wu"]) if a["Wu"] else None, a["F"], a["K"],
+                                 _vp(a["x"]), a["xdt"], a["ldx"], a["M"], _vp(a["h"]), a["hdt"], a["ldh"], None)
+        assert st == want, (over, st, q.last_error())
+
+
+def test_ffn_decode_validation(q):
+    L = q.lib()
+    assert q.ffn_decode_workspace(3, 14336) == (3 * 14336 * 2 + 255) // 256 * 256
+    assert q.ffn_decode_workspace(0, 128) == 0 and q.ffn_decode_workspace(9, 128) == 0
+    assert q.ffn_decode_workspace(1, 100) == 0
+    nws = q.ffn_decode_workspace(2, 256)
+    ok = dict(fmt=2, Wg=0x1000, Wu=0x2000, Wd=0x3000, H=512, F=256, x=0x4000, xdt=1, ldx=512, M=2, y=0x5000,
+              ldy=512, ws=0x100000, nws=nws)
+    for over, want in [(dict(ws=0), -3), (dict(nws=nws - 1), -3), (dict(ws=0x100010), -4), (dict(F=100), -1),
+                       (dict(Wd=None), -1), (dict(Wd=0x3008), -4), (dict(ldy=100), -1), (dict(y=0x5002), -4),
+                       (dict(M=0), -1), (dict(fmt=0), -2)]:
+        a = dict(ok)
+        a.update(over)
+        st = L.q4q8_ffn_decode(a["fmt"], _vp(a["Wg"]), _vp(a["Wu"]), _vp(a["Wd"]) if a["Wd"] else None, a["H"],
+                               a["F"], _vp(a["x"]), a["xdt"], a["ldx"], a["M"], _vp(a["y"]), a["ldy"],
+                               _vp(a["ws"]) if a["ws"] else None, a["nws"], None)
+        assert st == want, (over, st, q.last_error())
+
+
 def test_qgemm_validation(q):
     L = q.lib()
     ok = dict(fmt=1, W=0x1000, N=64, K=256, X=0x2000, xdt=2, ldx=256, M=17, Y=0x3000, ydt=2, ldy=64)

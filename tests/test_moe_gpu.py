@@ -1,5 +1,9 @@
 """GPU parity of the MoE path against the CPU oracle.
 
+Two kernel paths sit behind q4q8_moe_qgemm: MFMA row tiles for prefill
+(T > 8 tokens) and GEMV kernels for decode (T <= 8); the cases below cover
+both, including the benchmark's MoE shape at T = 1 and 8.
+
 Routing and the permutation (ids, counts, offsets, sorted_pairs) must match
 bit for bit; gates within 2e-3 relative; h (the bf16 SwiGLU output, read back
 through h_out) within the first-order bound propagated from the per-dot-
@@ -133,6 +137,43 @@ def test_moe_parity(q, fmt, xdt, T, E, k, H, F):
     _check_moe(fmt, logits, x, wg, wu, wd, k, H, F, got, f"moe fmt{fmt} T{T} E{E} k{k} H{H} F{F}")
 
 
+DECODE_CASES = [
+    # fmt, xdt, T, E, k, H, F
+    (synth.Q8_0, synth.F16, 3, 16, 4, 512, 384),
+    (synth.Q4_0, synth.F16, 5, 8, 8, 256, 128),      # topk = E: every expert takes all 5 tokens
+    (synth.Q8_0, synth.BF16, 8, 4, 2, 128, 256),     # up to 8 rows per expert
+    (synth.Q4_0, synth.BF16, 2, 1024, 16, 128, 128),
+    (synth.Q4_0, synth.BF16, 7, 64, 8, 1024, 512),
+    (synth.Q8_0, synth.BF16, 1, 32, 1, 384, 128),
+]
+
+
+@pytest.mark.parametrize("fmt,xdt,T,E,k,H,F", DECODE_CASES)
+def test_moe_decode_parity(q, fmt, xdt, T, E, k, H, F):
+    seed = 120 + T + E + k
+    logits = synth.router_logits(synth.rng_for(seed, 0), T, E)
+    x = synth.activation(synth.rng_for(seed, 1), (T, H), xdt)
+    wg = [synth.q_weight(synth.rng_for(seed, 1000 + e), fmt, F, H) for e in range(E)]
+    wu = [synth.q_weight(synth.rng_for(seed, 2000 + e), fmt, F, H) for e in range(E)]
+    wd = [synth.q_weight(synth.rng_for(seed, 3000 + e), fmt, H, F) for e in range(E)]
+    got = _run_moe(q, fmt, logits, x, wg, wu, wd, k, H, F)
+    _check_moe(fmt, logits, x, wg, wu, wd, k, H, F, got, f"moe decode fmt{fmt} T{T} E{E} k{k} H{H} F{F}")
+
+
+def test_moe_decode_full_shape(q):
+    """The MoE workload's experts (E 128, top-8, H 2048, F 768, Q4_0) with
+    T = 1, 2, 8 decode tokens (every output), and T = 9 (the first prefill
+    size) on the same weights."""
+    cfg = synth.MOE
+    E, k, H, F = cfg["E"], cfg["topk"], cfg["H"], cfg["F"]
+    _, _, wg, wu, wd = synth.moe(T=1)
+    for T in (1, 2, 8, 9):
+        logits = synth.router_logits(synth.rng_for(130, T), T, E)
+        x = synth.activation(synth.rng_for(131, T), (T, H), synth.BF16)
+        got = _run_moe(q, synth.Q4_0, logits, x, wg, wu, wd, k, H, F)
+        _check_moe(synth.Q4_0, logits, x, wg, wu, wd, k, H, F, got, f"moe full shape T{T}")
+
+
 def test_moe_deterministic(q):
     T, E, k, H, F = 64, 8, 2, 256, 128
     logits = synth.router_logits(synth.rng_for(90, 0), T, E)
@@ -142,6 +183,11 @@ def test_moe_deterministic(q):
     wd = [synth.q_weight(synth.rng_for(90, 3000 + e), synth.Q4_0, H, F) for e in range(E)]
     a = _run_moe(q, synth.Q4_0, logits, x, wg, wu, wd, k, H, F)
     b = _run_moe(q, synth.Q4_0, logits, x, wg, wu, wd, k, H, F)
+    assert np.array_equal(a["out"], b["out"]) and np.array_equal(a["h"], b["h"])
+    # decode path (6 tokens)
+    a = _run_moe(q, synth.Q4_0, logits[:6], x6 := synth.act_from_values(x.values[:6], synth.BF16), wg, wu, wd, k,
+                 H, F)
+    b = _run_moe(q, synth.Q4_0, logits[:6], x6, wg, wu, wd, k, H, F)
     assert np.array_equal(a["out"], b["out"]) and np.array_equal(a["h"], b["h"])
 
 

@@ -394,3 +394,77 @@ def test_moe_bounds_catch_a_planted_error():
     g_bad = r["gates"][:, ::-1].copy()
     bad2 = oracle.moe_ffn(synth.Q4_0, cg, cu, cd, x.values, r["ids"], g_bad, r["sorted_pairs"], H, F)
     assert np.any(np.abs(bad2["out"] - r["out"]) > ob)
+
+
+# ----------------------------------------------------------------------------
+# Dense decode FFN (fused gate/up SwiGLU, then down)
+# ----------------------------------------------------------------------------
+def _logical(w, fmt):
+    """Dense weights from the logical draw (scales and codes, not the bytes)."""
+    off = 8 if fmt == synth.Q4_0 else 0
+    return w.scales.astype(np.float64).repeat(32, axis=1) * (w.codes.astype(np.float64) - off)
+
+
+def _ffn_weights(fmt, H, F, seed):
+    rng = [synth.rng_for(seed, i) for i in range(3)]
+    return (synth.q_weight(rng[0], fmt, F, H), synth.q_weight(rng[1], fmt, F, H),
+            synth.q_weight(rng[2], fmt, H, F))
+
+
+@pytest.mark.parametrize("fmt", [synth.Q4_0, synth.Q8_0])
+def test_ffn_matches_the_logical_draw(fmt):
+    H, F, M = 96, 64, 3
+    wg, wu, wd = _ffn_weights(fmt, H, F, 36)
+    x = synth.activation(synth.rng_for(36, 9), (M, H), synth.BF16).values
+    r = oracle.ffn(fmt, wg.canon, wu.canon, wd.canon, x, H, F)
+    zg, zu = x @ _logical(wg, fmt).T, x @ _logical(wu, fmt).T
+    h = [[a / (1.0 + math.exp(-a)) * b for a, b in zip(ra, rb)] for ra, rb in zip(zg, zu)]
+    assert np.allclose(r["h"], h, rtol=1e-12, atol=1e-13)
+    assert np.allclose(r["y"], np.array(h) @ _logical(wd, fmt).T, rtol=1e-12, atol=1e-12)
+
+
+def test_ffn_one_hot_closed_form():
+    """x = e_c: h[f] = silu(Wg[f, c]) * Wu[f, c], y = Wd h, from one column of codes."""
+    H, F = 64, 32
+    wg, wu, wd = _ffn_weights(synth.Q4_0, H, F, 37)
+    for c in (0, 31, 32, 63):
+        x = np.zeros((1, H))
+        x[0, c] = 1.0
+        r = oracle.ffn(synth.Q4_0, wg.canon, wu.canon, wd.canon, x, H, F)
+        g = [float(wg.scales[f, c // 32]) * (int(wg.codes[f, c]) - 8) for f in range(F)]
+        u = [float(wu.scales[f, c // 32]) * (int(wu.codes[f, c]) - 8) for f in range(F)]
+        h = np.array([a / (1.0 + math.exp(-a)) * b for a, b in zip(g, u)])
+        assert np.allclose(r["h"][0], h, rtol=1e-13, atol=1e-15)
+        y = [sum(float(wd.scales[n, f // 32]) * (int(wd.codes[n, f]) - 8) * h[f] for f in range(F))
+             for n in range(H)]
+        assert np.allclose(r["y"][0], y, rtol=1e-12, atol=1e-14)
+
+
+def test_ffn_is_a_one_expert_moe():
+    """With one expert and top-1 the gate is exactly 1 and the MoE layer is the FFN."""
+    H, F, T = 64, 32, 5
+    wg, wu, wd = _ffn_weights(synth.Q8_0, H, F, 38)
+    x = synth.activation(synth.rng_for(38, 9), (T, H), synth.F16).values
+    logits = synth.router_logits(synth.rng_for(38, 10), T, 1)
+    m = oracle.moe(synth.Q8_0, [wg.canon], [wu.canon], [wd.canon], x, logits, 1, H, F)
+    r = oracle.ffn(synth.Q8_0, wg.canon, wu.canon, wd.canon, x, H, F)
+    assert np.all(m["gates"] == 1.0)
+    assert np.array_equal(m["out"], r["y"])
+
+
+def test_ffn_bounds_catch_a_planted_error():
+    """h_bound / ffn_out_bound accept the oracle and reject silu on the wrong
+    projection and a transposed down matrix."""
+    H = F = 64
+    wg, wu, wd = _ffn_weights(synth.Q4_0, H, F, 39)
+    x = synth.activation(synth.rng_for(39, 9), (4, H), synth.BF16).values
+    r = oracle.ffn(synth.Q4_0, wg.canon, wu.canon, wd.canon, x, H, F)
+    hb = oracle.h_bound(r)
+    ob = oracle.ffn_out_bound(synth.Q4_0, wd.canon, r, hb, H, F)
+    assert np.all(ob > 0)
+    swapped = oracle.silu(r["zu"]) * r["zg"]
+    assert np.any(np.abs(swapped - r["h"]) > hb)
+    bad = oracle.ffn(synth.Q4_0, wg.canon, wu.canon, wd.canon, x, H, F, h_override=swapped)
+    assert np.any(np.abs(bad["y"] - r["y"]) > ob)
+    yt = r["h"] @ _logical(wd, synth.Q4_0)
+    assert np.any(np.abs(yt - r["y"]) > ob)
