@@ -33,9 +33,9 @@ the same layer (all seven matrices, M = 1).
 Other workloads (the dependency-order step at M = 1, one-launch steps at
 M = 2/4/8, the single 2048x2048 GEMV, the Q8_0 3B-shaped matrices, the
 layer's fused decode FFN at M = 1 and 8, the prefill GEMM at M = 512 and
-2048, the MoE layer at 512 tokens and its decode at 1 and 8 tokens) are
-reported under "workloads", each with its own algorithmic bytes / flops and
-time.
+2048, the MoE layer at 512 tokens and its decode at 1 and 8 tokens,
+prefill attention at S = 512 and 2048) are reported under "workloads", each
+with its own algorithmic bytes / flops and time.
 """
 from __future__ import annotations
 
@@ -338,6 +338,35 @@ def extra_workloads(q, torch, synth, ev: HipEvents, quick: bool):
     out += prefill_workloads(q, torch, synth, ev, quick)
     out.append(moe_workload(q, torch, synth))
     out += moe_decode_workloads(q, torch, synth, quick)
+    out += attn_workloads(q, torch, synth, ev, quick)
+    return out
+
+
+def attn_workloads(q, torch, synth, ev: HipEvents, quick: bool):
+    """Prefill attention, 8B-shaped heads (Hq 32, Hkv 8, D 128), causal, bf16,
+    S = 512 and 2048.  Flops = 4 D Hq B (S (S + 1) / 2) (QK^T and PV over the
+    visible pairs); time from dispatch events."""
+    out = []
+    dev = torch.device("cuda:0")
+    c = synth.ATTN
+    for S in ([2048] if quick else [512, 2048]):
+        qa, ka, va = synth.attention_inputs(c["B"], S, c["Hq"], c["Hkv"], c["D"], c["dt"], c["seed"])
+        t = [torch.from_numpy(a.bits.view("int16")).view(torch.bfloat16).to(dev) for a in (qa, ka, va)]
+        o = torch.empty_like(t[0])
+        reps = 24
+        pairs = [(ev.create(), ev.create()) for _ in range(reps + 4)]
+        for pr in pairs:
+            q.attn_prefill(*t, causal=True, out=o, events=pr)
+        d = sorted(ev.elapsed_ms(a, b) * 1e-3 for a, b in pairs[4:])
+        for a, b in pairs:
+            ev.destroy(a)
+            ev.destroy(b)
+        mean = sum(d) / len(d)
+        fl = 4.0 * c["D"] * c["Hq"] * c["B"] * S * (S + 1) / 2
+        out.append({"workload": f"prefill attention S={S} Hq={c['Hq']} Hkv={c['Hkv']} D={c['D']} causal bf16",
+                    "kernel_us_mean": round(mean * 1e6, 2), "kernel_us_min": round(d[0] * 1e6, 2),
+                    "TFLOP/s": round(fl / mean / 1e12, 1),
+                    "mfma_frac": round(fl / mean / 1e12 / F16_MFMA_PEAK_TFLOPS, 4)})
     return out
 
 

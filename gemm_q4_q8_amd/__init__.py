@@ -61,6 +61,9 @@ def _declare(lib):
         "q4q8_ffn_decode": (i32, [i32, vp, vp, vp, i64, i64, vp, i32, i64, i32, vp, i64, vp, sz, vp]),
         "q4q8_ffn_decode_timed": (i32, [i32, vp, vp, vp, i64, i64, vp, i32, i64, i32, vp, i64, vp, sz, vp,
                                         vp, vp]),
+        "q4q8_attn_prefill": (i32, [i32, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, ctypes.c_float, vp]),
+        "q4q8_attn_prefill_timed": (i32, [i32, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, ctypes.c_float, vp,
+                                          vp, vp]),
         "q4q8_qgemm_workspace": (sz, [i32, i64, i64]),
         "q4q8_qgemm": (i32, [i32, vp, i64, i64, vp, i32, i64, i64, vp, i32, i64, vp, sz, vp]),
         "q4q8_qgemm_timed": (i32, [i32, vp, i64, i64, vp, i32, i64, i64, vp, i32, i64, vp, sz, vp, vp, vp]),
@@ -321,4 +324,26 @@ def moe_qgemm(fmt: int, Wg, Wu, Wd, E: int, H: int, F: int, X: torch.Tensor, top
                                 _ptr(gates), _ptr(offsets), _ptr(sorted_pairs), _ptr(out),
                                 _ptr(h_out), _ptr(ws), ws.numel() * ws.element_size(), _stream(X)),
            "moe_qgemm")
+    return out
+
+
+def attn_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = True, scale=None,
+                 out: torch.Tensor | None = None, events=None) -> torch.Tensor:
+    """O [B, S, Hq, D] = softmax(scale Q K^T) V per head (GQA), bf16/fp16."""
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _dev(t, n)
+    B, S, Hq, D = q.shape
+    Hkv = k.shape[2]
+    if k.shape != (B, S, Hkv, D) or v.shape != k.shape or k.dtype != q.dtype or v.dtype != q.dtype:
+        raise ValueError("k and v must be [B, S, Hkv, D] of q's dtype")
+    if out is None:
+        out = torch.empty_like(q)
+    _dev(out, "out")
+    sc = (1.0 / D ** 0.5) if scale is None else float(scale)
+    args = (_DT[q.dtype], _ptr(q), _ptr(k), _ptr(v), _ptr(out), B, S, Hq, Hkv, D, 1 if causal else 0, sc, _stream(q))
+    if events is None:
+        st = lib().q4q8_attn_prefill(*args)
+    else:
+        st = lib().q4q8_attn_prefill_timed(*args, ctypes.c_void_p(events[0]), ctypes.c_void_p(events[1]))
+    _check(st, "attn_prefill")
     return out

@@ -395,4 +395,35 @@ int q4q8_moe_qgemm(int fmt, const void* Wg, const void* Wu, const void* Wd, int 
                     "moe_qgemm launch");
 }
 
+static int attn_impl(int dt, const void* Q, const void* K, const void* V, void* O, int B, int S, int Hq, int Hkv,
+                     int D, int causal, float scale, void* stream, const q4q8::LaunchEvents& ev) {
+  if (!act_ok(dt)) return fail(Q4Q8_ERR_UNSUPPORTED, "attn_prefill: dtype %d not F16/BF16", dt);
+  if (D != 128) return fail(Q4Q8_ERR_UNSUPPORTED, "attn_prefill: head dimension %d (128 supported)", D);
+  if (!Q || !K || !V || !O) return fail(Q4Q8_ERR_INVALID_ARG, "attn_prefill: null pointer");
+  if (B < 1 || S < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv)
+    return fail(Q4Q8_ERR_INVALID_ARG, "attn_prefill: B=%d S=%d Hq=%d Hkv=%d (Hq a multiple of Hkv)", B, S, Hq, Hkv);
+  if (!(scale > 0.0f) || scale > 1e30f) return fail(Q4Q8_ERR_INVALID_ARG, "attn_prefill: scale must be positive");
+  if ((int64_t)B * Hq * ((S + 127) / 128) >= (1LL << 31) || (int64_t)B * S * Hq * D >= (1LL << 40))
+    return fail(Q4Q8_ERR_UNSUPPORTED, "attn_prefill: sizes beyond limits");
+  if (!aligned(Q, 16) || !aligned(K, 16) || !aligned(V, 16) || !aligned(O, 8))
+    return fail(Q4Q8_ERR_ALIGNMENT, "attn_prefill: Q, K, V must be 16-byte aligned, O 8-byte aligned");
+  clear_hip_error();
+  return hip_status(q4q8::launch_attn_prefill(dt, Q, K, V, O, B, S, Hq, Hkv, causal ? 1 : 0, scale,
+                                              (hipStream_t)stream, ev),
+                    "attn_prefill launch");
+}
+
+int q4q8_attn_prefill(int dt, const void* Q, const void* K, const void* V, void* O, int B, int S, int Hq, int Hkv,
+                      int D, int causal, float scale, void* stream) {
+  return attn_impl(dt, Q, K, V, O, B, S, Hq, Hkv, D, causal, scale, stream, q4q8::LaunchEvents());
+}
+
+int q4q8_attn_prefill_timed(int dt, const void* Q, const void* K, const void* V, void* O, int B, int S, int Hq,
+                            int Hkv, int D, int causal, float scale, void* stream, void* ev_start, void* ev_stop) {
+  q4q8::LaunchEvents ev;
+  ev.start = (hipEvent_t)ev_start;
+  ev.stop = (hipEvent_t)ev_stop;
+  return attn_impl(dt, Q, K, V, O, B, S, Hq, Hkv, D, causal, scale, stream, ev);
+}
+
 }  // extern "C"

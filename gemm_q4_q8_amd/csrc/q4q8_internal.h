@@ -82,4 +82,9 @@ hipError_t launch_moe_qgemm(int fmt, int xdt, const void* Wg, const void* Wu, co
                             const void* X, int T, int topk, const float* gates, const int32_t* offsets,
                             const int32_t* sorted_pairs, float* out, void* h_out, void* ws, hipStream_t stream);
 
+// Prefill attention, head dimension 128: Q/O [B, S, Hq, 128], K/V
+// [B, S, Hkv, 128], dtype dt (kF16 or kBF16).
+hipError_t launch_attn_prefill(int dt, const void* q, const void* k, const void* v, void* o, int B, int S, int Hq,
+                               int Hkv, int causal, float scale, hipStream_t s, const LaunchEvents& ev);
+
 }  // namespace q4q8

@@ -309,6 +309,34 @@ int q4q8_moe_qgemm(int fmt, const void* Wg, const void* Wu, const void* Wd,
                    float* out, void* h_out, void* ws, size_t ws_bytes,
                    void* stream);
 
+/* ------------------------------------------------------------------------ */
+/* Prefill attention (technical summary, "Methodologie", prefill            */
+/* optimisation: tiled attention with an online softmax, O(n) memory;       */
+/* review, "Method": prefill attention on the matrix units)                 */
+/* ------------------------------------------------------------------------ */
+
+/* O[b, i, h, :] = sum_j p_j V[b, j, h / (Hq/Hkv), :],
+ *   p = softmax_j(scale * Q[b, i, h, :] . K[b, j, h / (Hq/Hkv), :])
+ * over keys j < S, and j <= i when causal != 0.  The S x S scores are never
+ * stored: keys are processed in blocks with a running max and sum.
+ *   Q, O: device [B, S, Hq, D] row-major; K, V: device [B, S, Hkv, D]; all
+ *         of dtype dt (F16 or BF16).  Q, K, V 16-byte aligned, O 8-byte.
+ *   D:    head dimension, 128.  Hq a multiple of Hkv.  scale > 0 (usually
+ *         1/sqrt(D)).
+ * Scores and the softmax statistics are fp32; the probabilities enter the
+ * P.V product rounded to dt; O is rounded once to dt.
+ * Errors: Q4Q8_ERR_UNSUPPORTED for other D or dtypes. */
+int q4q8_attn_prefill(int dt, const void* Q, const void* K, const void* V,
+                      void* O, int B, int S, int Hq, int Hkv, int D,
+                      int causal, float scale, void* stream);
+
+/* As q4q8_attn_prefill, with dispatch-recorded events (see
+ * q4q8_qgemv_grouped_timed).  For measurement; the result is identical. */
+int q4q8_attn_prefill_timed(int dt, const void* Q, const void* K,
+                            const void* V, void* O, int B, int S, int Hq,
+                            int Hkv, int D, int causal, float scale,
+                            void* stream, void* ev_start, void* ev_stop);
+
 #ifdef __cplusplus
 }
 #endif

@@ -28,6 +28,9 @@ the pages; the oracle takes these readings:
   logits.
 * Sorting: pairs p = t*k + j are ordered by (expert, p); counts and offsets are
   the histogram and its exclusive scan.
+* Attention (prefill): softmax(scale q k^T) v per head, causal, GQA by
+  contiguous groups of query heads (readings: the pages name the tiled
+  online-softmax method but no masking, head layout or scale).
 * Expert: h = silu(x W_gate^T) * (x W_up^T), y = h W_down^T,
   out[t] = sum_j gate[t, j] * y[pair(t, j)].  The decode FFN (ffn) is the
   same SwiGLU block on a dense layer; the pages credit fusing such
@@ -286,6 +289,42 @@ def moe(fmt: int, wg, wu, wd, x, logits, topk: int, H: int, F: int):
     r = moe_ffn(fmt, wg, wu, wd, x, ids, gates, sp, H, F)
     r.update(ids=ids, gates=gates, counts=counts, offsets=offsets, sorted_pairs=sp)
     return r
+
+
+def attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, causal: bool = True, scale=None, rows=None):
+    """Prefill attention: per query head h and query i,
+        s_j = scale * q_i . k_j   over keys j (j <= i when causal),
+        p   = softmax(s),  o_i = sum_j p_j v_j,
+    with GQA: query head h reads key/value head h // (Hq / Hkv).
+
+    q [B, S, Hq, D], k and v [B, S, Hkv, D] (fp64 values).  Returns o and the
+    bound sum_j p_j |v_j| (both [B, S, Hq, D]; with rows given, only those
+    query positions, [B, len(rows), Hq, D]).  scale defaults to 1/sqrt(D).
+    The technical summary ("Methodologie", prefill optimisation) names tiled
+    attention with an online softmax; this is the quantity it computes.
+    """
+    q, k, v = (np.asarray(a, dtype=np.float64) for a in (q, k, v))
+    B, S, Hq, D = q.shape
+    Hkv = k.shape[2]
+    if Hq % Hkv:
+        raise ValueError("Hq must be a multiple of Hkv")
+    group = Hq // Hkv
+    scale = 1.0 / np.sqrt(D) if scale is None else float(scale)
+    rows = np.arange(S) if rows is None else np.asarray(rows)
+    o = np.zeros((B, len(rows), Hq, D))
+    bound = np.zeros_like(o)
+    for b in range(B):
+        for h in range(Hq):
+            kk, vv = k[b, :, h // group], v[b, :, h // group]
+            s = scale * (q[b, rows, h] @ kk.T)                  # [len(rows), S]
+            if causal:
+                s = np.where(np.arange(S)[None, :] <= rows[:, None], s, -np.inf)
+            s = s - s.max(axis=1, keepdims=True)
+            e = np.exp(s)
+            p = e / e.sum(axis=1, keepdims=True)
+            o[b, :, h] = p @ vv
+            bound[b, :, h] = p @ np.abs(vv)
+    return o, bound
 
 
 def h_bound(r: dict, rel: float = 2e-3, storage_rel: float = 2.0 ** -8, abs_tol: float = 1e-5):

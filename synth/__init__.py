@@ -174,6 +174,16 @@ MOE = dict(name="q4_0 moe prefill E128 top8 H2048 F768 T512", fmt=Q4_0, xdt=BF16
            E=128, topk=8, H=2048, F=768, T=512, seed=SEED_BASE + 4)
 
 
+ATTN = dict(name="prefill attention 8B-shape (Hq 32, Hkv 8, D 128), causal", B=1, S=2048, Hq=32, Hkv=8, D=128,
+            dt=BF16, seed=SEED_BASE + 5)
+
+
+def attention_inputs(B: int, S: int, Hq: int, Hkv: int, D: int, dtype: int, seed: int):
+    """q [B, S, Hq, D], k and v [B, S, Hkv, D]: N(0,1) rounded to dtype."""
+    return (activation(rng_for(seed, 0), (B, S, Hq, D), dtype), activation(rng_for(seed, 1), (B, S, Hkv, D), dtype),
+            activation(rng_for(seed, 2), (B, S, Hkv, D), dtype))
+
+
 def gemv_problem(fmt: int, N: int, K: int, M: int, xdt: int, seed: int):
     """One matrix and one activation block, for parity cases of any size."""
     w = q_weight(rng_for(seed, 0), fmt, N, K)

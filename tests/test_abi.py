@@ -28,7 +28,8 @@ def _declared_functions():
 def test_header_declares_the_entry_points():
     names = _declared_functions()
     for need in ["q4q8_repack", "q4q8_repack_host", "q4q8_qgemv", "q4q8_qgemv_grouped", "q4q8_qgemm",
-                 "q4q8_moe_route", "q4q8_moe_qgemm", "q4q8_moe_workspace", "q4q8_last_error"]:
+                 "q4q8_moe_route", "q4q8_moe_qgemm", "q4q8_moe_workspace", "q4q8_last_error", "q4q8_qgemv_swiglu",
+                 "q4q8_ffn_decode", "q4q8_attn_prefill"]:
         assert need in names
 
 
@@ -168,6 +169,19 @@ def test_ffn_decode_validation(q):
         st = L.q4q8_ffn_decode(a["fmt"], _vp(a["Wg"]), _vp(a["Wu"]), _vp(a["Wd"]) if a["Wd"] else None, a["H"],
                                a["F"], _vp(a["x"]), a["xdt"], a["ldx"], a["M"], _vp(a["y"]), a["ldy"],
                                _vp(a["ws"]) if a["ws"] else None, a["nws"], None)
+        assert st == want, (over, st, q.last_error())
+
+
+def test_attn_validation(q):
+    L = q.lib()
+    ok = dict(dt=2, Q=0x1000, K=0x2000, V=0x3000, O=0x4000, B=1, S=64, Hq=8, Hkv=2, D=128, causal=1, scale=0.088)
+    for over, want in [(dict(dt=3), -2), (dict(D=64), -2), (dict(Q=None), -1), (dict(Hkv=3), -1), (dict(S=0), -1),
+                       (dict(scale=0.0), -1), (dict(scale=-1.0), -1), (dict(K=0x2008), -4), (dict(O=0x4004), -4),
+                       (dict(B=0), -1)]:
+        a = dict(ok)
+        a.update(over)
+        st = L.q4q8_attn_prefill(a["dt"], _vp(a["Q"]) if a["Q"] else None, _vp(a["K"]), _vp(a["V"]), _vp(a["O"]),
+                                 a["B"], a["S"], a["Hq"], a["Hkv"], a["D"], a["causal"], a["scale"], None)
         assert st == want, (over, st, q.last_error())
 
 

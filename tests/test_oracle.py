@@ -468,3 +468,82 @@ def test_ffn_bounds_catch_a_planted_error():
     assert np.any(np.abs(bad["y"] - r["y"]) > ob)
     yt = r["h"] @ _logical(wd, synth.Q4_0)
     assert np.any(np.abs(yt - r["y"]) > ob)
+
+
+# ----------------------------------------------------------------------------
+# Prefill attention
+# ----------------------------------------------------------------------------
+def _qkv(B, S, Hq, Hkv, D, seed):
+    rng = np.random.default_rng(seed)
+    return (rng.standard_normal((B, S, Hq, D)), rng.standard_normal((B, S, Hkv, D)),
+            rng.standard_normal((B, S, Hkv, D)))
+
+
+def test_attention_zero_queries_give_prefix_means():
+    """q = 0: every visible score is 0, so o_i is the mean of v_0..v_i
+    (causal) or of all v (not causal)."""
+    _, k, v = _qkv(2, 9, 4, 2, 8, 70)
+    q = np.zeros((2, 9, 4, 8))
+    o, _ = oracle.attention(q, k, v, causal=True)
+    for h in range(4):
+        want = np.cumsum(v[:, :, h // 2], axis=1) / np.arange(1, 10)[None, :, None]
+        assert np.allclose(o[:, :, h], want, rtol=1e-13, atol=1e-14)
+    o, _ = oracle.attention(q, k, v, causal=False)
+    assert np.allclose(o[:, :, 3], v[:, :, 1].mean(axis=1, keepdims=True), rtol=1e-13, atol=1e-14)
+
+
+def test_attention_two_keys_is_a_sigmoid_mix():
+    q, k, v = _qkv(1, 2, 1, 1, 16, 71)
+    o, _ = oracle.attention(q, k, v, causal=False, scale=0.3)
+    for i in range(2):
+        s0, s1 = 0.3 * q[0, i, 0] @ k[0, 0, 0], 0.3 * q[0, i, 0] @ k[0, 1, 0]
+        w0 = 1.0 / (1.0 + math.exp(s1 - s0))
+        assert np.allclose(o[0, i, 0], w0 * v[0, 0, 0] + (1 - w0) * v[0, 1, 0], rtol=1e-13, atol=1e-14)
+
+
+def test_attention_dominant_key_selects_its_value():
+    """One key scores 200 above the rest: o equals its v to e^-200."""
+    B, S, D = 1, 6, 4
+    q = np.zeros((B, S, 1, D))
+    k = np.zeros((B, S, 1, D))
+    v = np.random.default_rng(72).standard_normal((B, S, 1, D))
+    q[0, 5, 0, 0] = 400.0
+    k[0, 3, 0, 0] = 1.0
+    o, _ = oracle.attention(q, k, v, causal=True, scale=0.5)
+    assert np.allclose(o[0, 5, 0], v[0, 3, 0], rtol=0, atol=1e-60)
+    assert np.allclose(o[0, 0, 0], v[0, 0, 0], rtol=0, atol=0)      # causal: query 0 sees key 0 only
+
+
+def test_attention_gqa_maps_contiguous_head_groups():
+    """Query head h reads kv head h // (Hq/Hkv): each head equals a one-head
+    call on its own kv head, and differs from the call on the other one."""
+    q, k, v = _qkv(1, 7, 4, 2, 8, 73)
+    o, _ = oracle.attention(q, k, v)
+    for h in range(4):
+        one, _ = oracle.attention(q[:, :, h:h + 1], k[:, :, h // 2:h // 2 + 1], v[:, :, h // 2:h // 2 + 1])
+        other, _ = oracle.attention(q[:, :, h:h + 1], k[:, :, 1 - h // 2:2 - h // 2], v[:, :, 1 - h // 2:2 - h // 2])
+        assert np.array_equal(o[:, :, h:h + 1], one)
+        assert not np.allclose(o[:, 1:, h:h + 1], other[:, 1:])
+
+
+def test_attention_key_permutation_invariance_without_mask():
+    q, k, v = _qkv(1, 11, 2, 1, 8, 74)
+    perm = np.random.default_rng(75).permutation(11)
+    o1, b1 = oracle.attention(q, k, v, causal=False)
+    o2, b2 = oracle.attention(q, k[:, perm], v[:, perm], causal=False)
+    assert np.allclose(o1, o2, rtol=1e-12, atol=1e-13) and np.allclose(b1, b2, rtol=1e-12, atol=1e-13)
+
+
+def test_attention_rows_subset_and_bound():
+    q, k, v = _qkv(2, 13, 2, 2, 8, 76)
+    o, b = oracle.attention(q, k, v)
+    rows = [0, 5, 12]
+    o2, b2 = oracle.attention(q, k, v, rows=rows)
+    assert np.array_equal(o[:, rows], o2) and np.array_equal(b[:, rows], b2)
+    assert np.all(b >= np.abs(o) - 1e-12)
+    # the acceptance bound rejects the plausible slips: no causal mask, scale missing
+    tol = 2.0 ** -7 * b + 1e-5
+    bad, _ = oracle.attention(q, k, v, causal=False)
+    assert np.any(np.abs(bad - o) > tol)
+    bad, _ = oracle.attention(q, k, v, scale=1.0)
+    assert np.any(np.abs(bad - o) > tol)
