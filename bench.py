@@ -32,7 +32,7 @@ the same layer (all seven matrices, M = 1).
 
 Other workloads (the dependency-order step at M = 1, one-launch steps at
 M = 2/4/8, the single 2048x2048 GEMV, the Q8_0 3B-shaped matrices, the
-layer's fused decode FFN at M = 1 and 8, the prefill GEMM at M = 512 and
+layer with plain fp16 weights, the layer's fused decode FFN at M = 1 and 8, the prefill GEMM at M = 512 and
 2048, the MoE layer at 512 tokens and its decode at 1 and 8 tokens,
 prefill attention at S = 512 and 2048) are reported under "workloads", each
 with its own algorithmic bytes / flops and time.
@@ -334,6 +334,7 @@ def extra_workloads(q, torch, synth, ev: HipEvents, quick: bool):
                     "GB/s": round(tot_b / kd / 1e9, 1)})
         del Ws, copies, probs, descs
         torch.cuda.empty_cache()
+    out.append(fp16_layer_workload(q, torch, synth, ev))
     out += ffn_workloads(q, torch, synth, ev, quick)
     out += prefill_workloads(q, torch, synth, ev, quick)
     out.append(moe_workload(q, torch, synth))
@@ -368,6 +369,34 @@ def attn_workloads(q, torch, synth, ev: HipEvents, quick: bool):
                     "TFLOP/s": round(fl / mean / 1e12, 1),
                     "mfma_frac": round(fl / mean / 1e12 / F16_MFMA_PEAK_TFLOPS, 4)})
     return out
+
+
+def fp16_layer_workload(q, torch, synth, ev: HipEvents):
+    """Plain fp16 weights of the 8B-shaped layer (434 MB), M = 1 bf16
+    activations, the seven projections in one grouped launch; two weight
+    copies alternate (868 MB)."""
+    dev = torch.device("cuda:0")
+    mats = synth.LAYER_8B["mats"]
+    base = [q.repack(synth.FP16, torch.from_numpy(synth.fp16_weight(synth.rng_for(59, i), N, K).canon).to(dev), N, K)
+            for i, (n, N, K) in enumerate(mats)]
+    copies = [base, [t.clone() for t in base]]
+    xs = {K: torch.randn((1, K), device=dev).to(torch.bfloat16) for _, _, K in mats}
+    ys = [torch.empty((1, N), dtype=torch.float32, device=dev) for _, N, _ in mats]
+    probs = [[(c[i], N, K, xs[K], ys[i]) for i, (_, N, K) in enumerate(mats)] for c in copies]
+    descs = [q.gemv_descs(p) for p in probs]
+    pairs = [(ev.create(), ev.create()) for _ in range(36)]
+    for i, pr in enumerate(pairs):
+        q.qgemv_grouped(synth.FP16, probs[i % 2], 1, descs=descs[i % 2], events=pr)
+    kd = sum(ev.elapsed_ms(a, b) for a, b in pairs[4:]) / 32 * 1e-3
+    for a, b in pairs:
+        ev.destroy(a)
+        ev.destroy(b)
+    nb = sum(q.repacked_bytes(synth.FP16, N, K) + N * 4 for _, N, K in mats) + 3 * 4096 * 2 + 12288 * 2
+    del base, copies
+    torch.cuda.empty_cache()
+    return {"workload": "fp16 weights, 8B-shape layer 7 matrices M=1 (bf16 x), one grouped launch",
+            "kernel_us": round(kd * 1e6, 2), "GB/s": round(nb / kd / 1e9, 1),
+            "hbm_frac": round(nb / kd / 1e9 / HBM_PEAK_GBS, 4)}
 
 
 def ffn_workloads(q, torch, synth, ev: HipEvents, quick: bool):

@@ -5,9 +5,9 @@ kernels.  Tensors are passed by data pointer together with the current HIP
 stream of their device.  If the library is not built the first call raises;
 there is no fallback path.
 
-Formats: Q4_0 = 1, Q8_0 = 2.  Activation dtypes: torch.float16 or
-torch.bfloat16.  Weights are uint8 tensors holding repacked blocks
-(see repack()).
+Formats: Q4_0 = 1, Q8_0 = 2, FP16 = 3 (plain fp16 weights: layout and GEMV
+calls only).  Activation dtypes: torch.float16 or torch.bfloat16.  Weights
+are uint8 tensors holding repacked blocks (see repack()).
 """
 from __future__ import annotations
 
@@ -18,6 +18,7 @@ import torch
 
 Q4_0 = 1
 Q8_0 = 2
+FP16 = 3
 F16 = 1
 BF16 = 2
 F32 = 3

@@ -24,16 +24,18 @@ int hip_status(hipError_t e, const char* what) {
   return fail(Q4Q8_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
 }
 
-bool fmt_ok(int fmt) { return fmt == Q4Q8_Q4_0 || fmt == Q4Q8_Q8_0; }
+bool fmt_ok(int fmt) { return fmt == Q4Q8_Q4_0 || fmt == Q4Q8_Q8_0; }   // quantised formats
+bool any_fmt_ok(int fmt) { return fmt_ok(fmt) || fmt == Q4Q8_FP16; }    // + plain fp16 (layout, GEMV)
 bool act_ok(int dt) { return dt == Q4Q8_F16 || dt == Q4Q8_BF16; }
 bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
-int64_t canon_block(int fmt) { return fmt == Q4Q8_Q4_0 ? 18 : 34; }
-int64_t rec_bytes(int fmt) { return fmt == Q4Q8_Q4_0 ? 1152 : 2176; }
+int64_t canon_block(int fmt) { return fmt == Q4Q8_Q4_0 ? 18 : fmt == Q4Q8_Q8_0 ? 34 : 64; }
+int64_t rec_bytes(int fmt) { return fmt == Q4Q8_Q4_0 ? 1152 : fmt == Q4Q8_Q8_0 ? 2176 : 4096; }
 
-// Shape rules common to every weight matrix.
+// Shape rules common to every weight matrix (any format; the products that
+// take only the quantised formats check that themselves).
 int check_matrix(int fmt, int64_t N, int64_t K) {
-  if (!fmt_ok(fmt)) return fail(Q4Q8_ERR_UNSUPPORTED, "unknown weight format %d", fmt);
+  if (!any_fmt_ok(fmt)) return fail(Q4Q8_ERR_UNSUPPORTED, "unknown weight format %d", fmt);
   if (N < 1 || K < 32) return fail(Q4Q8_ERR_INVALID_ARG, "bad shape N=%lld K=%lld", (long long)N, (long long)K);
   if (K % 32) return fail(Q4Q8_ERR_INVALID_ARG, "K=%lld is not a multiple of 32", (long long)K);
   if (N > (1LL << 30) || K > (1LL << 24))
@@ -69,12 +71,12 @@ const char* q4q8_status_string(int s) {
 const char* q4q8_last_error(void) { return g_last_error; }
 
 size_t q4q8_canonical_bytes(int fmt, int64_t N, int64_t K) {
-  if (!fmt_ok(fmt) || N < 1 || K < 32 || K % 32) return 0;
+  if (!any_fmt_ok(fmt) || N < 1 || K < 32 || K % 32) return 0;
   return (size_t)(N * (K / 32) * canon_block(fmt));
 }
 
 size_t q4q8_repacked_bytes(int fmt, int64_t N, int64_t K) {
-  if (!fmt_ok(fmt) || N < 1 || K < 32 || K % 32) return 0;
+  if (!any_fmt_ok(fmt) || N < 1 || K < 32 || K % 32) return 0;
   return (size_t)repacked(fmt, N, K);
 }
 
@@ -138,7 +140,7 @@ static int check_gemv_prob(int fmt, const GemvIn& d, int M, int idx) {
 }
 
 static int check_gemv_common(int fmt, int xdt, int M, int count) {
-  if (!fmt_ok(fmt)) return fail(Q4Q8_ERR_UNSUPPORTED, "unknown weight format %d", fmt);
+  if (!any_fmt_ok(fmt)) return fail(Q4Q8_ERR_UNSUPPORTED, "unknown weight format %d", fmt);
   if (!act_ok(xdt)) return fail(Q4Q8_ERR_UNSUPPORTED, "qgemv: activation dtype %d not F16/BF16", xdt);
   if (M < 1 || M > 8) return fail(Q4Q8_ERR_INVALID_ARG, "qgemv: M=%d outside 1..8", M);
   if (count < 1 || count > Q4Q8_MAX_GROUP)
@@ -303,6 +305,7 @@ extern "C" {
 static int qgemm_impl(int fmt, const void* W, int64_t N, int64_t K, const void* X, int xdt, int64_t ldx, int64_t M,
                       void* Y, int ydt, int64_t ldy, void* ws, size_t ws_bytes, void* stream,
                       const q4q8::LaunchEvents& ev) {
+  if (!fmt_ok(fmt)) return fail(Q4Q8_ERR_UNSUPPORTED, "qgemm: weight format %d (Q4_0 and Q8_0 only)", fmt);
   int st = check_matrix(fmt, N, K);
   if (st) return st;
   if (!act_ok(xdt)) return fail(Q4Q8_ERR_UNSUPPORTED, "qgemm: activation dtype %d not F16/BF16", xdt);

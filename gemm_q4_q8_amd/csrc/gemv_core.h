@@ -1,5 +1,6 @@
 // Weight streaming and block products shared by the GEMV kernels (decode
-// GEMV and the mixture-of-experts decode path).
+// GEMV and the mixture-of-experts decode path); plain fp16 weights use the
+// same tiles with the weights themselves as the B operand.
 //
 // A wavefront owns a tile of 16 weight rows.  Per chunk of 128 k (4 blocks)
 // each lane loads 16 (Q4_0) or 32 (Q8_0) contiguous bytes of codes -- the
@@ -23,9 +24,9 @@ constexpr int kGemvBufFlags = 0x00020000;   // raw buffer, 32-bit data format (g
 // One chunk of a tile's weights in registers.
 template <int FMT>
 struct GemvStage {
-  static constexpr int NV = FMT == kQ4_0 ? 1 : 2;
+  static constexpr int NV = FMT == kQ4_0 ? 1 : FMT == kQ8_0 ? 2 : 4;
   u32x4_t codes[NV];
-  u32x2_t sc;
+  u32x2_t sc;   // unused for plain fp16 weights
 };
 
 // Loads chunk c of the tile behind `wres` (a buffer over the tile's records:
@@ -36,7 +37,28 @@ __device__ __forceinline__ void gemv_load(GemvStage<FMT>& st, __amdgpu_buffer_rs
 #pragma unroll
   for (int v = 0; v < GemvStage<FMT>::NV; ++v)
     st.codes[v] = __builtin_amdgcn_raw_buffer_load_b128(wres, off + v * 1024 + lane * 16, 0, Q4Q8_WEIGHT_AUX);
-  st.sc = __builtin_amdgcn_raw_buffer_load_b64(wres, off + Fmt<FMT>::kCodeBytes + r * 8, 0, Q4Q8_WEIGHT_AUX);
+  if constexpr (FMT != kFP16W)
+    st.sc = __builtin_amdgcn_raw_buffer_load_b64(wres, off + Fmt<FMT>::kCodeBytes + r * 8, 0, Q4Q8_WEIGHT_AUX);
+}
+
+// Plain fp16 weights: the slots are the B operands themselves; the A
+// fragments are fp16 (bf16 activations are converted by the caller).
+template <int NI>
+__device__ __forceinline__ void gemv_mma_fp16w(const GemvStage<kFP16W>& s, const half8_t (&a)[kBlocksPerChunk],
+                                               float (&acc)[NI]) {
+  float4_t d = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+  for (int j = 0; j < kBlocksPerChunk; ++j)
+    d = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[j], __builtin_bit_cast(half8_t, s.codes[j]), d, 0, 0, 0);
+#pragma unroll
+  for (int i = 0; i < NI; ++i) acc[i] += d[i];
+}
+
+// bf16 -> fp16 of one A fragment, round to nearest even (exact for
+// 2^-14 <= |x| < 65520).
+__device__ __forceinline__ half8_t bf16x8_to_half8(bf16x8_t v) {
+  typedef float float8_t __attribute__((ext_vector_type(8)));
+  return __builtin_convertvector(__builtin_convertvector(v, float8_t), half8_t);
 }
 
 // acc[i] += sum over the chunk's 4 blocks of scale_j * (A_j . B_j)[register i].

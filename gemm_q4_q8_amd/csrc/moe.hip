@@ -238,10 +238,10 @@ hipError_t launch_moe_route(const float* logits, int T, int E, int topk, int32_t
 // ---------------------------------------------------------------------------
 enum { kGateUp = 0, kDown = 1 };
 constexpr int kStreamBM = 64;
-constexpr int kStreamKP = 1024;   // LDS phase: 64 rows x 1024 fp16 = 128 KB
 
-template <int FMT, int MODE, int NT, int P>
-__global__ __launch_bounds__(512) void moe_stream_kernel(
+// WAVES waves per workgroup; KP columns per LDS phase (64 rows x KP fp16).
+template <int FMT, int MODE, int NT, int P, int WAVES, int KP>
+__global__ __launch_bounds__(WAVES * 64) void moe_stream_kernel(
     const uint8_t* __restrict__ W0, const uint8_t* __restrict__ W1, int64_t wstride, int N, int K,
     const uint16_t* __restrict__ src, int src_rows, int T, int topk, int Ptot,
     const int32_t* __restrict__ offsets, const int32_t* __restrict__ sorted_pairs, uint16_t* __restrict__ out16,
@@ -251,7 +251,9 @@ __global__ __launch_bounds__(512) void moe_stream_kernel(
   constexpr int REC = Fmt<FMT>::kRecBytes;
   constexpr int CODE = Fmt<FMT>::kCodeBytes;
   constexpr int NV = FMT == kQ4_0 ? 1 : 2;
-  __shared__ __attribute__((aligned(1024))) uint16_t xs[BM * kStreamKP];
+  constexpr int THREADS = WAVES * 64;
+  constexpr int NH = BM * 16 / THREADS;   // row offsets per thread in one LDS chunk
+  __shared__ __attribute__((aligned(1024))) uint16_t xs[BM * KP];
 
   const int e = blockIdx.y;
   const int seg = offsets[e];
@@ -262,13 +264,13 @@ __global__ __launch_bounds__(512) void moe_stream_kernel(
   const int r = lane & 15, g = lane >> 4;
   const int nchunks = K / kChunkK;
   const int tiles = N / kTileRows;
-  const int kpc = K < kStreamKP ? K : kStreamKP;     // columns per LDS phase
+  const int kpc = K < KP ? K : KP;                    // columns per LDS phase
   const int cpp = kpc / kChunkK;                      // chunks per phase
   const int n_rt = (cnt + BM - 1) / BM;
   const int total = n_rt * groups * nchunks;
 
   // This wave's tiles: t_w0 .. t_w0 + tv - 1 of the expert's matrix.
-  const int t_w0 = (blockIdx.x * 8 + wave) * tiles_per_wave;
+  const int t_w0 = (blockIdx.x * WAVES + wave) * tiles_per_wave;
   const int tv = min(max(tiles - t_w0, 0), tiles_per_wave);
   const int64_t woff = e * wstride + (int64_t)(tv > 0 ? t_w0 : 0) * nchunks * REC;
   __amdgpu_buffer_rsrc_t wres[NW];
@@ -305,17 +307,17 @@ __global__ __launch_bounds__(512) void moe_stream_kernel(
   };
 
   // Activation rows of row tile rt, LDS phase kph -> xs.  Copy p of this
-  // thread fills slot 512 p + tid of the phase: chunk slot / (BM 16), then
-  // row / column group as in the tile engine.
+  // thread fills slot THREADS p + tid of the phase: chunk slot / (BM 16),
+  // then row / column group as in the tile engine.
   const __amdgpu_buffer_rsrc_t xres = uniform_rsrc(src, (int)((int64_t)src_rows * K * 2));
   auto load_x = [&](int rt, int kph) __attribute__((always_inline)) {
     const int col0 = kph * kpc;
     const int ncols = min(kpc, K - col0);
     const int nslots = BM * ncols / 8;
-    int rowoff[2];
+    int rowoff[NH];
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {   // slot % (BM 16) takes two values per thread: rows (h 512 + tid) / 16
-      const int row = (h * 512 + tid) >> 4;
+    for (int h = 0; h < NH; ++h) {   // slot % (BM 16) takes NH values per thread: rows (h THREADS + tid) / 16
+      const int row = (h * THREADS + tid) >> 4;
       const int i = rt * BM + row;
       int base = -1;
       if (i < cnt) {
@@ -326,14 +328,14 @@ __global__ __launch_bounds__(512) void moe_stream_kernel(
       }
       rowoff[h] = base;
     }
-    for (int p = 0; p * 512 < nslots; ++p) {
-      const int slot = p * 512 + tid;
+    for (int p = 0; p * THREADS < nslots; ++p) {
+      const int slot = p * THREADS + tid;
       const int cc = slot / (BM * 16), q = slot % (BM * 16);
       const int row = q >> 4, cg = (q & 15) ^ (row & 15);
-      const int base = rowoff[p & 1];
+      const int base = rowoff[p % NH];
       const uint32_t v =
           (base >= 0 && slot < nslots) ? (uint32_t)(((int64_t)base * K + col0 + cc * kChunkK + cg * 8) * 2) : kOOB;
-      uint16_t* dst = xs + (p * 512 + wave * 64) * 8;   // wave-uniform
+      uint16_t* dst = xs + (p * THREADS + wave * 64) * 8;   // wave-uniform
       __builtin_amdgcn_raw_ptr_buffer_load_lds(xres, (__attribute__((address_space(3))) void*)dst, 16, v, 0, 0, 0);
     }
   };
@@ -476,6 +478,13 @@ __global__ __launch_bounds__(256) void moe_combine_kernel(const uint16_t* __rest
 
 namespace {
 
+// Streaming-kernel configuration (measured on MI355X).
+constexpr int kMoeWaves = 8;     // waves per workgroup
+constexpr int kMoeKP = 1024;     // LDS phase columns (64 rows x kMoeKP fp16)
+constexpr int kMoeSlots = 1;     // workgroups per CU the split aims at
+constexpr int kMoeNTG4 = 3, kMoeNTG8 = 2, kMoePG = 2;   // gate+up
+constexpr int kMoeNTD = 4, kMoePD = 3;                  // down
+
 size_t round256(size_t b) { return (b + 255) / 256 * 256; }
 
 struct MoeWs {
@@ -503,23 +512,26 @@ void launch_experts(const void* Wg, const void* Wu, const void* Wd, int E, int H
   const int P = T * topk;
   const int64_t sg = (int64_t)(F / kTileRows) * (H / kChunkK) * Fmt<FMT>::kRecBytes;   // repacked [F, H]
   const int64_t sd = (int64_t)(H / kTileRows) * (F / kChunkK) * Fmt<FMT>::kRecBytes;   // repacked [H, F]
-  // Workgroups per expert: about one per CU over all experts.
-  auto split = [&](int tiles, int nt, int& nwe, int& tpw, int& groups) {
-    nwe = std::max(1, std::min(tiles, 256 / std::max(E, 1)));
+  // Workgroups per expert: about kMoeSlots per CU over all experts.
+  auto split = [&](int tiles, int nt, int waves, int& nwe, int& tpw, int& groups) {
+    nwe = std::max(1, std::min(tiles, 256 * kMoeSlots / std::max(E, 1)));
     const int per_wg = (tiles + nwe - 1) / nwe;
-    tpw = (per_wg + 7) / 8;
-    nwe = (tiles + 8 * tpw - 1) / (8 * tpw);
+    tpw = (per_wg + waves - 1) / waves;
+    nwe = (tiles + waves * tpw - 1) / (waves * tpw);
     groups = (tpw + nt - 1) / nt;
   };
-  constexpr int NTG = FMT == kQ4_0 ? 3 : 2, PG = 2;   // gate+up: tile pairs per group (Q8_0 codes are twice as large)
-  constexpr int NTD = 4, PD = 3;   // down: 4 tiles per group, 3 stages
+  // gate+up: tile pairs per group (Q8_0 codes are twice as large), stages.
+  constexpr int NTG = FMT == kQ4_0 ? kMoeNTG4 : kMoeNTG8, PG = kMoePG;
+  constexpr int NTD = kMoeNTD, PD = kMoePD;   // down: tiles per group, stages
   int nwe, tpw, groups;
-  split(F / kTileRows, NTG, nwe, tpw, groups);
-  moe_stream_kernel<FMT, kGateUp, NTG, PG><<<dim3((unsigned)nwe, (unsigned)E), dim3(512), 0, s>>>(
+  split(F / kTileRows, NTG, kMoeWaves, nwe, tpw, groups);
+  moe_stream_kernel<FMT, kGateUp, NTG, PG, kMoeWaves, kMoeKP><<<dim3((unsigned)nwe, (unsigned)E),
+                                                                 dim3(kMoeWaves * 64), 0, s>>>(
       (const uint8_t*)Wg, (const uint8_t*)Wu, sg, F, H, x16, T, T, topk, P, offsets, sorted_pairs, w.h16,
       (uint16_t*)h_out, tpw, groups);
-  split(H / kTileRows, NTD, nwe, tpw, groups);
-  moe_stream_kernel<FMT, kDown, NTD, PD><<<dim3((unsigned)nwe, (unsigned)E), dim3(512), 0, s>>>(
+  split(H / kTileRows, NTD, kMoeWaves, nwe, tpw, groups);
+  moe_stream_kernel<FMT, kDown, NTD, PD, kMoeWaves, kMoeKP><<<dim3((unsigned)nwe, (unsigned)E),
+                                                              dim3(kMoeWaves * 64), 0, s>>>(
       (const uint8_t*)Wd, nullptr, sd, H, F, w.h16, P, T, topk, P, offsets, sorted_pairs, w.y16, nullptr, tpw,
       groups);
   moe_combine_kernel<<<dim3((unsigned)((H / 8 + 255) / 256), (unsigned)T), dim3(256), 0, s>>>(w.y16, gates, T, topk,

@@ -17,7 +17,8 @@
 //             second kilobyte of the record) carries blocks 2h and 2h+1, 8
 //             bytes each, in natural order.
 //   * then 128 bytes of scales, fp16 [row r][block j].
-// Padding rows / blocks carry scale 0 and code 0.
+// Padding rows / blocks carry scale 0 and code 0.  Plain fp16 weights use the
+// same tiles with the weights themselves in the slots (Fmt<kFP16W>).
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -25,7 +26,7 @@
 
 namespace q4q8 {
 
-enum { kQ4_0 = 1, kQ8_0 = 2 };
+enum { kQ4_0 = 1, kQ8_0 = 2, kFP16W = 3 };   // weight formats (kFP16W: plain fp16 weights)
 enum { kF16 = 1, kBF16 = 2, kF32 = 3 };
 
 constexpr int kTileRows = 16;
@@ -43,6 +44,13 @@ template <> struct Fmt<kQ8_0> {
   static constexpr int kCanonBlock = 34;
   static constexpr int kCodeBytes = 2048;
   static constexpr int kRecBytes = 2048 + kScaleBytes;
+};
+// Plain fp16: four 1 KB planes per record (block j at j * 1024, lane slot l
+// at l * 16 holding row r's 8 weights k = 32 j + 8 g .. + 7), no scales.
+template <> struct Fmt<kFP16W> {
+  static constexpr int kCanonBlock = 64;
+  static constexpr int kCodeBytes = 4096;
+  static constexpr int kRecBytes = 4096;
 };
 
 __host__ __device__ constexpr int q4_nibble_shift(int e) { return 4 * ((e & 1) * 4 + (e >> 1)); }

@@ -138,7 +138,17 @@ __global__ __launch_bounds__(WAVES * 64) void qgemv_kernel(const GemvArgs args) 
         a[j] = *(const vec*)(xrow_g + blk * 32);
       }
     }
-    gemv_mma<FMT, XDT, NI>(s, a, acc);
+    if constexpr (FMT == kFP16W) {
+      half8_t ah[kBlocksPerChunk];
+#pragma unroll
+      for (int j = 0; j < kBlocksPerChunk; ++j) {
+        if constexpr (XDT == kBF16) ah[j] = bf16x8_to_half8(a[j]);
+        else ah[j] = a[j];
+      }
+      gemv_mma_fp16w<NI>(s, ah, acc);
+    } else {
+      gemv_mma<FMT, XDT, NI>(s, a, acc);
+    }
   };
 
   // Chunks of this wave: ks + i KSH for i < nw.  Stage p holds chunk i with
@@ -247,15 +257,12 @@ static void launch_p(int waves, bool xlds, const GemvArgs& args, int wgs, size_t
 template <int FMT, int XDT, int NI>
 static void launch_ni(int waves, const GemvShape& c, const GemvArgs& args, int wgs, size_t lds, hipStream_t s,
                       const LaunchEvents& ev) {
-  if (c.p == 8)
-    launch_p<FMT, XDT, NI, 8>(waves, c.xlds, args, wgs, lds, s, ev);
-  else
-    launch_p<FMT, XDT, NI, 4>(waves, c.xlds, args, wgs, lds, s, ev);
+  launch_p<FMT, XDT, NI, 4>(waves, c.xlds, args, wgs, lds, s, ev);
 }
 
 // K-shares per tile: about 2048 waves over the chip (8 per CU) with at least
 // 8 chunks each; a ring of 4 chunks in flight per wave.  (Measured on MI355X:
-// more waves or a deeper ring both lose, as does a split below 8 chunks.)
+// more waves or a ring of 8 both lose, as does a split below 8 chunks.)
 // The activation block goes to LDS when it fits in 160 KB; above 80 KB a
 // workgroup gets at least 8 waves since few workgroups then share a CU.
 static GemvShape pick_shape(int tiles, int max_chunks, int M, int max_k) {
@@ -271,10 +278,6 @@ static GemvShape pick_shape(int tiles, int max_chunks, int M, int max_k) {
   c.ks = ks;
   c.tpw = ks >= 4 ? 1 : 4 / ks;
   c.p = 4;
-  if (const char* e = getenv("Q4Q8_GEMV_P")) {    // tuning experiments only
-    const int v = atoi(e);
-    if (v == 4 || v == 8) c.p = v;
-  }
   c.xlds = lds <= kLdsCap;
   return c;
 }
@@ -325,6 +328,14 @@ hipError_t launch_qgemv(int fmt, int xdt, GemvArgs args, int max_chunks, int max
     } else {
       if (args.M > 4) launch_ni<kQ4_0, kBF16, 2>(waves, c, args, wgs, lds, s, ev);
       else launch_ni<kQ4_0, kBF16, 1>(waves, c, args, wgs, lds, s, ev);
+    }
+  } else if (fmt == kFP16W) {
+    if (xdt == kF16) {
+      if (args.M > 4) launch_ni<kFP16W, kF16, 2>(waves, c, args, wgs, lds, s, ev);
+      else launch_ni<kFP16W, kF16, 1>(waves, c, args, wgs, lds, s, ev);
+    } else {
+      if (args.M > 4) launch_ni<kFP16W, kBF16, 2>(waves, c, args, wgs, lds, s, ev);
+      else launch_ni<kFP16W, kBF16, 1>(waves, c, args, wgs, lds, s, ev);
     }
   } else {
     if (xdt == kF16) {

@@ -1,5 +1,5 @@
-// Load-time conversion of canonical Q4_0 / Q8_0 blocks into the gfx950 tile
-// layout described in q4q8_dev.h.  The runtime on the pages converts
+// Load-time conversion of canonical Q4_0 / Q8_0 blocks (and plain fp16
+// weights) into the gfx950 tile layout described in q4q8_dev.h.  The runtime on the pages converts
 // checkpoints once into its own weight format ("BaseRT: Advancing
 // Best-in-Class LLM Inference with Apple M5 Neural Accelerators", review,
 // section "Comparison"); this is that step for MI355X.  Only bytes move: the
@@ -23,6 +23,11 @@ __host__ __device__ inline void repack_slot(const uint8_t* canon, uint8_t* rec, 
     const int64_t blk = chunk * kBlocksPerChunk + j;
     const bool valid = n < N && blk < nblocks;
     const uint8_t* b = canon + (n * nblocks + blk) * CB;
+    if (FMT == kFP16W) {   // 8 weights (16 bytes) of row n, block blk, elements 8 g .. 8 g + 7
+      uint8_t* dst = rec + j * 1024 + slot * 16;
+      for (int e = 0; e < 16; ++e) dst[e] = valid ? b[16 * g + e] : 0;
+      continue;
+    }
     if (FMT == kQ4_0) {
       uint32_t word = 0;
       if (valid) {
@@ -65,23 +70,28 @@ hipError_t launch_repack(int fmt, const void* canon, int64_t N, int64_t K, void*
   if (fmt == kQ4_0)
     repack_kernel<kQ4_0><<<dim3((unsigned)grid), dim3(256), 0, stream>>>((const uint8_t*)canon, (uint8_t*)dst, N, K,
                                                                          nchunks, nslots);
-  else
+  else if (fmt == kQ8_0)
     repack_kernel<kQ8_0><<<dim3((unsigned)grid), dim3(256), 0, stream>>>((const uint8_t*)canon, (uint8_t*)dst, N, K,
                                                                          nchunks, nslots);
+  else
+    repack_kernel<kFP16W><<<dim3((unsigned)grid), dim3(256), 0, stream>>>((const uint8_t*)canon, (uint8_t*)dst, N,
+                                                                          K, nchunks, nslots);
   return hipGetLastError();
 }
 
 void repack_host(int fmt, const void* canon, int64_t N, int64_t K, void* dst) {
   const int64_t tiles = (N + kTileRows - 1) / kTileRows;
   const int64_t nchunks = (K + kChunkK - 1) / kChunkK;
-  const int rb = fmt == kQ4_0 ? Fmt<kQ4_0>::kRecBytes : Fmt<kQ8_0>::kRecBytes;
+  const int rb = fmt == kQ4_0 ? Fmt<kQ4_0>::kRecBytes : fmt == kQ8_0 ? Fmt<kQ8_0>::kRecBytes : Fmt<kFP16W>::kRecBytes;
   for (int64_t rec = 0; rec < tiles * nchunks; ++rec) {
     uint8_t* out = (uint8_t*)dst + rec * rb;
     for (int slot = 0; slot < 64; ++slot) {
       if (fmt == kQ4_0)
         repack_slot<kQ4_0>((const uint8_t*)canon, out, N, K, rec / nchunks, rec % nchunks, slot);
-      else
+      else if (fmt == kQ8_0)
         repack_slot<kQ8_0>((const uint8_t*)canon, out, N, K, rec / nchunks, rec % nchunks, slot);
+      else
+        repack_slot<kFP16W>((const uint8_t*)canon, out, N, K, rec / nchunks, rec % nchunks, slot);
     }
   }
 }

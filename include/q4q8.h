@@ -20,7 +20,12 @@
  *   Q8_0: int8 codes q,          weight = s * q
  * Canonical (interchange) blocks: Q4_0 = 18 bytes [s][16 bytes, byte i =
  * q[i] | q[i+16] << 4]; Q8_0 = 34 bytes [s][32 int8].  Blocks run along K,
- * rows n = 0..N-1 follow one another.
+ * rows n = 0..N-1 follow one another.  FP16 (plain weights, the top of the
+ * technical summary's Q2..FP16 format range, abstract): row-major fp16
+ * [N, K], 64 bytes per 32 weights.  Repacked FP16 records are 4096 bytes:
+ * four 1 KB planes, block j's lane slot l at j * 1024 + l * 16 holding the
+ * slot's 8 weights; no scales.  In the GEMV, BF16 activations meet FP16
+ * weights as fp16 operands (converted, exact for 2^-14 <= |x| < 65520).
  *
  * Conventions for every call below.
  *   - Ownership: the caller allocates and frees everything (weights,
@@ -69,7 +74,10 @@ typedef enum {
   Q4Q8_ERR_HIP = -5            /* the HIP runtime refused a launch or copy   */
 } q4q8_status;
 
-typedef enum { Q4Q8_Q4_0 = 1, Q4Q8_Q8_0 = 2 } q4q8_format;
+/* Q4Q8_FP16: plain fp16 weights (no quantisation), accepted by the layout
+ * calls and the GEMV entry points (q4q8_qgemv, _grouped, _swiglu,
+ * q4q8_ffn_decode); the GEMM and MoE calls take Q4_0 and Q8_0 only. */
+typedef enum { Q4Q8_Q4_0 = 1, Q4Q8_Q8_0 = 2, Q4Q8_FP16 = 3 } q4q8_format;
 typedef enum { Q4Q8_F16 = 1, Q4Q8_BF16 = 2, Q4Q8_F32 = 3 } q4q8_dtype;
 
 /* Version of this interface (Q4Q8_ABI_VERSION of the built library). */

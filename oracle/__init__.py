@@ -23,6 +23,8 @@ the pages; the oracle takes these readings:
 * Q4_0: 32 weights per block, fp16 scale s, 4-bit codes q; w = s*(q-8).
   Byte i of the 16 code bytes holds q[i] (low nibble) and q[i+16] (high).
 * Q8_0: 32 weights per block, fp16 scale s, int8 codes q; w = s*q.
+* FP16: plain fp16 weights, row-major little-endian (the pages' format list
+  runs up to FP16; technical summary abstract).
 * Routing: per token, the top-k experts by logit, descending, equal logits
   broken towards the lower expert id; gates = softmax over the k selected
   logits.
@@ -49,6 +51,7 @@ import numpy as np
 
 Q4_0 = 1
 Q8_0 = 2
+FP16 = 3
 QK = 32
 _BLOCK_BYTES = {Q4_0: 18, Q8_0: 34}
 
@@ -89,7 +92,16 @@ def decode(fmt: int, canon, N: int, K: int):
 
 
 def dequant(fmt: int, canon, N: int, K: int) -> np.ndarray:
-    """W [N, K] fp64: s*(q-8) for Q4_0, s*q for Q8_0 (exact in fp64)."""
+    """W [N, K] fp64: s*(q-8) for Q4_0, s*q for Q8_0 (exact in fp64); for
+    FP16 the little-endian fp16 values themselves."""
+    if fmt == FP16:
+        if K % QK:
+            raise ValueError("K must be a multiple of 32")
+        b = np.frombuffer(np.ascontiguousarray(canon, dtype=np.uint8).tobytes(), dtype=np.uint8)
+        if b.size != N * K * 2:
+            raise ValueError("canonical buffer has the wrong size")
+        raw = b[0::2].astype(np.uint16) | (b[1::2].astype(np.uint16) << 8)
+        return raw.view(np.float16).astype(np.float64).reshape(N, K)
     s, q = decode(fmt, canon, N, K)
     off = 8 if fmt == Q4_0 else 0
     return (np.repeat(s, QK, axis=1) * (q - off)).astype(np.float64)

@@ -25,13 +25,14 @@ import numpy as np
 
 Q4_0 = 1
 Q8_0 = 2
+FP16 = 3            # plain fp16 weights (no quantisation)
 F16 = 1
 BF16 = 2
 F32 = 3
 
 BLOCK = 32
-BLOCK_BYTES = {Q4_0: 18, Q8_0: 34}
-FORMAT_NAME = {Q4_0: "q4_0", Q8_0: "q8_0"}
+BLOCK_BYTES = {Q4_0: 18, Q8_0: 34, FP16: 64}
+FORMAT_NAME = {Q4_0: "q4_0", Q8_0: "q8_0", FP16: "fp16"}
 DTYPE_NAME = {F16: "f16", BF16: "bf16", F32: "f32"}
 
 # Scale / code distributions of the workloads.
@@ -47,8 +48,8 @@ class QWeight:
     N: int
     K: int
     canon: np.ndarray       # uint8 [N * K/32 * block_bytes]
-    scales: np.ndarray      # float16 [N, K/32]
-    codes: np.ndarray       # uint8 (Q4_0, 0..15) or int8 (Q8_0) [N, K]
+    scales: np.ndarray      # float16 [N, K/32] (None for FP16)
+    codes: np.ndarray       # uint8 (Q4_0, 0..15), int8 (Q8_0) or float16 (FP16: the weights) [N, K]
 
 
 @dataclass
@@ -96,6 +97,20 @@ def q_weight(rng: np.random.Generator, fmt: int, N: int, K: int,
     c = rng.integers(code_range[0], code_range[1] + 1, size=(N, K), dtype=np.int16)
     codes = c.astype(np.uint8) if fmt == Q4_0 else c.astype(np.int8)
     return QWeight(fmt, N, K, pack_blocks(fmt, scales, codes), scales, codes)
+
+
+def fp16_weight(rng: np.random.Generator, N: int, K: int, sigma: float = 0.02) -> QWeight:
+    """Plain fp16 weights N(0, sigma^2) rounded to fp16; canonical = row-major
+    little-endian fp16 [N, K]."""
+    if K % BLOCK:
+        raise ValueError("K must be a multiple of 32")
+    w = (rng.standard_normal(size=(N, K)) * sigma).astype(np.float16)
+    return QWeight(FP16, N, K, np.ascontiguousarray(w).view(np.uint8).reshape(-1).copy(), None, w)
+
+
+def weight(rng: np.random.Generator, fmt: int, N: int, K: int) -> QWeight:
+    """A matrix of any format with the workloads' distributions."""
+    return fp16_weight(rng, N, K) if fmt == FP16 else q_weight(rng, fmt, N, K)
 
 
 def f32_to_bf16_bits(a: np.ndarray) -> np.ndarray:

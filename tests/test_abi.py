@@ -46,13 +46,43 @@ def test_status_strings(q):
         assert q.status_string(s) not in ("ok", "unknown status")
 
 
+def test_fp16_sizes_and_gemm_rejects_it(q):
+    assert q.canonical_bytes(synth.FP16, 100, 96) == 100 * 96 * 2
+    assert q.repacked_bytes(synth.FP16, 100, 96) == 7 * 1 * 4096
+    assert q.repacked_bytes(synth.FP16, 4096, 4096) == 4096 * 4096 * 2
+    L = q.lib()
+    st = L.q4q8_qgemm(synth.FP16, _vp(0x1000), 64, 256, _vp(0x2000), 1, 256, 16, _vp(0x3000), 1, 64, None, 0, None)
+    assert st == -2
+    nws = q.moe_workspace(1, 4, 8, 2, 256, 256)
+    assert q.moe_workspace(synth.FP16, 4, 8, 2, 256, 256) == 0 and nws > 0
+
+
+@pytest.mark.parametrize("N,K", [(16, 128), (17, 160), (33, 256), (1, 32)])
+def test_host_repack_fp16(q, N, K):
+    """Plain fp16 records: block j's slot l (= 16 g + r) at j * 1024 + 16 l holds
+    row r's weights 8 g .. 8 g + 7 of the block; padding is zero."""
+    w = synth.fp16_weight(synth.rng_for(43, N + K), N, K)
+    rep = q.repack_host(synth.FP16, w.canon, N, K)
+    tiles, chunks = (N + 15) // 16, (K + 127) // 128
+    assert rep.size == tiles * chunks * 4096
+    recs = rep.view(np.float16).reshape(tiles, chunks, 4, 64, 8)
+    full = np.zeros((tiles * 16, chunks * 128), dtype=np.float16)
+    full[:N, :K] = w.codes
+    for j in range(4):
+        for l in range(64):
+            r, g = l % 16, l // 16
+            k0 = 32 * j + 8 * g
+            want = full[r::16, :].reshape(tiles, chunks, 128)[:, :, k0:k0 + 8]
+            assert np.array_equal(recs[:, :, j, l, :].view(np.uint16), want.view(np.uint16))
+
+
 @pytest.mark.parametrize("fmt,bb", [(synth.Q4_0, 18), (synth.Q8_0, 34)])
 def test_sizes(q, fmt, bb):
     assert q.canonical_bytes(fmt, 4096, 4096) == 4096 * 128 * bb
     assert q.repacked_bytes(fmt, 4096, 4096) == 4096 * 128 * bb      # aligned: no padding
     assert q.repacked_bytes(fmt, 17, 160) == 2 * 2 * (64 * 16 * (bb - 2) // 16 + 128)
     assert q.canonical_bytes(fmt, 4, 33) == 0
-    assert q.repacked_bytes(3, 4, 32) == 0
+    assert q.repacked_bytes(4, 4, 32) == 0
 
 
 def _unrepack(fmt, rep, N, K):
@@ -113,7 +143,7 @@ def test_qgemv_validation(q):
     L = q.lib()
     Q4, F16 = synth.Q4_0, synth.F16
     cases = [
-        (dict(fmt=3), -2), (dict(N=0), -1), (dict(K=48), -1), (dict(K=0), -1), (dict(M=0), -1), (dict(M=9), -1),
+        (dict(fmt=4), -2), (dict(N=0), -1), (dict(K=48), -1), (dict(K=0), -1), (dict(M=0), -1), (dict(M=9), -1),
         (dict(xdt=3), -2), (dict(W=None), -1), (dict(x=None), -1), (dict(y=None), -1),
         (dict(W=0x1008), -4), (dict(x=0x1004), -4), (dict(M=2, ldx=4100), -4), (dict(M=2, ldx=100), -1),
         (dict(M=2, ldy=10), -1),

@@ -30,7 +30,7 @@ def q():
 
 def _weights(fmt, H, F, seed, down=True):
     shapes = [(F, H), (F, H), (H, F)] if down else [(F, H), (F, H)]
-    ws = [synth.q_weight(synth.rng_for(seed, i), fmt, n, k) for i, (n, k) in enumerate(shapes)]
+    ws = [synth.weight(synth.rng_for(seed, i), fmt, n, k) for i, (n, k) in enumerate(shapes)]
     return ws if down else ws + [None]
 
 
@@ -53,6 +53,7 @@ SWIGLU_CASES = [
     (synth.Q8_0, synth.F16, 70, 4096),
     (synth.Q4_0, synth.BF16, 1, 32),
     (synth.Q4_0, synth.F16, 48, 12288),
+    (synth.FP16, synth.BF16, 100, 640),
 ]
 
 
@@ -115,6 +116,7 @@ FFN_CASES = [
     (synth.Q4_0, synth.BF16, 160, 96),
     (synth.Q8_0, synth.BF16, 512, 1056),
     (synth.Q8_0, synth.F16, 96, 32),
+    (synth.FP16, synth.F16, 256, 384),
 ]
 
 

@@ -25,10 +25,10 @@ def _run(q, w, x, out=None):
     return y.cpu().numpy()
 
 
-@pytest.mark.parametrize("fmt", [synth.Q4_0, synth.Q8_0])
+@pytest.mark.parametrize("fmt", [synth.Q4_0, synth.Q8_0, synth.FP16])
 @pytest.mark.parametrize("N,K", [(16, 128), (17, 160), (1, 32), (300, 1056), (64, 4096)])
 def test_repack_device_matches_host(q, fmt, N, K):
-    w = synth.q_weight(synth.rng_for(51, N + K + fmt), fmt, N, K)
+    w = synth.weight(synth.rng_for(51, N + K + fmt), fmt, N, K)
     dev_bytes = q.repack(fmt, bytes_tensor(w.canon), N, K)
     torch.cuda.synchronize()
     assert np.array_equal(dev_bytes.cpu().numpy(), q.repack_host(fmt, w.canon, N, K))
@@ -38,11 +38,12 @@ SHAPES = [(16, 128), (17, 160), (1, 32), (100, 32), (257, 1056), (64, 4096), (48
 
 
 @pytest.mark.parametrize("fmt,xdt", [(synth.Q4_0, synth.F16), (synth.Q4_0, synth.BF16),
-                                     (synth.Q8_0, synth.BF16), (synth.Q8_0, synth.F16)])
+                                     (synth.Q8_0, synth.BF16), (synth.Q8_0, synth.F16),
+                                     (synth.FP16, synth.F16), (synth.FP16, synth.BF16)])
 @pytest.mark.parametrize("N,K", SHAPES)
 def test_qgemv_parity_small(q, fmt, xdt, N, K):
     """Every M = 1..8 on shapes spanning tiles, ragged rows and a K tail."""
-    w = synth.q_weight(synth.rng_for(52, N * 7 + K + fmt), fmt, N, K)
+    w = synth.weight(synth.rng_for(52, N * 7 + K + fmt), fmt, N, K)
     Wd = q.repack(fmt, bytes_tensor(w.canon), N, K)
     for M in range(1, 9):
         x = synth.activation(synth.rng_for(53, 100 * M + K + xdt), (M, K), xdt)
@@ -182,3 +183,15 @@ def test_qgemv_q8_3b_one_launch(q, M):
     ws, xs = synth.q8_3b(M)
     names = list(ws)
     _grouped_check(q, synth.Q8_0, [ws[n] for n in names], [xs[n] for n in names], M, f"q8 3B one launch M{M}")
+
+
+@pytest.mark.parametrize("M", [1, 8])
+def test_fp16_layer_8b_one_launch(q, M):
+    """Plain fp16 weights of the 8B-shaped layer's seven projections in one
+    grouped launch (bf16 activations meet fp16 weights as fp16 operands)."""
+    names = [n for n, _, _ in synth.LAYER_8B["mats"]]
+    shapes = {n: (N, K) for n, N, K in synth.LAYER_8B["mats"]}
+    ws = [synth.fp16_weight(synth.rng_for(59, i), *shapes[n]) for i, n in enumerate(names)]
+    _, xs = synth.layer_8b(M, mats=[])
+    xb = {k: synth.act_from_values(v.values, synth.BF16) for k, v in xs.items()}
+    _grouped_check(q, synth.FP16, ws, [xb[synth.LAYER_8B_INPUT[n]] for n in names], M, f"fp16 8B layer M{M}")

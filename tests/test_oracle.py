@@ -547,3 +547,28 @@ def test_attention_rows_subset_and_bound():
     assert np.any(np.abs(bad - o) > tol)
     bad, _ = oracle.attention(q, k, v, scale=1.0)
     assert np.any(np.abs(bad - o) > tol)
+
+
+# ----------------------------------------------------------------------------
+# Plain fp16 weights
+# ----------------------------------------------------------------------------
+def test_fp16_dequant_reads_little_endian_rows():
+    """Hand-built bytes: 1.0 = 0x3C00, -2.0 = 0xC000, 0.5 = 0x3800, 65504 = 0x7BFF."""
+    vals = [1.0, -2.0, 0.5, 65504.0]
+    raw = []
+    for v in ([0x3C00, 0xC000, 0x3800, 0x7BFF] * 16):
+        raw += [v & 0xFF, v >> 8]
+    W = oracle.dequant(oracle.FP16, np.array(raw, dtype=np.uint8), 2, 32)
+    assert W.shape == (2, 32)
+    assert list(W[0, :4]) == vals and list(W[1, -4:]) == vals
+
+
+def test_fp16_gemv_matches_exact_rationals():
+    w = synth.fp16_weight(synth.rng_for(44, 0), 5, 64)
+    x = synth.activation(synth.rng_for(44, 1), (2, 64), synth.BF16)
+    y, b = oracle.qgemv(oracle.FP16, w.canon, 5, 64, x.values)
+    for m in range(2):
+        for n in range(5):
+            exact = sum(Fraction(float(w.codes[n, k])) * Fraction(float(x.values[m, k])) for k in range(64))
+            assert abs(Fraction(y[m, n]) - exact) <= Fraction(1, 2 ** 40) * (1 + abs(exact))
+            assert b[m, n] == pytest.approx(sum(abs(float(w.codes[n, k]) * x.values[m, k]) for k in range(64)))
