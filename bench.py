@@ -57,7 +57,7 @@ LAYER_COPIES = 8
 
 def _kernel_source_hash() -> str:
     h = hashlib.sha256()
-    for f in ("qgemv.hip", "q4q8_dev.h", "q4q8_internal.h"):
+    for f in ("qgemv.hip", "gemv_core.h", "q4q8_dev.h", "q4q8_internal.h"):
         with open(os.path.join(ROOT, "gemm_q4_q8_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
