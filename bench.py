@@ -32,8 +32,9 @@ the same layer (all seven matrices, M = 1).
 
 Other workloads (the dependency-order step at M = 1, one-launch steps at
 M = 2/4/8, the single 2048x2048 GEMV, the Q8_0 3B-shaped matrices, the
-layer with plain fp16 weights, the layer's fused decode FFN at M = 1 and 8, the prefill GEMM at M = 512 and
-2048, the MoE layer at 512 tokens and its decode at 1 and 8 tokens,
+layer with plain fp16 weights, the layer's fused decode FFN at M = 1 and 8,
+the prefill GEMM at M = 512 and 2048 (Q8_0 at 512), the MoE layer at 512
+tokens (Q4_0 and Q8_0) and its decode at 1 and 8 tokens,
 prefill attention at S = 512 and 2048) are reported under "workloads", each
 with its own algorithmic bytes / flops and time.
 """
@@ -232,7 +233,7 @@ def cpu_baseline(synth, budget_s: float = 25.0):
             oracle.qgemv(w.fmt, w.canon, w.N, w.K, x.values)
             total_bytes += w.canon.size + 2 * w.K + 4 * w.N
         steps += 1
-        if time.perf_counter() - t0 > budget_s / 3 or steps >= 3:
+        if time.perf_counter() - t0 > budget_s / 2 or steps >= 24:
             break
     dt = time.perf_counter() - t0
     del np
@@ -338,6 +339,8 @@ def extra_workloads(q, torch, synth, ev: HipEvents, quick: bool):
     out += ffn_workloads(q, torch, synth, ev, quick)
     out += prefill_workloads(q, torch, synth, ev, quick)
     out.append(moe_workload(q, torch, synth))
+    if not quick:
+        out.append(moe_workload(q, torch, synth, fmt=2))
     out += moe_decode_workloads(q, torch, synth, quick)
     out += attn_workloads(q, torch, synth, ev, quick)
     return out
@@ -462,14 +465,17 @@ def ffn_workloads(q, torch, synth, ev: HipEvents, quick: bool):
 
 
 def prefill_workloads(q, torch, synth, ev: HipEvents, quick: bool):
-    """Prefill GEMM Y[M, 12288] = X[M, 4096] W^T, Q4_0, bf16 in and out.  The
-    timed span of one call covers both of its kernels (bf16 -> fp16 pre-pass
-    and the GEMM), from the first dispatch's start to the last one's end."""
+    """Prefill GEMM Y[M, 12288] = X[M, 4096] W^T, Q4_0 (and Q8_0 at M = 512),
+    bf16 in and out.  The timed span of one call covers both of its kernels
+    (bf16 -> fp16 pre-pass and the GEMM), from the first dispatch's start to
+    the last one's end."""
     out = []
     dev = torch.device("cuda:0")
-    for M in ([512] if quick else [512, 2048]):
+    for fmt, M in ([(1, 512)] if quick else [(1, 512), (1, 2048), (2, 512)]):
         w, x = synth.prefill(M)
-        W0 = q.repack(1, torch.from_numpy(w.canon).to(dev), w.N, w.K)
+        if fmt == 2:
+            w = synth.q_weight(synth.rng_for(synth.PREFILL["seed"], 50), 2, w.N, w.K)
+        W0 = q.repack(fmt, torch.from_numpy(w.canon).to(dev), w.N, w.K)
         Ws = [W0] + [W0.clone() for _ in range(3)]
         X = torch.from_numpy(x.bits.view("int16")).view(torch.bfloat16).to(dev)
         Y = torch.empty((M, w.N), dtype=torch.bfloat16, device=dev)
@@ -477,11 +483,11 @@ def prefill_workloads(q, torch, synth, ev: HipEvents, quick: bool):
         reps = 24
         pairs = [(ev.create(), ev.create()) for _ in range(reps + 4)]
         for i in range(reps + 4):
-            q.qgemm(1, Ws[i % 4], w.N, w.K, X, out=Y, ws=wsp, events=pairs[i])
+            q.qgemm(fmt, Ws[i % 4], w.N, w.K, X, out=Y, ws=wsp, events=pairs[i])
         d = sorted(ev.elapsed_ms(a, b) * 1e-3 for a, b in pairs[4:])
         mean = sum(d) / len(d)
         fl = 2.0 * M * w.N * w.K
-        out.append({"workload": f"q4_0 prefill gemm M={M} K={w.K} N={w.N} (bf16 in/out)",
+        out.append({"workload": f"{synth.FORMAT_NAME[fmt]} prefill gemm M={M} K={w.K} N={w.N} (bf16 in/out)",
                     "call_us_mean": round(mean * 1e6, 2), "call_us_min": round(d[0] * 1e6, 2),
                     "TFLOP/s": round(fl / mean / 1e12, 1),
                     "mfma_frac": round(fl / mean / 1e12 / F16_MFMA_PEAK_TFLOPS, 4)})
@@ -490,37 +496,39 @@ def prefill_workloads(q, torch, synth, ev: HipEvents, quick: bool):
     return out
 
 
-def moe_workload(q, torch, synth):
-    """MoE layer: 512 bf16 tokens, 128 Q4_0 experts (gate/up 768x2048, down
-    2048x768), top-8.  One step = route + sort + expert GEMMs + combine,
-    timed with stream events (launch gaps included).  Expert weights are
-    340 MB (more than the Infinity Cache): the layer is HBM-bound, so the
-    roofline is max(weight bytes / 8 TB/s, flops / 2.5 PFLOP/s)."""
+def moe_workload(q, torch, synth, fmt: int = 1):
+    """MoE layer: 512 bf16 tokens, 128 Q4_0 (or Q8_0) experts (gate/up
+    768x2048, down 2048x768), top-8.  One step = route + sort + expert GEMMs
+    + combine, timed with stream events (launch gaps included).  Expert
+    weights are 340 MB at Q4_0 (642 MB at Q8_0), more than the Infinity
+    Cache: the layer is HBM-bound, so the roofline is max(weight bytes /
+    8 TB/s, flops / 2.5 PFLOP/s)."""
     dev = torch.device("cuda:0")
     cfg = synth.MOE
     T, E, k, H, F = cfg["T"], cfg["E"], cfg["topk"], cfg["H"], cfg["F"]
-    logits, x, wg, wu, wd = synth.moe()
+    logits, x, wg, wu, wd = synth.moe(fmt=fmt)
 
     def stack(ws, n, kk):
-        return torch.cat([q.repack(1, torch.from_numpy(w.canon).to(dev), n, kk) for w in ws])
+        return torch.cat([q.repack(fmt, torch.from_numpy(w.canon).to(dev), n, kk) for w in ws])
 
     Wg, Wu, Wd = stack(wg, F, H), stack(wu, F, H), stack(wd, H, F)
     L = torch.from_numpy(logits).to(dev)
     X = torch.from_numpy(x.bits.view("int16")).view(torch.bfloat16).to(dev)
     out = torch.empty((T, H), dtype=torch.float32, device=dev)
-    wsp = torch.empty(q.moe_workspace(1, T, E, k, H, F), dtype=torch.uint8, device=dev)
+    wsp = torch.empty(q.moe_workspace(fmt, T, E, k, H, F), dtype=torch.uint8, device=dev)
 
     def step(_):
         ids, gates, counts, offsets, sp = q.moe_route(L, k)
-        q.moe_qgemm(1, Wg, Wu, Wd, E, H, F, X, k, gates, offsets, sp, out=out, ws=wsp)
+        q.moe_qgemm(fmt, Wg, Wu, Wd, E, H, F, X, k, gates, offsets, sp, out=out, ws=wsp)
 
     dt = _time_launches(torch, step, 30)
     fl = 2.0 * T * k * 3 * F * H
-    wbytes = 3 * E * q.repacked_bytes(1, F, H)
+    wbytes = 3 * E * q.repacked_bytes(fmt, F, H)
     roof = max(wbytes / (HBM_PEAK_GBS * 1e9), fl / (F16_MFMA_PEAK_TFLOPS * 1e12))
     del Wg, Wu, Wd, wsp
     torch.cuda.empty_cache()
-    return {"workload": f"q4_0 moe T={T} E={E} top{k} H={H} F={F} (bf16 tokens)", "step_us": round(dt * 1e6, 2),
+    return {"workload": f"{synth.FORMAT_NAME[fmt]} moe T={T} E={E} top{k} H={H} F={F} (bf16 tokens)",
+            "step_us": round(dt * 1e6, 2),
             "TFLOP/s": round(fl / dt / 1e12, 1), "mfma_frac": round(fl / dt / 1e12 / F16_MFMA_PEAK_TFLOPS, 4),
             "weight_GB/s": round(wbytes / dt / 1e9, 1), "roofline_us": round(roof * 1e6, 2),
             "roofline_frac": round(roof / dt, 4)}
