@@ -406,8 +406,9 @@ static int attn_impl(int dt, const void* Q, const void* K, const void* V, void* 
   if (B < 1 || S < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv)
     return fail(Q4Q8_ERR_INVALID_ARG, "attn_prefill: B=%d S=%d Hq=%d Hkv=%d (Hq a multiple of Hkv)", B, S, Hq, Hkv);
   if (!(scale > 0.0f) || scale > 1e30f) return fail(Q4Q8_ERR_INVALID_ARG, "attn_prefill: scale must be positive");
-  if ((int64_t)B * Hq * ((S + 127) / 128) >= (1LL << 31) || (int64_t)B * S * Hq * D >= (1LL << 40))
-    return fail(Q4Q8_ERR_UNSUPPORTED, "attn_prefill: sizes beyond limits");
+  if ((int64_t)B * Hq * ((S + 127) / 128) >= (1LL << 31) || (int64_t)B * S * Hq * D >= (1LL << 40) ||
+      (int64_t)S * Hkv * D * 2 >= (1LL << 31))
+    return fail(Q4Q8_ERR_UNSUPPORTED, "attn_prefill: sizes beyond limits (S * Hkv * D below 2^30)");
   if (!aligned(Q, 16) || !aligned(K, 16) || !aligned(V, 16) || !aligned(O, 8))
     return fail(Q4Q8_ERR_ALIGNMENT, "attn_prefill: Q, K, V must be 16-byte aligned, O 8-byte aligned");
   clear_hip_error();

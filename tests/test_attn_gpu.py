@@ -60,6 +60,19 @@ def test_attn_parity(q, B, S, Hq, Hkv, causal, dt):
     _check(got, ref, bound, f"attn B{B} S{S} Hq{Hq} Hkv{Hkv} causal{causal} dt{dt}")
 
 
+@pytest.mark.parametrize("B,S", [(8, 512), (8, 640)])
+def test_attn_paired_query_blocks(q, B, S):
+    """Causal with enough (batch, head) pairs that each workgroup takes query
+    blocks i and last - i (640: an odd block count, the middle block alone);
+    sampled query positions of every head."""
+    Hq, Hkv = 32, 8
+    qa, ka, va = synth.attention_inputs(B, S, Hq, Hkv, 128, synth.BF16, 165 + S)
+    got = _run(q, qa, ka, va, True)
+    rows = sorted({0, 1, 63, 64, 127, 128, 255, 256, 300, S - 129, S - 128, S - 2, S - 1})
+    ref, bound = oracle.attention(qa.values, ka.values, va.values, causal=True, rows=rows)
+    _check(got[:, rows], ref, bound, f"attn paired B{B} S{S}")
+
+
 def test_attn_large_scores(q):
     """Scores far from 0 (inputs x 6): the running max must move often."""
     B, S, Hq, Hkv = 1, 384, 2, 1
