@@ -44,6 +44,7 @@ struct MoeDecArgs {
   const int32_t* sorted_pairs;
   int32_t N, K;              // output rows per expert, reduction length (multiples of 128)
   int32_t topk, E, npos;     // npos = T * topk sorted positions
+  int32_t T;
   int32_t groups;            // workgroups per sorted position
   int32_t ksh;               // K-shares per matrix, a power of 2
 };
@@ -66,7 +67,8 @@ __global__ __launch_bounds__(WAVES * 64) void moe_gemv_kernel(const MoeDecArgs a
   __shared__ int32_t s_off[kDecMaxExperts + 1];
   __shared__ int32_t s_pair[kMoeDecodeMaxTokens];
   for (int i = tid; i <= a.E; i += WAVES * 64) s_off[i] = a.offsets[i];
-  if (tid < kMoeDecodeMaxTokens && pos + tid < a.npos) s_pair[tid] = a.sorted_pairs[pos + tid];
+  if (tid < kMoeDecodeMaxTokens && pos + tid < a.npos)
+    s_pair[tid] = min(max(a.sorted_pairs[pos + tid], 0), a.npos - 1);   // clamped like the prefill path
   __syncthreads();
   // Expert owning sorted position pos: the largest e with offsets[e] <= pos.
   int lo = 0, hi = a.E;
@@ -78,7 +80,9 @@ __global__ __launch_bounds__(WAVES * 64) void moe_gemv_kernel(const MoeDecArgs a
   const int e = lo;
   const int r0 = s_off[e];
   if (r0 != pos) return;                      // not the expert's first position
-  const int M = s_off[e + 1] - r0;            // the expert's rows, 1..T
+  // The expert's rows: 1..T for routing from q4q8_moe_route (a token picks
+  // an expert at most once); clamped so malformed routing stays in bounds.
+  const int M = max(1, min(min(s_off[e + 1] - r0, a.T), a.npos - r0));
 
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -223,6 +227,7 @@ void launch_dec_fmt(int xdt, const void* Wg, const void* Wu, const void* Wd, int
   a.topk = topk;
   a.E = E;
   a.npos = npos;
+  a.T = T;
   // gate/up: [F, H] per expert, x = the tokens.
   a.W = (const uint8_t*)Wg;
   a.W2 = (const uint8_t*)Wu;
