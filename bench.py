@@ -260,11 +260,18 @@ def _time_launches(torch, fn, reps: int, warmup: int = 3):
     return e0.elapsed_time(e1) * 1e-3 / reps
 
 
-def extra_workloads(q, torch, synth, ev: HipEvents, quick: bool):
+EXTRA_GROUPS = ("layer", "gemv2048", "q8_3b", "fp16", "ffn", "prefill", "moe", "moe_decode", "attn")
+
+
+def extra_workloads(q, torch, synth, ev: HipEvents, quick: bool, only=None):
+    """Every other workload, or only the groups named in `only`."""
+    def want(name):
+        return only is None or name in only
+
     out = []
     dev = torch.device("cuda:0")
     # The M = 1 step in dependency order, and both forms at other M (graph replays as for the headline).
-    for M in ([1] if quick else [1, 2, 4, 8]):
+    for M in ([1] if quick else [1, 2, 4, 8]) if want("layer") else []:
         lay = DecodeLayer(q, torch, synth, M, LAYER_COPIES)
         for mode in (["chain"] if M == 1 else ["one", "chain"]):
             lay.mode = mode
@@ -279,7 +286,30 @@ def extra_workloads(q, torch, synth, ev: HipEvents, quick: bool):
             out.append(rec)
         del lay
         torch.cuda.empty_cache()
-    # Single 2048x2048 GEMV (latency-bound: 2.37 MB).
+    if want("gemv2048"):
+        out.append(gemv2048_workload(q, torch, synth, ev))
+    if want("q8_3b"):
+        out += q8_3b_workloads(q, torch, synth, ev, quick)
+    if want("fp16"):
+        out.append(fp16_layer_workload(q, torch, synth, ev))
+    if want("ffn"):
+        out += ffn_workloads(q, torch, synth, ev, quick)
+    if want("prefill"):
+        out += prefill_workloads(q, torch, synth, ev, quick)
+    if want("moe"):
+        out.append(moe_workload(q, torch, synth))
+        if not quick:
+            out.append(moe_workload(q, torch, synth, fmt=2))
+    if want("moe_decode"):
+        out += moe_decode_workloads(q, torch, synth, quick)
+    if want("attn"):
+        out += attn_workloads(q, torch, synth, ev, quick)
+    return out
+
+
+def gemv2048_workload(q, torch, synth, ev: HipEvents):
+    """Single 2048x2048 GEMV (latency-bound: 2.37 MB)."""
+    dev = torch.device("cuda:0")
     w, x = synth.gemv_problem(1, 2048, 2048, 1, synth.F16, synth.GEMV_2048["seed"])
     W0 = q.repack(1, torch.from_numpy(w.canon).to(dev), 2048, 2048)
     Ws = [W0] + [W0.clone() for _ in range(127)]          # 302 MB: more than the Infinity Cache
@@ -293,12 +323,18 @@ def extra_workloads(q, torch, synth, ev: HipEvents, quick: bool):
     kd = sum(ev.elapsed_ms(a, b) for a, b in pairs) / 64 * 1e-3
     nb = q.repacked_bytes(1, 2048, 2048) + 2048 * 2 + 2048 * 4
     b2b = _time_launches(torch, lambda i: q.qgemv_grouped(1, probs[i % 128], 1, descs=descs[i % 128]), 256)
-    out.append({"workload": "q4_0 gemv 2048x2048 M=1", "kernel_us": round(kd * 1e6, 2),
-                "kernel_GB/s": round(nb / kd / 1e9, 1), "back_to_back_us": round(b2b * 1e6, 2),
-                "back_to_back_GB/s": round(nb / b2b / 1e9, 1)})
+    rec = {"workload": "q4_0 gemv 2048x2048 M=1", "kernel_us": round(kd * 1e6, 2),
+           "kernel_GB/s": round(nb / kd / 1e9, 1), "back_to_back_us": round(b2b * 1e6, 2),
+           "back_to_back_GB/s": round(nb / b2b / 1e9, 1)}
     del Ws, probs, descs
     torch.cuda.empty_cache()
-    # Q8_0 3B-shaped matrices, M = 1 and 8: sum of kernel times.
+    return rec
+
+
+def q8_3b_workloads(q, torch, synth, ev: HipEvents, quick: bool):
+    """Q8_0 3B-shaped matrices, M = 1 and 8: one launch each, and one grouped launch."""
+    out = []
+    dev = torch.device("cuda:0")
     for M in ([1, 8] if not quick else [1]):
         ws, xs = synth.q8_3b(M)
         tot_b, tot_t = 0, 0.0
@@ -335,14 +371,6 @@ def extra_workloads(q, torch, synth, ev: HipEvents, quick: bool):
                     "GB/s": round(tot_b / kd / 1e9, 1)})
         del Ws, copies, probs, descs
         torch.cuda.empty_cache()
-    out.append(fp16_layer_workload(q, torch, synth, ev))
-    out += ffn_workloads(q, torch, synth, ev, quick)
-    out += prefill_workloads(q, torch, synth, ev, quick)
-    out.append(moe_workload(q, torch, synth))
-    if not quick:
-        out.append(moe_workload(q, torch, synth, fmt=2))
-    out += moe_decode_workloads(q, torch, synth, quick)
-    out += attn_workloads(q, torch, synth, ev, quick)
     return out
 
 
@@ -607,6 +635,8 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-extra", action="store_true", help="skip the other workloads")
     ap.add_argument("--quick-extra", action="store_true")
+    ap.add_argument("--only", nargs="+", choices=EXTRA_GROUPS, default=None,
+                    help="run only these groups of the other workloads (e.g. for a profiled run)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a 256 MiB device copy (known HBM bytes) for counter calibration")
     args = ap.parse_args()
@@ -663,7 +693,7 @@ def main():
     torch.cuda.empty_cache()
     workloads = []
     if not args.no_extra:
-        workloads = extra_workloads(q, torch, synth, ev, args.quick_extra)
+        workloads = extra_workloads(q, torch, synth, ev, args.quick_extra, args.only)
         for w in workloads:
             log(json.dumps(w))
 
