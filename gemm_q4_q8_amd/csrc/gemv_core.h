@@ -18,7 +18,8 @@ namespace q4q8 {
 
 constexpr int kGemvBufFlags = 0x00020000;   // raw buffer, 32-bit data format (gfx9)
 #ifndef Q4Q8_WEIGHT_AUX
-#define Q4Q8_WEIGHT_AUX 0                   // cache policy bits of the weight loads
+#define Q4Q8_WEIGHT_AUX 2                   // cache policy of the weight loads: nt (streamed once; measured
+                                            // +9% on the decode step over the default policy)
 #endif
 
 // One chunk of a tile's weights in registers.
