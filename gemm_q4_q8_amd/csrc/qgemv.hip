@@ -291,8 +291,9 @@ hipError_t launch_qgemv(int fmt, int xdt, GemvArgs args, int max_chunks, int max
                         const LaunchEvents& ev) {
   const GemvShape c = pick_shape(args.total_tiles, max_chunks, args.M, max_k);
   // Problems of one K share the launch-wide split.  When K differs, the
-  // workgroup is 8 waves and each problem takes the power-of-2 split closest
-  // to 16 chunks per wave, so the long-K problems do not trail the launch.
+  // workgroup is 8 waves and each problem takes the finest power-of-2 split
+  // that keeps at least 8 chunks a wave (up to the workgroup), so the long-K
+  // problems do not trail the launch.
   // A SwiGLU pair takes twice its K-shares in waves (gate and up halves).
   bool mixed = false, pairs = false;
   for (int i = 1; i < args.count; ++i) mixed |= args.p[i].K != args.p[0].K;
@@ -304,7 +305,7 @@ hipError_t launch_qgemv(int fmt, int xdt, GemvArgs args, int max_chunks, int max
       const int nch = (args.p[i].K + kChunkK - 1) / kChunkK;
       const int mats = args.p[i].W2 ? 2 : 1;
       int ks = 1;
-      while (ks * mats < waves && nch >= 24 * ks) ks *= 2;   // nch / ks nearest 16 among powers of 2
+      while (ks * mats < waves && nch >= 16 * ks) ks *= 2;   // >= 8 chunks a wave (measured: 24 -> 16 gave -4%)
       args.ks[i] = ks * mats;
     }
   } else {
