@@ -244,17 +244,19 @@ static int ffn_impl(int fmt, const void* Wg, const void* Wu, const void* Wd, int
   int st = check_gemv_common(fmt, xdt, M, 1);
   if (st) return st;
   if (!Wg || !Wu || !Wd) return fail(Q4Q8_ERR_INVALID_ARG, "ffn_decode: null pointer");
-  // Validate both launches before enqueuing either.
-  const GemvIn gu{Wg, Wu, x, ws ? ws : (void*)Wg, F, H, ldx, F, Q4Q8_BF16};
-  st = check_gemv_prob(fmt, gu, M, 0);
-  if (st) return st;
-  const GemvIn dn{Wd, nullptr, ws ? ws : (void*)Wd, y, H, F, F, ldy, Q4Q8_F32};
-  st = check_gemv_prob(fmt, dn, M, 1);
-  if (st) return st;
+  if (F < 32 || F % 32) return fail(Q4Q8_ERR_INVALID_ARG, "ffn_decode: F=%lld not a positive multiple of 32", (long long)F);
   const size_t need = ffn_ws(M, F);
   if (!ws || ws_bytes < need)
     return fail(Q4Q8_ERR_WORKSPACE, "ffn_decode: workspace holds %zu bytes, needs %zu", ws ? ws_bytes : 0, need);
   if (!aligned(ws, 256)) return fail(Q4Q8_ERR_ALIGNMENT, "ffn_decode: workspace not 256-byte aligned");
+  // Validate both launches before enqueuing either: gate/up writes h (bf16,
+  // rows of F) into ws, down reads it.
+  const GemvIn gu{Wg, Wu, x, ws, F, H, ldx, F, Q4Q8_BF16};
+  st = check_gemv_prob(fmt, gu, M, 0);
+  if (st) return st;
+  const GemvIn dn{Wd, nullptr, ws, y, H, F, F, ldy, Q4Q8_F32};
+  st = check_gemv_prob(fmt, dn, M, 1);
+  if (st) return st;
   q4q8::LaunchEvents e1, e2;
   e1.start = ev.start;
   e2.stop = ev.stop;

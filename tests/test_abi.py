@@ -192,6 +192,7 @@ def test_ffn_decode_validation(q):
     ok = dict(fmt=2, Wg=0x1000, Wu=0x2000, Wd=0x3000, H=512, F=256, x=0x4000, xdt=1, ldx=512, M=2, y=0x5000,
               ldy=512, ws=0x100000, nws=nws)
     for over, want in [(dict(ws=0), -3), (dict(nws=nws - 1), -3), (dict(ws=0x100010), -4), (dict(F=100), -1),
+                       (dict(F=0), -1), (dict(H=0), -1),
                        (dict(Wd=None), -1), (dict(Wd=0x3008), -4), (dict(ldy=100), -1), (dict(y=0x5002), -4),
                        (dict(M=0), -1), (dict(fmt=0), -2)]:
         a = dict(ok)
@@ -238,6 +239,9 @@ def test_moe_validation(q):
     assert L.q4q8_moe_route(p[0], 512, 128, 129, *p[1:], None) == -1
     assert L.q4q8_moe_route(p[0], 512, 2048, 8, *p[1:], None) == -2
     assert L.q4q8_moe_route(None, 512, 128, 8, *p[1:], None) == -1
+    assert L.q4q8_moe_route(p[0], 0, 128, 8, *p[1:], None) == -1          # no tokens
+    assert L.q4q8_moe_route(p[0], 512, 0, 1, *p[1:], None) == -1          # no experts
+    assert q.moe_workspace(1, 0, 128, 8, 2048, 768) == 0
     nws = q.moe_workspace(1, 512, 128, 8, 2048, 768)
     assert nws > 0
     args = [1, _vp(0x1000), _vp(0x2000), _vp(0x3000), 128, 2048, 768, _vp(0x4000), 2, 512, 8,
@@ -250,6 +254,9 @@ def test_moe_validation(q):
     assert L.q4q8_moe_qgemm(*a) == -3
     a = list(args)
     a[5] = 2000
+    assert L.q4q8_moe_qgemm(*a) == -1
+    a = list(args)
+    a[9] = 0                       # T = 0
     assert L.q4q8_moe_qgemm(*a) == -1
     a = list(args)
     a[16] = _vp(0x10010)
