@@ -247,7 +247,7 @@ __global__ __launch_bounds__(WAVES * 64) void moe_stream_kernel(
     const int32_t* __restrict__ offsets, const int32_t* __restrict__ sorted_pairs, uint16_t* __restrict__ out16,
     uint16_t* __restrict__ h_out, int tiles_per_wave, int groups) {
   constexpr int NW = MODE == kGateUp ? 2 : 1;
-  constexpr int MT = 4, BM = kStreamBM;
+  constexpr int MT = kStreamBM / 16, BM = kStreamBM;
   constexpr int REC = Fmt<FMT>::kRecBytes;
   constexpr int CODE = Fmt<FMT>::kCodeBytes;
   constexpr int NV = FMT == kQ4_0 ? 1 : 2;

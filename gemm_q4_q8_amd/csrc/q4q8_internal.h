@@ -46,7 +46,7 @@ struct GemvArgs {
   int32_t count;
   int32_t M;
   int32_t total_tiles;
-  int32_t pad;
+  int32_t xk;               // problems with K <= xk stage x in LDS (set by the launcher)
   GemvProb p[kMaxGroup];
 };
 

@@ -27,6 +27,7 @@
 
 #include <algorithm>
 #include <mutex>
+#include <type_traits>
 
 namespace q4q8 {
 
@@ -35,8 +36,17 @@ constexpr int XP = 4;                   // x pieces per thread staged before the
 constexpr int64_t kLdsTotal = 160 * 1024;          // LDS per workgroup on gfx950
 constexpr int64_t kLdsCap = kLdsTotal - 8 * 1024;  // dynamic LDS for the activations
 
-template <int FMT, int XDT, int NI, int WAVES, int P, bool XLDS>
-__global__ __launch_bounds__(WAVES * 64) void qgemv_kernel(const GemvArgs args) {
+// Where the activation rows come from: global memory, LDS, or LDS for the
+// problems with K <= args.xk and global memory for the rest.
+enum { kXGlobal = 0, kXLds = 1, kXMixed = 2 };
+
+// The mixed form holds both paths; for Q4_0 at M > 4 it is held to 64
+// registers like the other forms (no spills there), so that two 16-wave
+// workgroups still share a CU.
+template <int FMT, int XDT, int NI, int WAVES, int P, int XM>
+__global__ __launch_bounds__(WAVES * 64)
+__attribute__((amdgpu_waves_per_eu(XM == kXMixed && NI == 2 && FMT == kQ4_0 ? 8 : 1)))
+void qgemv_kernel(const GemvArgs args) {
   constexpr int REC = Fmt<FMT>::kRecBytes;
   typedef typename Op<XDT>::vec vec;
   typedef GemvStage<FMT> Stage;
@@ -88,123 +98,138 @@ __global__ __launch_bounds__(WAVES * 64) void qgemv_kernel(const GemvArgs args) 
   const int ldsx = K + 8;
   const int M = args.M;
   const uint16_t* __restrict__ xg = prob.x;
-  Stage st[P];
-  if constexpr (XLDS) {
-    const int per_row = K / 8 + 1;                 // 16-byte pieces incl. the pad
-    const int pieces = M * per_row + kXSlack / 16;
-    u32x4_t xv[XP];
-#pragma unroll
-    for (int u = 0; u < XP; ++u) {
-      const int i = tid + u * WAVES * 64;
-      const int mm = i / per_row, k8 = i - mm * per_row;
-      xv[u] = (mm < M && k8 < K / 8) ? *(const u32x4_t*)(xg + (int64_t)mm * prob.ldx + k8 * 8) : u32x4_t{0, 0, 0, 0};
-    }
-#pragma unroll
-    for (int p = 0; p < P; ++p) load(st[p], ks + p * KSH);   // past the tile: zero, no memory traffic
-#pragma unroll
-    for (int u = 0; u < XP; ++u) {
-      const int i = tid + u * WAVES * 64;
-      if (i < pieces) *(u32x4_t*)(xs + i * 8) = xv[u];
-    }
-    for (int i = tid + XP * WAVES * 64; i < pieces; i += WAVES * 64) {
-      const int mm = i / per_row, k8 = i - mm * per_row;
-      const u32x4_t v =
-          (mm < M && k8 < K / 8) ? *(const u32x4_t*)(xg + (int64_t)mm * prob.ldx + k8 * 8) : u32x4_t{0, 0, 0, 0};
-      *(u32x4_t*)(xs + i * 8) = v;
-    }
-    __syncthreads();
-  } else {
-#pragma unroll
-    for (int p = 0; p < P; ++p) load(st[p], ks + p * KSH);
-  }
-  const int xrow_lds = (mvalid ? m : 0) * ldsx + 8 * g;
-  const uint16_t* __restrict__ xrow_g = xg + (mvalid ? (int64_t)m * prob.ldx : 0) + 8 * g;
+  __shared__ float red[WAVES][NI][64];   // split-K partial sums
 
-  float acc[NI];
+  // The rest of the kernel, with x read from LDS (xl) or global memory.
+  auto run = [&](auto xlc) __attribute__((always_inline)) {
+    constexpr bool xl = decltype(xlc)::value;
+    Stage st[P];
+    if constexpr (xl) {
+      const int per_row = K / 8 + 1;                 // 16-byte pieces incl. the pad
+      const int pieces = M * per_row + kXSlack / 16;
+      u32x4_t xv[XP];
 #pragma unroll
-  for (int i = 0; i < NI; ++i) acc[i] = 0.0f;
-
-  auto compute = [&](const Stage& s, int c) {
-    vec a[kBlocksPerChunk];
-    if constexpr (XLDS) {
-      const int cx = c < nchunks ? c : nchunks - 1;   // chunks past the tile are all zero-scale
-      const uint16_t* xa = xs + xrow_lds + cx * kChunkK;
+      for (int u = 0; u < XP; ++u) {
+        const int i = tid + u * WAVES * 64;
+        const int mm = i / per_row, k8 = i - mm * per_row;
+        xv[u] = (mm < M && k8 < K / 8) ? *(const u32x4_t*)(xg + (int64_t)mm * prob.ldx + k8 * 8) : u32x4_t{0, 0, 0, 0};
+      }
 #pragma unroll
-      for (int j = 0; j < kBlocksPerChunk; ++j) a[j] = *(const vec*)(xa + j * 32);
+      for (int p = 0; p < P; ++p) load(st[p], ks + p * KSH);   // past the tile: zero, no memory traffic
+#pragma unroll
+      for (int u = 0; u < XP; ++u) {
+        const int i = tid + u * WAVES * 64;
+        if (i < pieces) *(u32x4_t*)(xs + i * 8) = xv[u];
+      }
+      for (int i = tid + XP * WAVES * 64; i < pieces; i += WAVES * 64) {
+        const int mm = i / per_row, k8 = i - mm * per_row;
+        const u32x4_t v =
+            (mm < M && k8 < K / 8) ? *(const u32x4_t*)(xg + (int64_t)mm * prob.ldx + k8 * 8) : u32x4_t{0, 0, 0, 0};
+        *(u32x4_t*)(xs + i * 8) = v;
+      }
+      __syncthreads();
     } else {
 #pragma unroll
-      for (int j = 0; j < kBlocksPerChunk; ++j) {
-        int blk = c * kBlocksPerChunk + j;
-        blk = blk < nblocks ? blk : nblocks - 1;     // past-K blocks have scale 0
-        a[j] = *(const vec*)(xrow_g + blk * 32);
+      for (int p = 0; p < P; ++p) load(st[p], ks + p * KSH);
+    }
+    const int xrow_lds = (mvalid ? m : 0) * ldsx + 8 * g;
+    const uint16_t* __restrict__ xrow_g = xg + (mvalid ? (int64_t)m * prob.ldx : 0) + 8 * g;
+
+    float acc[NI];
+#pragma unroll
+    for (int i = 0; i < NI; ++i) acc[i] = 0.0f;
+
+    auto compute = [&](const Stage& s, int c) {
+      vec a[kBlocksPerChunk];
+      if constexpr (xl) {
+        const int cx = c < nchunks ? c : nchunks - 1;   // chunks past the tile are all zero-scale
+        const uint16_t* xa = xs + xrow_lds + cx * kChunkK;
+#pragma unroll
+        for (int j = 0; j < kBlocksPerChunk; ++j) a[j] = *(const vec*)(xa + j * 32);
+      } else {
+#pragma unroll
+        for (int j = 0; j < kBlocksPerChunk; ++j) {
+          int blk = c * kBlocksPerChunk + j;
+          blk = blk < nblocks ? blk : nblocks - 1;     // past-K blocks have scale 0
+          a[j] = *(const vec*)(xrow_g + blk * 32);
+        }
+      }
+      if constexpr (FMT == kFP16W) {
+        half8_t ah[kBlocksPerChunk];
+#pragma unroll
+        for (int j = 0; j < kBlocksPerChunk; ++j) {
+          if constexpr (XDT == kBF16) ah[j] = bf16x8_to_half8(a[j]);
+          else ah[j] = a[j];
+        }
+        gemv_mma_fp16w<NI>(s, ah, acc);
+      } else {
+        gemv_mma<FMT, XDT, NI>(s, a, acc);
+      }
+    };
+
+    // Chunks of this wave: ks + i KSH for i < nw.  Stage p holds chunk i with
+    // i % P == p; full groups of P prefetch the next group, the last group
+    // (possibly partial) issues no loads, so no load runs past the wave's share.
+    const int nw = (nchunks - ks + KSH - 1) / KSH;
+    int i0 = 0;
+    for (; i0 + P < nw; i0 += P) {
+#pragma unroll
+      for (int p = 0; p < P; ++p) {
+        const int c = ks + (i0 + p) * KSH;
+        compute(st[p], c);
+        __builtin_amdgcn_sched_barrier(0);
+        load(st[p], c + P * KSH);
       }
     }
-    if constexpr (FMT == kFP16W) {
-      half8_t ah[kBlocksPerChunk];
 #pragma unroll
-      for (int j = 0; j < kBlocksPerChunk; ++j) {
-        if constexpr (XDT == kBF16) ah[j] = bf16x8_to_half8(a[j]);
-        else ah[j] = a[j];
+    for (int p = 0; p < P; ++p)
+      if (i0 + p < nw) compute(st[p], ks + (i0 + p) * KSH);
+
+    if (KS > 1) {   // uniform over the workgroup
+#pragma unroll
+      for (int i = 0; i < NI; ++i) red[wave][i][lane] = acc[i];
+      __syncthreads();
+      if (kw != 0) return;
+      // Fixed order: K-shares 0..KSH-1 of the gate (or plain) rows, then of the
+      // up rows; SwiGLU in fp32.
+#pragma unroll
+      for (int i = 0; i < NI; ++i) {
+        float v = red[wave][i][lane];
+        for (int w = 1; w < KSH; ++w) v += red[wave + w][i][lane];
+        if (pair) {
+          float u = red[wave + KSH][i][lane];
+          for (int w = 1; w < KSH; ++w) u += red[wave + KSH + w][i][lane];
+          v = silu_f32(v) * u;
+        }
+        acc[i] = v;
       }
-      gemv_mma_fp16w<NI>(s, ah, acc);
-    } else {
-      gemv_mma<FMT, XDT, NI>(s, a, acc);
+    }
+    if (!tile_ok) return;
+    // Lane (r, g), register i holds y[m = 4 i + g][n = 16 tile + r].
+    const int n = tile * kTileRows + r;
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const int mo = 4 * i + g;
+      if (mo < args.M && n < N) {
+        const int64_t o = (int64_t)mo * prob.ldy + n;
+        if (!pair || prob.ydt == kF32)
+          ((float*)prob.y)[o] = acc[i];
+        else if (prob.ydt == kBF16)
+          ((__bf16*)prob.y)[o] = (__bf16)acc[i];
+        else
+          ((_Float16*)prob.y)[o] = (_Float16)acc[i];
+      }
     }
   };
 
-  // Chunks of this wave: ks + i KSH for i < nw.  Stage p holds chunk i with
-  // i % P == p; full groups of P prefetch the next group, the last group
-  // (possibly partial) issues no loads, so no load runs past the wave's share.
-  const int nw = (nchunks - ks + KSH - 1) / KSH;
-  int i0 = 0;
-  for (; i0 + P < nw; i0 += P) {
-#pragma unroll
-    for (int p = 0; p < P; ++p) {
-      const int c = ks + (i0 + p) * KSH;
-      compute(st[p], c);
-      __builtin_amdgcn_sched_barrier(0);
-      load(st[p], c + P * KSH);
-    }
-  }
-#pragma unroll
-  for (int p = 0; p < P; ++p)
-    if (i0 + p < nw) compute(st[p], ks + (i0 + p) * KSH);
-
-  if (KS > 1) {   // uniform over the workgroup
-    __shared__ float red[WAVES][NI][64];
-#pragma unroll
-    for (int i = 0; i < NI; ++i) red[wave][i][lane] = acc[i];
-    __syncthreads();
-    if (kw != 0) return;
-    // Fixed order: K-shares 0..KSH-1 of the gate (or plain) rows, then of the
-    // up rows; SwiGLU in fp32.
-#pragma unroll
-    for (int i = 0; i < NI; ++i) {
-      float v = red[wave][i][lane];
-      for (int w = 1; w < KSH; ++w) v += red[wave + w][i][lane];
-      if (pair) {
-        float u = red[wave + KSH][i][lane];
-        for (int w = 1; w < KSH; ++w) u += red[wave + KSH + w][i][lane];
-        v = silu_f32(v) * u;
-      }
-      acc[i] = v;
-    }
-  }
-  if (!tile_ok) return;
-  // Lane (r, g), register i holds y[m = 4 i + g][n = 16 tile + r].
-  const int n = tile * kTileRows + r;
-#pragma unroll
-  for (int i = 0; i < NI; ++i) {
-    const int mo = 4 * i + g;
-    if (mo < args.M && n < N) {
-      const int64_t o = (int64_t)mo * prob.ldy + n;
-      if (!pair || prob.ydt == kF32)
-        ((float*)prob.y)[o] = acc[i];
-      else if (prob.ydt == kBF16)
-        ((__bf16*)prob.y)[o] = (__bf16)acc[i];
-      else
-        ((_Float16*)prob.y)[o] = (_Float16)acc[i];
-    }
+  // Problems up to K = args.xk stage x in LDS; a longer one in the same
+  // launch (the LDS would not hold its rows) reads x from global memory.
+  // Uniform over the workgroup, so the barriers inside are safe.
+  if constexpr (XM == kXMixed) {
+    if (K <= args.xk) run(std::integral_constant<bool, true>{});
+    else run(std::integral_constant<bool, false>{});
+  } else {
+    run(std::integral_constant<bool, XM == kXLds>{});
   }
 }
 
@@ -213,52 +238,58 @@ __global__ __launch_bounds__(WAVES * 64) void qgemv_kernel(const GemvArgs args) 
 // ---------------------------------------------------------------------------
 struct GemvShape {
   int ks, tpw, p;
-  bool xlds;
+  int xmode;
 };
 
-template <int FMT, int XDT, int NI, int WAVES, int P>
-static void launch_cfg(bool xlds, const GemvArgs& args, int wgs, size_t lds, hipStream_t s, const LaunchEvents& ev) {
+template <int FMT, int XDT, int NI, int WAVES, int P, int XM>
+static void launch_mode(const GemvArgs& args, int wgs, size_t lds, hipStream_t s, const LaunchEvents& ev) {
   const dim3 grid((unsigned)wgs), block(WAVES * 64);
-  if (xlds) {
-    auto k = qgemv_kernel<FMT, XDT, NI, WAVES, P, true>;
-    if (lds > 64 * 1024) {
-      // Opt in once to dynamic LDS beyond 64 KB: the device's 160 KB per
-      // workgroup minus this kernel's static LDS (the split-K buffer).
-      static std::once_flag once;
-      static size_t dyn_max = 64 * 1024;
-      std::call_once(once, [&] {
-        hipFuncAttributes fa;
-        if (hipFuncGetAttributes(&fa, (const void*)k) == hipSuccess) {
-          const size_t avail = kLdsTotal - fa.sharedSizeBytes;
-          if (hipFuncSetAttribute((const void*)k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)avail) ==
-              hipSuccess)
-            dyn_max = avail;
-        }
-      });
-      if (lds > dyn_max) {   // does not fit: read x from global memory instead
-        launch(qgemv_kernel<FMT, XDT, NI, WAVES, P, false>, grid, block, 0, s, ev, args);
-        return;
+  auto k = qgemv_kernel<FMT, XDT, NI, WAVES, P, XM>;
+  if (XM != kXGlobal && lds > 64 * 1024) {
+    // Opt in once to dynamic LDS beyond 64 KB: the device's 160 KB per
+    // workgroup minus this kernel's static LDS (the split-K buffer).
+    static std::once_flag once;
+    static size_t dyn_max = 64 * 1024;
+    std::call_once(once, [&] {
+      hipFuncAttributes fa;
+      if (hipFuncGetAttributes(&fa, (const void*)k) == hipSuccess) {
+        const size_t avail = kLdsTotal - fa.sharedSizeBytes;
+        if (hipFuncSetAttribute((const void*)k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)avail) ==
+            hipSuccess)
+          dyn_max = avail;
       }
+    });
+    if (lds > dyn_max) {   // does not fit: read x from global memory instead
+      launch(qgemv_kernel<FMT, XDT, NI, WAVES, P, kXGlobal>, grid, block, 0, s, ev, args);
+      return;
     }
-    launch(k, grid, block, (uint32_t)lds, s, ev, args);
-  } else
-    launch(qgemv_kernel<FMT, XDT, NI, WAVES, P, false>, grid, block, 0, s, ev, args);
+  }
+  launch(k, grid, block, XM == kXGlobal ? 0u : (uint32_t)lds, s, ev, args);
+}
+
+template <int FMT, int XDT, int NI, int WAVES, int P>
+static void launch_cfg(int xmode, const GemvArgs& args, int wgs, size_t lds, hipStream_t s, const LaunchEvents& ev) {
+  switch (xmode) {
+    case kXLds: launch_mode<FMT, XDT, NI, WAVES, P, kXLds>(args, wgs, lds, s, ev); break;
+    case kXMixed: launch_mode<FMT, XDT, NI, WAVES, P, kXMixed>(args, wgs, lds, s, ev); break;
+    default: launch_mode<FMT, XDT, NI, WAVES, P, kXGlobal>(args, wgs, lds, s, ev); break;
+  }
 }
 
 template <int FMT, int XDT, int NI, int P>
-static void launch_p(int waves, bool xlds, const GemvArgs& args, int wgs, size_t lds, hipStream_t s,
+static void launch_p(int waves, int xmode, const GemvArgs& args, int wgs, size_t lds, hipStream_t s,
                      const LaunchEvents& ev) {
   switch (waves) {
-    case 4: launch_cfg<FMT, XDT, NI, 4, P>(xlds, args, wgs, lds, s, ev); break;
-    case 8: launch_cfg<FMT, XDT, NI, 8, P>(xlds, args, wgs, lds, s, ev); break;
-    default: launch_cfg<FMT, XDT, NI, 16, P>(xlds, args, wgs, lds, s, ev); break;
+    case 4: launch_cfg<FMT, XDT, NI, 4, P>(xmode, args, wgs, lds, s, ev); break;
+    case 8: launch_cfg<FMT, XDT, NI, 8, P>(xmode, args, wgs, lds, s, ev); break;
+    default: launch_cfg<FMT, XDT, NI, 16, P>(xmode, args, wgs, lds, s, ev); break;
   }
 }
 
 template <int FMT, int XDT, int NI>
 static void launch_ni(int waves, const GemvShape& c, const GemvArgs& args, int wgs, size_t lds, hipStream_t s,
                       const LaunchEvents& ev) {
-  launch_p<FMT, XDT, NI, 4>(waves, c.xlds, args, wgs, lds, s, ev);
+  launch_p<FMT, XDT, NI, 4>(waves, c.xmode, args, wgs, lds, s, ev);
 }
 
 // K-shares per tile: about 2048 waves over the chip (8 per CU) with at least
@@ -283,13 +314,23 @@ static GemvShape pick_shape(int tiles, int max_chunks, int M, int max_k) {
   // (measured: M = 8 gate+up 23.3 -> 15.4 us, q/k/v 12.0 -> 8.9 us).
   if (lds > 32 * 1024 && lds <= kLdsCap) c.tpw = std::max(1, (tiles >= 1024 ? 16 : 8) / ks);
   c.p = 4;
-  c.xlds = lds <= kLdsCap;
+  c.xmode = lds <= kLdsCap ? kXLds : kXGlobal;
   return c;
 }
 
 hipError_t launch_qgemv(int fmt, int xdt, GemvArgs args, int max_chunks, int max_k, hipStream_t s,
                         const LaunchEvents& ev) {
-  const GemvShape c = pick_shape(args.total_tiles, max_chunks, args.M, max_k);
+  // x goes to LDS for every problem whose rows fit there; the LDS is sized
+  // for the longest of those, and a problem with a longer K reads x from
+  // global memory (M = 8 with K = 12288 next to K = 4096 problems).
+  int xk = 0;
+  for (int i = 0; i < args.count; ++i) {
+    const int k = args.p[i].K;
+    if ((int64_t)args.M * (k + 8) * 2 + kXSlack <= kLdsCap && k > xk) xk = k;
+  }
+  args.xk = xk;
+  GemvShape c = pick_shape(args.total_tiles, max_chunks, args.M, xk > 0 ? xk : max_k);
+  if (c.xmode == kXLds && xk < max_k) c.xmode = kXMixed;
   // Problems of one K share the launch-wide split.  When K differs, the
   // workgroup is 8 waves and each problem takes the finest power-of-2 split
   // that keeps at least 8 chunks a wave (up to the workgroup), so the long-K
@@ -326,7 +367,7 @@ hipError_t launch_qgemv(int fmt, int xdt, GemvArgs args, int max_chunks, int max
     args.wg0[i] = wgs;
     args.ks[i] = 1;
   }
-  const size_t lds = c.xlds ? (size_t)args.M * (max_k + 8) * 2 + kXSlack : 0;
+  const size_t lds = c.xmode != kXGlobal ? (size_t)args.M * (xk + 8) * 2 + kXSlack : 0;
   if (fmt == kQ4_0) {
     if (xdt == kF16) {
       if (args.M > 4) launch_ni<kQ4_0, kF16, 2>(waves, c, args, wgs, lds, s, ev);

@@ -168,6 +168,19 @@ def test_qgemv_grouped_mixed_k_ragged(q, M):
     _grouped_check(q, synth.Q4_0, ws, xs, M, f"mixed-K group M{M}")
 
 
+@pytest.mark.parametrize("fmt,xdt,M", [(synth.Q4_0, synth.F16, 4), (synth.Q8_0, synth.BF16, 8),
+                                        (synth.FP16, synth.BF16, 5), (synth.Q4_0, synth.BF16, 8)])
+def test_qgemv_grouped_lds_and_global_x(q, fmt, xdt, M):
+    """A launch where the shorter problems stage x in LDS and the longest
+    (K = 26624: its M rows exceed the LDS) reads x from global memory."""
+    shapes = [(100, 4096), (64, 26624), (33, 160), (300, 2080)]
+    mk = (lambda i, N, K: synth.fp16_weight(synth.rng_for(61, i), N, K)) if fmt == synth.FP16 else \
+        (lambda i, N, K: synth.q_weight(synth.rng_for(61, i), fmt, N, K))
+    ws = [mk(i, N, K) for i, (N, K) in enumerate(shapes)]
+    xs = [synth.activation(synth.rng_for(61, 10 + i), (M, K), xdt) for i, (N, K) in enumerate(shapes)]
+    _grouped_check(q, fmt, ws, xs, M, f"LDS + global x group fmt{fmt} M{M}")
+
+
 @pytest.mark.parametrize("M", [1, 8])
 def test_qgemv_layer_8b_one_launch(q, M):
     """The 8B-shaped layer's seven projections in one grouped launch (the
