@@ -375,36 +375,50 @@ __global__ __launch_bounds__(WAVES * 64) void moe_stream_kernel(
         for (int w = 0; w < NW; ++w)
 #pragma unroll
           for (int t = 0; t < NT; ++t)
-            acc[(w * NT + t) * MT + i] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b[w][t], acc[(w * NT + t) * MT + i], 0, 0, 0);
+            acc[(w * NT + t) * MT + i] = __builtin_amdgcn_mfma_f32_16x16x32_f16(b[w][t], a, acc[(w * NT + t) * MT + i], 0, 0, 0);
       }
     }
   };
 
-  // Lane (r, g), register k of tile (w, t, i): row 16 i + 4 g + k, column 16 (t_w0 + gi NT + t) + r.
+  // The weights are the MFMA's A operand and the activation rows its B
+  // operand, so the product comes out transposed: lane (r, g), register k of
+  // tile (w, t, i) holds row 16 i + r, column 16 (t_w0 + gi NT + t) + 4 g + k.
+  // Each lane thus stores its four adjacent columns as one 8-byte write.
   auto epilogue = [&](int rt, int gi) __attribute__((always_inline)) {
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
       const int lt = gi * NT + t;
-      const int n = (t_w0 + lt) * kTileRows + r;
+      const int n0 = (t_w0 + lt) * kTileRows + 4 * g;
       if (lt < tv) {
 #pragma unroll
-        for (int i = 0; i < MT; ++i)
+        for (int i = 0; i < MT; ++i) {
+          const int row = rt * BM + i * 16 + r;
+          if (row < cnt) {
+            if constexpr (MODE == kGateUp) {
+              const float4_t zg = acc[(0 * NT + t) * MT + i], zu = acc[(1 * NT + t) * MT + i];
+              uint32_t hf[2], hb[2];
 #pragma unroll
-          for (int k = 0; k < 4; ++k) {
-            const int row = rt * BM + i * 16 + 4 * g + k;
-            if (row < cnt) {
-              if constexpr (MODE == kGateUp) {
-                const float zg = acc[(0 * NT + t) * MT + i][k], zu = acc[(1 * NT + t) * MT + i][k];
-                const __bf16 hb = (__bf16)(silu_f32(zg) * zu);
-                const int64_t idx = (int64_t)(seg + row) * N + n;
-                out16[idx] = __builtin_bit_cast(uint16_t, (_Float16)(float)hb);
-                if (h_out) h_out[idx] = __builtin_bit_cast(uint16_t, hb);
-              } else {
-                const int64_t pair = min(max(sorted_pairs[seg + row], 0), Ptot - 1);
-                out16[pair * N + n] = __builtin_bit_cast(uint16_t, (_Float16)acc[t * MT + i][k]);
+              for (int k2 = 0; k2 < 2; ++k2) {
+                const __bf16 b0 = (__bf16)(silu_f32(zg[2 * k2]) * zu[2 * k2]);
+                const __bf16 b1 = (__bf16)(silu_f32(zg[2 * k2 + 1]) * zu[2 * k2 + 1]);
+                hf[k2] = (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)(float)b0) |
+                         ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)(float)b1) << 16);
+                hb[k2] = (uint32_t)__builtin_bit_cast(uint16_t, b0) | ((uint32_t)__builtin_bit_cast(uint16_t, b1) << 16);
               }
+              const int64_t idx = (int64_t)(seg + row) * N + n0;
+              *(u32x2_t*)(out16 + idx) = u32x2_t{hf[0], hf[1]};
+              if (h_out) *(u32x2_t*)(h_out + idx) = u32x2_t{hb[0], hb[1]};
+            } else {
+              const int64_t pair = min(max(sorted_pairs[seg + row], 0), Ptot - 1);
+              const float4_t v = acc[t * MT + i];
+              const uint32_t lo = (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)v[0]) |
+                                  ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)v[1]) << 16);
+              const uint32_t hi = (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)v[2]) |
+                                  ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)v[3]) << 16);
+              *(u32x2_t*)(out16 + pair * N + n0) = u32x2_t{lo, hi};
             }
           }
+        }
       }
     }
 #pragma unroll
