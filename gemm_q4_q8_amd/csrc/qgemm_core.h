@@ -1,6 +1,6 @@
-// The tile engine shared by the prefill GEMM and the MoE expert GEMMs: one
-// 512-thread workgroup computes a BM x BN block of X W^T for NW weight
-// matrices at once (NW = 2 gives gate and up of the same rows).
+// The tile engine of the prefill GEMM: one 512-thread workgroup computes a
+// BM x BN block of X W^T for NW weight matrices at once (NW = 2 would give
+// gate and up of the same rows).
 //
 //   * matrix cores: v_mfma_f32_16x16x32_f16, fp32 accumulation.  Weights are
 //     unpacked in registers and scaled to fp16 (one rounding, relative error

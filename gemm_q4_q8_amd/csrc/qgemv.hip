@@ -356,6 +356,29 @@ hipError_t launch_qgemv(int fmt, int xdt, GemvArgs args, int max_chunks, int max
       args.ks[i] = ks;
     }
   }
+  // Problems with the longest chain of chunks per wave first in the grid, so
+  // that their workgroups start in the first round and the launch's tail
+  // holds short ones.  (Each problem writes its own y; the order is free.)
+  {
+    int cpw[kMaxGroup], order[kMaxGroup];
+    for (int i = 0; i < args.count; ++i) {
+      const int nch = (args.p[i].K + kChunkK - 1) / kChunkK;
+      const int shares = args.p[i].W2 ? args.ks[i] / 2 : args.ks[i];
+      cpw[i] = (nch + shares - 1) / shares;
+      order[i] = i;
+    }
+    std::stable_sort(order, order + args.count, [&](int a, int b) { return cpw[a] > cpw[b]; });
+    GemvProb p[kMaxGroup];
+    int ks[kMaxGroup];
+    for (int i = 0; i < args.count; ++i) {
+      p[i] = args.p[order[i]];
+      ks[i] = args.ks[order[i]];
+    }
+    for (int i = 0; i < args.count; ++i) {
+      args.p[i] = p[i];
+      args.ks[i] = ks[i];
+    }
+  }
   // Workgroup ranges per problem.
   int wgs = 0;
   for (int i = 0; i < args.count; ++i) {
