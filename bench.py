@@ -96,6 +96,107 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+class ClockSampler:
+    """Samples the GPU's current shader clock (SCLK, MHz) from the device's
+    sysfs `pp_dpm_sclk` (the level marked `*`) on a background thread while a
+    workload runs.  The device is found by its PCI bus id; where the file is
+    missing or unreadable the summary is None."""
+
+    def __init__(self, hip, period_s: float = 0.005):
+        import threading
+        self.path = None
+        try:
+            buf = ctypes.create_string_buffer(64)
+            hip.hipDeviceGetPCIBusId.argtypes = [ctypes.c_char_p, ctypes.c_int, ctypes.c_int]
+            if hip.hipDeviceGetPCIBusId(buf, 64, 0) == 0:
+                p = f"/sys/bus/pci/devices/{buf.value.decode().lower()}/pp_dpm_sclk"
+                open(p).read()
+                self.path = p
+        except (OSError, AttributeError, UnicodeDecodeError):
+            self.path = None
+        self.period = period_s
+        self.samples = []
+        self._stop = threading.Event()
+        self._thread = threading.Thread(target=self._run, daemon=True)
+
+    def _read(self):
+        import re
+        for line in open(self.path):
+            if "*" in line:
+                m = re.search(r"(\d+)\s*[Mm][Hh][Zz]", line)
+                return int(m.group(1)) if m else None
+        return None
+
+    def _run(self):
+        while not self._stop.is_set():
+            try:
+                v = self._read()
+            except OSError:
+                return
+            if v is not None:
+                self.samples.append(v)
+            time.sleep(self.period)
+
+    def __enter__(self):
+        if self.path:
+            self._thread.start()
+        return self
+
+    def __exit__(self, *exc):
+        self._stop.set()
+        if self.path:
+            self._thread.join()
+
+    def summary(self):
+        if not self.samples:
+            return None
+        d = sorted(self.samples)
+        return {"sclk_mhz_median": d[len(d) // 2], "sclk_mhz_min": d[0], "sclk_mhz_max": d[-1],
+                "samples": len(d)}
+
+
+def stream_ceiling(q, torch, ev: HipEvents):
+    """Measured HBM ceiling on this machine.  Read: the library's read probe
+    (q4q8_stream_read_timed: 16-byte non-temporal loads, the GEMV's policy)
+    over 4 GiB, bytes / dispatch-event time.  Copy (context): a 1 GiB device
+    copy, bytes read + written / time.  Both far larger than the 256 MB
+    Infinity Cache; best and median of 10 repetitions after 2 warm-ups."""
+    out = {}
+    buf = torch.empty(1 << 32, dtype=torch.uint8, device="cuda:0")
+    digest = None
+    ts = []
+    for i in range(12):
+        e = (ev.create(), ev.create())
+        digest = q.stream_read(buf, digest=digest, events=e)
+        if i >= 2:
+            ts.append(ev.elapsed_ms(*e) * 1e-3)
+        ev.destroy(e[0])
+        ev.destroy(e[1])
+    ts.sort()
+    out["read_GB/s"] = round(buf.numel() / ts[0] / 1e9, 1)
+    out["read_GB/s_median"] = round(buf.numel() / ts[len(ts) // 2] / 1e9, 1)
+    del buf, digest
+    b = torch.empty(1 << 30, dtype=torch.uint8, device="cuda:0")
+    c = torch.empty_like(b)
+    ts = []
+    for i in range(12):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        c.copy_(b)
+        e1.record()
+        torch.cuda.synchronize()
+        if i >= 2:
+            ts.append(e0.elapsed_time(e1) * 1e-3)
+    ts.sort()
+    out["copy_GB/s"] = round(2 * b.numel() / ts[0] / 1e9, 1)
+    del b, c
+    torch.cuda.empty_cache()
+    out["how"] = ("read: q4q8_stream_read_timed over 4 GiB (non-temporal 16-byte loads), "
+                  "bytes / dispatch-event time, best of 10; copy: torch copy_ of 1 GiB, (read + written) bytes / "
+                  "time, best of 10")
+    return out
+
+
 # ----------------------------------------------------------------------------
 # Decode layer (8B-shaped), the headline workload
 # ----------------------------------------------------------------------------
@@ -237,7 +338,9 @@ def cpu_baseline(synth, budget_s: float = 25.0):
             break
     dt = time.perf_counter() - t0
     del np
+    flops = steps * sum(2.0 * w.N * w.K for w in ws.values())
     return {"value": total_bytes / dt / 1e9, "unit": "GB/s", "cores": blas_threads, "kind": "oracle",
+            "wall_s": round(dt, 2), "GFLOP/s": round(flops / dt / 1e9, 3), "cpu_count": os.cpu_count(),
             "sample": f"{steps} decode step(s) of the 8B-shaped layer at M=1 (7 matrices, "
                       f"{total_bytes // steps} algorithmic bytes each) through the fp64 NumPy oracle "
                       f"(dequantise then matmul), {dt:.1f} s; elementwise NumPy is single-threaded, "
@@ -515,10 +618,18 @@ def prefill_workloads(q, torch, synth, ev: HipEvents, quick: bool):
         d = sorted(ev.elapsed_ms(a, b) * 1e-3 for a, b in pairs[4:])
         mean = sum(d) / len(d)
         fl = 2.0 * M * w.N * w.K
+        # The MFMA peak assumes 2.4 GHz: sample the clock over ~0.25 s of back-to-back calls.
+        with ClockSampler(ev.hip) as clk:
+            n_sus = max(1, int(0.25 / max(mean, 1e-6)))
+            for i in range(n_sus):
+                q.qgemm(fmt, Ws[i % 4], w.N, w.K, X, out=Y, ws=wsp)
+            torch.cuda.synchronize()
         out.append({"workload": f"{synth.FORMAT_NAME[fmt]} prefill gemm M={M} K={w.K} N={w.N} (bf16 in/out)",
-                    "call_us_mean": round(mean * 1e6, 2), "call_us_min": round(d[0] * 1e6, 2),
+                    "call_us_mean": round(mean * 1e6, 2), "call_us_median": round(d[len(d) // 2] * 1e6, 2),
+                    "call_us_min": round(d[0] * 1e6, 2),
                     "TFLOP/s": round(fl / mean / 1e12, 1),
-                    "mfma_frac": round(fl / mean / 1e12 / F16_MFMA_PEAK_TFLOPS, 4)})
+                    "mfma_frac": round(fl / mean / 1e12 / F16_MFMA_PEAK_TFLOPS, 4),
+                    "sclk_during_calls": clk.summary()})
         del Ws, W0, X, Y, wsp
         torch.cuda.empty_cache()
     return out
@@ -637,6 +748,7 @@ def main():
     ap.add_argument("--quick-extra", action="store_true")
     ap.add_argument("--only", nargs="+", choices=EXTRA_GROUPS, default=None,
                     help="run only these groups of the other workloads (e.g. for a profiled run)")
+    ap.add_argument("--no-ceiling", action="store_true", help="skip the measured HBM stream ceiling")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a 256 MiB device copy (known HBM bytes) for counter calibration")
     args = ap.parse_args()
@@ -680,6 +792,13 @@ def main():
                 "launches_timed": len(durs), "kernel_source_hash": src_hash}
     log(f"step kernel mean {mean_k * 1e6:.2f} us (min {sd[0] * 1e6:.2f}, median {sd[len(sd) // 2] * 1e6:.2f}, "
         f"max {sd[-1] * 1e6:.2f}) -> {achieved:.1f} GB/s")
+
+    ceiling = None
+    if not args.no_ceiling:
+        ceiling = stream_ceiling(q, torch, ev)
+        ceiling["headline_kernel_frac_of_read"] = round(achieved / ceiling["read_GB/s"], 4)
+        roofline["measured_ceiling"] = ceiling
+        log(f"measured stream ceiling {json.dumps(ceiling)}")
 
     if args.calibrate_copy:
         a = torch.empty(1 << 28, dtype=torch.uint8, device="cuda:0")

@@ -72,6 +72,8 @@ def _declare(lib):
         "q4q8_moe_workspace": (sz, [i32, i32, i32, i32, i32, i32]),
         "q4q8_moe_qgemm": (i32, [i32, vp, vp, vp, i32, i32, i32, vp, i32, i32, i32,
                                  vp, vp, vp, vp, vp, vp, sz, vp]),
+        "q4q8_stream_read_digest_bytes": (sz, []),
+        "q4q8_stream_read_timed": (i32, [vp, sz, vp, sz, vp, vp, vp]),
     }
     for name, (res, args) in sig.items():
         f = getattr(lib, name)
@@ -348,3 +350,22 @@ def attn_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool
         st = lib().q4q8_attn_prefill_timed(*args, ctypes.c_void_p(events[0]), ctypes.c_void_p(events[1]))
     _check(st, "attn_prefill")
     return out
+
+
+# ----------------------------------------------------------------------------
+# Measurement helper
+# ----------------------------------------------------------------------------
+def stream_read(buf: torch.Tensor, digest: torch.Tensor = None, events=None) -> torch.Tensor:
+    """Read every byte of buf once on the GPU (the HBM read-ceiling probe);
+    returns the per-wave XOR digests (int32).  events: optional (start, stop)
+    hipEvent_t handles recorded around the kernel."""
+    _dev(buf, "buf")
+    n = int(lib().q4q8_stream_read_digest_bytes())
+    if digest is None:
+        digest = torch.empty(n // 4, dtype=torch.int32, device=buf.device)
+    ev = events or (None, None)
+    st = lib().q4q8_stream_read_timed(_ptr(buf), buf.numel() * buf.element_size(), _ptr(digest),
+                                      digest.numel() * digest.element_size(), _stream(buf),
+                                      ctypes.c_void_p(ev[0]), ctypes.c_void_p(ev[1]))
+    _check(st, "stream_read")
+    return digest

@@ -7,6 +7,13 @@
 #include "../../include/q4q8.h"
 #include "q4q8_internal.h"
 
+namespace q4q8 {
+// HBM read-ceiling probe (csrc/probe.hip), a measurement helper.
+size_t stream_read_digest_bytes();
+hipError_t launch_stream_read(const void* buf, size_t bytes, uint32_t* digest, hipStream_t s,
+                              const LaunchEvents& ev);
+}  // namespace q4q8
+
 namespace {
 
 thread_local char g_last_error[512];
@@ -349,6 +356,23 @@ int q4q8_qgemm_timed(int fmt, const void* W, int64_t N, int64_t K, const void* X
   ev.start = (hipEvent_t)ev_start;
   ev.stop = (hipEvent_t)ev_stop;
   return qgemm_impl(fmt, W, N, K, X, xdt, ldx, M, Y, ydt, ldy, ws, ws_bytes, stream, ev);
+}
+
+size_t q4q8_stream_read_digest_bytes(void) { return q4q8::stream_read_digest_bytes(); }
+
+int q4q8_stream_read_timed(const void* buf, size_t bytes, uint32_t* digest, size_t digest_bytes, void* stream,
+                           void* ev_start, void* ev_stop) {
+  if (!buf || !digest) return fail(Q4Q8_ERR_INVALID_ARG, "stream_read: null pointer");
+  if (bytes < 16 || bytes % 16) return fail(Q4Q8_ERR_INVALID_ARG, "stream_read: bytes=%zu is not a positive multiple of 16", bytes);
+  if (digest_bytes < q4q8::stream_read_digest_bytes())
+    return fail(Q4Q8_ERR_INVALID_ARG, "stream_read: digest needs %zu bytes, got %zu", q4q8::stream_read_digest_bytes(),
+                digest_bytes);
+  if (!aligned(buf, 16) || !aligned(digest, 4))
+    return fail(Q4Q8_ERR_ALIGNMENT, "stream_read: buf must be 16-byte and digest 4-byte aligned");
+  q4q8::LaunchEvents ev;
+  ev.start = (hipEvent_t)ev_start;
+  ev.stop = (hipEvent_t)ev_stop;
+  return hip_status(q4q8::launch_stream_read(buf, bytes, digest, (hipStream_t)stream, ev), "stream_read");
 }
 
 int q4q8_moe_route(const float* logits, int T, int E, int topk, int32_t* ids, float* gates, int32_t* counts,

@@ -345,6 +345,29 @@ int q4q8_attn_prefill_timed(int dt, const void* Q, const void* K,
                             int Hkv, int D, int causal, float scale,
                             void* stream, void* ev_start, void* ev_stop);
 
+/* ------------------------------------------------------------------------ */
+/* Measurement helper: the HBM read ceiling the decode GEMV is compared      */
+/* with (not a quantised product)                                           */
+/* ------------------------------------------------------------------------ */
+
+/* Bytes the digest of q4q8_stream_read_timed needs (one word per wave of its
+ * fixed grid). */
+size_t q4q8_stream_read_digest_bytes(void);
+
+/* Reads bytes of device memory at buf once, with 16-byte non-temporal loads
+ * (the GEMV's weight-load policy) over a grid that fills every CU, and writes
+ * per-wave XOR digests of the 32-bit words read to digest, so that XOR-ing
+ * every digest word gives the XOR of the buffer.  ev_start / ev_stop
+ * (optional, as in q4q8_qgemv_grouped_timed) bracket the kernel; bytes / that
+ * time is the streaming read rate.
+ *   buf:    device, 16-byte aligned; bytes a multiple of 16 (>= 16).
+ *   digest: device, >= q4q8_stream_read_digest_bytes() bytes, 4-byte aligned;
+ *           overwritten.
+ * Errors: Q4Q8_ERR_INVALID_ARG (null, size), Q4Q8_ERR_ALIGNMENT. */
+int q4q8_stream_read_timed(const void* buf, size_t bytes, uint32_t* digest,
+                           size_t digest_bytes, void* stream,
+                           void* ev_start, void* ev_stop);
+
 #ifdef __cplusplus
 }
 #endif

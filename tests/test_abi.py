@@ -269,3 +269,18 @@ def test_repack_validation(q):
     assert L.q4q8_repack(1, _vp(), 16, 128, _vp(0x2008), 1 << 20, None) == -4
     assert L.q4q8_repack(5, _vp(), 16, 128, _vp(0x2000), 1 << 20, None) == -2
     assert L.q4q8_repack_host(1, None, 16, 128, _vp(0x2000), 1 << 20) == -1
+
+
+def test_stream_read_validation(q):
+    """The read-ceiling probe rejects bad arguments before any launch."""
+    L = q.lib()
+    n = L.q4q8_stream_read_digest_bytes()
+    assert n > 0 and n % 4 == 0
+    ok = dict(buf=0x10000, bytes=1 << 20, digest=0x20000, dbytes=n)
+    for over, want in [(dict(buf=None), -1), (dict(digest=None), -1), (dict(bytes=0), -1), (dict(bytes=24), -1),
+                       (dict(dbytes=n - 4), -1), (dict(buf=0x10008), -4), (dict(digest=0x20002), -4)]:
+        a = dict(ok)
+        a.update(over)
+        st = L.q4q8_stream_read_timed(_vp(a["buf"]) if a["buf"] else None, a["bytes"],
+                                      _vp(a["digest"]) if a["digest"] else None, a["dbytes"], None, None, None)
+        assert st == want, (over, st, q.last_error())
