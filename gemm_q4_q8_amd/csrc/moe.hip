@@ -175,8 +175,9 @@ __global__ __launch_bounds__(1024) void moe_sort_kernel(const int32_t* __restric
 }
 
 // A few tokens (T <= kSortWaves): top-k and sort in one workgroup, one
-// launch.  Wave t takes token t; the sort reads ids once every wave's writes
-// are visible to the workgroup.
+// launch.  Wave t takes token t; the sort reads ids after the barrier, whose
+// workgroup-scope release/acquire makes every wave's writes visible (no
+// device-scope fence: it would write back the L2 for nothing).
 template <int NS>
 __global__ __launch_bounds__(1024) void moe_route_small_kernel(const float* __restrict__ logits, int T, int E,
                                                                int topk, int32_t* __restrict__ ids,
@@ -185,7 +186,6 @@ __global__ __launch_bounds__(1024) void moe_route_small_kernel(const float* __re
                                                                int32_t* __restrict__ sorted_pairs) {
   const int w = threadIdx.x >> 6;
   if (w < T) topk_token<NS>(logits, w, E, topk, threadIdx.x & 63, ids, gates);
-  __threadfence();
   __syncthreads();
   sort_pairs(ids, T * topk, E, counts, offsets, sorted_pairs);
 }

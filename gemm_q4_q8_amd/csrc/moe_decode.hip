@@ -19,9 +19,14 @@
 //     the gate rows, half on the up rows, K split in ksh shares each), x rows
 //     gathered from the tokens into LDS; h = silu(gate) * up rounded to bf16,
 //     stored in sorted-pair order;
-//   * down: x = the expert's h rows (contiguous in sorted order, bf16
-//     operands, exact), y rounded to fp16 per pair id, then the weighted
-//     combine kernel of the prefill path.
+//   * down: x = the expert's h rows (contiguous in sorted order), y rounded
+//     to fp16 per pair id, then the weighted combine kernel of the prefill
+//     path.
+// The rows are staged in LDS as fp16, bf16 sources converted on the way as
+// the prefill path's pre-pass does (exact for 2^-14 <= |x| < 65520, h
+// included): the fp16 operands take the Q4_0 unpack's two-instruction
+// fp16 form, where a bf16 operand would need a per-value integer conversion
+// (measured at T = 8: gate/up 36.5 -> 19 us, down 20 -> 12 us).
 // K-shares are reduced in a fixed order through LDS: results are bitwise
 // reproducible.
 #include "gemv_core.h"
@@ -52,9 +57,10 @@ struct MoeDecArgs {
 constexpr int kDecXSlack = 512;
 constexpr int kDecMaxExperts = 1024;
 
-template <int FMT, int XDT, int MODE, int NI, int WAVES, int P>
+// SRC: dtype of the rows in memory (kF16 or kBF16); the operands are fp16.
+template <int FMT, int SRC, int MODE, int NI, int WAVES, int P>
 __global__ __launch_bounds__(WAVES * 64) void moe_gemv_kernel(const MoeDecArgs a) {
-  typedef typename Op<XDT>::vec vec;
+  typedef typename Op<kF16>::vec vec;
   typedef GemvStage<FMT> Stage;
   constexpr int REC = Fmt<FMT>::kRecBytes;
   extern __shared__ __attribute__((aligned(16))) uint16_t xs[];
@@ -120,6 +126,14 @@ __global__ __launch_bounds__(WAVES * 64) void moe_gemv_kernel(const MoeDecArgs a
     if (mm < M && k8 < K / 8) {
       const int64_t row = MODE == kDecGateUp ? s_pair[mm] / a.topk : r0 + mm;
       v = *(const u32x4_t*)(a.X + row * a.ldx + k8 * 8);
+      if constexpr (SRC == kBF16) {   // bf16 -> fp16, as the prefill pre-pass
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const uint32_t b = v[q];
+          v[q] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(__builtin_bit_cast(float, b << 16),
+                                                                        __builtin_bit_cast(float, b & 0xFFFF0000u)));
+        }
+      }
     }
     *(u32x4_t*)(xs + i * 8) = v;
   }
@@ -133,7 +147,7 @@ __global__ __launch_bounds__(WAVES * 64) void moe_gemv_kernel(const MoeDecArgs a
     vec av[kBlocksPerChunk];
 #pragma unroll
     for (int j = 0; j < kBlocksPerChunk; ++j) av[j] = *(const vec*)(xrow + c * kChunkK + j * 32);
-    gemv_mma<FMT, XDT, NI>(s, av, acc);
+    gemv_mma<FMT, kF16, NI>(s, av, acc);
   };
   // Chunks of this wave: ks + i KSH, i < nw; full groups of P prefetch the
   // next group, the last (possibly partial) group issues no loads.
@@ -201,7 +215,7 @@ int dec_ksh(int nchunks, int mats, int64_t tile_waves) {
   return ksh;
 }
 
-template <int FMT, int XDT, int MODE>
+template <int FMT, int SRC, int MODE>
 void launch_dec(MoeDecArgs a, int T, int npos, hipStream_t s) {
   const int mats = MODE == kDecGateUp ? 2 : 1;
   const int64_t experts = std::min(npos, a.E);
@@ -211,9 +225,9 @@ void launch_dec(MoeDecArgs a, int T, int npos, hipStream_t s) {
   const dim3 grid((unsigned)(npos * a.groups)), block(kDecWaves * 64);
   const size_t lds = (size_t)T * (a.K + 8) * 2 + kDecXSlack;
   if (T > 4)
-    moe_gemv_kernel<FMT, XDT, MODE, 2, kDecWaves, kDecRing><<<grid, block, lds, s>>>(a);
+    moe_gemv_kernel<FMT, SRC, MODE, 2, kDecWaves, kDecRing><<<grid, block, lds, s>>>(a);
   else
-    moe_gemv_kernel<FMT, XDT, MODE, 1, kDecWaves, kDecRing><<<grid, block, lds, s>>>(a);
+    moe_gemv_kernel<FMT, SRC, MODE, 1, kDecWaves, kDecRing><<<grid, block, lds, s>>>(a);
 }
 
 template <int FMT>
