@@ -231,10 +231,10 @@ def ffn_decode_workspace(M: int, F: int) -> int:
 
 def ffn_decode(fmt: int, Wg: torch.Tensor, Wu: torch.Tensor, Wd: torch.Tensor, H: int, F: int, x: torch.Tensor,
                out: torch.Tensor | None = None, ws: torch.Tensor | None = None, events=None) -> torch.Tensor:
-    """y[M, H] fp32 = (silu(x Wg^T) * (x Wu^T)) Wd^T, h held as bf16; two launches.
+    """y[M, H] fp32 = (silu(x Wg^T) * (x Wu^T)) Wd^T, h rounded to bf16 and held as fp16; two launches.
 
     ws: optional uint8 workspace of >= ffn_decode_workspace(M, F) bytes (the
-    bf16 h rows; allocated per call if omitted).
+    h rows, fp16; allocated per call if omitted).
     """
     for t, n in ((Wg, "Wg"), (Wu, "Wu"), (Wd, "Wd")):
         _dev(t, n)

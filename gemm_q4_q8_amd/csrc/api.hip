@@ -256,20 +256,22 @@ static int ffn_impl(int fmt, const void* Wg, const void* Wu, const void* Wd, int
   if (!ws || ws_bytes < need)
     return fail(Q4Q8_ERR_WORKSPACE, "ffn_decode: workspace holds %zu bytes, needs %zu", ws ? ws_bytes : 0, need);
   if (!aligned(ws, 256)) return fail(Q4Q8_ERR_ALIGNMENT, "ffn_decode: workspace not 256-byte aligned");
-  // Validate both launches before enqueuing either: gate/up writes h (bf16,
-  // rows of F) into ws, down reads it.
-  const GemvIn gu{Wg, Wu, x, ws, F, H, ldx, F, Q4Q8_BF16};
+  // Validate both launches before enqueuing either: gate/up writes h (rows
+  // of F, 2 bytes each) into ws, down reads it.  h is rounded to bf16 and
+  // stored as fp16, so the down GEMV takes fp16 operands.
+  GemvIn gu{Wg, Wu, x, ws, F, H, ldx, F, Q4Q8_BF16};
   st = check_gemv_prob(fmt, gu, M, 0);
   if (st) return st;
   const GemvIn dn{Wd, nullptr, ws, y, H, F, F, ldy, Q4Q8_F32};
   st = check_gemv_prob(fmt, dn, M, 1);
   if (st) return st;
+  gu.ydt = q4q8::kYF16ViaBF16;
   q4q8::LaunchEvents e1, e2;
   e1.start = ev.start;
   e2.stop = ev.stop;
   st = run_gemv(fmt, &gu, 1, xdt, M, stream, e1);
   if (st) return st;
-  return run_gemv(fmt, &dn, 1, Q4Q8_BF16, M, stream, e2);
+  return run_gemv(fmt, &dn, 1, Q4Q8_F16, M, stream, e2);
 }
 
 extern "C" {

@@ -25,6 +25,10 @@ inline void launch(K kernel, dim3 grid, dim3 block, uint32_t shmem, hipStream_t 
 
 constexpr int kMaxGroup = 8;
 
+// Internal GEMV output dtype (SwiGLU pairs only): rounded to bf16, stored as
+// fp16 (the decode FFN's h).
+constexpr int kYF16ViaBF16 = 4;
+
 // One GEMV problem as the kernel sees it.  A SwiGLU pair has W = gate and
 // W2 = up weights (same shape, same x) and stores h = silu(W x) * (W2 x) as
 // ydt; a plain problem has W2 = null and stores fp32 dot products.

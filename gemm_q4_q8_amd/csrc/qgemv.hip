@@ -216,6 +216,8 @@ void qgemv_kernel(const GemvArgs args) {
           ((float*)prob.y)[o] = acc[i];
         else if (prob.ydt == kBF16)
           ((__bf16*)prob.y)[o] = (__bf16)acc[i];
+        else if (prob.ydt == kYF16ViaBF16)
+          ((_Float16*)prob.y)[o] = (_Float16)(float)(__bf16)acc[i];
         else
           ((_Float16*)prob.y)[o] = (_Float16)acc[i];
       }

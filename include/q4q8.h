@@ -198,19 +198,23 @@ int q4q8_qgemv_swiglu_timed(int fmt, const void* Wg, const void* Wu,
                             int64_t ldh, void* stream, void* ev_start,
                             void* ev_stop);
 
-/* Workspace bytes of q4q8_ffn_decode: the bf16 h rows, M * F * 2 rounded up
- * to 256.  0 for M outside 1..8 or F not a positive multiple of 32. */
+/* Workspace bytes of q4q8_ffn_decode: the h rows (2 bytes each), M * F * 2
+ * rounded up to 256.  0 for M outside 1..8 or F not a positive multiple of 32. */
 size_t q4q8_ffn_decode_workspace(int M, int64_t F);
 
 /* The decode FFN of a layer, two launches on `stream`:
- *   h = silu(x Wg^T) * (x Wu^T)   (q4q8_qgemv_swiglu, h as bf16 in ws)
+ *   h = silu(x Wg^T) * (x Wu^T)   (q4q8_qgemv_swiglu, rounded to bf16)
  *   y = h Wd^T                    (q4q8_qgemv, fp32)
+ * h is held in ws as fp16: its bf16 values, converted exactly for
+ * 2^-14 <= |h| < 65520 (outside that range as for BF16 activations in the
+ * GEMM), so that the down product takes fp16 operands and the Q4_0 unpack's
+ * fp16 form.
  *   Wg, Wu: repacked [F, H]; Wd: repacked [H, F]; one format.
  *   x:      M rows of H activations (F16/BF16), as for q4q8_qgemv.
  *   y:      device fp32, row m at y + m*ldy, ldy >= H when M > 1.
  *   ws:     device, >= q4q8_ffn_decode_workspace(M, F) bytes, 256-byte
  *           aligned; overwritten.  Once the stream has run the call it
- *           holds h, bf16 [M, F] row-major (row stride F).
+ *           holds h, fp16 [M, F] row-major (row stride F).
  * Every argument of both launches is validated before the first is
  * enqueued.  Errors: as q4q8_qgemv, plus Q4Q8_ERR_WORKSPACE. */
 int q4q8_ffn_decode(int fmt, const void* Wg, const void* Wu, const void* Wd,
