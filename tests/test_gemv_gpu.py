@@ -181,6 +181,17 @@ def test_qgemv_grouped_lds_and_global_x(q, fmt, xdt, M):
     _grouped_check(q, fmt, ws, xs, M, f"LDS + global x group fmt{fmt} M{M}")
 
 
+@pytest.mark.parametrize("fmt,xdt,M,N,K", [(synth.Q4_0, synth.F16, 8, 300, 26624), (synth.Q4_0, synth.BF16, 5, 77, 20000),
+                                           (synth.Q8_0, synth.BF16, 8, 64, 12288), (synth.FP16, synth.F16, 8, 40, 12320)])
+def test_qgemv_oversized_x(q, fmt, xdt, M, N, K):
+    """One problem whose M activation rows exceed the LDS, so x is read from
+    global memory (K not a multiple of 128 in two cases), every output."""
+    w = synth.fp16_weight(synth.rng_for(62, 0), N, K) if fmt == synth.FP16 else \
+        synth.q_weight(synth.rng_for(62, 0), fmt, N, K)
+    x = synth.activation(synth.rng_for(62, 1), (M, K), xdt)
+    _grouped_check(q, fmt, [w], [x], M, f"oversized x fmt{fmt} M{M} K{K}")
+
+
 @pytest.mark.parametrize("M", [1, 8])
 def test_qgemv_layer_8b_one_launch(q, M):
     """The 8B-shaped layer's seven projections in one grouped launch (the
