@@ -23,7 +23,6 @@
 #include "gemv_core.h"
 #include "q4q8_internal.h"
 
-#include <stdlib.h>
 
 #include <algorithm>
 #include <mutex>
@@ -305,10 +304,6 @@ static GemvShape pick_shape(int tiles, int max_chunks, int M, int max_k) {
   int ks = 1;
   while (ks < 16 && tiles * ks < 2048 && max_chunks >= 16 * ks) ks *= 2;
   if (lds > 80 * 1024 && ks < 8) ks = 8;
-  if (const char* e = getenv("Q4Q8_GEMV_KS")) {   // tuning experiments only
-    const int v = atoi(e);
-    if (v == 1 || v == 2 || v == 4 || v == 8 || v == 16) ks = v;
-  }
   c.ks = ks;
   c.tpw = ks >= 4 ? 1 : 4 / ks;
   // A large activation block in LDS (M >= 4) caps the workgroups per CU, so
@@ -342,7 +337,7 @@ hipError_t launch_qgemv(int fmt, int xdt, GemvArgs args, int max_chunks, int max
   for (int i = 1; i < args.count; ++i) mixed |= args.p[i].K != args.p[0].K;
   for (int i = 0; i < args.count; ++i) pairs |= args.p[i].W2 != nullptr;
   int waves = c.ks * c.tpw;
-  if (mixed && !getenv("Q4Q8_GEMV_KS")) {
+  if (mixed) {
     waves = c.ks * c.tpw > 8 ? c.ks * c.tpw : 8;
     for (int i = 0; i < args.count; ++i) {
       const int nch = (args.p[i].K + kChunkK - 1) / kChunkK;
