@@ -82,8 +82,11 @@ template <> struct Op<kBF16> {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
   }
   static __device__ __forceinline__ uint32_t pack(float lo, float hi) {
-    __bf16 l = (__bf16)lo, h = (__bf16)hi;
-    return (uint32_t)__builtin_bit_cast(uint16_t, l) | ((uint32_t)__builtin_bit_cast(uint16_t, h) << 16);
+    // One v_cvt_pk_bf16_f32 (round to nearest even) for the pair; two scalar
+    // casts compile to a conversion each plus a merge.
+    typedef float float2_t __attribute__((ext_vector_type(2)));
+    typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(float2_t{lo, hi}, bf16x2_t));
   }
 };
 
