@@ -36,8 +36,8 @@ namespace q4q8 {
 
 constexpr int kAttnD = 128;                  // head dimension
 constexpr int kAttnWaves = 4;
-constexpr int kAttnQT = 2;                   // 16-query tiles per wave
-constexpr int kAttnBM = 16 * kAttnQT * kAttnWaves;   // queries per workgroup
+// 16-query tiles per wave: QT (2, or 1 when the grid would leave CUs
+// without a second workgroup); 16 QT kAttnWaves queries per workgroup.
 constexpr int kAttnBN = 64;                  // keys per block
 constexpr int kVStride = kAttnBN + 12;       // V^T rows in LDS (halfs; +8 measured slower)
 
@@ -68,9 +68,11 @@ __device__ __forceinline__ uint32_t pack_rn(float lo, float hi) {
   }
 }
 
-template <int DT>
+template <int DT, int QT>
 __global__ __launch_bounds__(kAttnWaves * 64, 2) void attn_prefill_kernel(const AttnArgs a) {
   typedef typename Op<DT>::vec vec;
+  constexpr int kAttnQT = QT;
+  constexpr int kAttnBM = 16 * QT * kAttnWaves;   // queries per workgroup
   // Two buffers of K and V^T: block j + 1 is written while block j is read.
   // K: 16-byte column group cg of key k at slot 16 k + (cg ^ (k % 16)),
   // written by the buffer loads' LDS path (1 KB contiguous per wave
@@ -334,7 +336,12 @@ hipError_t launch_attn_prefill(int dt, const void* q, const void* k, const void*
   a.Hq = Hq;
   a.Hkv = Hkv;
   a.causal = causal;
-  a.mblocks = (S + kAttnBM - 1) / kAttnBM;
+  // Two 16-query tiles per wave (every K / V^T fragment serves both), or one
+  // when 128-query workgroups would not give every CU two of them (short
+  // sequences: S 512, 32 heads is 128 workgroups).
+  const int qt = (int64_t)((S + 127) / 128) * Hq * B >= 512 ? 2 : 1;
+  const int bm = 16 * qt * kAttnWaves;
+  a.mblocks = (S + bm - 1) / bm;
   // Pair query blocks when the paired grid still fills two workgroups per CU
   // (measured: S 4096 causal 249 -> 230 us; at S 2048, 32 heads, pairing
   // would leave half the CU slots empty).
@@ -342,8 +349,13 @@ hipError_t launch_attn_prefill(int dt, const void* q, const void* k, const void*
   a.per_bh = a.paired ? (a.mblocks + 1) / 2 : a.mblocks;
   a.scale_log2 = scale * 1.4426950408889634f;
   const dim3 grid((unsigned)(a.per_bh * Hq * B)), block(kAttnWaves * 64);
-  if (dt == kBF16) launch(attn_prefill_kernel<kBF16>, grid, block, 0, s, ev, a);
-  else launch(attn_prefill_kernel<kF16>, grid, block, 0, s, ev, a);
+  if (qt == 2) {
+    if (dt == kBF16) launch(attn_prefill_kernel<kBF16, 2>, grid, block, 0, s, ev, a);
+    else launch(attn_prefill_kernel<kF16, 2>, grid, block, 0, s, ev, a);
+  } else {
+    if (dt == kBF16) launch(attn_prefill_kernel<kBF16, 1>, grid, block, 0, s, ev, a);
+    else launch(attn_prefill_kernel<kF16, 1>, grid, block, 0, s, ev, a);
+  }
   return hipGetLastError();
 }
 
