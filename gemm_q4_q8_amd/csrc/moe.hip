@@ -567,9 +567,10 @@ hipError_t launch_moe_qgemm(int fmt, int xdt, const void* Wg, const void* Wu, co
   if (moe_decode_fits(T, H, F)) {
     // A few tokens: every expert product is a GEMV over the expert's weights.
     uint16_t* h = h_out ? (uint16_t*)h_out : w.h16;
-    launch_moe_decode(fmt, xdt, Wg, Wu, Wd, E, H, F, X, T, topk, offsets, sorted_pairs, h, w.y16, stream);
-    moe_combine_kernel<<<dim3((unsigned)((H / 8 + 255) / 256), (unsigned)T), dim3(256), 0, stream>>>(
-        w.y16, gates, T, topk, H, out);
+    if (!launch_moe_decode(fmt, xdt, Wg, Wu, Wd, E, H, F, X, T, topk, gates, offsets, sorted_pairs, h, w.y16, out,
+                           stream))
+      moe_combine_kernel<<<dim3((unsigned)((H / 8 + 255) / 256), (unsigned)T), dim3(256), 0, stream>>>(
+          w.y16, gates, T, topk, H, out);
     return hipGetLastError();
   }
   const uint16_t* x16 = (const uint16_t*)X;

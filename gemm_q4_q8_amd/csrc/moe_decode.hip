@@ -56,6 +56,7 @@ struct MoeDecArgs {
 
 constexpr int kDecXSlack = 512;
 constexpr int kDecMaxExperts = 1024;
+constexpr int kDecMaxTopk = 16;            // the route's top-k limit
 
 // SRC: dtype of the rows in memory (kF16 or kBF16); the operands are fp16.
 template <int FMT, int SRC, int MODE, int NI, int WAVES, int P>
@@ -201,6 +202,129 @@ __global__ __launch_bounds__(WAVES * 64) void moe_gemv_kernel(const MoeDecArgs a
   }
 }
 
+// Down projection fused with the weighted combine.  Workgroup (token t,
+// 16-row tile of H), WAVES waves: wave w < topk KQ takes the token's slot
+// j = w / KQ (expert e_j,
+// found from the pair's sorted position) and K-share w % KQ of the tile's
+// F-long rows, with the pair's h row (bf16, converted to fp16 in LDS) as its
+// activation row.  The reduction sums each slot's K-shares in order, rounds
+// y to fp16 as the unfused path stores it, and accumulates
+// out[t, n] = sum_j gates[t, j] y_j[n] over j = 0 .. topk-1 in the combine
+// kernel's order: the same values, one launch and no y round trip fewer.
+struct MoeDcArgs {
+  const uint8_t* W;          // down weights of expert 0
+  int64_t mat_bytes;         // repacked bytes of one expert's [H, F] matrix
+  const uint16_t* h;         // bf16 [positions, F], sorted-pair order
+  const float* gates;        // [T, topk]
+  const int32_t* offsets;    // [E + 1]
+  const int32_t* sorted_pairs;
+  float* out;                // [T, H]
+  int32_t H, F, topk, E, npos, kq;   // kq: K-shares per slot (topk kq <= WAVES)
+};
+
+template <int FMT, int WAVES, int P>
+__global__ __launch_bounds__(WAVES * 64) void moe_down_combine_kernel(const MoeDcArgs a) {
+  typedef typename Op<kF16>::vec vec;
+  typedef GemvStage<FMT> Stage;
+  constexpr int REC = Fmt<FMT>::kRecBytes;
+  extern __shared__ __attribute__((aligned(16))) uint16_t xs[];
+  __shared__ int32_t s_off[kDecMaxExperts + 1];
+  __shared__ int32_t s_pos[kDecMaxTopk];     // sorted position of each of token t's pairs
+  __shared__ float red[WAVES][64];
+
+  const int tiles = a.H / kTileRows;
+  const int t = blockIdx.x / tiles;
+  const int tile = blockIdx.x - t * tiles;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int topk = a.topk, KQ = a.kq;
+  for (int i = tid; i <= a.E; i += WAVES * 64) s_off[i] = a.offsets[i];
+  if (tid < kDecMaxTopk) s_pos[tid] = 0;   // stays in bounds for malformed routing
+  __syncthreads();
+  // Inverse of the sort for this token's pairs t topk .. t topk + topk - 1.
+  for (int i = tid; i < a.npos; i += WAVES * 64) {
+    const int p = a.sorted_pairs[i] - t * topk;
+    if (p >= 0 && p < topk) s_pos[p] = i;
+  }
+  __syncthreads();
+  const int j = wave / KQ, kw = wave - j * KQ;
+  const bool active = j < topk;                 // uniform per wave
+  const int pos = active ? s_pos[j] : 0;
+  // Expert owning sorted position pos: the largest e with offsets[e] <= pos.
+  int lo = 0, hi = a.E;
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (s_off[mid] <= pos) lo = mid;
+    else hi = mid;
+  }
+  const int e = lo;
+
+  const int F = a.F, nchunks = F / kChunkK;
+  const int r = lane & 15, g = lane >> 4;
+  const uint8_t* wbase = a.W + (int64_t)e * a.mat_bytes + (int64_t)tile * nchunks * REC;
+  const __amdgpu_buffer_rsrc_t wres =
+      __builtin_amdgcn_make_buffer_rsrc((void*)wbase, (short)0, active ? nchunks * REC : 0, kGemvBufFlags);
+  Stage st[P];
+#pragma unroll
+  for (int p = 0; p < P; ++p) gemv_load<FMT>(st[p], wres, kw + p * KQ, lane, r);
+  // The token's h rows (slot order) into LDS as fp16, rows of F + 8 halfs,
+  // then kDecXSlack zero bytes.
+  const int per_row = F / 8 + 1;
+  const int pieces = topk * per_row + kDecXSlack / 16;
+  for (int i = tid; i < pieces; i += WAVES * 64) {
+    const int jj = i / per_row, k8 = i - jj * per_row;
+    u32x4_t v = u32x4_t{0, 0, 0, 0};
+    if (jj < topk && k8 < F / 8) {
+      v = *(const u32x4_t*)(a.h + (int64_t)s_pos[jj] * F + k8 * 8);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const uint32_t b = v[q];
+        v[q] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(__builtin_bit_cast(float, b << 16),
+                                                                      __builtin_bit_cast(float, b & 0xFFFF0000u)));
+      }
+    }
+    *(u32x4_t*)(xs + i * 8) = v;
+  }
+  __syncthreads();
+  // One activation row per wave: every lane reads the slot's row (rows of the
+  // MFMA tile other than 0 are not used).
+  const uint16_t* xrow = xs + (active ? j : 0) * (F + 8) + 8 * g;
+  float acc[1] = {0.0f};
+  auto compute = [&](const Stage& s, int c) {
+    vec av[kBlocksPerChunk];
+#pragma unroll
+    for (int q = 0; q < kBlocksPerChunk; ++q) av[q] = *(const vec*)(xrow + c * kChunkK + q * 32);
+    gemv_mma<FMT, kF16, 1>(s, av, acc);
+  };
+  const int nw = active ? (nchunks - kw + KQ - 1) / KQ : 0;
+  int i0 = 0;
+  for (; i0 + P < nw; i0 += P) {
+#pragma unroll
+    for (int p = 0; p < P; ++p) {
+      const int c = kw + (i0 + p) * KQ;
+      compute(st[p], c);
+      __builtin_amdgcn_sched_barrier(0);
+      gemv_load<FMT>(st[p], wres, c + P * KQ, lane, r);
+    }
+  }
+#pragma unroll
+  for (int p = 0; p < P; ++p)
+    if (i0 + p < nw) compute(st[p], kw + (i0 + p) * KQ);
+
+  red[wave][lane] = acc[0];
+  __syncthreads();
+  if (wave != 0 || g != 0) return;
+  // Lane (r, 0) holds row 0, output n = 16 tile + r.
+  float sum = 0.0f;
+  for (int jj = 0; jj < topk; ++jj) {
+    float v = red[jj * KQ][lane];
+    for (int w = 1; w < KQ; ++w) v += red[jj * KQ + w][lane];
+    const float y = (float)(_Float16)v;               // y as the unfused path stores it
+    sum += a.gates[(int64_t)t * topk + jj] * y;       // the combine kernel's order
+  }
+  a.out[(int64_t)t * a.H + tile * kTileRows + r] = sum;
+}
+
 namespace {
 
 constexpr int kDecWaves = 8;
@@ -230,10 +354,22 @@ void launch_dec(MoeDecArgs a, int T, int npos, hipStream_t s) {
     moe_gemv_kernel<FMT, SRC, MODE, 1, kDecWaves, kDecRing><<<grid, block, lds, s>>>(a);
 }
 
+// The fused down + combine kernel: topk K-share groups of KQ waves in at most
+// kDcWaves waves, and the token's topk h rows in a 52 KB activation buffer.
+constexpr int kDcWaves = 16;
+// Past 4 tokens the unfused down (one pass over each expert's weights for all
+// of its tokens) plus the combine is faster (measured on MI355X, E 128 top-8
+// H 2048 F 768: fused 21.7/24.5/31.1/44.7 us per step at T = 1/2/4/8 against
+// 23.1/26.5/32.3/42.8 unfused).
+constexpr int kDcMaxTokens = 4;
+bool down_combine_fits(int topk, int F) {
+  return topk >= 1 && topk <= kDecMaxTopk && (int64_t)topk * (F + 8) * 2 + kDecXSlack <= 52 * 1024;
+}
+
 template <int FMT>
-void launch_dec_fmt(int xdt, const void* Wg, const void* Wu, const void* Wd, int E, int H, int F, const void* X,
-                    int T, int topk, const int32_t* offsets, const int32_t* sorted_pairs, uint16_t* h,
-                    uint16_t* y16, hipStream_t s) {
+bool launch_dec_fmt(int xdt, const void* Wg, const void* Wu, const void* Wd, int E, int H, int F, const void* X,
+                    int T, int topk, const float* gates, const int32_t* offsets, const int32_t* sorted_pairs,
+                    uint16_t* h, uint16_t* y16, float* out, hipStream_t s) {
   const int npos = T * topk;
   MoeDecArgs a;
   a.offsets = offsets;
@@ -254,15 +390,43 @@ void launch_dec_fmt(int xdt, const void* Wg, const void* Wu, const void* Wd, int
   if (xdt == kF16) launch_dec<FMT, kF16, kDecGateUp>(a, T, npos, s);
   else launch_dec<FMT, kBF16, kDecGateUp>(a, T, npos, s);
   // down: [H, F] per expert, x = the h rows.
+  const int64_t dbytes = (int64_t)(H / kTileRows) * (F / kChunkK) * Fmt<FMT>::kRecBytes;
+  if (T <= kDcMaxTokens && down_combine_fits(topk, F)) {
+    // Fused with the combine: one workgroup per (token, 16-row tile), the
+    // same K split per slot as the unfused down kernel would take.
+    MoeDcArgs d;
+    d.W = (const uint8_t*)Wd;
+    d.mat_bytes = dbytes;
+    d.h = h;
+    d.gates = gates;
+    d.offsets = offsets;
+    d.sorted_pairs = sorted_pairs;
+    d.out = out;
+    d.H = H;
+    d.F = F;
+    d.topk = topk;
+    d.E = E;
+    d.npos = npos;
+    const int64_t experts = std::min(npos, E);
+    d.kq = dec_ksh(F / kChunkK, 1, experts * (H / kTileRows));
+    while (d.kq > 1 && topk * d.kq > kDcWaves) d.kq /= 2;
+    // Always kDcWaves waves (the kernel's strides assume it); waves past
+    // topk kq stay idle.
+    const dim3 grid((unsigned)(T * (H / kTileRows))), block(kDcWaves * 64);
+    const size_t lds = (size_t)topk * (F + 8) * 2 + kDecXSlack;
+    moe_down_combine_kernel<FMT, kDcWaves, kDecRing><<<grid, block, lds, s>>>(d);
+    return true;
+  }
   a.W = (const uint8_t*)Wd;
   a.W2 = nullptr;
-  a.mat_bytes = (int64_t)(H / kTileRows) * (F / kChunkK) * Fmt<FMT>::kRecBytes;
+  a.mat_bytes = dbytes;
   a.X = h;
   a.ldx = F;
   a.out = y16;
   a.N = H;
   a.K = F;
   launch_dec<FMT, kBF16, kDecDown>(a, T, npos, s);
+  return false;
 }
 
 }  // namespace
@@ -273,13 +437,13 @@ bool moe_decode_fits(int T, int H, int F) {
   return T >= 1 && T <= kMoeDecodeMaxTokens && (int64_t)T * (k + 8) * 2 + kDecXSlack <= 52 * 1024;
 }
 
-void launch_moe_decode(int fmt, int xdt, const void* Wg, const void* Wu, const void* Wd, int E, int H, int F,
-                       const void* X, int T, int topk, const int32_t* offsets, const int32_t* sorted_pairs,
-                       uint16_t* h, uint16_t* y16, hipStream_t s) {
+bool launch_moe_decode(int fmt, int xdt, const void* Wg, const void* Wu, const void* Wd, int E, int H, int F,
+                       const void* X, int T, int topk, const float* gates, const int32_t* offsets,
+                       const int32_t* sorted_pairs, uint16_t* h, uint16_t* y16, float* out, hipStream_t s) {
   if (fmt == kQ4_0)
-    launch_dec_fmt<kQ4_0>(xdt, Wg, Wu, Wd, E, H, F, X, T, topk, offsets, sorted_pairs, h, y16, s);
-  else
-    launch_dec_fmt<kQ8_0>(xdt, Wg, Wu, Wd, E, H, F, X, T, topk, offsets, sorted_pairs, h, y16, s);
+    return launch_dec_fmt<kQ4_0>(xdt, Wg, Wu, Wd, E, H, F, X, T, topk, gates, offsets, sorted_pairs, h, y16, out,
+                                 s);
+  return launch_dec_fmt<kQ8_0>(xdt, Wg, Wu, Wd, E, H, F, X, T, topk, gates, offsets, sorted_pairs, h, y16, out, s);
 }
 
 }  // namespace q4q8

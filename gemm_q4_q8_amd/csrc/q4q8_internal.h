@@ -76,11 +76,13 @@ size_t moe_workspace_bytes(int fmt, int T, int E, int topk, int H, int F);
 // Decode path of the expert products (GEMV kernels), used for T <= 8 tokens
 // when the token rows fit the workgroup's activation buffer.  h: bf16
 // [T*topk, F] in sorted-pair order; y16: fp16 [T*topk, H] by pair id.
+// Returns true when it also formed out (down fused with the combine);
+// otherwise y16 holds the per-pair outputs for the combine kernel.
 constexpr int kMoeDecodeMaxTokens = 8;
 bool moe_decode_fits(int T, int H, int F);
-void launch_moe_decode(int fmt, int xdt, const void* Wg, const void* Wu, const void* Wd, int E, int H, int F,
-                       const void* X, int T, int topk, const int32_t* offsets, const int32_t* sorted_pairs,
-                       uint16_t* h, uint16_t* y16, hipStream_t s);
+bool launch_moe_decode(int fmt, int xdt, const void* Wg, const void* Wu, const void* Wd, int E, int H, int F,
+                       const void* X, int T, int topk, const float* gates, const int32_t* offsets,
+                       const int32_t* sorted_pairs, uint16_t* h, uint16_t* y16, float* out, hipStream_t s);
 
 hipError_t launch_moe_qgemm(int fmt, int xdt, const void* Wg, const void* Wu, const void* Wd, int E, int H, int F,
                             const void* X, int T, int topk, const float* gates, const int32_t* offsets,

@@ -145,6 +145,7 @@ DECODE_CASES = [
     (synth.Q4_0, synth.BF16, 2, 1024, 16, 128, 128),
     (synth.Q4_0, synth.BF16, 7, 64, 8, 1024, 512),
     (synth.Q8_0, synth.BF16, 1, 32, 1, 384, 128),
+    (synth.Q8_0, synth.F16, 2, 32, 16, 256, 1792),  # topk x F past the fused down+combine's buffer
 ]
 
 
