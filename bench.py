@@ -596,16 +596,16 @@ def ffn_workloads(q, torch, synth, ev: HipEvents, quick: bool):
 
 
 def prefill_workloads(q, torch, synth, ev: HipEvents, quick: bool):
-    """Prefill GEMM Y[M, 12288] = X[M, 4096] W^T, Q4_0 (and Q8_0 at M = 512),
-    bf16 in and out.  The timed span of one call covers both of its kernels
+    """Prefill GEMM Y[M, 12288] = X[M, 4096] W^T, Q4_0 (and Q8_0 and plain
+    fp16 weights at M = 512), bf16 in and out.  The timed span of one call covers both of its kernels
     (bf16 -> fp16 pre-pass and the GEMM), from the first dispatch's start to
     the last one's end."""
     out = []
     dev = torch.device("cuda:0")
-    for fmt, M in ([(1, 512)] if quick else [(1, 512), (1, 2048), (2, 512)]):
+    for fmt, M in ([(1, 512)] if quick else [(1, 512), (1, 2048), (2, 512), (3, 512)]):
         w, x = synth.prefill(M)
-        if fmt == 2:
-            w = synth.q_weight(synth.rng_for(synth.PREFILL["seed"], 50), 2, w.N, w.K)
+        if fmt != 1:
+            w = synth.weight(synth.rng_for(synth.PREFILL["seed"], 50), fmt, w.N, w.K)
         W0 = q.repack(fmt, torch.from_numpy(w.canon).to(dev), w.N, w.K)
         Ws = [W0] + [W0.clone() for _ in range(3)]
         X = torch.from_numpy(x.bits.view("int16")).view(torch.bfloat16).to(dev)

@@ -5,8 +5,8 @@ kernels.  Tensors are passed by data pointer together with the current HIP
 stream of their device.  If the library is not built the first call raises;
 there is no fallback path.
 
-Formats: Q4_0 = 1, Q8_0 = 2, FP16 = 3 (plain fp16 weights: layout and GEMV
-calls only).  Activation dtypes: torch.float16 or torch.bfloat16.  Weights
+Formats: Q4_0 = 1, Q8_0 = 2, FP16 = 3 (plain fp16 weights: layout, GEMV and
+GEMM calls).  Activation dtypes: torch.float16 or torch.bfloat16.  Weights
 are uint8 tensors holding repacked blocks (see repack()).
 """
 from __future__ import annotations

@@ -316,7 +316,7 @@ extern "C" {
 static int qgemm_impl(int fmt, const void* W, int64_t N, int64_t K, const void* X, int xdt, int64_t ldx, int64_t M,
                       void* Y, int ydt, int64_t ldy, void* ws, size_t ws_bytes, void* stream,
                       const q4q8::LaunchEvents& ev) {
-  if (!fmt_ok(fmt)) return fail(Q4Q8_ERR_UNSUPPORTED, "qgemm: weight format %d (Q4_0 and Q8_0 only)", fmt);
+  if (!any_fmt_ok(fmt)) return fail(Q4Q8_ERR_UNSUPPORTED, "qgemm: weight format %d", fmt);
   int st = check_matrix(fmt, N, K);
   if (st) return st;
   if (!act_ok(xdt)) return fail(Q4Q8_ERR_UNSUPPORTED, "qgemm: activation dtype %d not F16/BF16", xdt);

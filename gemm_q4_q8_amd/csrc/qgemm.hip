@@ -1,4 +1,5 @@
-// Prefill GEMM over repacked Q4_0 / Q8_0 weights: Y[M, N] = X[M, K] W[N, K]^T.
+// Prefill GEMM over repacked Q4_0 / Q8_0 (or plain fp16) weights:
+// Y[M, N] = X[M, K] W[N, K]^T.
 //
 // The pages run prefill on tiled GEMM kernels on matrix intrinsics, one per
 // quantisation format, dequantising in the inner loop ("BaseRT:
@@ -162,7 +163,7 @@ static void launch_tile(const void* W, int64_t N, int64_t K, const void* X, int6
 template <int FMT, int YDT>
 static void launch_shape(const void* W, int64_t N, int64_t K, const void* X, int64_t ldx, int64_t M, void* Y,
                          int64_t ldy, hipStream_t s, const LaunchEvents& ev) {
-  constexpr int S = FMT == kQ4_0 ? Q4Q8_GEMM_STAGES_Q4 : Q4Q8_GEMM_STAGES_Q8;
+  constexpr int S = FMT == kQ4_0 ? Q4Q8_GEMM_STAGES_Q4 : Q4Q8_GEMM_STAGES_Q8;   // fp16: as Q8_0
   if (M <= 64)
     launch_tile<FMT, YDT, 4, 1, S>(W, N, K, X, ldx, M, Y, ldy, s, ev);
   else
@@ -199,10 +200,14 @@ hipError_t launch_qgemm(int fmt, int xdt, int ydt, const void* W, int64_t N, int
     if (ydt == kBF16) launch_shape<kQ4_0, kBF16>(W, N, K, Xh, ldh, M, Y, ldy, s, gev);
     else if (ydt == kF16) launch_shape<kQ4_0, kF16>(W, N, K, Xh, ldh, M, Y, ldy, s, gev);
     else launch_shape<kQ4_0, kF32>(W, N, K, Xh, ldh, M, Y, ldy, s, gev);
-  } else {
+  } else if (fmt == kQ8_0) {
     if (ydt == kBF16) launch_shape<kQ8_0, kBF16>(W, N, K, Xh, ldh, M, Y, ldy, s, gev);
     else if (ydt == kF16) launch_shape<kQ8_0, kF16>(W, N, K, Xh, ldh, M, Y, ldy, s, gev);
     else launch_shape<kQ8_0, kF32>(W, N, K, Xh, ldh, M, Y, ldy, s, gev);
+  } else {
+    if (ydt == kBF16) launch_shape<kFP16W, kBF16>(W, N, K, Xh, ldh, M, Y, ldy, s, gev);
+    else if (ydt == kF16) launch_shape<kFP16W, kF16>(W, N, K, Xh, ldh, M, Y, ldy, s, gev);
+    else launch_shape<kFP16W, kF32>(W, N, K, Xh, ldh, M, Y, ldy, s, gev);
   }
   return hipGetLastError();
 }

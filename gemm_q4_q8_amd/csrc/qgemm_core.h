@@ -86,12 +86,19 @@ __device__ __forceinline__ void tile_mainloop(const __amdgpu_buffer_rsrc_t (&wre
   // 2 kw + 1.  Q4_0: dwords 2 kw, 2 kw + 1 of the lane's slot; Q8_0: the
   // lane's slot in half kw.  Lane offsets are loop-invariant; the chunk
   // enters through the scalar offset.  Chunks past the last re-read the last.
-  typedef typename std::conditional<FMT == kQ4_0, u32x2_t, u32x4_t>::type CodeT;
+  // Plain fp16: the lane's slot of blocks 2 kw and 2 kw + 1 (two 16-byte
+  // loads, no scales).
+  struct F16Pair {
+    u32x4_t h[2];
+  };
+  typedef typename std::conditional<FMT == kQ4_0, u32x2_t,
+                                    typename std::conditional<FMT == kQ8_0, u32x4_t, F16Pair>::type>::type CodeT;
   struct WStage {
     CodeT codes[NW][NT];
     uint32_t sc[NW][NT];
   };
-  const uint32_t wv_code = FMT == kQ4_0 ? lane * 16 + kw * 8 : kw * 1024 + lane * 16;
+  const uint32_t wv_code = FMT == kQ4_0 ? lane * 16 + kw * 8 : FMT == kQ8_0 ? kw * 1024 + lane * 16
+                                                                             : 2 * kw * 1024 + lane * 16;
   const uint32_t wv_scale = C::CODE + r * 8 + kw * 4;
   auto load_w = [&](WStage& s, int c) __attribute__((always_inline)) {
     const int cc = c < nchunks ? c : nchunks - 1;
@@ -101,11 +108,16 @@ __device__ __forceinline__ void tile_mainloop(const __amdgpu_buffer_rsrc_t (&wre
       for (int t = 0; t < NT; ++t) {
         const int so = (t * nchunks + cc) * C::REC;
         const uint32_t vc = t < tv ? wv_code : kOOB, vs = t < tv ? wv_scale : kOOB;
-        if constexpr (FMT == kQ4_0)
-          s.codes[w][t] = __builtin_amdgcn_raw_buffer_load_b64(wres[w], vc, so, 0);
-        else
-          s.codes[w][t] = __builtin_amdgcn_raw_buffer_load_b128(wres[w], vc, so, 0);
-        s.sc[w][t] = __builtin_amdgcn_raw_buffer_load_b32(wres[w], vs, so, 0);
+        if constexpr (FMT == kFP16W) {   // two loads, as the quantised formats' codes + scales
+          s.codes[w][t].h[0] = __builtin_amdgcn_raw_buffer_load_b128(wres[w], vc, so, 0);
+          s.codes[w][t].h[1] = __builtin_amdgcn_raw_buffer_load_b128(wres[w], t < tv ? vc + 1024 : kOOB, so, 0);
+        } else {
+          if constexpr (FMT == kQ4_0)
+            s.codes[w][t] = __builtin_amdgcn_raw_buffer_load_b64(wres[w], vc, so, 0);
+          else
+            s.codes[w][t] = __builtin_amdgcn_raw_buffer_load_b128(wres[w], vc, so, 0);
+          s.sc[w][t] = __builtin_amdgcn_raw_buffer_load_b32(wres[w], vs, so, 0);
+        }
       }
   };
   // Copy chunk c of the activation tile into LDS stage st.  Chunks past the
@@ -141,18 +153,22 @@ __device__ __forceinline__ void tile_mainloop(const __amdgpu_buffer_rsrc_t (&wre
     for (int w = 0; w < NW; ++w)
 #pragma unroll
       for (int t = 0; t < NT; ++t) {
-        u32x4_t q;
-        if constexpr (FMT == kQ4_0) {
-          const uint32_t wd = s.codes[w][t][jj];
-          q = deq_q4_f16(wd);
+        if constexpr (FMT == kFP16W) {
+          b[w][t] = __builtin_bit_cast(half8_t, s.codes[w][t].h[jj]);
         } else {
-          const uint32_t d0 = s.codes[w][t][2 * jj], d1 = s.codes[w][t][2 * jj + 1];
-          q = deq_q8<kF16>(d0, d1);
+          u32x4_t q;
+          if constexpr (FMT == kQ4_0) {
+            const uint32_t wd = s.codes[w][t][jj];
+            q = deq_q4_f16(wd);
+          } else {
+            const uint32_t d0 = s.codes[w][t][2 * jj], d1 = s.codes[w][t][2 * jj + 1];
+            q = deq_q8<kF16>(d0, d1);
+          }
+          const uint32_t sbits = jj ? (s.sc[w][t] >> 16) : (s.sc[w][t] & 0xFFFFu);
+          const _Float16 sh = __builtin_bit_cast(_Float16, (uint16_t)sbits);
+          const half2_t s2 = {sh, sh};
+          b[w][t] = __builtin_bit_cast(half8_t, scale_f16x8(q, s2));
         }
-        const uint32_t sbits = jj ? (s.sc[w][t] >> 16) : (s.sc[w][t] & 0xFFFFu);
-        const _Float16 sh = __builtin_bit_cast(_Float16, (uint16_t)sbits);
-        const half2_t s2 = {sh, sh};
-        b[w][t] = __builtin_bit_cast(half8_t, scale_f16x8(q, s2));
       }
   };
   // NW x MT x NT MFMAs of block jj of the chunk in LDS stage st.

@@ -75,8 +75,8 @@ typedef enum {
 } q4q8_status;
 
 /* Q4Q8_FP16: plain fp16 weights (no quantisation), accepted by the layout
- * calls and the GEMV entry points (q4q8_qgemv, _grouped, _swiglu,
- * q4q8_ffn_decode); the GEMM and MoE calls take Q4_0 and Q8_0 only. */
+ * calls, the GEMV entry points (q4q8_qgemv, _grouped, _swiglu,
+ * q4q8_ffn_decode) and q4q8_qgemm; the MoE calls take Q4_0 and Q8_0 only. */
 typedef enum { Q4Q8_Q4_0 = 1, Q4Q8_Q8_0 = 2, Q4Q8_FP16 = 3 } q4q8_format;
 typedef enum { Q4Q8_F16 = 1, Q4Q8_BF16 = 2, Q4Q8_F32 = 3 } q4q8_dtype;
 
@@ -248,9 +248,12 @@ size_t q4q8_qgemm_workspace(int xdt, int64_t M, int64_t K);
  *        aligned to its element size.
  *   ws:  device workspace of >= q4q8_qgemm_workspace(xdt, M, K) bytes,
  *        256-byte aligned (may be NULL when that is 0); clobbered.
+ *   fmt: Q4Q8_Q4_0, Q4Q8_Q8_0 or Q4Q8_FP16 (plain fp16 weights, the same
+ *        repacked tiles; the pages' format list runs up to FP16).
  * fp32 accumulation on fp16 matrix-core operands (weights dequantised and
- * scaled to fp16, relative rounding <= 2^-11; BF16 activations converted to
- * fp16, exact for 2^-14 <= |x| < 65520); result rounded once to ydt.
+ * scaled to fp16, relative rounding <= 2^-11, or fp16 weights as they are;
+ * BF16 activations converted to fp16, exact for 2^-14 <= |x| < 65520);
+ * result rounded once to ydt.
  * M >= 1 (any).  Errors: Q4Q8_ERR_WORKSPACE if ws is missing or short. */
 int q4q8_qgemm(int fmt, const void* W, int64_t N, int64_t K,
                const void* X, int xdt, int64_t ldx, int64_t M,

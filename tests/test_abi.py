@@ -46,12 +46,14 @@ def test_status_strings(q):
         assert q.status_string(s) not in ("ok", "unknown status")
 
 
-def test_fp16_sizes_and_gemm_rejects_it(q):
+def test_fp16_sizes(q):
     assert q.canonical_bytes(synth.FP16, 100, 96) == 100 * 96 * 2
     assert q.repacked_bytes(synth.FP16, 100, 96) == 7 * 1 * 4096
     assert q.repacked_bytes(synth.FP16, 4096, 4096) == 4096 * 4096 * 2
     L = q.lib()
-    st = L.q4q8_qgemm(synth.FP16, _vp(0x1000), 64, 256, _vp(0x2000), 1, 256, 16, _vp(0x3000), 1, 64, None, 0, None)
+    st = L.q4q8_qgemm(synth.FP16, None, 64, 256, _vp(0x2000), 1, 256, 16, _vp(0x3000), 1, 64, None, 0, None)
+    assert st == -1     # the format is accepted; the null weight pointer is not
+    st = L.q4q8_qgemm(4, _vp(0x1000), 64, 256, _vp(0x2000), 1, 256, 16, _vp(0x3000), 1, 64, None, 0, None)
     assert st == -2
     nws = q.moe_workspace(1, 4, 8, 2, 256, 256)
     assert q.moe_workspace(synth.FP16, 4, 8, 2, 256, 256) == 0 and nws > 0

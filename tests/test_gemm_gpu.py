@@ -31,10 +31,11 @@ SMALL = [(1, 16, 128), (17, 48, 160), (64, 256, 256), (100, 200, 1056), (128, 19
 
 
 @pytest.mark.parametrize("fmt,xdt,ydt", [(synth.Q4_0, synth.BF16, "bf16"), (synth.Q4_0, synth.F16, "f32"),
-                                         (synth.Q8_0, synth.BF16, "bf16"), (synth.Q8_0, synth.F16, "f16")])
+                                         (synth.Q8_0, synth.BF16, "bf16"), (synth.Q8_0, synth.F16, "f16"),
+                                         (synth.FP16, synth.BF16, "bf16"), (synth.FP16, synth.F16, "f32")])
 @pytest.mark.parametrize("M,N,K", SMALL)
 def test_qgemm_parity_small(q, fmt, xdt, ydt, M, N, K):
-    w = synth.q_weight(synth.rng_for(61, M + N + K + fmt), fmt, N, K)
+    w = synth.weight(synth.rng_for(61, M + N + K + fmt), fmt, N, K)
     x = synth.activation(synth.rng_for(62, M * 3 + K + xdt), (M, K), xdt)
     Wd = q.repack(fmt, bytes_tensor(w.canon), N, K)
     y = q.qgemm(fmt, Wd, N, K, act_tensor(x), out_dtype=OUT[ydt])
