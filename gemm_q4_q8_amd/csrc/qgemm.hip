@@ -24,6 +24,9 @@
 #ifndef Q4Q8_GEMM_STAGES_Q8
 #define Q4Q8_GEMM_STAGES_Q8 3
 #endif
+#ifndef Q4Q8_GEMM_STAGES_F16
+#define Q4Q8_GEMM_STAGES_F16 4
+#endif
 
 namespace q4q8 {
 
@@ -163,7 +166,7 @@ static void launch_tile(const void* W, int64_t N, int64_t K, const void* X, int6
 template <int FMT, int YDT>
 static void launch_shape(const void* W, int64_t N, int64_t K, const void* X, int64_t ldx, int64_t M, void* Y,
                          int64_t ldy, hipStream_t s, const LaunchEvents& ev) {
-  constexpr int S = FMT == kQ4_0 ? Q4Q8_GEMM_STAGES_Q4 : Q4Q8_GEMM_STAGES_Q8;   // fp16: as Q8_0
+  constexpr int S = FMT == kQ4_0 ? Q4Q8_GEMM_STAGES_Q4 : FMT == kQ8_0 ? Q4Q8_GEMM_STAGES_Q8 : Q4Q8_GEMM_STAGES_F16;
   if (M <= 64)
     launch_tile<FMT, YDT, 4, 1, S>(W, N, K, X, ldx, M, Y, ldy, s, ev);
   else

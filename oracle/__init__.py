@@ -129,11 +129,16 @@ def qgemm_rows(fmt: int, canon, N: int, K: int, X: np.ndarray, rows, cols):
     """Y[rows[i], cols[i]] and bounds for sampled output elements only."""
     rows = np.asarray(rows)
     cols = np.asarray(cols)
-    s, q = decode_rows(fmt, canon, N, K, np.unique(cols))
     ucols = np.unique(cols)
     pos = {int(c): i for i, c in enumerate(ucols)}
-    off = 8 if fmt == Q4_0 else 0
-    W = np.repeat(s, QK, axis=1) * (q - off)
+    if fmt == FP16:
+        nbytes = K * 2
+        c = np.ascontiguousarray(canon, dtype=np.uint8).reshape(N, nbytes)[ucols]
+        W = dequant(FP16, c.reshape(-1), len(ucols), K)
+    else:
+        s, q = decode_rows(fmt, canon, N, K, ucols)
+        off = 8 if fmt == Q4_0 else 0
+        W = np.repeat(s, QK, axis=1) * (q - off)
     Xr = np.asarray(X, dtype=np.float64)
     y = np.empty(rows.size)
     b = np.empty(rows.size)

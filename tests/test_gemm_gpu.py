@@ -79,23 +79,26 @@ def test_qgemm_zero_weights(q):
     assert torch.all(y.abs() <= 1e-5)
 
 
-@pytest.mark.parametrize("M", [512, 2048])
-def test_qgemm_prefill_full_size_sampled(q, M):
-    """The prefill shapes (K 4096, N 12288) in the benchmark's launch shape;
-    4096 sampled outputs plus every output of the first and last 16-row
-    block against the oracle, and NaN/Inf-free everywhere."""
+@pytest.mark.parametrize("fmt,M", [(synth.Q4_0, 512), (synth.Q4_0, 2048), (synth.Q8_0, 512), (synth.FP16, 512)])
+def test_qgemm_prefill_full_size_sampled(q, fmt, M):
+    """The prefill shapes (K 4096, N 12288) in the benchmark's launch shape
+    (Q8_0 and fp16 weights drawn as the benchmark draws them); 4096 sampled
+    outputs plus every output of the first and last 16-row block against the
+    oracle, and NaN/Inf-free everywhere."""
     w, x = synth.prefill(M)
+    if fmt != synth.Q4_0:
+        w = synth.weight(synth.rng_for(synth.PREFILL["seed"], 50), fmt, w.N, w.K)
     N, K = w.N, w.K
-    Wd = q.repack(synth.Q4_0, bytes_tensor(w.canon), N, K)
-    y = q.qgemm(synth.Q4_0, Wd, N, K, act_tensor(x), out_dtype=torch.bfloat16)
+    Wd = q.repack(fmt, bytes_tensor(w.canon), N, K)
+    y = q.qgemm(fmt, Wd, N, K, act_tensor(x), out_dtype=torch.bfloat16)
     torch.cuda.synchronize()
     yv = values(y)
     assert np.all(np.isfinite(yv))
     rng = np.random.default_rng(65 + M)
     rows = np.concatenate([rng.integers(0, M, 4096), np.zeros(64, int), np.full(64, M - 1)])
     cols = np.concatenate([rng.integers(0, N, 4096), np.arange(64), N - 1 - np.arange(64)])
-    ref, bound = oracle.qgemm_rows(synth.Q4_0, w.canon, N, K, x.values, rows, cols)
-    check_rounded(yv[rows, cols], ref, bound, f"prefill M{M} sampled")
+    ref, bound = oracle.qgemm_rows(fmt, w.canon, N, K, x.values, rows, cols)
+    check_rounded(yv[rows, cols], ref, bound, f"prefill fmt{fmt} M{M} sampled")
     for r0 in (0, M - 16):
-        ref, bound = oracle.qgemm(synth.Q4_0, w.canon, N, K, x.values[r0:r0 + 16])
-        check_rounded(yv[r0:r0 + 16], ref, bound, f"prefill M{M} rows {r0}..")
+        ref, bound = oracle.qgemm(fmt, w.canon, N, K, x.values[r0:r0 + 16])
+        check_rounded(yv[r0:r0 + 16], ref, bound, f"prefill fmt{fmt} M{M} rows {r0}..")

@@ -188,15 +188,21 @@ def test_gemv_linear_in_x():
     assert np.allclose(ys, 3 * ya - yc, rtol=0, atol=1e-13 * (3 * ba + bc).max())
 
 
-def test_gemm_rows_agree_with_full_product():
-    w = synth.q_weight(synth.rng_for(9, 0), synth.Q4_0, 40, 128)
+@pytest.mark.parametrize("fmt", [synth.Q4_0, synth.FP16])
+def test_gemm_rows_agree_with_full_product(fmt):
+    w = synth.weight(synth.rng_for(9, 0), fmt, 40, 128)
     X = synth.activation(synth.rng_for(9, 1), (17, 128), synth.BF16).values
-    Y, B = oracle.qgemm(synth.Q4_0, w.canon, 40, 128, X)
+    Y, B = oracle.qgemm(fmt, w.canon, 40, 128, X)
     rows = [0, 3, 16, 16, 9]
     cols = [39, 0, 7, 8, 20]
-    y, b = oracle.qgemm_rows(synth.Q4_0, w.canon, 40, 128, X, rows, cols)
+    y, b = oracle.qgemm_rows(fmt, w.canon, 40, 128, X, rows, cols)
     assert np.allclose(y, Y[rows, cols], rtol=1e-14, atol=1e-14)
     assert np.allclose(b, B[rows, cols], rtol=1e-14)
+    if fmt == synth.FP16:
+        # brute force from the generator's fp16 matrix (not the byte decode)
+        for i, (r, c) in enumerate(zip(rows, cols)):
+            exact = sum(float(w.codes[c, k]) * float(X[r, k]) for k in range(128))
+            assert abs(y[i] - exact) <= 1e-12 * b[i]
 
 
 # ----------------------------------------------------------------------------
