@@ -676,7 +676,8 @@ def moe_workload(q, torch, synth, fmt: int = 1):
 def moe_decode_workloads(q, torch, synth, quick: bool):
     """MoE decode: T = 1 and 8 tokens over the MoE layer's experts (E 128,
     top-8, H 2048, F 768, Q4_0).  One step = route + expert GEMVs (gate/up
-    SwiGLU, down) + combine, captured in a HIP graph.  Steps cycle through 16
+    SwiGLU, down) + combine, captured in a HIP graph, in both forms: the
+    routing call and the expert call, and the one-call entry point.  Steps cycle through 16
     token sets and two copies of the expert weights (680 MB, more than the
     Infinity Cache).  Algorithmic bytes = the distinct selected experts'
     three matrices + x + out."""
@@ -704,34 +705,40 @@ def moe_decode_workloads(q, torch, synth, quick: bool):
               torch.empty(T * k, dtype=torch.int32, device=dev))
         wsp = torch.empty(q.moe_workspace(1, T, E, k, H, F), dtype=torch.uint8, device=dev)
 
-        def step(i):
+        def step_two(i):      # q4q8_moe_route, then q4q8_moe_qgemm
             Wg, Wu, Wd = copies[i % 2]
             ids, gates, counts, offsets, sp = q.moe_route(Ls[i % sets], k, out=rt)
             q.moe_qgemm(1, Wg, Wu, Wd, E, H, F, X, k, gates, offsets, sp, out=o, ws=wsp)
 
+        def step_one(i):      # q4q8_moe_decode: routing inside the first expert kernel
+            Wg, Wu, Wd = copies[i % 2]
+            q.moe_decode(1, Wg, Wu, Wd, E, H, F, Ls[i % sets], X, k, route=rt, out=o, ws=wsp)
+
         nbytes = 0
         for i in range(sets):
-            step(i)
+            step_two(i)
             torch.cuda.synchronize()
             nbytes += int((rt[2] > 0).sum().item()) * 3 * mat + T * H * 2 + T * H * 4
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g):
-            for i in range(sets):
-                step(i)
-        for _ in range(3):
-            g.replay()
-        torch.cuda.synchronize()
-        reps = 20
-        t0 = time.perf_counter()
-        for _ in range(reps):
-            g.replay()
-        torch.cuda.synchronize()
-        dt = (time.perf_counter() - t0) / (reps * sets)
         per = nbytes / sets
-        out.append({"workload": f"q4_0 moe decode T={T} E={E} top{k} H={H} F={F} (route + GEMV path + combine)",
-                    "step_us": round(dt * 1e6, 2), "bytes_per_step": int(per), "GB/s": round(per / dt / 1e9, 1),
-                    "hbm_frac": round(per / dt / 1e9 / HBM_PEAK_GBS, 4)})
-        del g
+        for name, step in (("route + moe_qgemm: route, GEMV path, combine", step_two),
+                           ("one call, moe_decode: routing inside the gate/up kernel", step_one)):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                for i in range(sets):
+                    step(i)
+            for _ in range(3):
+                g.replay()
+            torch.cuda.synchronize()
+            reps = 20
+            t0 = time.perf_counter()
+            for _ in range(reps):
+                g.replay()
+            torch.cuda.synchronize()
+            dt = (time.perf_counter() - t0) / (reps * sets)
+            out.append({"workload": f"q4_0 moe decode T={T} E={E} top{k} H={H} F={F} ({name})",
+                        "step_us": round(dt * 1e6, 2), "bytes_per_step": int(per), "GB/s": round(per / dt / 1e9, 1),
+                        "hbm_frac": round(per / dt / 1e9 / HBM_PEAK_GBS, 4)})
+            del g
     del base, copies
     torch.cuda.empty_cache()
     return out

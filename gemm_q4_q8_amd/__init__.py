@@ -72,6 +72,8 @@ def _declare(lib):
         "q4q8_moe_workspace": (sz, [i32, i32, i32, i32, i32, i32]),
         "q4q8_moe_qgemm": (i32, [i32, vp, vp, vp, i32, i32, i32, vp, i32, i32, i32,
                                  vp, vp, vp, vp, vp, vp, sz, vp]),
+        "q4q8_moe_decode": (i32, [i32, vp, vp, vp, i32, i32, i32, vp, vp, i32, i32, i32,
+                                  vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]),
         "q4q8_stream_read_digest_bytes": (sz, []),
         "q4q8_stream_read_timed": (i32, [vp, sz, vp, sz, vp, vp, vp]),
     }
@@ -328,6 +330,34 @@ def moe_qgemm(fmt: int, Wg, Wu, Wd, E: int, H: int, F: int, X: torch.Tensor, top
                                 _ptr(h_out), _ptr(ws), ws.numel() * ws.element_size(), _stream(X)),
            "moe_qgemm")
     return out
+
+
+def moe_decode(fmt: int, Wg, Wu, Wd, E: int, H: int, F: int, logits: torch.Tensor, X: torch.Tensor, topk: int,
+               route=None, out=None, h_out=None, ws=None):
+    """Routing and expert products of a few tokens in one call ->
+    (out [T, H] fp32, (ids, gates, counts, offsets, sorted_pairs)).
+
+    route: optional preallocated routing arrays, as moe_route's out."""
+    _dev(logits, "logits")
+    T = X.shape[0]
+    d = X.device
+    if logits.shape != (T, E):
+        raise ValueError("logits must be [T, E]")
+    if route is None:
+        route = (torch.empty((T, topk), dtype=torch.int32, device=d), torch.empty((T, topk), dtype=torch.float32, device=d),
+                 torch.empty(E, dtype=torch.int32, device=d), torch.empty(E + 1, dtype=torch.int32, device=d),
+                 torch.empty(T * topk, dtype=torch.int32, device=d))
+    if out is None:
+        out = torch.empty((T, H), dtype=torch.float32, device=d)
+    nws = moe_workspace(fmt, T, E, topk, H, F)
+    if ws is None:
+        ws = torch.empty(nws, dtype=torch.uint8, device=d)
+    ids, gates, counts, offsets, sp = route
+    _check(lib().q4q8_moe_decode(fmt, _ptr(Wg), _ptr(Wu), _ptr(Wd), E, H, F, _ptr(logits), _ptr(X), _DT[X.dtype], T,
+                                 topk, _ptr(ids), _ptr(gates), _ptr(counts), _ptr(offsets), _ptr(sp), _ptr(out),
+                                 _ptr(h_out), _ptr(ws), ws.numel() * ws.element_size(), _stream(X)),
+           "moe_decode")
+    return out, route
 
 
 def attn_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = True, scale=None,

@@ -426,6 +426,39 @@ int q4q8_moe_qgemm(int fmt, const void* Wg, const void* Wu, const void* Wd, int 
                     "moe_qgemm launch");
 }
 
+int q4q8_moe_decode(int fmt, const void* Wg, const void* Wu, const void* Wd, int E, int H, int F,
+                    const float* logits, const void* X, int xdt, int T, int topk, int32_t* ids, float* gates,
+                    int32_t* counts, int32_t* offsets, int32_t* sorted_pairs, float* out, void* h_out, void* ws,
+                    size_t ws_bytes, void* stream) {
+  if (!fmt_ok(fmt)) return fail(Q4Q8_ERR_UNSUPPORTED, "unknown weight format %d", fmt);
+  if (!act_ok(xdt)) return fail(Q4Q8_ERR_UNSUPPORTED, "moe_decode: activation dtype %d not F16/BF16", xdt);
+  if (!Wg || !Wu || !Wd || !logits || !X || !ids || !gates || !counts || !offsets || !sorted_pairs || !out)
+    return fail(Q4Q8_ERR_INVALID_ARG, "moe_decode: null pointer");
+  if (T < 1 || E < 1 || topk < 1 || topk > E || topk > 16 || E > 1024)
+    return fail(Q4Q8_ERR_INVALID_ARG, "moe_decode: T=%d E=%d topk=%d", T, E, topk);
+  if (H < 128 || F < 128 || H % 128 || F % 128)
+    return fail(Q4Q8_ERR_INVALID_ARG, "moe_decode: H=%d and F=%d must be positive multiples of 128", H, F);
+  if (H > (1 << 20) || F > (1 << 20) || !q4q8::moe_decode_fits(T, H, F))
+    return fail(Q4Q8_ERR_UNSUPPORTED,
+                "moe_decode: T=%d H=%d F=%d beyond the decode path (T <= 8 and T*(max(H,F)+8)*2 + 512 <= 52 KB; "
+                "use q4q8_moe_route + q4q8_moe_qgemm)",
+                T, H, F);
+  const size_t need = q4q8::moe_workspace_bytes(fmt, T, E, topk, H, F);
+  if (!ws || ws_bytes < need)
+    return fail(Q4Q8_ERR_WORKSPACE, "moe_decode: workspace holds %zu bytes, needs %zu", ws_bytes, need);
+  if (!aligned(ws, 256)) return fail(Q4Q8_ERR_ALIGNMENT, "moe_decode: workspace not 256-byte aligned");
+  if (!aligned(Wg, 16) || !aligned(Wu, 16) || !aligned(Wd, 16) || !aligned(X, 16) || !aligned(out, 16) ||
+      (h_out && !aligned(h_out, 16)) || !aligned(logits, 4) || !aligned(ids, 4) || !aligned(gates, 4) ||
+      !aligned(counts, 4) || !aligned(offsets, 4) || !aligned(sorted_pairs, 4))
+    return fail(Q4Q8_ERR_ALIGNMENT, "moe_decode: weights, X, out and h_out must be 16-byte aligned, the routing "
+                                    "arrays 4-byte aligned");
+  clear_hip_error();
+  const q4q8::MoeRouteOut ro = {logits, ids, gates, counts, offsets, sorted_pairs};
+  return hip_status(q4q8::launch_moe_decode_call(fmt, xdt, Wg, Wu, Wd, E, H, F, X, T, topk, ro, out, h_out, ws,
+                                                 (hipStream_t)stream),
+                    "moe_decode launch");
+}
+
 static int attn_impl(int dt, const void* Q, const void* K, const void* V, void* O, int B, int S, int Hq, int Hkv,
                      int D, int causal, float scale, void* stream, const q4q8::LaunchEvents& ev) {
   if (!act_ok(dt)) return fail(Q4Q8_ERR_UNSUPPORTED, "attn_prefill: dtype %d not F16/BF16", dt);

@@ -23,6 +23,7 @@
 //                     deterministic (no atomics).
 #include "q4q8_dev.h"
 #include "q4q8_internal.h"
+#include "moe_route.h"
 #include "qgemm_core.h"   // static_for, x_slot, kOOB
 
 #include <math.h>
@@ -38,56 +39,6 @@ constexpr int kSortWaves = 16;
 // ---------------------------------------------------------------------------
 // Route: ids[t, j], gates[t, j]
 // ---------------------------------------------------------------------------
-
-// (v, i) ranks before (bv, bi): larger value, then lower expert id.
-__device__ __forceinline__ bool route_before(float v, int i, float bv, int bi) {
-  return v > bv || (v == bv && i < bi);
-}
-
-// Top-k of token t by one wave.  NS: 64-expert slots per lane (E <= 64 NS).
-// Branch-free: out-of-range and taken experts compare as never better.
-template <int NS>
-__device__ __forceinline__ void topk_token(const float* __restrict__ logits, int t, int E, int topk, int lane,
-                                           int32_t* __restrict__ ids, float* __restrict__ gates) {
-  // Lane holds experts lane + 64 i.  NaN ranks as -inf.
-  const __amdgpu_buffer_rsrc_t rs = uniform_rsrc(logits + (int64_t)t * E, E * 4);
-  float v[NS];
-#pragma unroll
-  for (int i = 0; i < NS; ++i) {
-    const float x = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, (lane + 64 * i) * 4, 0, 0));
-    v[i] = (lane + 64 * i < E && x == x) ? x : -INFINITY;
-  }
-  uint32_t live = 0;   // bit i: expert lane + 64 i exists and is not taken yet
-#pragma unroll
-  for (int i = 0; i < NS; ++i) live |= (lane + 64 * i < E ? 1u : 0u) << i;
-  float v0 = 0.0f, my_exp = 0.0f, sum = 0.0f;
-  for (int j = 0; j < topk; ++j) {
-    float bv = -INFINITY;
-    int bi = 0x7fffffff;
-#pragma unroll
-    for (int i = 0; i < NS; ++i) {
-      const bool better = ((live >> i) & 1u) && route_before(v[i], lane + 64 * i, bv, bi);
-      bv = better ? v[i] : bv;
-      bi = better ? lane + 64 * i : bi;
-    }
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) {
-      const float ov = __shfl_xor(bv, off);
-      const int oi = __shfl_xor(bi, off);
-      const bool better = route_before(ov, oi, bv, bi);
-      bv = better ? ov : bv;
-      bi = better ? oi : bi;
-    }
-    // Every lane now holds the winner; its owner marks it taken.
-    live &= ~(((bi & 63) == lane ? 1u : 0u) << (bi >> 6));
-    v0 = j == 0 ? bv : v0;
-    const float ex = expf(bv - v0);
-    sum += ex;
-    my_exp = lane == j ? ex : my_exp;
-    if (lane == 0) ids[(int64_t)t * topk + j] = bi;
-  }
-  if (lane < topk) gates[(int64_t)t * topk + lane] = my_exp / sum;
-}
 
 template <int NS>
 __global__ __launch_bounds__(256) void moe_topk_kernel(const float* __restrict__ logits, int T, int E, int topk,
@@ -558,6 +509,17 @@ size_t moe_workspace_bytes(int fmt, int T, int E, int topk, int H, int F) {
   (void)E;
   const size_t P = (size_t)T * topk;
   return round256((size_t)T * H * 2) + round256(P * F * 2) + round256(P * H * 2);
+}
+
+hipError_t launch_moe_decode_call(int fmt, int xdt, const void* Wg, const void* Wu, const void* Wd, int E, int H,
+                                  int F, const void* X, int T, int topk, const MoeRouteOut& ro, float* out,
+                                  void* h_out, void* ws, hipStream_t stream) {
+  const MoeWs w = moe_ws_layout(ws, T, topk, H, F);
+  uint16_t* h = h_out ? (uint16_t*)h_out : w.h16;
+  if (!launch_moe_decode_routed(fmt, xdt, Wg, Wu, Wd, E, H, F, X, T, topk, ro, h, w.y16, out, stream))
+    moe_combine_kernel<<<dim3((unsigned)((H / 8 + 255) / 256), (unsigned)T), dim3(256), 0, stream>>>(
+        w.y16, ro.gates, T, topk, H, out);
+  return hipGetLastError();
 }
 
 hipError_t launch_moe_qgemm(int fmt, int xdt, const void* Wg, const void* Wu, const void* Wd, int E, int H, int F,

@@ -30,6 +30,7 @@
 // K-shares are reduced in a fixed order through LDS: results are bitwise
 // reproducible.
 #include "gemv_core.h"
+#include "moe_route.h"
 #include "q4q8_internal.h"
 
 #include <algorithm>
@@ -52,6 +53,14 @@ struct MoeDecArgs {
   int32_t T;
   int32_t groups;            // workgroups per sorted position
   int32_t ksh;               // K-shares per matrix, a power of 2
+  // Routed gate/up only: the router logits [T, E], and where workgroup 0
+  // stores the routing it derives (the routing step's five outputs).
+  const float* logits;
+  int32_t* r_ids;
+  float* r_gates;
+  int32_t* r_counts;
+  int32_t* r_offsets;
+  int32_t* r_sorted;
 };
 
 constexpr int kDecXSlack = 512;
@@ -59,37 +68,89 @@ constexpr int kDecMaxExperts = 1024;
 constexpr int kDecMaxTopk = 16;            // the route's top-k limit
 
 // SRC: dtype of the rows in memory (kF16 or kBF16); the operands are fp16.
-template <int FMT, int SRC, int MODE, int NI, int WAVES, int P>
+// RNS > 0 (gate/up only): the routing is derived in the kernel from the
+// logits instead of read from the routing step's outputs, RNS 64-expert slots
+// per lane (E <= 64 RNS).  Every workgroup derives it (T <= 8 tokens: one
+// wave per token, then the pairs' stable order by (expert, pair id));
+// workgroup 0 also stores it.
+template <int FMT, int SRC, int MODE, int NI, int WAVES, int P, int RNS>
 __global__ __launch_bounds__(WAVES * 64) void moe_gemv_kernel(const MoeDecArgs a) {
   typedef typename Op<kF16>::vec vec;
   typedef GemvStage<FMT> Stage;
   constexpr int REC = Fmt<FMT>::kRecBytes;
   extern __shared__ __attribute__((aligned(16))) uint16_t xs[];
+  constexpr bool ROUTED = RNS > 0;
+  static_assert(!ROUTED || (MODE == kDecGateUp && WAVES >= kMoeDecodeMaxTokens && WAVES * 64 >= 128),
+                "routed form: gate/up, a wave per token, a thread per pair");
 
   const int pos = blockIdx.x / a.groups;
   const int grp = blockIdx.x - pos * a.groups;
   const int tid = threadIdx.x;
-  // One round trip for the routing data: offsets into LDS, and the pair ids
-  // of positions pos .. pos + 7 (this workgroup's rows if it leads).
-  __shared__ int32_t s_off[kDecMaxExperts + 1];
   __shared__ int32_t s_pair[kMoeDecodeMaxTokens];
-  for (int i = tid; i <= a.E; i += WAVES * 64) s_off[i] = a.offsets[i];
-  if (tid < kMoeDecodeMaxTokens && pos + tid < a.npos)
-    s_pair[tid] = min(max(a.sorted_pairs[pos + tid], 0), a.npos - 1);   // clamped like the prefill path
-  __syncthreads();
-  // Expert owning sorted position pos: the largest e with offsets[e] <= pos.
-  int lo = 0, hi = a.E;
-  while (hi - lo > 1) {
-    const int mid = (lo + hi) >> 1;
-    if (s_off[mid] <= pos) lo = mid;
-    else hi = mid;
+  int e, r0, M;
+  if constexpr (ROUTED) {
+    __shared__ int32_t s_ids[kMoeDecodeMaxTokens * kDecMaxTopk];
+    __shared__ float s_gates[kMoeDecodeMaxTokens * kDecMaxTopk];
+    __shared__ int32_t s_sorted[kMoeDecodeMaxTokens * kDecMaxTopk];
+    const int npos = a.npos;
+    if ((tid >> 6) < a.T) topk_token<ROUTED ? RNS : 1>(a.logits, tid >> 6, a.E, a.topk, tid & 63, s_ids, s_gates);
+    __syncthreads();
+    if (tid < npos) {   // rank of pair tid in the stable order by (expert, pair id)
+      const int ep = s_ids[tid];
+      int rank = 0;
+      for (int q = 0; q < npos; ++q) rank += (s_ids[q] < ep || (s_ids[q] == ep && q < tid)) ? 1 : 0;
+      s_sorted[rank] = tid;
+    }
+    __syncthreads();
+    if (blockIdx.x == 0) {
+      for (int p = tid; p < npos; p += WAVES * 64) {
+        a.r_ids[p] = s_ids[p];
+        a.r_gates[p] = s_gates[p];
+        a.r_sorted[p] = s_sorted[p];
+      }
+      for (int x = tid; x <= a.E; x += WAVES * 64) {
+        int below = 0, same = 0;
+        for (int q = 0; q < npos; ++q) {
+          below += s_ids[q] < x ? 1 : 0;
+          same += s_ids[q] == x ? 1 : 0;
+        }
+        a.r_offsets[x] = below;
+        if (x < a.E) a.r_counts[x] = same;
+      }
+    }
+    e = s_ids[s_sorted[pos]];
+    int below = 0, same = 0;
+    for (int q = 0; q < npos; ++q) {
+      below += s_ids[q] < e ? 1 : 0;
+      same += s_ids[q] == e ? 1 : 0;
+    }
+    r0 = below;
+    if (r0 != pos) return;                    // not the expert's first position (uniform)
+    M = min(same, a.T);                       // a token picks an expert at most once
+    if (tid < kMoeDecodeMaxTokens && pos + tid < npos) s_pair[tid] = s_sorted[pos + tid];
+    __syncthreads();
+  } else {
+    // One round trip for the routing data: offsets into LDS, and the pair ids
+    // of positions pos .. pos + 7 (this workgroup's rows if it leads).
+    __shared__ int32_t s_off[kDecMaxExperts + 1];
+    for (int i = tid; i <= a.E; i += WAVES * 64) s_off[i] = a.offsets[i];
+    if (tid < kMoeDecodeMaxTokens && pos + tid < a.npos)
+      s_pair[tid] = min(max(a.sorted_pairs[pos + tid], 0), a.npos - 1);   // clamped like the prefill path
+    __syncthreads();
+    // Expert owning sorted position pos: the largest e with offsets[e] <= pos.
+    int lo = 0, hi = a.E;
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (s_off[mid] <= pos) lo = mid;
+      else hi = mid;
+    }
+    e = lo;
+    r0 = s_off[e];
+    if (r0 != pos) return;                    // not the expert's first position
+    // The expert's rows: 1..T for routing from q4q8_moe_route (a token picks
+    // an expert at most once); clamped so malformed routing stays in bounds.
+    M = max(1, min(min(s_off[e + 1] - r0, a.T), a.npos - r0));
   }
-  const int e = lo;
-  const int r0 = s_off[e];
-  if (r0 != pos) return;                      // not the expert's first position
-  // The expert's rows: 1..T for routing from q4q8_moe_route (a token picks
-  // an expert at most once); clamped so malformed routing stays in bounds.
-  const int M = max(1, min(min(s_off[e + 1] - r0, a.T), a.npos - r0));
 
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -339,7 +400,7 @@ int dec_ksh(int nchunks, int mats, int64_t tile_waves) {
   return ksh;
 }
 
-template <int FMT, int SRC, int MODE>
+template <int FMT, int SRC, int MODE, int RNS = 0>
 void launch_dec(MoeDecArgs a, int T, int npos, hipStream_t s) {
   const int mats = MODE == kDecGateUp ? 2 : 1;
   const int64_t experts = std::min(npos, a.E);
@@ -349,9 +410,9 @@ void launch_dec(MoeDecArgs a, int T, int npos, hipStream_t s) {
   const dim3 grid((unsigned)(npos * a.groups)), block(kDecWaves * 64);
   const size_t lds = (size_t)T * (a.K + 8) * 2 + kDecXSlack;
   if (T > 4)
-    moe_gemv_kernel<FMT, SRC, MODE, 2, kDecWaves, kDecRing><<<grid, block, lds, s>>>(a);
+    moe_gemv_kernel<FMT, SRC, MODE, 2, kDecWaves, kDecRing, RNS><<<grid, block, lds, s>>>(a);
   else
-    moe_gemv_kernel<FMT, SRC, MODE, 1, kDecWaves, kDecRing><<<grid, block, lds, s>>>(a);
+    moe_gemv_kernel<FMT, SRC, MODE, 1, kDecWaves, kDecRing, RNS><<<grid, block, lds, s>>>(a);
 }
 
 // The fused down + combine kernel: topk K-share groups of KQ waves in at most
@@ -366,12 +427,25 @@ bool down_combine_fits(int topk, int F) {
   return topk >= 1 && topk <= kDecMaxTopk && (int64_t)topk * (F + 8) * 2 + kDecXSlack <= 52 * 1024;
 }
 
+// ro: null, or the routed form (the gate/up kernel derives the routing from
+// ro->logits and stores it in ro's arrays, which the later kernels read).
 template <int FMT>
 bool launch_dec_fmt(int xdt, const void* Wg, const void* Wu, const void* Wd, int E, int H, int F, const void* X,
                     int T, int topk, const float* gates, const int32_t* offsets, const int32_t* sorted_pairs,
-                    uint16_t* h, uint16_t* y16, float* out, hipStream_t s) {
+                    uint16_t* h, uint16_t* y16, float* out, hipStream_t s, const MoeRouteOut* ro) {
   const int npos = T * topk;
-  MoeDecArgs a;
+  MoeDecArgs a = {};
+  if (ro) {
+    a.logits = ro->logits;
+    a.r_ids = ro->ids;
+    a.r_gates = ro->gates;
+    a.r_counts = ro->counts;
+    a.r_offsets = ro->offsets;
+    a.r_sorted = ro->sorted_pairs;
+    gates = ro->gates;
+    offsets = ro->offsets;
+    sorted_pairs = ro->sorted_pairs;
+  }
   a.offsets = offsets;
   a.sorted_pairs = sorted_pairs;
   a.topk = topk;
@@ -387,8 +461,18 @@ bool launch_dec_fmt(int xdt, const void* Wg, const void* Wu, const void* Wd, int
   a.out = h;
   a.N = F;
   a.K = H;
-  if (xdt == kF16) launch_dec<FMT, kF16, kDecGateUp>(a, T, npos, s);
-  else launch_dec<FMT, kBF16, kDecGateUp>(a, T, npos, s);
+  if (ro) {   // 2 expert slots a lane up to 128 experts, else 16 (up to 1024)
+    if (xdt == kF16) {
+      if (E <= 128) launch_dec<FMT, kF16, kDecGateUp, 2>(a, T, npos, s);
+      else launch_dec<FMT, kF16, kDecGateUp, 16>(a, T, npos, s);
+    } else {
+      if (E <= 128) launch_dec<FMT, kBF16, kDecGateUp, 2>(a, T, npos, s);
+      else launch_dec<FMT, kBF16, kDecGateUp, 16>(a, T, npos, s);
+    }
+  } else {
+    if (xdt == kF16) launch_dec<FMT, kF16, kDecGateUp>(a, T, npos, s);
+    else launch_dec<FMT, kBF16, kDecGateUp>(a, T, npos, s);
+  }
   // down: [H, F] per expert, x = the h rows.
   const int64_t dbytes = (int64_t)(H / kTileRows) * (F / kChunkK) * Fmt<FMT>::kRecBytes;
   if (T <= kDcMaxTokens && down_combine_fits(topk, F)) {
@@ -442,8 +526,19 @@ bool launch_moe_decode(int fmt, int xdt, const void* Wg, const void* Wu, const v
                        const int32_t* sorted_pairs, uint16_t* h, uint16_t* y16, float* out, hipStream_t s) {
   if (fmt == kQ4_0)
     return launch_dec_fmt<kQ4_0>(xdt, Wg, Wu, Wd, E, H, F, X, T, topk, gates, offsets, sorted_pairs, h, y16, out,
-                                 s);
-  return launch_dec_fmt<kQ8_0>(xdt, Wg, Wu, Wd, E, H, F, X, T, topk, gates, offsets, sorted_pairs, h, y16, out, s);
+                                 s, nullptr);
+  return launch_dec_fmt<kQ8_0>(xdt, Wg, Wu, Wd, E, H, F, X, T, topk, gates, offsets, sorted_pairs, h, y16, out, s,
+                               nullptr);
+}
+
+bool launch_moe_decode_routed(int fmt, int xdt, const void* Wg, const void* Wu, const void* Wd, int E, int H, int F,
+                              const void* X, int T, int topk, const MoeRouteOut& ro, uint16_t* h, uint16_t* y16,
+                              float* out, hipStream_t s) {
+  if (fmt == kQ4_0)
+    return launch_dec_fmt<kQ4_0>(xdt, Wg, Wu, Wd, E, H, F, X, T, topk, nullptr, nullptr, nullptr, h, y16, out, s,
+                                 &ro);
+  return launch_dec_fmt<kQ8_0>(xdt, Wg, Wu, Wd, E, H, F, X, T, topk, nullptr, nullptr, nullptr, h, y16, out, s,
+                               &ro);
 }
 
 }  // namespace q4q8

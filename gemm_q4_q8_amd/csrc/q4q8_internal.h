@@ -84,6 +84,23 @@ bool launch_moe_decode(int fmt, int xdt, const void* Wg, const void* Wu, const v
                        const void* X, int T, int topk, const float* gates, const int32_t* offsets,
                        const int32_t* sorted_pairs, uint16_t* h, uint16_t* y16, float* out, hipStream_t s);
 
+// The routed decode call: the gate/up kernel derives the routing from the
+// logits (as launch_moe_route would) and stores it in these arrays.
+struct MoeRouteOut {
+  const float* logits;
+  int32_t* ids;
+  float* gates;
+  int32_t* counts;
+  int32_t* offsets;
+  int32_t* sorted_pairs;
+};
+bool launch_moe_decode_routed(int fmt, int xdt, const void* Wg, const void* Wu, const void* Wd, int E, int H, int F,
+                              const void* X, int T, int topk, const MoeRouteOut& ro, uint16_t* h, uint16_t* y16,
+                              float* out, hipStream_t s);
+hipError_t launch_moe_decode_call(int fmt, int xdt, const void* Wg, const void* Wu, const void* Wd, int E, int H,
+                                  int F, const void* X, int T, int topk, const MoeRouteOut& ro, float* out,
+                                  void* h_out, void* ws, hipStream_t s);
+
 hipError_t launch_moe_qgemm(int fmt, int xdt, const void* Wg, const void* Wu, const void* Wd, int E, int H, int F,
                             const void* X, int T, int topk, const float* gates, const int32_t* offsets,
                             const int32_t* sorted_pairs, float* out, void* h_out, void* ws, hipStream_t stream);

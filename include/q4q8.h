@@ -324,6 +324,26 @@ int q4q8_moe_qgemm(int fmt, const void* Wg, const void* Wu, const void* Wd,
                    float* out, void* h_out, void* ws, size_t ws_bytes,
                    void* stream);
 
+/* MoE decode in one call: q4q8_moe_route followed by q4q8_moe_qgemm for a
+ * few tokens, with the routing derived inside the first expert kernel
+ * instead of by a kernel of its own (one launch fewer on the short decode
+ * step; review, "Method": decode on the GEMV kernels).
+ *   logits:  device fp32 [T, E].
+ *   ids, gates, counts, offsets, sorted_pairs: outputs, exactly as
+ *            q4q8_moe_route defines them (same bits), 4-byte aligned.
+ *   Wg, Wu, Wd, X, xdt, out, h_out, ws: as q4q8_moe_qgemm (ws of
+ *            q4q8_moe_workspace(fmt, T, E, topk, H, F) bytes).
+ * out and h_out equal those of q4q8_moe_route + q4q8_moe_qgemm bit for bit.
+ * Limits: the decode path only -- T <= 8 and T * (max(H, F) + 8) * 2 + 512
+ * <= 52 KB, else Q4Q8_ERR_UNSUPPORTED; otherwise as q4q8_moe_route and
+ * q4q8_moe_qgemm. */
+int q4q8_moe_decode(int fmt, const void* Wg, const void* Wu, const void* Wd,
+                    int E, int H, int F, const float* logits, const void* X,
+                    int xdt, int T, int topk, int32_t* ids, float* gates,
+                    int32_t* counts, int32_t* offsets, int32_t* sorted_pairs,
+                    float* out, void* h_out, void* ws, size_t ws_bytes,
+                    void* stream);
+
 /* ------------------------------------------------------------------------ */
 /* Prefill attention (technical summary, "Methodologie", prefill            */
 /* optimisation: tiled attention with an online softmax, O(n) memory;       */

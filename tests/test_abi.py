@@ -265,6 +265,25 @@ def test_moe_validation(q):
     assert L.q4q8_moe_qgemm(*a) == -4
 
 
+def test_moe_decode_validation(q):
+    L = q.lib()
+    nws = q.moe_workspace(1, 4, 128, 8, 2048, 768)
+    v = lambda i: _vp(0x1000 * (i + 1))
+    # fmt, Wg, Wu, Wd, E, H, F, logits, X, xdt, T, topk, ids, gates, counts, offsets, sorted, out, h_out, ws, bytes, s
+    args = [1, v(0), v(1), v(2), 128, 2048, 768, v(3), v(4), 2, 4, 8, v(5), v(6), v(7), v(8), v(9), v(10), None,
+            _vp(0x100000), nws, None]
+    for i, val, want in [(0, 3, -2), (9, 3, -2), (1, None, -1), (7, None, -1), (12, None, -1), (10, 0, -1),
+                         (11, 129, -1), (11, 17, -1), (4, 2048, -1), (5, 2000, -1), (10, 9, -2),
+                         (19, None, -3), (20, nws - 1, -3), (19, _vp(0x100010), -4), (13, _vp(0x6002), -4)]:
+        a = list(args)
+        a[i] = val
+        assert L.q4q8_moe_decode(*a) == want, (i, val)
+    a = list(args)
+    a[5], a[6] = 8192, 8192          # 4 rows of 8192 halfs exceed the decode path's LDS buffer
+    a[20] = q.moe_workspace(1, 4, 128, 8, 8192, 8192)
+    assert L.q4q8_moe_decode(*a) == -2
+
+
 def test_repack_validation(q):
     L = q.lib()
     assert L.q4q8_repack(1, _vp(), 16, 128, _vp(0x2000), 10, None) == -1

@@ -102,6 +102,26 @@ def test_graph_moe(q, T):
     _replays_match(step, [out, *route], _noise(q))
 
 
+@pytest.mark.parametrize("T", [2, 7])
+def test_graph_moe_decode_one_call(q, T):
+    """The one-call decode entry point (routing inside the first kernel),
+    with the fused down + combine (T = 2) and the separate combine (T = 7)."""
+    E, k, H, F = 16, 4, 256, 384
+    logits = torch.from_numpy(synth.router_logits(synth.rng_for(76, T), T, E)).to(dev())
+    mk = lambda i, n, kk: synth.q_weight(synth.rng_for(77, i), synth.Q4_0, n, kk)
+    Wg = torch.cat([q.repack(synth.Q4_0, bytes_tensor(mk(e, F, H).canon), F, H) for e in range(E)])
+    Wu = torch.cat([q.repack(synth.Q4_0, bytes_tensor(mk(100 + e, F, H).canon), F, H) for e in range(E)])
+    Wd = torch.cat([q.repack(synth.Q4_0, bytes_tensor(mk(200 + e, H, F).canon), H, F) for e in range(E)])
+    X = act_tensor(synth.activation(synth.rng_for(78, T), (T, H), synth.BF16))
+    route = (torch.empty((T, k), dtype=torch.int32, device=dev()), torch.empty((T, k), dtype=torch.float32, device=dev()),
+             torch.empty(E, dtype=torch.int32, device=dev()), torch.empty(E + 1, dtype=torch.int32, device=dev()),
+             torch.empty(T * k, dtype=torch.int32, device=dev()))
+    out = torch.empty((T, H), dtype=torch.float32, device=dev())
+    ws = torch.empty(q.moe_workspace(synth.Q4_0, T, E, k, H, F), dtype=torch.uint8, device=dev())
+    _replays_match(lambda: q.moe_decode(synth.Q4_0, Wg, Wu, Wd, E, H, F, logits, X, k, route=route, out=out, ws=ws),
+                   [out, *route], _noise(q))
+
+
 def test_graph_prefill_gemm(q):
     """The bf16 pre-pass and the GEMM in one graph."""
     M, N, K = 200, 640, 1024

@@ -161,6 +161,60 @@ def test_moe_decode_parity(q, fmt, xdt, T, E, k, H, F):
     _check_moe(fmt, logits, x, wg, wu, wd, k, H, F, got, f"moe decode fmt{fmt} T{T} E{E} k{k} H{H} F{F}")
 
 
+def _run_moe_decode(q, fmt, logits, x, wg, wu, wd, k, H, F):
+    """The one-call decode entry point, with every output read back."""
+    E = len(wg)
+    Wg, Wu, Wd = _stack(q, fmt, wg, F, H), _stack(q, fmt, wu, F, H), _stack(q, fmt, wd, H, F)
+    L = torch.from_numpy(logits).to(dev())
+    T = logits.shape[0]
+    h = torch.full((T * k, F), float("nan"), dtype=torch.bfloat16, device=dev())
+    route = (torch.full((T, k), -7, dtype=torch.int32, device=dev()), torch.full((T, k), -7.0, device=dev()),
+             torch.full((E,), -7, dtype=torch.int32, device=dev()), torch.full((E + 1,), -7, dtype=torch.int32, device=dev()),
+             torch.full((T * k,), -7, dtype=torch.int32, device=dev()))
+    out, (ids, gates, counts, offsets, sp) = q.moe_decode(fmt, Wg, Wu, Wd, E, H, F, L, act_tensor(x), k, route=route,
+                                                          h_out=h)
+    torch.cuda.synchronize()
+    return dict(ids=ids.cpu().numpy(), gates=gates.cpu().numpy(), counts=counts.cpu().numpy(),
+                offsets=offsets.cpu().numpy(), sp=sp.cpu().numpy(), h=values(h),
+                out=out.cpu().numpy().astype(np.float64))
+
+
+@pytest.mark.parametrize("fmt,xdt,T,E,k,H,F", DECODE_CASES)
+def test_moe_decode_one_call(q, fmt, xdt, T, E, k, H, F):
+    """q4q8_moe_decode (routing inside the first expert kernel) against the
+    oracle, and bit for bit against q4q8_moe_route + q4q8_moe_qgemm."""
+    seed = 120 + T + E + k
+    logits = synth.router_logits(synth.rng_for(seed, 0), T, E)
+    x = synth.activation(synth.rng_for(seed, 1), (T, H), xdt)
+    wg = [synth.q_weight(synth.rng_for(seed, 1000 + e), fmt, F, H) for e in range(E)]
+    wu = [synth.q_weight(synth.rng_for(seed, 2000 + e), fmt, F, H) for e in range(E)]
+    wd = [synth.q_weight(synth.rng_for(seed, 3000 + e), fmt, H, F) for e in range(E)]
+    one = _run_moe_decode(q, fmt, logits, x, wg, wu, wd, k, H, F)
+    two = _run_moe(q, fmt, logits, x, wg, wu, wd, k, H, F)
+    for key in ("ids", "gates", "offsets", "sp"):
+        assert np.array_equal(one[key], two[key]), key
+    assert np.array_equal(one["counts"], np.diff(two["offsets"]))
+    assert np.array_equal(one["h"], two["h"], equal_nan=False)
+    assert np.array_equal(one["out"], two["out"])
+    _check_moe(fmt, logits, x, wg, wu, wd, k, H, F, one, f"moe_decode fmt{fmt} T{T} E{E} k{k} H{H} F{F}")
+
+
+def test_moe_decode_one_call_full_shape(q):
+    """The MoE workload's experts at T = 1, 2, 8 through the one-call entry
+    point: bitwise equal to the two-call path, and against the oracle."""
+    cfg = synth.MOE
+    E, k, H, F = cfg["E"], cfg["topk"], cfg["H"], cfg["F"]
+    _, _, wg, wu, wd = synth.moe(T=1)
+    for T in (1, 2, 8):
+        logits = synth.router_logits(synth.rng_for(132, T), T, E)
+        x = synth.activation(synth.rng_for(133, T), (T, H), synth.BF16)
+        one = _run_moe_decode(q, synth.Q4_0, logits, x, wg, wu, wd, k, H, F)
+        two = _run_moe(q, synth.Q4_0, logits, x, wg, wu, wd, k, H, F)
+        assert np.array_equal(one["out"], two["out"]) and np.array_equal(one["h"], two["h"])
+        assert np.array_equal(one["gates"], two["gates"]) and np.array_equal(one["sp"], two["sp"])
+        _check_moe(synth.Q4_0, logits, x, wg, wu, wd, k, H, F, one, f"moe_decode full shape T{T}")
+
+
 def test_moe_decode_full_shape(q):
     """The MoE workload's experts (E 128, top-8, H 2048, F 768, Q4_0) with
     T = 1, 2, 8 decode tokens (every output), and T = 9 (the first prefill
