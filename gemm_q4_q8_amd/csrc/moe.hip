@@ -296,7 +296,7 @@ __global__ __launch_bounds__(WAVES * 64) void moe_stream_kernel(
   for (int i = 0; i < NW * NT * MT; ++i) acc[i] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
 
   // Products of chunk lcl of the loaded phase with one weight stage.
-  auto compute = [&](const WStage& s, int lcl) __attribute__((always_inline)) {
+  auto compute = [&](const WStage& s, int lcl, int mtn) __attribute__((always_inline)) {
     const uint16_t* xb = xs + lcl * BM * kChunkK;
 #pragma unroll
     for (int j = 0; j < kBlocksPerChunk; ++j) {
@@ -320,6 +320,7 @@ __global__ __launch_bounds__(WAVES * 64) void moe_stream_kernel(
         }
 #pragma unroll
       for (int i = 0; i < MT; ++i) {
+        if (i >= mtn) break;   // uniform: 16-row tiles past the expert's rows
         const int row = i * 16 + r;
         const half8_t a = *(const half8_t*)(xb + (row * 16 + ((4 * j + g) ^ r)) * 8);
 #pragma unroll
@@ -398,7 +399,7 @@ __global__ __launch_bounds__(WAVES * 64) void moe_stream_kernel(
           cur_rt = rt;
           cur_kph = kph;
         }
-        compute(ws[J], c - kph * cpp);
+        compute(ws[J], c - kph * cpp, __builtin_amdgcn_readfirstlane(min(MT, (cnt - rt * BM + 15) / 16)));
         if (c == nchunks - 1) epilogue(rt, gi);
         if (++c == nchunks) {
           c = 0;
