@@ -16,6 +16,18 @@ __device__ __forceinline__ bool route_before(float v, int i, float bv, int bi) {
   return v > bv || (v == bv && i < bi);
 }
 
+// One step of the wave's arg-max: each lane takes the better of its own
+// (value, id) and the one DPP pattern C brings from another lane of its row.
+template <int C>
+__device__ __forceinline__ void route_dpp_step(float& bv, int& bi) {
+  const float ov = __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, bv), C, 0xF, 0xF,
+                                                                         false));
+  const int oi = __builtin_amdgcn_update_dpp(0, bi, C, 0xF, 0xF, false);
+  const bool better = route_before(ov, oi, bv, bi);
+  bv = better ? ov : bv;
+  bi = better ? oi : bi;
+}
+
 // Top-k of token t by one wave.  NS: 64-expert slots per lane (E <= 64 NS).
 // Branch-free: out-of-range and taken experts compare as never better.
 template <int NS>
@@ -42,13 +54,28 @@ __device__ __forceinline__ void topk_token(const float* __restrict__ logits, int
       bv = better ? v[i] : bv;
       bi = better ? lane + 64 * i : bi;
     }
+    // Arg-max over the wave under the strict order route_before (unique, so
+    // the order of combination does not matter): within each 16-lane row by
+    // DPP (swap neighbours, swap pairs, mirror each half-row, mirror the row;
+    // a few cycles each, where a general lane shuffle is a round trip
+    // through the LDS crossbar), then over the four rows' lane 0.
+    route_dpp_step<0xB1>(bv, bi);    // quad_perm [1, 0, 3, 2]
+    route_dpp_step<0x4E>(bv, bi);    // quad_perm [2, 3, 0, 1]
+    route_dpp_step<0x141>(bv, bi);   // row_half_mirror
+    route_dpp_step<0x140>(bv, bi);   // row_mirror
+    {
+      float rv = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, bv), 0));
+      int ri = __builtin_amdgcn_readlane(bi, 0);
 #pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) {
-      const float ov = __shfl_xor(bv, off);
-      const int oi = __shfl_xor(bi, off);
-      const bool better = route_before(ov, oi, bv, bi);
-      bv = better ? ov : bv;
-      bi = better ? oi : bi;
+      for (int row = 1; row < 4; ++row) {
+        const float ov = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, bv), 16 * row));
+        const int oi = __builtin_amdgcn_readlane(bi, 16 * row);
+        const bool better = route_before(ov, oi, rv, ri);
+        rv = better ? ov : rv;
+        ri = better ? oi : ri;
+      }
+      bv = rv;
+      bi = ri;
     }
     // Every lane now holds the winner; its owner marks it taken.
     live &= ~(((bi & 63) == lane ? 1u : 0u) << (bi >> 6));
