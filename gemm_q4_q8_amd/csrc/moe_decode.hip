@@ -29,6 +29,10 @@
 // (measured at T = 8: gate/up 36.5 -> 19 us, down 20 -> 12 us).
 // K-shares are reduced in a fixed order through LDS: results are bitwise
 // reproducible.
+// Routed form (q4q8_moe_decode): the gate/up kernel derives the routing
+// itself from the logits (every workgroup: one wave per token's top-k, then
+// the pairs' stable order in LDS), so no routing kernel runs before it;
+// workgroup 0 stores the routing arrays the later kernels read.
 #include "gemv_core.h"
 #include "moe_route.h"
 #include "q4q8_internal.h"
