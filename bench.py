@@ -721,7 +721,7 @@ def moe_decode_workloads(q, torch, synth, quick: bool):
             nbytes += int((rt[2] > 0).sum().item()) * 3 * mat + T * H * 2 + T * H * 4
         per = nbytes / sets
         for name, step in (("route + moe_qgemm: route, GEMV path, combine", step_two),
-                           ("one call, moe_decode: routing inside the gate/up kernel", step_one)):
+                           ("one call, moe_decode: routing inside the gate/up kernel up to 4 tokens", step_one)):
             g = torch.cuda.CUDAGraph()
             with torch.cuda.graph(g):
                 for i in range(sets):

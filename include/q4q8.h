@@ -333,6 +333,9 @@ int q4q8_moe_qgemm(int fmt, const void* Wg, const void* Wu, const void* Wd,
  *            q4q8_moe_route defines them (same bits), 4-byte aligned.
  *   Wg, Wu, Wd, X, xdt, out, h_out, ws: as q4q8_moe_qgemm (ws of
  *            q4q8_moe_workspace(fmt, T, E, topk, H, F) bytes).
+ * Up to 4 tokens the routing runs inside the first expert kernel; past 4
+ * (where one wave per token in every workgroup costs more than a launch) the
+ * call runs the routing kernel first.
  * out and h_out equal those of q4q8_moe_route + q4q8_moe_qgemm bit for bit.
  * Limits: the decode path only -- T <= 8 and T * (max(H, F) + 8) * 2 + 512
  * <= 52 KB, else Q4Q8_ERR_UNSUPPORTED; otherwise as q4q8_moe_route and
