@@ -35,6 +35,7 @@ namespace q4q8 {
 constexpr int kRouteMaxE = 1024;
 constexpr int kRouteMaxK = 16;
 constexpr int kSortWaves = 16;
+constexpr int kRankSortMaxPairs = 32;
 
 // ---------------------------------------------------------------------------
 // Route: ids[t, j], gates[t, j]
@@ -126,19 +127,47 @@ __global__ __launch_bounds__(1024) void moe_sort_kernel(const int32_t* __restric
 }
 
 // A few tokens (T <= kSortWaves): top-k and sort in one workgroup, one
-// launch.  Wave t takes token t; the sort reads ids after the barrier, whose
-// workgroup-scope release/acquire makes every wave's writes visible (no
-// device-scope fence: it would write back the L2 for nothing).
+// launch.  Wave t takes token t.
 template <int NS>
 __global__ __launch_bounds__(1024) void moe_route_small_kernel(const float* __restrict__ logits, int T, int E,
                                                                int topk, int32_t* __restrict__ ids,
                                                                float* __restrict__ gates, int32_t* __restrict__ counts,
                                                                int32_t* __restrict__ offsets,
                                                                int32_t* __restrict__ sorted_pairs) {
-  const int w = threadIdx.x >> 6;
-  if (w < T) topk_token<NS>(logits, w, E, topk, threadIdx.x & 63, ids, gates);
+  const int tid = threadIdx.x, w = tid >> 6;
+  const int P = T * topk;
+  if (P > kRankSortMaxPairs) {   // uniform
+    if (w < T) topk_token<NS>(logits, w, E, topk, tid & 63, ids, gates);
+    __syncthreads();
+    sort_pairs(ids, P, E, counts, offsets, sorted_pairs);
+    return;
+  }
+  // Up to 32 pairs the routing stays in LDS: top-k per wave, then each
+  // pair's rank in the stable order by (expert, pair id) and each expert's
+  // count and offset by direct counting (no histogram passes; measured on
+  // MI355X, E 128 top-8: 1.0-1.3 us less per step at T = 1, 2, 1 us more at
+  // T = 8, where the counting loops grow with the pairs).
+  __shared__ int32_t s_ids[kRankSortMaxPairs];
+  __shared__ float s_gates[kRankSortMaxPairs];
+  if (w < T) topk_token<NS>(logits, w, E, topk, tid & 63, s_ids, s_gates);
   __syncthreads();
-  sort_pairs(ids, T * topk, E, counts, offsets, sorted_pairs);
+  if (tid < P) {
+    const int ep = s_ids[tid];
+    int rank = 0;
+    for (int q = 0; q < P; ++q) rank += (s_ids[q] < ep || (s_ids[q] == ep && q < tid)) ? 1 : 0;
+    ids[tid] = ep;
+    gates[tid] = s_gates[tid];
+    sorted_pairs[rank] = tid;
+  }
+  for (int x = tid; x <= E; x += 1024) {
+    int below = 0, same = 0;
+    for (int q = 0; q < P; ++q) {
+      below += s_ids[q] < x ? 1 : 0;
+      same += s_ids[q] == x ? 1 : 0;
+    }
+    offsets[x] = below;
+    if (x < E) counts[x] = same;
+  }
 }
 
 hipError_t launch_moe_route(const float* logits, int T, int E, int topk, int32_t* ids, float* gates,
