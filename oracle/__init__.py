@@ -26,8 +26,8 @@ the pages; the oracle takes these readings:
 * FP16: plain fp16 weights, row-major little-endian (the pages' format list
   runs up to FP16; technical summary abstract).
 * Routing: per token, the top-k experts by logit, descending, equal logits
-  broken towards the lower expert id; gates = softmax over the k selected
-  logits.
+  broken towards the lower expert id, NaN ranked as -inf; gates = softmax
+  over the k selected logits.
 * Sorting: pairs p = t*k + j are ordered by (expert, p); counts and offsets are
   the histogram and its exclusive scan.
 * Attention (prefill): softmax(scale q k^T) v per head, causal, GQA by
@@ -181,8 +181,14 @@ def moe_route(logits: np.ndarray, topk: int):
     Order: descending logit, ties to the lower expert id.  The comparison is
     on the fp32 values themselves (exact in fp64).  Gates are the softmax over
     the k selected logits, taken relative to the largest one.
+
+    A NaN logit ranks as -inf (reading for degenerate router rows: the pages
+    define no routing; a NaN expert is then chosen only after every finite
+    one, among the -inf entries by expert id, and its gate is 0).  A row whose
+    selected logits are all -inf has no softmax; its gates come out NaN.
     """
     lg = np.asarray(logits, dtype=np.float32).astype(np.float64)
+    lg = np.where(np.isnan(lg), -np.inf, lg)
     T, E = lg.shape
     if not (1 <= topk <= E):
         raise ValueError("topk out of range")

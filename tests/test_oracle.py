@@ -240,6 +240,37 @@ def test_route_matches_brute_force_with_ties():
     assert list(ids[3][:2]) == [5, 4]
 
 
+def test_route_nan_ranks_as_minus_infinity():
+    """Reading for degenerate router rows: a NaN logit ranks as -inf (after
+    every finite logit, among the -inf entries by expert id) and gets gate 0."""
+    lg = np.array([[1.0, np.nan, 0.5, -np.inf, -np.inf],
+                   [np.nan, 0.0, 0.5, np.nan, 2.0],
+                   [-np.inf, np.nan, 3.0, -np.inf, 3.0]], dtype=np.float32)
+    ids, g = oracle.moe_route(lg, 4)
+    assert ids.tolist() == [[0, 2, 1, 3], [4, 2, 1, 0], [2, 4, 0, 1]]
+    e = math.exp(-0.5)
+    assert np.allclose(g[0], [1 / (1 + e), e / (1 + e), 0.0, 0.0], rtol=1e-15, atol=0)
+    assert np.all(np.isfinite(g)) and np.allclose(g.sum(axis=1), 1.0, rtol=0, atol=1e-15)
+    assert g[2].tolist() == [0.5, 0.5, 0.0, 0.0]
+    # Brute force on random rows mixing NaN, -inf and exact ties: sort key
+    # (class, -value, id) with class 0 for numbers above -inf, 1 for -inf and NaN.
+    rng = synth.rng_for(24, 0)
+    lg = rng.integers(-2, 3, size=(300, 9)).astype(np.float32)
+    lg[rng.random(lg.shape) < 0.2] = np.nan
+    lg[rng.random(lg.shape) < 0.2] = -np.inf
+    lg[:, 0] = np.where(np.all(~np.isfinite(lg), axis=1), 1.0, lg[:, 0])   # keep one finite logit
+    for k in (1, 4, 9):
+        ids, g = oracle.moe_route(lg, k)
+        for t, row in enumerate(lg):
+            key = lambda i: (1, 0.0, i) if (np.isnan(row[i]) or row[i] == -np.inf) else (0, -float(row[i]), i)
+            want = sorted(range(9), key=key)[:k]
+            assert ids[t].tolist() == want
+            fin = [float(row[i]) for i in want if np.isfinite(row[i])]
+            m = max(fin)
+            ex = [math.exp(float(row[i]) - m) if np.isfinite(row[i]) else 0.0 for i in want]
+            assert np.allclose(g[t], np.array(ex) / math.fsum(ex), rtol=1e-15, atol=0)
+
+
 def test_route_gates_are_a_softmax():
     lg = synth.router_logits(synth.rng_for(22, 0), 64, 128)
     ids, g = oracle.moe_route(lg, 8)
