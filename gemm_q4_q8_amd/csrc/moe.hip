@@ -224,8 +224,8 @@ template <int FMT, int MODE, int NT, int P, int WAVES, int KP>
 __global__ __launch_bounds__(WAVES * 64) void moe_stream_kernel(
     const uint8_t* __restrict__ W0, const uint8_t* __restrict__ W1, int64_t wstride, int N, int K,
     const uint16_t* __restrict__ src, int src_rows, int T, int topk, int Ptot,
-    const int32_t* __restrict__ offsets, const int32_t* __restrict__ sorted_pairs, uint16_t* __restrict__ out16,
-    uint16_t* __restrict__ h_out, int tiles_per_wave, int groups) {
+    const int32_t* __restrict__ offsets, const int32_t* __restrict__ sorted_pairs, const int32_t* __restrict__ xexp,
+    uint16_t* __restrict__ out16, uint16_t* __restrict__ h_out, int tiles_per_wave, int groups) {
   constexpr int NW = MODE == kGateUp ? 2 : 1;
   constexpr int MT = kStreamBM / 16, BM = kStreamBM;
   constexpr int REC = Fmt<FMT>::kRecBytes;
@@ -236,8 +236,10 @@ __global__ __launch_bounds__(WAVES * 64) void moe_stream_kernel(
   __shared__ __attribute__((aligned(1024))) uint16_t xs[BM * KP];
 
   const int e = blockIdx.y;
-  const int seg = offsets[e];
-  const int cnt = offsets[e + 1] - seg;
+  // Clamped to the Ptot pairs, so malformed offsets cannot send the row
+  // stores past h / y (the decode path clamps the same way).
+  const int seg = min(max(offsets[e], 0), Ptot);
+  const int cnt = min(offsets[e + 1], Ptot) - seg;
   if (cnt <= 0) return;   // uniform over the workgroup
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -376,14 +378,22 @@ __global__ __launch_bounds__(WAVES * 64) void moe_stream_kernel(
           const int row = rt * BM + i * 16 + r;
           if (row < cnt) {
             if constexpr (MODE == kGateUp) {
+              // The token's row was scaled by 2^-ex: z = 2^ex acc exactly.  h
+              // is formed at its true scale and rounded to bf16 (its storage
+              // precision); the down product's fp16 copy carries 2^-2ex
+              // (|h| <= |z_gate| |z_up|), undone by the combine.
+              const int ex = xexp[min(max(sorted_pairs[seg + row], 0), Ptot - 1) / topk];
               const float4_t zg = acc[(0 * NT + t) * MT + i], zu = acc[(1 * NT + t) * MT + i];
               uint32_t hf[2], hb[2];
 #pragma unroll
               for (int k2 = 0; k2 < 2; ++k2) {
-                const __bf16 b0 = (__bf16)(silu_f32(zg[2 * k2]) * zu[2 * k2]);
-                const __bf16 b1 = (__bf16)(silu_f32(zg[2 * k2 + 1]) * zu[2 * k2 + 1]);
-                hf[k2] = (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)(float)b0) |
-                         ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)(float)b1) << 16);
+                const __bf16 b0 = (__bf16)(silu_f32(__builtin_ldexpf(zg[2 * k2], ex)) *
+                                           __builtin_ldexpf(zu[2 * k2], ex));
+                const __bf16 b1 = (__bf16)(silu_f32(__builtin_ldexpf(zg[2 * k2 + 1], ex)) *
+                                           __builtin_ldexpf(zu[2 * k2 + 1], ex));
+                hf[k2] = (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)__builtin_ldexpf((float)b0, -2 * ex)) |
+                         ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)__builtin_ldexpf((float)b1, -2 * ex))
+                          << 16);
                 hb[k2] = (uint32_t)__builtin_bit_cast(uint16_t, b0) | ((uint32_t)__builtin_bit_cast(uint16_t, b1) << 16);
               }
               const int64_t idx = (int64_t)(seg + row) * N + n0;
@@ -443,9 +453,11 @@ __global__ __launch_bounds__(WAVES * 64) void moe_stream_kernel(
   }
 }
 
-// out[t, n] = sum_j gates[t, j] y16[t k + j, n]; 8 columns per thread.
+// out[t, n] = 2^(2 xexp[t]) sum_j gates[t, j] y16[t k + j, n] (y16 carries
+// the token's 2^-2xexp scale); 8 columns per thread.
 __global__ __launch_bounds__(256) void moe_combine_kernel(const uint16_t* __restrict__ y16,
-                                                          const float* __restrict__ gates, int T, int topk, int H,
+                                                          const float* __restrict__ gates,
+                                                          const int32_t* __restrict__ xexp, int T, int topk, int H,
                                                           float* __restrict__ out) {
   const int c8 = blockIdx.x * 256 + threadIdx.x;
   const int t = blockIdx.y;
@@ -462,6 +474,9 @@ __global__ __launch_bounds__(256) void moe_combine_kernel(const uint16_t* __rest
       s[2 * q + 1] += gj * (float)h[1];
     }
   }
+  const int ex2 = 2 * xexp[t];
+#pragma unroll
+  for (int q = 0; q < 8; ++q) s[q] = __builtin_ldexpf(s[q], ex2);
   float4_t* o = (float4_t*)(out + (int64_t)t * H + c8 * 8);
   o[0] = float4_t{s[0], s[1], s[2], s[3]};
   o[1] = float4_t{s[4], s[5], s[6], s[7]};
@@ -486,6 +501,7 @@ struct MoeWs {
   uint16_t* x16;
   uint16_t* h16;
   uint16_t* y16;
+  int32_t* xexp;   // per token: its row was scaled by 2^-xexp
 };
 
 MoeWs moe_ws_layout(void* ws, int T, int topk, int H, int F) {
@@ -497,6 +513,8 @@ MoeWs moe_ws_layout(void* ws, int T, int topk, int H, int F) {
   w.h16 = (uint16_t*)b;
   b += round256(P * F * 2);
   w.y16 = (uint16_t*)b;
+  b += round256(P * H * 2);
+  w.xexp = (int32_t*)b;
   return w;
 }
 
@@ -522,15 +540,15 @@ void launch_experts(const void* Wg, const void* Wu, const void* Wd, int E, int H
   split(F / kTileRows, NTG, kMoeWaves, nwe, tpw, groups);
   moe_stream_kernel<FMT, kGateUp, NTG, PG, kMoeWaves, kMoeKP><<<dim3((unsigned)nwe, (unsigned)E),
                                                                  dim3(kMoeWaves * 64), 0, s>>>(
-      (const uint8_t*)Wg, (const uint8_t*)Wu, sg, F, H, x16, T, T, topk, P, offsets, sorted_pairs, w.h16,
+      (const uint8_t*)Wg, (const uint8_t*)Wu, sg, F, H, x16, T, T, topk, P, offsets, sorted_pairs, w.xexp, w.h16,
       (uint16_t*)h_out, tpw, groups);
   split(H / kTileRows, NTD, kMoeWaves, nwe, tpw, groups);
   moe_stream_kernel<FMT, kDown, NTD, PD, kMoeWaves, kMoeKP><<<dim3((unsigned)nwe, (unsigned)E),
                                                               dim3(kMoeWaves * 64), 0, s>>>(
-      (const uint8_t*)Wd, nullptr, sd, H, F, w.h16, P, T, topk, P, offsets, sorted_pairs, w.y16, nullptr, tpw,
-      groups);
-  moe_combine_kernel<<<dim3((unsigned)((H / 8 + 255) / 256), (unsigned)T), dim3(256), 0, s>>>(w.y16, gates, T, topk,
-                                                                                              H, out);
+      (const uint8_t*)Wd, nullptr, sd, H, F, w.h16, P, T, topk, P, offsets, sorted_pairs, w.xexp, w.y16, nullptr,
+      tpw, groups);
+  moe_combine_kernel<<<dim3((unsigned)((H / 8 + 255) / 256), (unsigned)T), dim3(256), 0, s>>>(w.y16, gates, w.xexp,
+                                                                                              T, topk, H, out);
 }
 }  // namespace
 
@@ -538,7 +556,7 @@ size_t moe_workspace_bytes(int fmt, int T, int E, int topk, int H, int F) {
   (void)fmt;
   (void)E;
   const size_t P = (size_t)T * topk;
-  return round256((size_t)T * H * 2) + round256(P * F * 2) + round256(P * H * 2);
+  return round256((size_t)T * H * 2) + round256(P * F * 2) + round256(P * H * 2) + round256((size_t)T * 4);
 }
 
 constexpr int kMoeRoutedMaxTokens = 4;
@@ -558,14 +576,14 @@ hipError_t launch_moe_decode_call(int fmt, int xdt, const void* Wg, const void* 
                                           ro.sorted_pairs, stream);
     if (e != hipSuccess) return e;
     if (!launch_moe_decode(fmt, xdt, Wg, Wu, Wd, E, H, F, X, T, topk, ro.gates, ro.offsets, ro.sorted_pairs, h,
-                           w.y16, out, stream))
+                           w.y16, w.xexp, out, stream))
       moe_combine_kernel<<<dim3((unsigned)((H / 8 + 255) / 256), (unsigned)T), dim3(256), 0, stream>>>(
-          w.y16, ro.gates, T, topk, H, out);
+          w.y16, ro.gates, w.xexp, T, topk, H, out);
     return hipGetLastError();
   }
-  if (!launch_moe_decode_routed(fmt, xdt, Wg, Wu, Wd, E, H, F, X, T, topk, ro, h, w.y16, out, stream))
+  if (!launch_moe_decode_routed(fmt, xdt, Wg, Wu, Wd, E, H, F, X, T, topk, ro, h, w.y16, w.xexp, out, stream))
     moe_combine_kernel<<<dim3((unsigned)((H / 8 + 255) / 256), (unsigned)T), dim3(256), 0, stream>>>(
-        w.y16, ro.gates, T, topk, H, out);
+        w.y16, ro.gates, w.xexp, T, topk, H, out);
   return hipGetLastError();
 }
 
@@ -576,18 +594,17 @@ hipError_t launch_moe_qgemm(int fmt, int xdt, const void* Wg, const void* Wu, co
   if (moe_decode_fits(T, H, F)) {
     // A few tokens: every expert product is a GEMV over the expert's weights.
     uint16_t* h = h_out ? (uint16_t*)h_out : w.h16;
-    if (!launch_moe_decode(fmt, xdt, Wg, Wu, Wd, E, H, F, X, T, topk, gates, offsets, sorted_pairs, h, w.y16, out,
-                           stream))
+    if (!launch_moe_decode(fmt, xdt, Wg, Wu, Wd, E, H, F, X, T, topk, gates, offsets, sorted_pairs, h, w.y16,
+                           w.xexp, out, stream))
       moe_combine_kernel<<<dim3((unsigned)((H / 8 + 255) / 256), (unsigned)T), dim3(256), 0, stream>>>(
-          w.y16, gates, T, topk, H, out);
+          w.y16, gates, w.xexp, T, topk, H, out);
     return hipGetLastError();
   }
-  const uint16_t* x16 = (const uint16_t*)X;
-  if (xdt == kBF16) {
-    const hipError_t e = launch_bf16_to_f16(X, H, w.x16, H, T, H, H, stream, LaunchEvents());
-    if (e != hipSuccess) return e;
-    x16 = w.x16;
-  }
+  // Both dtypes: each token row scaled by a power of two (its exponent in
+  // w.xexp), which also keeps h and y in the fp16 range.
+  const hipError_t e = launch_rowscale_f16(xdt, X, H, w.x16, H, T, H, H, w.xexp, stream, LaunchEvents());
+  if (e != hipSuccess) return e;
+  const uint16_t* x16 = w.x16;
   if (fmt == kQ4_0)
     launch_experts<kQ4_0>(Wg, Wu, Wd, E, H, F, x16, T, topk, gates, offsets, sorted_pairs, out, h_out, w, stream);
   else

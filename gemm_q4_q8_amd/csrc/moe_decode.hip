@@ -22,10 +22,10 @@
 //   * down: x = the expert's h rows (contiguous in sorted order), y rounded
 //     to fp16 per pair id, then the weighted combine kernel of the prefill
 //     path.
-// The rows are staged in LDS as fp16, bf16 sources converted on the way as
-// the prefill path's pre-pass does (exact for 2^-14 <= |x| < 65520, h
-// included): the fp16 operands take the Q4_0 unpack's two-instruction
-// fp16 form, where a bf16 operand would need a per-value integer conversion
+// The rows are staged in LDS as fp16, each token row scaled by a power of
+// two as the prefill path's pre-pass does (its largest magnitude in [4, 8);
+// h rows by the square of the token's factor, undone after the combine):
+// the fp16 operands take the Q4_0 unpack's two-instruction fp16 form, where a bf16 operand would need a per-value integer conversion
 // (measured at T = 8: gate/up 36.5 -> 19 us, down 20 -> 12 us).
 // K-shares are reduced in a fixed order through LDS: results are bitwise
 // reproducible.
@@ -57,6 +57,9 @@ struct MoeDecArgs {
   int32_t T;
   int32_t groups;            // workgroups per sorted position
   int32_t ksh;               // K-shares per matrix, a power of 2
+  // Per token: gate/up stores, down reads the power of two its row was
+  // scaled by (2^-xexp; h carries 2^-2 xexp into the down product).
+  int32_t* xexp;
   // Routed gate/up only: the router logits [T, E], and where workgroup 0
   // stores the routing it derives (the routing step's five outputs).
   const float* logits;
@@ -91,6 +94,9 @@ __global__ __launch_bounds__(WAVES * 64) void moe_gemv_kernel(const MoeDecArgs a
   const int grp = blockIdx.x - pos * a.groups;
   const int tid = threadIdx.x;
   __shared__ int32_t s_pair[kMoeDecodeMaxTokens];
+  __shared__ uint32_t s_rmax[kMoeDecodeMaxTokens];   // gate/up: magnitude bits of each row's largest |x|
+  __shared__ int32_t s_ex[kMoeDecodeMaxTokens];      // each row's exponent
+  if (tid < kMoeDecodeMaxTokens) s_rmax[tid] = 0;    // ordered by the routing's barriers below
   int e, r0, M;
   if constexpr (ROUTED) {
     __shared__ int32_t s_ids[kMoeDecodeMaxTokens * kDecMaxTopk];
@@ -180,7 +186,10 @@ __global__ __launch_bounds__(WAVES * 64) void moe_gemv_kernel(const MoeDecArgs a
       kGemvBufFlags);
 
   // Weight prefetch first (it does not depend on x), then the x rows into
-  // LDS: rows of K + 8 halfs, then kDecXSlack zero bytes.
+  // LDS as fp16: rows of K + 8 halfs, then kDecXSlack zero bytes.  Each row
+  // is scaled by a power of two, as the prefill path's pre-pass does: gate/up
+  // finds each token row's largest magnitude while staging it raw, then
+  // converts its own pieces in place; down takes the h rows' 2^-2 xexp.
   Stage st[P];
 #pragma unroll
   for (int p = 0; p < P; ++p) gemv_load<FMT>(st[p], wres, ks + p * KSH, lane, r);
@@ -190,18 +199,29 @@ __global__ __launch_bounds__(WAVES * 64) void moe_gemv_kernel(const MoeDecArgs a
     const int mm = i / per_row, k8 = i - mm * per_row;
     u32x4_t v = u32x4_t{0, 0, 0, 0};
     if (mm < M && k8 < K / 8) {
-      const int64_t row = MODE == kDecGateUp ? s_pair[mm] / a.topk : r0 + mm;
-      v = *(const u32x4_t*)(a.X + row * a.ldx + k8 * 8);
-      if constexpr (SRC == kBF16) {   // bf16 -> fp16, as the prefill pre-pass
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const uint32_t b = v[q];
-          v[q] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(__builtin_bit_cast(float, b << 16),
-                                                                        __builtin_bit_cast(float, b & 0xFFFF0000u)));
-        }
+      if constexpr (MODE == kDecGateUp) {
+        v = *(const u32x4_t*)(a.X + (int64_t)(s_pair[mm] / a.topk) * a.ldx + k8 * 8);
+        atomicMax(&s_rmax[mm], max_mag_bits8(v));
+      } else {
+        v = *(const u32x4_t*)(a.X + (int64_t)(r0 + mm) * a.ldx + k8 * 8);
+        v = f16x8_scaled<SRC>(v, -2 * a.xexp[s_pair[mm] / a.topk]);
       }
     }
     *(u32x4_t*)(xs + i * 8) = v;
+  }
+  if constexpr (MODE == kDecGateUp) {
+    __syncthreads();
+    if (tid < kMoeDecodeMaxTokens) {
+      const int ex = row_exponent<SRC>(s_rmax[tid]);
+      s_ex[tid] = ex;
+      if (grp == 0 && tid < M) a.xexp[s_pair[tid] / a.topk] = ex;   // the down kernel's and combine's copy
+    }
+    __syncthreads();
+    for (int i = tid; i < M * per_row; i += WAVES * 64) {   // the pieces this thread staged
+      const int mm = i / per_row;
+      if (i - mm * per_row < K / 8) *(u32x4_t*)(xs + i * 8) = f16x8_scaled<SRC>(*(const u32x4_t*)(xs + i * 8),
+                                                                               -s_ex[mm]);
+    }
   }
   __syncthreads();
   const uint16_t* xrow = xs + (mvalid ? m : 0) * (K + 8) + 8 * g;
@@ -242,10 +262,11 @@ __global__ __launch_bounds__(WAVES * 64) void moe_gemv_kernel(const MoeDecArgs a
     for (int i = 0; i < NI; ++i) {
       float v = red[wave][i][lane];
       for (int w = 1; w < KSH; ++w) v += red[wave + w][i][lane];
-      if (MODE == kDecGateUp) {
+      if (MODE == kDecGateUp) {   // z = 2^ex acc: h at its true scale
         float u = red[wave + KSH][i][lane];
         for (int w = 1; w < KSH; ++w) u += red[wave + KSH + w][i][lane];
-        v = silu_f32(v) * u;
+        const int ex = s_ex[min(4 * i + g, kMoeDecodeMaxTokens - 1)];
+        v = silu_f32(__builtin_ldexpf(v, ex)) * __builtin_ldexpf(u, ex);
       }
       acc[i] = v;
     }
@@ -283,6 +304,7 @@ struct MoeDcArgs {
   const float* gates;        // [T, topk]
   const int32_t* offsets;    // [E + 1]
   const int32_t* sorted_pairs;
+  const int32_t* xexp;       // [T]: token t's h rows carry 2^-2 xexp[t]
   float* out;                // [T, H]
   int32_t H, F, topk, E, npos, kq;   // kq: K-shares per slot (topk kq <= WAVES)
 };
@@ -336,18 +358,12 @@ __global__ __launch_bounds__(WAVES * 64) void moe_down_combine_kernel(const MoeD
   // then kDecXSlack zero bytes.
   const int per_row = F / 8 + 1;
   const int pieces = topk * per_row + kDecXSlack / 16;
+  const int ex = a.xexp[t];
   for (int i = tid; i < pieces; i += WAVES * 64) {
     const int jj = i / per_row, k8 = i - jj * per_row;
     u32x4_t v = u32x4_t{0, 0, 0, 0};
-    if (jj < topk && k8 < F / 8) {
-      v = *(const u32x4_t*)(a.h + (int64_t)s_pos[jj] * F + k8 * 8);
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const uint32_t b = v[q];
-        v[q] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(__builtin_bit_cast(float, b << 16),
-                                                                      __builtin_bit_cast(float, b & 0xFFFF0000u)));
-      }
-    }
+    if (jj < topk && k8 < F / 8) v = f16x8_scaled<kBF16>(*(const u32x4_t*)(a.h + (int64_t)s_pos[jj] * F + k8 * 8),
+                                                          -2 * ex);
     *(u32x4_t*)(xs + i * 8) = v;
   }
   __syncthreads();
@@ -387,7 +403,7 @@ __global__ __launch_bounds__(WAVES * 64) void moe_down_combine_kernel(const MoeD
     const float y = (float)(_Float16)v;               // y as the unfused path stores it
     sum += a.gates[(int64_t)t * topk + jj] * y;       // the combine kernel's order
   }
-  a.out[(int64_t)t * a.H + tile * kTileRows + r] = sum;
+  a.out[(int64_t)t * a.H + tile * kTileRows + r] = __builtin_ldexpf(sum, 2 * ex);
 }
 
 namespace {
@@ -436,9 +452,10 @@ bool down_combine_fits(int topk, int F) {
 template <int FMT>
 bool launch_dec_fmt(int xdt, const void* Wg, const void* Wu, const void* Wd, int E, int H, int F, const void* X,
                     int T, int topk, const float* gates, const int32_t* offsets, const int32_t* sorted_pairs,
-                    uint16_t* h, uint16_t* y16, float* out, hipStream_t s, const MoeRouteOut* ro) {
+                    uint16_t* h, uint16_t* y16, int32_t* xexp, float* out, hipStream_t s, const MoeRouteOut* ro) {
   const int npos = T * topk;
   MoeDecArgs a = {};
+  a.xexp = xexp;
   if (ro) {
     a.logits = ro->logits;
     a.r_ids = ro->ids;
@@ -489,6 +506,7 @@ bool launch_dec_fmt(int xdt, const void* Wg, const void* Wu, const void* Wd, int
     d.gates = gates;
     d.offsets = offsets;
     d.sorted_pairs = sorted_pairs;
+    d.xexp = xexp;
     d.out = out;
     d.H = H;
     d.F = F;
@@ -527,21 +545,22 @@ bool moe_decode_fits(int T, int H, int F) {
 
 bool launch_moe_decode(int fmt, int xdt, const void* Wg, const void* Wu, const void* Wd, int E, int H, int F,
                        const void* X, int T, int topk, const float* gates, const int32_t* offsets,
-                       const int32_t* sorted_pairs, uint16_t* h, uint16_t* y16, float* out, hipStream_t s) {
+                       const int32_t* sorted_pairs, uint16_t* h, uint16_t* y16, int32_t* xexp, float* out,
+                       hipStream_t s) {
   if (fmt == kQ4_0)
-    return launch_dec_fmt<kQ4_0>(xdt, Wg, Wu, Wd, E, H, F, X, T, topk, gates, offsets, sorted_pairs, h, y16, out,
-                                 s, nullptr);
-  return launch_dec_fmt<kQ8_0>(xdt, Wg, Wu, Wd, E, H, F, X, T, topk, gates, offsets, sorted_pairs, h, y16, out, s,
-                               nullptr);
+    return launch_dec_fmt<kQ4_0>(xdt, Wg, Wu, Wd, E, H, F, X, T, topk, gates, offsets, sorted_pairs, h, y16, xexp,
+                                 out, s, nullptr);
+  return launch_dec_fmt<kQ8_0>(xdt, Wg, Wu, Wd, E, H, F, X, T, topk, gates, offsets, sorted_pairs, h, y16, xexp, out,
+                               s, nullptr);
 }
 
 bool launch_moe_decode_routed(int fmt, int xdt, const void* Wg, const void* Wu, const void* Wd, int E, int H, int F,
                               const void* X, int T, int topk, const MoeRouteOut& ro, uint16_t* h, uint16_t* y16,
-                              float* out, hipStream_t s) {
+                              int32_t* xexp, float* out, hipStream_t s) {
   if (fmt == kQ4_0)
-    return launch_dec_fmt<kQ4_0>(xdt, Wg, Wu, Wd, E, H, F, X, T, topk, nullptr, nullptr, nullptr, h, y16, out, s,
-                                 &ro);
-  return launch_dec_fmt<kQ8_0>(xdt, Wg, Wu, Wd, E, H, F, X, T, topk, nullptr, nullptr, nullptr, h, y16, out, s,
+    return launch_dec_fmt<kQ4_0>(xdt, Wg, Wu, Wd, E, H, F, X, T, topk, nullptr, nullptr, nullptr, h, y16, xexp, out,
+                                 s, &ro);
+  return launch_dec_fmt<kQ8_0>(xdt, Wg, Wu, Wd, E, H, F, X, T, topk, nullptr, nullptr, nullptr, h, y16, xexp, out, s,
                                &ro);
 }
 

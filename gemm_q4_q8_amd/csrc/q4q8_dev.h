@@ -174,6 +174,55 @@ __device__ __forceinline__ u32x4_t scale_f16x8(const u32x4_t q, const half2_t s2
   return o;
 }
 
+// Activation row scaling (the GEMM and MoE paths): exponent of a row whose
+// largest magnitude has the bits m (sign cleared; the bits order bf16 and
+// fp16 magnitudes, inf and NaN above every finite value): ilogb(max) - 2,
+// so the row times 2^-e has its largest magnitude in [4, 8); 0 for a zero
+// or non-finite row.
+template <int SRC>
+__device__ __forceinline__ int row_exponent(uint32_t m) {
+  constexpr uint32_t kInf = SRC == kBF16 ? 0x7F80u : 0x7C00u;
+  if (m == 0 || m >= kInf) return 0;
+  const float big =
+      SRC == kBF16 ? __builtin_bit_cast(float, m << 16) : (float)__builtin_bit_cast(_Float16, (uint16_t)m);
+  return __builtin_amdgcn_frexp_expf(big) - 3;   // big = f 2^x, f in [0.5, 1): ilogb = x - 1
+}
+
+// Two bf16 / fp16 values (one word) -> fp16 of x 2^sh, round to nearest even.
+template <int SRC>
+__device__ __forceinline__ uint32_t f16x2_scaled(uint32_t w, int sh) {
+  float lo, hi;
+  if constexpr (SRC == kBF16) {
+    lo = __builtin_bit_cast(float, w << 16);
+    hi = __builtin_bit_cast(float, w & 0xFFFF0000u);
+  } else {
+    lo = (float)__builtin_bit_cast(_Float16, (uint16_t)(w & 0xFFFFu));
+    hi = (float)__builtin_bit_cast(_Float16, (uint16_t)(w >> 16));
+  }
+  const half2_t r = {(_Float16)__builtin_ldexpf(lo, sh), (_Float16)__builtin_ldexpf(hi, sh)};
+  return __builtin_bit_cast(uint32_t, r);
+}
+
+// Eight values; the words are copied to scalars first (see scale_f16x8).
+template <int SRC>
+__device__ __forceinline__ u32x4_t f16x8_scaled(const u32x4_t v, int sh) {
+  const uint32_t w0 = v[0], w1 = v[1], w2 = v[2], w3 = v[3];
+  u32x4_t o;
+  o[0] = f16x2_scaled<SRC>(w0, sh);
+  o[1] = f16x2_scaled<SRC>(w1, sh);
+  o[2] = f16x2_scaled<SRC>(w2, sh);
+  o[3] = f16x2_scaled<SRC>(w3, sh);
+  return o;
+}
+
+// Largest magnitude bits (sign cleared) of eight bf16 / fp16 values.
+__device__ __forceinline__ uint32_t max_mag_bits8(const u32x4_t v) {
+  const uint32_t w0 = v[0], w1 = v[1], w2 = v[2], w3 = v[3];
+  const uint32_t a = max(max(w0 & 0x7FFFu, (w0 >> 16) & 0x7FFFu), max(w1 & 0x7FFFu, (w1 >> 16) & 0x7FFFu));
+  const uint32_t b = max(max(w2 & 0x7FFFu, (w2 >> 16) & 0x7FFFu), max(w3 & 0x7FFFu, (w3 >> 16) & 0x7FFFu));
+  return max(a, b);
+}
+
 // A raw buffer resource whose base and size are provably wave-uniform (built
 // from readfirstlane'd values), so loads through it take the descriptor from
 // SGPRs instead of a per-lane waterfall loop.

@@ -61,10 +61,12 @@ hipError_t launch_qgemv(int fmt, int xdt, GemvArgs args, int max_chunks, int max
                         const LaunchEvents& ev);
 
 size_t qgemm_workspace_bytes(int xdt, int64_t M, int64_t K);
-// bf16 [rows, cols] (row stride lds_) -> fp16 [rows, colsp] (row stride ldd),
-// columns cols .. colsp - 1 zero.  cols and colsp multiples of 8.
-hipError_t launch_bf16_to_f16(const void* src, int64_t lds_, void* dst, int64_t ldd, int64_t rows, int64_t cols,
-                              int64_t colsp, hipStream_t s, const LaunchEvents& ev);
+// bf16 / fp16 (src_dt) [rows, cols] (row stride lds_) -> fp16 [rows, colsp]
+// (row stride ldd), columns cols .. colsp - 1 zero, row m scaled by 2^-rexp[m]
+// so its largest magnitude lands in [4, 8) (rexp[m] = 0 for a zero or
+// non-finite row).  cols and colsp multiples of 8.
+hipError_t launch_rowscale_f16(int src_dt, const void* src, int64_t lds_, void* dst, int64_t ldd, int64_t rows,
+                               int64_t cols, int64_t colsp, int32_t* rexp, hipStream_t s, const LaunchEvents& ev);
 hipError_t launch_qgemm(int fmt, int xdt, int ydt, const void* W, int64_t N, int64_t K, const void* X, int64_t ldx,
                         int64_t M, void* Y, int64_t ldy, void* ws, hipStream_t stream, const LaunchEvents& ev);
 
@@ -75,14 +77,17 @@ size_t moe_workspace_bytes(int fmt, int T, int E, int topk, int H, int F);
 
 // Decode path of the expert products (GEMV kernels), used for T <= 8 tokens
 // when the token rows fit the workgroup's activation buffer.  h: bf16
-// [T*topk, F] in sorted-pair order; y16: fp16 [T*topk, H] by pair id.
+// [T*topk, F] in sorted-pair order; y16: fp16 [T*topk, H] by pair id, in
+// the token's scale (y 2^-2 xexp[t]); xexp: int32 [T], each token row's
+// power-of-two exponent (written by the gate/up kernel).
 // Returns true when it also formed out (down fused with the combine);
 // otherwise y16 holds the per-pair outputs for the combine kernel.
 constexpr int kMoeDecodeMaxTokens = 8;
 bool moe_decode_fits(int T, int H, int F);
 bool launch_moe_decode(int fmt, int xdt, const void* Wg, const void* Wu, const void* Wd, int E, int H, int F,
                        const void* X, int T, int topk, const float* gates, const int32_t* offsets,
-                       const int32_t* sorted_pairs, uint16_t* h, uint16_t* y16, float* out, hipStream_t s);
+                       const int32_t* sorted_pairs, uint16_t* h, uint16_t* y16, int32_t* xexp, float* out,
+                       hipStream_t s);
 
 // The routed decode call: the gate/up kernel derives the routing from the
 // logits (as launch_moe_route would) and stores it in these arrays.
@@ -96,7 +101,7 @@ struct MoeRouteOut {
 };
 bool launch_moe_decode_routed(int fmt, int xdt, const void* Wg, const void* Wu, const void* Wd, int E, int H, int F,
                               const void* X, int T, int topk, const MoeRouteOut& ro, uint16_t* h, uint16_t* y16,
-                              float* out, hipStream_t s);
+                              int32_t* xexp, float* out, hipStream_t s);
 hipError_t launch_moe_decode_call(int fmt, int xdt, const void* Wg, const void* Wu, const void* Wd, int E, int H,
                                   int F, const void* X, int T, int topk, const MoeRouteOut& ro, float* out,
                                   void* h_out, void* ws, hipStream_t s);

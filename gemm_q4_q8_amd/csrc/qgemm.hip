@@ -8,8 +8,9 @@
 // the M5 follow-up review, "Method", routes the prefill GEMM to the matrix
 // units).  Here one workgroup computes a 128 x 192 block (64 x 64 for small
 // M) with the tile engine of qgemm_core.h.  BF16 activations are converted
-// once to fp16 by a small pre-pass into the caller's workspace (exact for
-// 2^-14 <= |x| < 65520).  Workgroup ids are remapped so each XCD (ids
+// once to fp16 by a small pre-pass into the caller's workspace, each row
+// scaled by a power of two so its largest magnitude lands in [4, 8); the
+// epilogue multiplies the row's results back.  Workgroup ids are remapped so each XCD (ids
 // i % 8) works through a contiguous range of weight slabs: a slab is read
 // from HBM once per XCD and then served by that XCD's L2.
 #include "q4q8_dev.h"
@@ -43,11 +44,13 @@ __device__ __forceinline__ void store_y(void* Y, int64_t idx, float v) {
 
 // MT m-tiles of 16 rows (BM = 16 MT), NT weight tiles per wave (BN = 64 NT),
 // S pipeline stages.  X is fp16 [M, ldx].  TAIL: K is not a multiple of 128,
-// so the last chunk's copies are masked per column.
+// so the last chunk's copies are masked per column.  rexp (nullable): row m
+// of X holds the activations times 2^-rexp[m]; results are scaled back.
 template <int FMT, int YDT, int MT, int NT, int S, bool TAIL>
 __global__ __launch_bounds__(512) void qgemm_kernel(const uint8_t* __restrict__ W, int N, int K,
                                                     const uint16_t* __restrict__ X, int64_t ldx, int M,
-                                                    void* __restrict__ Y, int64_t ldy, int m_tiles, int n_tiles) {
+                                                    const int32_t* __restrict__ rexp, void* __restrict__ Y,
+                                                    int64_t ldy, int m_tiles, int n_tiles) {
   using C = TileCfg<FMT, MT, NT, 1, S>;
   __shared__ __attribute__((aligned(1024))) uint16_t xs[C::LDS_HALFS];
 
@@ -98,6 +101,14 @@ __global__ __launch_bounds__(512) void qgemm_kernel(const uint8_t* __restrict__ 
   // Lane (r, g), register e of kept tile (i, t):
   // Y[m0 + 16 (kw MT/2 + i) + 4 g + e][16 (t0 + t) + r].
   const int mk = m0 + (wave >> 2) * (MT / 2) * 16 + 4 * g;
+  int ex[MT / 2][4];
+#pragma unroll
+  for (int i = 0; i < MT / 2; ++i)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int m = mk + i * 16 + e;
+      ex[i][e] = (rexp && m < M) ? rexp[m] : 0;
+    }
 #pragma unroll
   for (int t = 0; t < NT; ++t) {
     const int n = (t0 + t) * kTileRows + r;
@@ -107,110 +118,127 @@ __global__ __launch_bounds__(512) void qgemm_kernel(const uint8_t* __restrict__ 
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int m = mk + i * 16 + e;
-          if (m < M) store_y<YDT>(Y, (int64_t)m * ldy + n, kept[i * NT + t][e]);
+          if (m < M) store_y<YDT>(Y, (int64_t)m * ldy + n, __builtin_ldexpf(kept[i * NT + t][e], ex[i][e]));
         }
     }
   }
 }
 
-// bf16 -> fp16, 8 values per thread (exact for fp16-normal magnitudes;
-// round-toward-zero otherwise).  Block (x, y) covers row y, groups of 8
-// columns 256 x .. 256 x + 255; row y of dst holds cols8p groups: the
-// converted cols8 groups, then zeros.
-__global__ __launch_bounds__(256) void bf16_to_f16_kernel(const uint16_t* __restrict__ src, int64_t lds_,
-                                                          uint16_t* __restrict__ dst, int64_t ldd, int cols8,
-                                                          int cols8p) {
-  const int c8 = blockIdx.x * 256 + threadIdx.x;
-  if (c8 >= cols8p) return;
-  const int64_t row = blockIdx.y;
-  u32x4_t o = {0u, 0u, 0u, 0u};
-  if (c8 < cols8) {
-    const u32x4_t v = *(const u32x4_t*)(src + row * lds_ + c8 * 8);
-    const uint32_t v0 = v[0], v1 = v[1], v2 = v[2], v3 = v[3];
-    o[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(__builtin_bit_cast(float, v0 << 16),
-                                                                    __builtin_bit_cast(float, v0 & 0xFFFF0000u)));
-    o[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(__builtin_bit_cast(float, v1 << 16),
-                                                                    __builtin_bit_cast(float, v1 & 0xFFFF0000u)));
-    o[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(__builtin_bit_cast(float, v2 << 16),
-                                                                    __builtin_bit_cast(float, v2 & 0xFFFF0000u)));
-    o[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(__builtin_bit_cast(float, v3 << 16),
-                                                                    __builtin_bit_cast(float, v3 & 0xFFFF0000u)));
+// Row scaling to fp16.  Row m of src (bf16 or fp16, row stride lds_) is
+// written to dst (fp16, row stride ldd) as x * 2^-e[m], columns cols ..
+// colsp - 1 zero, with e[m] = ilogb(max_k |x[m, k]|) - 2, so the row's
+// largest magnitude lands in [4, 8) (e = 0 for a zero row or one holding
+// inf / NaN).  A power of two is exact both ways: every value of the row
+// within 2^20 of its largest magnitude converts exactly (bf16 has 8
+// significant bits, fp16 keeps them down to 2^-17), the rest rounds to
+// nearest even with an absolute error below 2^-25 of the scaled row, and the
+// consumer multiplies its fp32 results by 2^e[m].  One workgroup per row:
+// a max pass, then a convert pass that re-reads the row (from L2).
+template <int SRC>
+__global__ __launch_bounds__(256) void rowscale_f16_kernel(const uint16_t* __restrict__ src, int64_t lds_,
+                                                           uint16_t* __restrict__ dst, int64_t ldd, int cols8,
+                                                           int cols8p, int32_t* __restrict__ rexp) {
+  const int64_t row = blockIdx.x;
+  const int tid = threadIdx.x;
+  const uint16_t* s = src + row * lds_;
+  // Magnitude bits (sign cleared) order bf16 and fp16 values like their
+  // absolute values, with inf and NaN above every finite value.
+  uint32_t m = 0;
+  for (int c8 = tid; c8 < cols8; c8 += 256) m = max(m, max_mag_bits8(*(const u32x4_t*)(s + c8 * 8)));
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, off));
+  __shared__ uint32_t wmax[4];
+  if ((tid & 63) == 0) wmax[tid >> 6] = m;
+  __syncthreads();
+  m = max(max(wmax[0], wmax[1]), max(wmax[2], wmax[3]));
+  const int e = row_exponent<SRC>(m);
+  if (tid == 0) rexp[row] = e;
+  for (int c8 = tid; c8 < cols8p; c8 += 256) {
+    const u32x4_t o = c8 < cols8 ? f16x8_scaled<SRC>(*(const u32x4_t*)(s + c8 * 8), -e) : u32x4_t{0u, 0u, 0u, 0u};
+    *(u32x4_t*)(dst + row * ldd + c8 * 8) = o;
   }
-  *(u32x4_t*)(dst + row * ldd + c8 * 8) = o;
 }
 
-// rows <= 2^30 (grid y is 32-bit on gfx950; larger M is rejected earlier).
-hipError_t launch_bf16_to_f16(const void* src, int64_t lds_, void* dst, int64_t ldd, int64_t rows, int64_t cols,
-                              int64_t colsp, hipStream_t s, const LaunchEvents& ev) {
+// rows <= 2^31 - 1 (grid x).
+hipError_t launch_rowscale_f16(int src_dt, const void* src, int64_t lds_, void* dst, int64_t ldd, int64_t rows,
+                               int64_t cols, int64_t colsp, int32_t* rexp, hipStream_t s, const LaunchEvents& ev) {
   const int cols8 = (int)(cols / 8), cols8p = (int)(colsp / 8);
-  launch(bf16_to_f16_kernel, dim3((unsigned)((cols8p + 255) / 256), (unsigned)rows), dim3(256), 0, s, ev,
-         (const uint16_t*)src, lds_, (uint16_t*)dst, ldd, cols8, cols8p);
+  if (src_dt == kBF16)
+    launch(rowscale_f16_kernel<kBF16>, dim3((unsigned)rows), dim3(256), 0, s, ev, (const uint16_t*)src, lds_,
+           (uint16_t*)dst, ldd, cols8, cols8p, rexp);
+  else
+    launch(rowscale_f16_kernel<kF16>, dim3((unsigned)rows), dim3(256), 0, s, ev, (const uint16_t*)src, lds_,
+           (uint16_t*)dst, ldd, cols8, cols8p, rexp);
   return hipGetLastError();
 }
 
 template <int FMT, int YDT, int MT, int NT, int S>
-static void launch_tile(const void* W, int64_t N, int64_t K, const void* X, int64_t ldx, int64_t M, void* Y,
-                        int64_t ldy, hipStream_t s, const LaunchEvents& ev) {
+static void launch_tile(const void* W, int64_t N, int64_t K, const void* X, int64_t ldx, int64_t M,
+                        const int32_t* rexp, void* Y, int64_t ldy, hipStream_t s, const LaunchEvents& ev) {
   const int m_tiles = (int)((M + 16 * MT - 1) / (16 * MT));
   const int n_tiles = (int)((N + 64 * NT - 1) / (64 * NT));
   if (K % kChunkK)
     launch(qgemm_kernel<FMT, YDT, MT, NT, S, true>, dim3((unsigned)(m_tiles * n_tiles)), dim3(512), 0, s, ev,
-           (const uint8_t*)W, (int)N, (int)K, (const uint16_t*)X, ldx, (int)M, Y, ldy, m_tiles, n_tiles);
+           (const uint8_t*)W, (int)N, (int)K, (const uint16_t*)X, ldx, (int)M, rexp, Y, ldy, m_tiles, n_tiles);
   else
     launch(qgemm_kernel<FMT, YDT, MT, NT, S, false>, dim3((unsigned)(m_tiles * n_tiles)), dim3(512), 0, s, ev,
-           (const uint8_t*)W, (int)N, (int)K, (const uint16_t*)X, ldx, (int)M, Y, ldy, m_tiles, n_tiles);
+           (const uint8_t*)W, (int)N, (int)K, (const uint16_t*)X, ldx, (int)M, rexp, Y, ldy, m_tiles, n_tiles);
 }
 
 // Tile shape: 128 rows x 192 columns (3 weight tiles per wave); 64 x 64 for
 // small M, where more workgroups matter more than operand reuse.
 template <int FMT, int YDT>
-static void launch_shape(const void* W, int64_t N, int64_t K, const void* X, int64_t ldx, int64_t M, void* Y,
-                         int64_t ldy, hipStream_t s, const LaunchEvents& ev) {
+static void launch_shape(const void* W, int64_t N, int64_t K, const void* X, int64_t ldx, int64_t M,
+                         const int32_t* rexp, void* Y, int64_t ldy, hipStream_t s, const LaunchEvents& ev) {
   constexpr int S = FMT == kQ4_0 ? Q4Q8_GEMM_STAGES_Q4 : FMT == kQ8_0 ? Q4Q8_GEMM_STAGES_Q8 : Q4Q8_GEMM_STAGES_F16;
   if (M <= 64)
-    launch_tile<FMT, YDT, 4, 1, S>(W, N, K, X, ldx, M, Y, ldy, s, ev);
+    launch_tile<FMT, YDT, 4, 1, S>(W, N, K, X, ldx, M, rexp, Y, ldy, s, ev);
   else
-    launch_tile<FMT, YDT, 8, 3, S>(W, N, K, X, ldx, M, Y, ldy, s, ev);
+    launch_tile<FMT, YDT, 8, 3, S>(W, N, K, X, ldx, M, rexp, Y, ldy, s, ev);
 }
 
-// BF16 activations: one fp16 copy [M, Kp], Kp = K rounded up to 128 and the
-// extra columns zero (the weights there are zero too), so the GEMM never
-// masks columns.
+// BF16 activations: one row-scaled fp16 copy [M, Kp], Kp = K rounded up to
+// 128 and the extra columns zero (the weights there are zero too), so the
+// GEMM never masks columns, then the rows' exponents (int32 [M]).
 static int64_t padded_k(int64_t K) { return (K + kChunkK - 1) / kChunkK * kChunkK; }
+static size_t round256(size_t b) { return (b + 255) / 256 * 256; }
 
 size_t qgemm_workspace_bytes(int xdt, int64_t M, int64_t K) {
   if (xdt != kBF16) return 0;
-  return (size_t)(((M * padded_k(K) * 2) + 255) / 256 * 256);
+  return round256((size_t)(M * padded_k(K) * 2)) + round256((size_t)M * 4);
 }
 
 hipError_t launch_qgemm(int fmt, int xdt, int ydt, const void* W, int64_t N, int64_t K, const void* X, int64_t ldx,
                         int64_t M, void* Y, int64_t ldy, void* ws, hipStream_t s, const LaunchEvents& ev) {
   const void* Xh = X;
   int64_t ldh = ldx;
+  const int32_t* rexp = nullptr;
   LaunchEvents gev = ev;
   if (xdt == kBF16) {   // the timed span covers both kernels
     LaunchEvents pev;
     pev.start = ev.start;
     gev.start = nullptr;
     const int64_t Kp = padded_k(K);
-    const hipError_t e = launch_bf16_to_f16(X, ldx, ws, Kp, M, K, Kp, s, pev);
+    int32_t* ex = (int32_t*)((uint8_t*)ws + round256((size_t)(M * Kp * 2)));
+    const hipError_t e = launch_rowscale_f16(kBF16, X, ldx, ws, Kp, M, K, Kp, ex, s, pev);
     if (e != hipSuccess) return e;
     Xh = ws;
     ldh = Kp;
     K = Kp;
+    rexp = ex;
   }
   if (fmt == kQ4_0) {
-    if (ydt == kBF16) launch_shape<kQ4_0, kBF16>(W, N, K, Xh, ldh, M, Y, ldy, s, gev);
-    else if (ydt == kF16) launch_shape<kQ4_0, kF16>(W, N, K, Xh, ldh, M, Y, ldy, s, gev);
-    else launch_shape<kQ4_0, kF32>(W, N, K, Xh, ldh, M, Y, ldy, s, gev);
+    if (ydt == kBF16) launch_shape<kQ4_0, kBF16>(W, N, K, Xh, ldh, M, rexp, Y, ldy, s, gev);
+    else if (ydt == kF16) launch_shape<kQ4_0, kF16>(W, N, K, Xh, ldh, M, rexp, Y, ldy, s, gev);
+    else launch_shape<kQ4_0, kF32>(W, N, K, Xh, ldh, M, rexp, Y, ldy, s, gev);
   } else if (fmt == kQ8_0) {
-    if (ydt == kBF16) launch_shape<kQ8_0, kBF16>(W, N, K, Xh, ldh, M, Y, ldy, s, gev);
-    else if (ydt == kF16) launch_shape<kQ8_0, kF16>(W, N, K, Xh, ldh, M, Y, ldy, s, gev);
-    else launch_shape<kQ8_0, kF32>(W, N, K, Xh, ldh, M, Y, ldy, s, gev);
+    if (ydt == kBF16) launch_shape<kQ8_0, kBF16>(W, N, K, Xh, ldh, M, rexp, Y, ldy, s, gev);
+    else if (ydt == kF16) launch_shape<kQ8_0, kF16>(W, N, K, Xh, ldh, M, rexp, Y, ldy, s, gev);
+    else launch_shape<kQ8_0, kF32>(W, N, K, Xh, ldh, M, rexp, Y, ldy, s, gev);
   } else {
-    if (ydt == kBF16) launch_shape<kFP16W, kBF16>(W, N, K, Xh, ldh, M, Y, ldy, s, gev);
-    else if (ydt == kF16) launch_shape<kFP16W, kF16>(W, N, K, Xh, ldh, M, Y, ldy, s, gev);
-    else launch_shape<kFP16W, kF32>(W, N, K, Xh, ldh, M, Y, ldy, s, gev);
+    if (ydt == kBF16) launch_shape<kFP16W, kBF16>(W, N, K, Xh, ldh, M, rexp, Y, ldy, s, gev);
+    else if (ydt == kF16) launch_shape<kFP16W, kF16>(W, N, K, Xh, ldh, M, rexp, Y, ldy, s, gev);
+    else launch_shape<kFP16W, kF32>(W, N, K, Xh, ldh, M, rexp, Y, ldy, s, gev);
   }
   return hipGetLastError();
 }

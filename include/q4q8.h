@@ -25,7 +25,8 @@
  * [N, K], 64 bytes per 32 weights.  Repacked FP16 records are 4096 bytes:
  * four 1 KB planes, block j's lane slot l at j * 1024 + l * 16 holding the
  * slot's 8 weights; no scales.  In the GEMV, BF16 activations meet FP16
- * weights as fp16 operands (converted, exact for 2^-14 <= |x| < 65520).
+ * weights as fp16 operands (converted to nearest: exact for
+ * 2^-14 <= |x| < 65520, |x| >= 65520 becomes +-inf).
  *
  * Conventions for every call below.
  *   - Ownership: the caller allocates and frees everything (weights,
@@ -49,9 +50,15 @@
  *     rows must be 16-byte aligned (leading dimensions multiples of 8
  *     elements).  Activation values are finite.
  *   - Activations of dtype F16 are used as fp16.  BF16 activations are
- *     exact in the GEMV; in the GEMM and the MoE path they are converted to
- *     fp16 for the matrix cores, exactly for 2^-14 <= |x| < 65520 (smaller
- *     magnitudes keep an absolute error below 2^-24, larger ones saturate).
+ *     exact in the GEMV.  In the GEMM and the MoE calls every activation
+ *     row is scaled by a power of two 2^-e chosen so that its largest
+ *     magnitude lands in [4, 8), converted to fp16 for the matrix cores
+ *     (exact for every value within a factor 2^20 of the row's largest;
+ *     smaller ones round to nearest with an absolute error below 2^-25 of
+ *     the scaled row) and the results are multiplied back by 2^e, so any
+ *     finite bf16 row is accepted.  In the MoE calls h and y carry the
+ *     token's 2^-2e inside the library (|h| <= |x W_gate^T| |x W_up^T|), and
+ *     F16 rows are scaled the same way.
  */
 #ifndef Q4Q8_H
 #define Q4Q8_H
@@ -205,10 +212,9 @@ size_t q4q8_ffn_decode_workspace(int M, int64_t F);
 /* The decode FFN of a layer, two launches on `stream`:
  *   h = silu(x Wg^T) * (x Wu^T)   (q4q8_qgemv_swiglu, rounded to bf16)
  *   y = h Wd^T                    (q4q8_qgemv, fp32)
- * h is held in ws as fp16: its bf16 values, converted exactly for
- * 2^-14 <= |h| < 65520 (outside that range as for BF16 activations in the
- * GEMM), so that the down product takes fp16 operands and the Q4_0 unpack's
- * fp16 form.
+ * h is held in ws as fp16: its bf16 values, converted to nearest (exact for
+ * 2^-14 <= |h| < 65520; |h| >= 65520 becomes +-inf), so that the down
+ * product takes fp16 operands and the Q4_0 unpack's fp16 form.
  *   Wg, Wu: repacked [F, H]; Wd: repacked [H, F]; one format.
  *   x:      M rows of H activations (F16/BF16), as for q4q8_qgemv.
  *   y:      device fp32, row m at y + m*ldy, ldy >= H when M > 1.
@@ -236,9 +242,10 @@ int q4q8_ffn_decode_timed(int fmt, const void* Wg, const void* Wu,
 /*  matrix intrinsics; review, "Method": prefill GEMM on the matrix units)  */
 /* ------------------------------------------------------------------------ */
 
-/* Workspace bytes q4q8_qgemm needs: for BF16 activations their fp16 copy,
- * M * Kp * 2 with Kp = K rounded up to 128, rounded up to 256 bytes; 0 for
- * F16.  0 also for invalid xdt/M/K. */
+/* Workspace bytes q4q8_qgemm needs: for BF16 activations their row-scaled
+ * fp16 copy, M * Kp * 2 with Kp = K rounded up to 128, rounded up to 256
+ * bytes, then the rows' exponents, M * 4 rounded up to 256; 0 for F16.
+ * 0 also for invalid xdt/M/K. */
 size_t q4q8_qgemm_workspace(int xdt, int64_t M, int64_t K);
 
 /* Y[m, n] = sum_k X[m, k] * W[n, k]   for m < M, n < N.
@@ -252,8 +259,8 @@ size_t q4q8_qgemm_workspace(int xdt, int64_t M, int64_t K);
  *        repacked tiles; the pages' format list runs up to FP16).
  * fp32 accumulation on fp16 matrix-core operands (weights dequantised and
  * scaled to fp16, relative rounding <= 2^-11, or fp16 weights as they are;
- * BF16 activations converted to fp16, exact for 2^-14 <= |x| < 65520);
- * result rounded once to ydt.
+ * BF16 activation rows scaled by a power of two and converted to fp16 as
+ * the conventions above state); result rounded once to ydt.
  * M >= 1 (any).  Errors: Q4Q8_ERR_WORKSPACE if ws is missing or short. */
 int q4q8_qgemm(int fmt, const void* W, int64_t N, int64_t K,
                const void* X, int xdt, int64_t ldx, int64_t M,

@@ -222,7 +222,8 @@ def test_qgemm_validation(q):
     L = q.lib()
     ok = dict(fmt=1, W=0x1000, N=64, K=256, X=0x2000, xdt=2, ldx=256, M=17, Y=0x3000, ydt=2, ldy=64)
     ok["ws"], ok["nws"] = 0x100000, q.qgemm_workspace(2, 17, 256)
-    assert ok["nws"] == 17 * 256 * 2 // 256 * 256 + 256 * (17 * 256 * 2 % 256 != 0)
+    # the row-scaled fp16 copy (M x Kp halfs) and the rows' int32 exponents, each rounded up to 256 bytes
+    assert ok["nws"] == -(-17 * 256 * 2 // 256) * 256 + -(-17 * 4 // 256) * 256
     assert q.qgemm_workspace(1, 17, 256) == 0 and q.qgemm_workspace(5, 17, 256) == 0
     for over, want in [(dict(ydt=7), -2), (dict(xdt=3), -2), (dict(M=0), -1), (dict(ldx=128), -1),
                        (dict(ldy=32), -1), (dict(Y=0x3001), -4), (dict(ydt=3, Y=0x3002), -4), (dict(ldx=260), -4), (dict(K=100), -1),

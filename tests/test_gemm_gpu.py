@@ -102,3 +102,38 @@ def test_qgemm_prefill_full_size_sampled(q, fmt, M):
     for r0 in (0, M - 16):
         ref, bound = oracle.qgemm(fmt, w.canon, N, K, x.values[r0:r0 + 16])
         check_rounded(yv[r0:r0 + 16], ref, bound, f"prefill fmt{fmt} M{M} rows {r0}..")
+
+
+@pytest.mark.parametrize("fmt", [synth.Q4_0, synth.Q8_0, synth.FP16])
+def test_qgemm_activation_range(q, fmt):
+    """BF16 rows far outside the fp16 range (scaled by 2^20, 2^60, 2^-20,
+    2^-60), a zero row, a row with one large outlier and rows spanning 40
+    binades: each row is scaled by a power of two before its fp16 conversion,
+    so every output keeps the tolerance relative to its own row's scale."""
+    M, N, K = 80, 200, 352
+    w = synth.weight(synth.rng_for(66, fmt), fmt, N, K)
+    base = synth.activation(synth.rng_for(66, 10), (M, K), synth.BF16).values
+    row_scale = np.ones(M)
+    row_scale[0:10] = 2.0 ** 20
+    row_scale[10:20] = 2.0 ** -20
+    row_scale[20:25] = 2.0 ** 60
+    row_scale[25:30] = 2.0 ** -60
+    xv = base * row_scale[:, None]
+    xv[30] = 0.0
+    xv[31, 7] = 3.0e5                                   # one outlier, the rest N(0, 1)
+    span = synth.rng_for(66, 11).uniform(-30, 10, size=(8, K))
+    xv[32:40] = np.sign(base[32:40]) * 2.0 ** span      # magnitudes 2^-30 .. 2^10 within a row
+    x = synth.act_from_values(xv, synth.BF16)
+    Wd = q.repack(fmt, bytes_tensor(w.canon), N, K)
+    ref, bound = oracle.qgemm(fmt, w.canon, N, K, x.values)
+    y = q.qgemm(fmt, Wd, N, K, act_tensor(x), out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    got = values(y)
+    assert np.all(np.isfinite(got))
+    tol = 2e-3 * bound + 1e-5 * row_scale[:, None]
+    err = np.abs(got - ref)
+    assert np.all(err <= tol), f"max err/tol {(err / tol).max():.3g} at row {np.unravel_index(np.argmax(err / tol), err.shape)}"
+    assert np.all(got[30] == 0.0)
+    yb = q.qgemm(fmt, Wd, N, K, act_tensor(x), out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    check_rounded(values(yb)[:20], ref[:20], bound[:20], "bf16 out, rows scaled by 2^20 / 2^-20 (abs term 1e-5)")

@@ -71,6 +71,51 @@ def test_route_ties_and_infinities(q):
     _check_route(logits, 6, _route(q, logits, 6))
 
 
+def _nan_logits(seed, T, E):
+    """Integer logits (many exact ties) with NaN and -inf entries; every row
+    keeps at least one finite logit (with every selected logit -inf the
+    softmax is undefined)."""
+    rng = synth.rng_for(seed, T * 1000 + E)
+    lg = rng.integers(-2, 3, size=(T, E)).astype(np.float32)
+    lg[rng.random(lg.shape) < 0.2] = np.nan
+    lg[rng.random(lg.shape) < 0.15] = -np.inf
+    lg[:, 0] = np.where(np.isfinite(lg[:, 0]), lg[:, 0], 1.0)
+    return lg
+
+
+@pytest.mark.parametrize("T,E,k", [(1, 5, 4), (3, 16, 4), (12, 40, 6), (200, 40, 6), (9, 128, 8), (40, 300, 16)])
+def test_route_nan_logits(q, T, E, k):
+    """NaN logits rank as -inf, on each routing kernel: the one-workgroup
+    kernel with the LDS rank sort (<= 32 pairs) and with the histogram sort,
+    and the top-k + sort kernels (T > 16)."""
+    logits = _nan_logits(74, T, E)
+    if T == 1:
+        logits[0] = [1.0, np.nan, 0.5, -np.inf, -np.inf]
+    got = _route(q, logits, k)
+    if T == 1:
+        assert got[0].tolist() == [[0, 2, 1, 3]]
+    _check_route(logits, k, got)
+
+
+def test_moe_nan_logits(q):
+    """NaN router logits through the whole layer: the one-call decode entry
+    point (routing inside the gate/up kernel at T <= 4, the routing kernel
+    above), the two-call decode path, and the prefill path."""
+    E, k, H, F = 24, 4, 256, 128
+    wg = [synth.q_weight(synth.rng_for(75, 1000 + e), synth.Q4_0, F, H) for e in range(E)]
+    wu = [synth.q_weight(synth.rng_for(75, 2000 + e), synth.Q4_0, F, H) for e in range(E)]
+    wd = [synth.q_weight(synth.rng_for(75, 3000 + e), synth.Q4_0, H, F) for e in range(E)]
+    for T in (2, 6, 40):
+        logits = _nan_logits(76, T, E)
+        x = synth.activation(synth.rng_for(77, T), (T, H), synth.BF16)
+        two = _run_moe(q, synth.Q4_0, logits, x, wg, wu, wd, k, H, F)
+        _check_moe(synth.Q4_0, logits, x, wg, wu, wd, k, H, F, two, f"moe NaN logits T{T}")
+        if T <= 8:
+            one = _run_moe_decode(q, synth.Q4_0, logits, x, wg, wu, wd, k, H, F)
+            for key in ("ids", "gates", "offsets", "sp", "h", "out"):
+                assert np.array_equal(one[key], two[key]), key
+
+
 def test_route_many_pairs(q):
     """65536 pairs: every wave of the sort handles several rounds of 64."""
     logits = synth.router_logits(synth.rng_for(72, 0), 8192, 128)
@@ -94,22 +139,22 @@ def _run_moe(q, fmt, logits, x, wg, wu, wd, k, H, F):
                 sp=sp.cpu().numpy(), h=values(h), out=out.cpu().numpy().astype(np.float64))
 
 
-def _check_moe(fmt, logits, x, wg, wu, wd, k, H, F, got, what):
+def _check_moe(fmt, logits, x, wg, wu, wd, k, H, F, got, what, abs_tol=1e-5):
     cg, cu, cd = [w.canon for w in wg], [w.canon for w in wu], [w.canon for w in wd]
     r = oracle.moe(fmt, cg, cu, cd, x.values, logits, k, H, F)
     assert np.array_equal(got["ids"], r["ids"]) and np.array_equal(got["sp"], r["sorted_pairs"])
-    hb = oracle.h_bound(r)
+    hb = oracle.h_bound(r, abs_tol=abs_tol)
     herr = np.abs(got["h"] - r["h"])
     assert np.all(np.isfinite(got["h"])), f"{what}: h not finite"
     assert np.all(herr <= hb), f"{what}: h err/bound {(herr / hb).max():.3g}"
-    ob = oracle.moe_out_bound(fmt, cd, r, r["ids"], r["gates"], r["sorted_pairs"], H, F, hb)
+    ob = oracle.moe_out_bound(fmt, cd, r, r["ids"], r["gates"], r["sorted_pairs"], H, F, hb, abs_tol=abs_tol)
     oerr = np.abs(got["out"] - r["out"])
     assert np.all(oerr <= ob), f"{what}: out err/bound {(oerr / ob).max():.3g}"
     # Down projection + combine on their own: the oracle takes the GPU's h.
     r2 = oracle.moe_ffn(fmt, cg, cu, cd, x.values, r["ids"], r["gates"], r["sorted_pairs"], H, F,
                         h_override=got["h"])
     ob2 = oracle.moe_out_bound(fmt, cd, r2, r["ids"], r["gates"], r["sorted_pairs"], H, F,
-                               np.zeros_like(got["h"]))
+                               np.zeros_like(got["h"]), abs_tol=abs_tol)
     oerr2 = np.abs(got["out"] - r2["out"])
     assert np.all(oerr2 <= ob2), f"{what}: isolated out err/bound {(oerr2 / ob2).max():.3g}"
 
@@ -122,6 +167,11 @@ MOE_CASES = [
     (synth.Q4_0, synth.F16, 200, 4, 2, 128, 256),    # ~100 pairs per expert: two row tiles
     (synth.Q8_0, synth.BF16, 10, 16, 1, 128, 128),   # most experts empty
     (synth.Q4_0, synth.BF16, 1, 3, 3, 128, 128),     # one token
+    # H or F past one 1024-column LDS phase and not a multiple of it: the
+    # expert kernels reload a partial second phase.
+    (synth.Q4_0, synth.BF16, 64, 4, 2, 1536, 256),
+    (synth.Q8_0, synth.BF16, 48, 4, 2, 1536, 1152),
+    (synth.Q4_0, synth.F16, 90, 6, 3, 384, 1152),
 ]
 
 
@@ -290,3 +340,78 @@ def test_moe_full_size_sampled(q):
             ref += rg[t, j] * y
             bound += rg[t, j] * (2e-3 * by + 1e-5) + (2e-3 * rg[t, j] + 1e-5) * np.abs(y)
         assert np.all(np.abs(got["out"][t] - ref) <= bound), f"token {t}: out"
+
+
+@pytest.mark.parametrize("fmt", [synth.Q4_0, synth.Q8_0])
+def test_moe_full_size_chain(q, fmt):
+    """The MoE workload (T 512, E 128, top-8, H 2048, F 768, bf16 X) in both
+    formats, in the benchmark's launch shape, against the oracle's own chain:
+    routing bit-exact, every h value within the propagated bound, every out
+    value within the bound carried through the whole chain, and every out
+    value against the oracle's down projection and combine fed the GPU's h."""
+    cfg = synth.MOE
+    T, E, k, H, F = cfg["T"], cfg["E"], cfg["topk"], cfg["H"], cfg["F"]
+    logits, x, wg, wu, wd = synth.moe(fmt=fmt)
+    got = _run_moe(q, fmt, logits, x, wg, wu, wd, k, H, F)
+    _check_moe(fmt, logits, x, wg, wu, wd, k, H, F, got, f"moe full size fmt{fmt}")
+
+
+def test_moe_malformed_offsets_stay_in_bounds(q):
+    """Offsets past T*topk (malformed routing) on the matrix-core path: the
+    results are unspecified, but no store may land outside h_out or out."""
+    T, E, k, H, F = 24, 4, 2, 256, 128
+    P = T * k
+    fmt = synth.Q4_0
+    wg = [synth.q_weight(synth.rng_for(78, 1000 + e), fmt, F, H) for e in range(E)]
+    wu = [synth.q_weight(synth.rng_for(78, 2000 + e), fmt, F, H) for e in range(E)]
+    wd = [synth.q_weight(synth.rng_for(78, 3000 + e), fmt, H, F) for e in range(E)]
+    Wg, Wu, Wd = _stack(q, fmt, wg, F, H), _stack(q, fmt, wu, F, H), _stack(q, fmt, wd, H, F)
+    x = synth.activation(synth.rng_for(78, 1), (T, H), synth.BF16)
+    gates = torch.full((T, k), 0.5, device=dev())
+    offsets = torch.tensor([0, 10, 30, P + 40, P + 200], dtype=torch.int32, device=dev())
+    sp = torch.arange(P, dtype=torch.int32, device=dev())
+    guard = 4096
+    hbuf = torch.full((P * F + guard,), 7.0, dtype=torch.bfloat16, device=dev())
+    obuf = torch.full((T * H + guard,), 7.0, dtype=torch.float32, device=dev())
+    ws = torch.full((q.moe_workspace(fmt, T, E, k, H, F) + guard,), 0x5A, dtype=torch.uint8, device=dev())
+    q.moe_qgemm(fmt, Wg, Wu, Wd, E, H, F, act_tensor(x), k, gates, offsets, sp,
+                out=obuf[:T * H].view(T, H), h_out=hbuf[:P * F].view(P, F), ws=ws[:-guard])
+    torch.cuda.synchronize()
+    assert torch.all(hbuf[P * F:] == 7.0)
+    assert torch.all(obuf[T * H:] == 7.0)
+    assert torch.all(ws[-guard:] == 0x5A)
+
+
+@pytest.mark.parametrize("T", [2, 6, 40])
+@pytest.mark.parametrize("xdt", [synth.BF16, synth.F16])
+def test_moe_activation_range(q, T, xdt):
+    """Token rows far outside the fp16 range: each token row is scaled by a
+    power of two before its fp16 conversion and h and y carry the square of
+    that factor, so neither saturates.  bf16 tokens scaled by 2^20 next to
+    unscaled ones and ones scaled by 2^-20 (standard tolerance), then every
+    token scaled by 2^-20 with the absolute term scaled to match (h and out
+    scale with the square); fp16 tokens with entries near the fp16 maximum.
+    T = 2 (routing inside the first kernel, fused down + combine), 6 (decode
+    kernels) and 40 (matrix-core path); the one-call entry point must equal
+    the two-call path bit for bit."""
+    E, k, H, F = 16, 4, 256, 256
+    fmt = synth.Q4_0
+    wg = [synth.q_weight(synth.rng_for(79, 1000 + e), fmt, F, H) for e in range(E)]
+    wu = [synth.q_weight(synth.rng_for(79, 2000 + e), fmt, F, H) for e in range(E)]
+    wd = [synth.q_weight(synth.rng_for(79, 3000 + e), fmt, H, F) for e in range(E)]
+    logits = synth.router_logits(synth.rng_for(79, T), T, E)
+    base = synth.activation(synth.rng_for(79, 100 + T), (T, H), synth.BF16).values
+    if xdt == synth.BF16:
+        scale = np.where(np.arange(T) % 3 == 0, 2.0 ** 20, np.where(np.arange(T) % 3 == 1, 1.0, 2.0 ** -20))
+        cases = [(scale, 1e-5), (np.full(T, 2.0 ** -20), 1e-5 * 2.0 ** -40)]
+    else:
+        cases = [(np.full(T, 2.0 ** 13), 1e-5)]       # |x| up to ~4 * 8192: near the fp16 maximum
+    for sc, abs_tol in cases:
+        x = synth.act_from_values(base * sc[:, None], xdt)
+        two = _run_moe(q, fmt, logits, x, wg, wu, wd, k, H, F)
+        assert np.all(np.isfinite(two["out"])) and np.all(np.isfinite(two["h"]))
+        _check_moe(fmt, logits, x, wg, wu, wd, k, H, F, two, f"moe range T{T} xdt{xdt}", abs_tol=abs_tol)
+        if T <= 8:
+            one = _run_moe_decode(q, fmt, logits, x, wg, wu, wd, k, H, F)
+            for key in ("h", "out"):
+                assert np.array_equal(one[key], two[key]), key
