@@ -4,6 +4,8 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "../../include/q4q8.h"
 #include "q4q8_internal.h"
 
@@ -426,10 +428,51 @@ int q4q8_moe_qgemm(int fmt, const void* Wg, const void* Wu, const void* Wd, int 
                     "moe_qgemm launch");
 }
 
-int q4q8_moe_decode(int fmt, const void* Wg, const void* Wu, const void* Wd, int E, int H, int F,
-                    const float* logits, const void* X, int xdt, int T, int topk, int32_t* ids, float* gates,
-                    int32_t* counts, int32_t* offsets, int32_t* sorted_pairs, float* out, void* h_out, void* ws,
-                    size_t ws_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// The no-allocation decode call's scratch: one array per GPU, resident from
+// module load until the process ends.  Host code never passes `scratch`
+// itself to a kernel (on the host it names a stand-in, not device memory);
+// it uses the device address hipGetSymbolAddress returns, looked up once per
+// device with that device current.
+constexpr size_t kScratchBytes = (size_t)1 << 20;
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];
+
+// Device address of `scratch` on the device that runs `stream`.
+int scratch_for(void* stream, void** out) {
+  int dev = 0;
+  hipError_t e = stream ? hipStreamGetDevice((hipStream_t)stream, &dev) : hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_status(e, "moe_decode_noalloc: device of the stream");
+  if (dev < 0 || dev >= kMaxDevices) return fail(Q4Q8_ERR_UNSUPPORTED, "moe_decode_noalloc: device %d", dev);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    int cur = 0;
+    e = hipGetDevice(&cur);
+    if (e == hipSuccess && cur != dev) e = hipSetDevice(dev);
+    void* p = nullptr;
+    if (e == hipSuccess) e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (cur != dev) {
+      const hipError_t e2 = hipSetDevice(cur);
+      if (e == hipSuccess) e = e2;
+    }
+    if (e != hipSuccess) return hip_status(e, "moe_decode_noalloc: scratch address");
+    if (!p) return fail(Q4Q8_ERR_HIP, "moe_decode_noalloc: scratch address is null");
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return Q4Q8_OK;
+}
+
+int moe_decode_impl(int fmt, const void* Wg, const void* Wu, const void* Wd, int E, int H, int F, const float* logits,
+                    const void* X, int xdt, int T, int topk, int32_t* ids, float* gates, int32_t* counts,
+                    int32_t* offsets, int32_t* sorted_pairs, float* out, void* h_out, void* ws, size_t ws_bytes,
+                    void* stream, bool use_scratch) {
   if (!fmt_ok(fmt)) return fail(Q4Q8_ERR_UNSUPPORTED, "unknown weight format %d", fmt);
   if (!act_ok(xdt)) return fail(Q4Q8_ERR_UNSUPPORTED, "moe_decode: activation dtype %d not F16/BF16", xdt);
   if (!Wg || !Wu || !Wd || !logits || !X || !ids || !gates || !counts || !offsets || !sorted_pairs || !out)
@@ -444,20 +487,54 @@ int q4q8_moe_decode(int fmt, const void* Wg, const void* Wu, const void* Wd, int
                 "use q4q8_moe_route + q4q8_moe_qgemm)",
                 T, H, F);
   const size_t need = q4q8::moe_workspace_bytes(fmt, T, E, topk, H, F);
-  if (!ws || ws_bytes < need)
-    return fail(Q4Q8_ERR_WORKSPACE, "moe_decode: workspace holds %zu bytes, needs %zu", ws_bytes, need);
-  if (!aligned(ws, 256)) return fail(Q4Q8_ERR_ALIGNMENT, "moe_decode: workspace not 256-byte aligned");
+  if (use_scratch) {
+    if (need > kScratchBytes)
+      return fail(Q4Q8_ERR_UNSUPPORTED,
+                  "moe_decode_noalloc: T=%d topk=%d H=%d F=%d need %zu bytes of scratch, beyond its %zu (use "
+                  "q4q8_moe_decode with a workspace)",
+                  T, topk, H, F, need, kScratchBytes);
+  } else {
+    if (!ws || ws_bytes < need)
+      return fail(Q4Q8_ERR_WORKSPACE, "moe_decode: workspace holds %zu bytes, needs %zu", ws_bytes, need);
+    if (!aligned(ws, 256)) return fail(Q4Q8_ERR_ALIGNMENT, "moe_decode: workspace not 256-byte aligned");
+  }
   if (!aligned(Wg, 16) || !aligned(Wu, 16) || !aligned(Wd, 16) || !aligned(X, 16) || !aligned(out, 16) ||
       (h_out && !aligned(h_out, 16)) || !aligned(logits, 4) || !aligned(ids, 4) || !aligned(gates, 4) ||
       !aligned(counts, 4) || !aligned(offsets, 4) || !aligned(sorted_pairs, 4))
     return fail(Q4Q8_ERR_ALIGNMENT, "moe_decode: weights, X, out and h_out must be 16-byte aligned, the routing "
                                     "arrays 4-byte aligned");
+  if (use_scratch) {
+    const int st = scratch_for(stream, &ws);
+    if (st != Q4Q8_OK) return st;
+  }
   clear_hip_error();
   const q4q8::MoeRouteOut ro = {logits, ids, gates, counts, offsets, sorted_pairs};
   return hip_status(q4q8::launch_moe_decode_call(fmt, xdt, Wg, Wu, Wd, E, H, F, X, T, topk, ro, out, h_out, ws,
                                                  (hipStream_t)stream),
                     "moe_decode launch");
 }
+
+}  // namespace
+
+extern "C" {
+
+int q4q8_moe_decode(int fmt, const void* Wg, const void* Wu, const void* Wd, int E, int H, int F,
+                    const float* logits, const void* X, int xdt, int T, int topk, int32_t* ids, float* gates,
+                    int32_t* counts, int32_t* offsets, int32_t* sorted_pairs, float* out, void* h_out, void* ws,
+                    size_t ws_bytes, void* stream) {
+  return moe_decode_impl(fmt, Wg, Wu, Wd, E, H, F, logits, X, xdt, T, topk, ids, gates, counts, offsets,
+                         sorted_pairs, out, h_out, ws, ws_bytes, stream, false);
+}
+
+int q4q8_moe_decode_noalloc(int fmt, const void* Wg, const void* Wu, const void* Wd, int E, int H, int F,
+                            const float* logits, const void* X, int xdt, int T, int topk, int32_t* ids,
+                            float* gates, int32_t* counts, int32_t* offsets, int32_t* sorted_pairs, float* out,
+                            void* h_out, void* stream) {
+  return moe_decode_impl(fmt, Wg, Wu, Wd, E, H, F, logits, X, xdt, T, topk, ids, gates, counts, offsets,
+                         sorted_pairs, out, h_out, nullptr, 0, stream, true);
+}
+
+size_t q4q8_moe_decode_noalloc_max_scratch(void) { return kScratchBytes; }
 
 static int attn_impl(int dt, const void* Q, const void* K, const void* V, void* O, int B, int S, int Hq, int Hkv,
                      int D, int causal, float scale, void* stream, const q4q8::LaunchEvents& ev) {

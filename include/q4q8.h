@@ -354,6 +354,32 @@ int q4q8_moe_decode(int fmt, const void* Wg, const void* Wu, const void* Wd,
                     float* out, void* h_out, void* ws, size_t ws_bytes,
                     void* stream);
 
+/* q4q8_moe_decode without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation).  The call allocates nothing and calls
+ * no allocating routine: its scratch is a static device array of
+ * q4q8_moe_decode_noalloc_max_scratch() bytes (1 MiB) that the library's
+ * module holds on every GPU it runs on until the process ends; its address
+ * on the stream's device is looked up once, on that device's first call.
+ * Arguments, results and limits are those of q4q8_moe_decode (same kernels,
+ * same bits); a call whose q4q8_moe_workspace(fmt, T, E, topk, H, F)
+ * exceeds the scratch returns Q4Q8_ERR_UNSUPPORTED and enqueues nothing
+ * (the MoE shape of E 128, top-8, H 2048, F 768 needs 0.4 MB at T = 8).
+ * The scratch needs no initialisation and keeps the last call's contents.
+ * Every call on one GPU shares that GPU's scratch: calls that can overlap on
+ * one GPU (different streams, or different threads without ordering) race
+ * and must be serialised by the caller. */
+int q4q8_moe_decode_noalloc(int fmt, const void* Wg, const void* Wu,
+                            const void* Wd, int E, int H, int F,
+                            const float* logits, const void* X, int xdt,
+                            int T, int topk, int32_t* ids, float* gates,
+                            int32_t* counts, int32_t* offsets,
+                            int32_t* sorted_pairs, float* out, void* h_out,
+                            void* stream);
+
+/* Bytes of q4q8_moe_decode_noalloc's per-GPU scratch. */
+size_t q4q8_moe_decode_noalloc_max_scratch(void);
+
 /* ------------------------------------------------------------------------ */
 /* Prefill attention (technical summary, "Methodologie", prefill            */
 /* optimisation: tiled attention with an online softmax, O(n) memory;       */
