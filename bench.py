@@ -400,9 +400,9 @@ def extra_workloads(q, torch, synth, ev: HipEvents, quick: bool, only=None):
     if want("prefill"):
         out += prefill_workloads(q, torch, synth, ev, quick)
     if want("moe"):
-        out.append(moe_workload(q, torch, synth))
+        out += moe_workload(q, torch, synth)
         if not quick:
-            out.append(moe_workload(q, torch, synth, fmt=2))
+            out += moe_workload(q, torch, synth, fmt=2)
     if want("moe_decode"):
         out += moe_decode_workloads(q, torch, synth, quick)
     if want("attn"):
@@ -656,21 +656,32 @@ def moe_workload(q, torch, synth, fmt: int = 1):
     out = torch.empty((T, H), dtype=torch.float32, device=dev)
     wsp = torch.empty(q.moe_workspace(fmt, T, E, k, H, F), dtype=torch.uint8, device=dev)
 
-    def step(_):
-        ids, gates, counts, offsets, sp = q.moe_route(L, k)
+    route = (torch.empty((T, k), dtype=torch.int32, device=dev), torch.empty((T, k), dtype=torch.float32, device=dev),
+             torch.empty(E, dtype=torch.int32, device=dev), torch.empty(E + 1, dtype=torch.int32, device=dev),
+             torch.empty(T * k, dtype=torch.int32, device=dev))
+
+    def step_two(_):     # q4q8_moe_route, then q4q8_moe_qgemm
+        ids, gates, counts, offsets, sp = q.moe_route(L, k, out=route)
         q.moe_qgemm(fmt, Wg, Wu, Wd, E, H, F, X, k, gates, offsets, sp, out=out, ws=wsp)
 
-    dt = _time_launches(torch, step, 30)
+    def step_one(_):     # q4q8_moe_forward: the sort formed inside the gate+up kernel
+        q.moe_forward(fmt, Wg, Wu, Wd, E, H, F, L, X, k, route=route, out=out, ws=wsp)
+
     fl = 2.0 * T * k * 3 * F * H
     wbytes = 3 * E * q.repacked_bytes(fmt, F, H)
     roof = max(wbytes / (HBM_PEAK_GBS * 1e9), fl / (F16_MFMA_PEAK_TFLOPS * 1e12))
+    res = []
+    for name, step in (("one call, moe_forward", step_one), ("moe_route + moe_qgemm", step_two)):
+        dt = _time_launches(torch, step, 30)
+        res.append({"workload": f"{synth.FORMAT_NAME[fmt]} moe T={T} E={E} top{k} H={H} F={F} (bf16 tokens; {name})",
+                    "step_us": round(dt * 1e6, 2),
+                    "TFLOP/s": round(fl / dt / 1e12, 1),
+                    "mfma_frac": round(fl / dt / 1e12 / F16_MFMA_PEAK_TFLOPS, 4),
+                    "weight_GB/s": round(wbytes / dt / 1e9, 1), "roofline_us": round(roof * 1e6, 2),
+                    "roofline_frac": round(roof / dt, 4)})
     del Wg, Wu, Wd, wsp
     torch.cuda.empty_cache()
-    return {"workload": f"{synth.FORMAT_NAME[fmt]} moe T={T} E={E} top{k} H={H} F={F} (bf16 tokens)",
-            "step_us": round(dt * 1e6, 2),
-            "TFLOP/s": round(fl / dt / 1e12, 1), "mfma_frac": round(fl / dt / 1e12 / F16_MFMA_PEAK_TFLOPS, 4),
-            "weight_GB/s": round(wbytes / dt / 1e9, 1), "roofline_us": round(roof * 1e6, 2),
-            "roofline_frac": round(roof / dt, 4)}
+    return res
 
 
 def moe_decode_workloads(q, torch, synth, quick: bool):

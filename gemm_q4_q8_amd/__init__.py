@@ -74,6 +74,8 @@ def _declare(lib):
                                  vp, vp, vp, vp, vp, vp, sz, vp]),
         "q4q8_moe_decode": (i32, [i32, vp, vp, vp, i32, i32, i32, vp, vp, i32, i32, i32,
                                   vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]),
+        "q4q8_moe_forward": (i32, [i32, vp, vp, vp, i32, i32, i32, vp, vp, i32, i32, i32,
+                                   vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]),
         "q4q8_moe_decode_noalloc": (i32, [i32, vp, vp, vp, i32, i32, i32, vp, vp, i32, i32, i32,
                                           vp, vp, vp, vp, vp, vp, vp, vp]),
         "q4q8_moe_decode_noalloc_max_scratch": (sz, []),
@@ -360,6 +362,32 @@ def moe_decode(fmt: int, Wg, Wu, Wd, E: int, H: int, F: int, logits: torch.Tenso
                                  topk, _ptr(ids), _ptr(gates), _ptr(counts), _ptr(offsets), _ptr(sp), _ptr(out),
                                  _ptr(h_out), _ptr(ws), ws.numel() * ws.element_size(), _stream(X)),
            "moe_decode")
+    return out, route
+
+
+def moe_forward(fmt: int, Wg, Wu, Wd, E: int, H: int, F: int, logits: torch.Tensor, X: torch.Tensor, topk: int,
+                route=None, out=None, h_out=None, ws=None):
+    """The whole MoE layer for any T in one call (q4q8_moe_forward) ->
+    (out [T, H] fp32, (ids, gates, counts, offsets, sorted_pairs))."""
+    _dev(logits, "logits")
+    T = X.shape[0]
+    d = X.device
+    if logits.shape != (T, E):
+        raise ValueError("logits must be [T, E]")
+    if route is None:
+        route = (torch.empty((T, topk), dtype=torch.int32, device=d), torch.empty((T, topk), dtype=torch.float32, device=d),
+                 torch.empty(E, dtype=torch.int32, device=d), torch.empty(E + 1, dtype=torch.int32, device=d),
+                 torch.empty(T * topk, dtype=torch.int32, device=d))
+    if out is None:
+        out = torch.empty((T, H), dtype=torch.float32, device=d)
+    nws = moe_workspace(fmt, T, E, topk, H, F)
+    if ws is None:
+        ws = torch.empty(nws, dtype=torch.uint8, device=d)
+    ids, gates, counts, offsets, sp = route
+    _check(lib().q4q8_moe_forward(fmt, _ptr(Wg), _ptr(Wu), _ptr(Wd), E, H, F, _ptr(logits), _ptr(X), _DT[X.dtype],
+                                  T, topk, _ptr(ids), _ptr(gates), _ptr(counts), _ptr(offsets), _ptr(sp), _ptr(out),
+                                  _ptr(h_out), _ptr(ws), ws.numel() * ws.element_size(), _stream(X)),
+           "moe_forward")
     return out, route
 
 

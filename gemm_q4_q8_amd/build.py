@@ -33,12 +33,35 @@ def _hipcc() -> str:
     raise RuntimeError("hipcc not found")
 
 
+# Kernels whose pipelines wait on hand-counted outstanding loads
+# (s_waitcnt vmcnt(N) in qgemm_core.h): a register spill would add scratch
+# loads and stores to those counts and break the waits silently, so the
+# build fails if any of them uses scratch.
+NO_SCRATCH = ("qgemm_kernel",)
+
+
+def _scratch_users(remarks: str):
+    """(kernel, bytes/lane) of every kernel the compiler reports with scratch."""
+    out, name = [], None
+    for line in remarks.splitlines():
+        if "Function Name:" in line:
+            name = line.split("Function Name:", 1)[1].strip()
+        elif name and "ScratchSize [bytes/lane]:" in line:
+            n = int(line.split("ScratchSize [bytes/lane]:", 1)[1].split()[0])
+            if n:
+                out.append((name, n))
+    return out
+
+
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [_hipcc(), *CFLAGS, "-c", src, "-o", obj]
+    cmd = [_hipcc(), *CFLAGS, "-Rpass-analysis=kernel-resource-usage", "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode:
         raise RuntimeError(f"hipcc failed on {src}:\n{r.stderr}")
+    bad = [(k, n) for k, n in _scratch_users(r.stderr) if any(s in k for s in NO_SCRATCH)]
+    if bad:
+        raise RuntimeError(f"{src}: kernels with hand-counted load waits use scratch (register spills): {bad}")
     return obj
 
 

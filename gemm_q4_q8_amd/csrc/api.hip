@@ -472,7 +472,7 @@ int scratch_for(void* stream, void** out) {
 int moe_decode_impl(int fmt, const void* Wg, const void* Wu, const void* Wd, int E, int H, int F, const float* logits,
                     const void* X, int xdt, int T, int topk, int32_t* ids, float* gates, int32_t* counts,
                     int32_t* offsets, int32_t* sorted_pairs, float* out, void* h_out, void* ws, size_t ws_bytes,
-                    void* stream, bool use_scratch) {
+                    void* stream, bool use_scratch, bool any_t = false) {
   if (!fmt_ok(fmt)) return fail(Q4Q8_ERR_UNSUPPORTED, "unknown weight format %d", fmt);
   if (!act_ok(xdt)) return fail(Q4Q8_ERR_UNSUPPORTED, "moe_decode: activation dtype %d not F16/BF16", xdt);
   if (!Wg || !Wu || !Wd || !logits || !X || !ids || !gates || !counts || !offsets || !sorted_pairs || !out)
@@ -481,11 +481,18 @@ int moe_decode_impl(int fmt, const void* Wg, const void* Wu, const void* Wd, int
     return fail(Q4Q8_ERR_INVALID_ARG, "moe_decode: T=%d E=%d topk=%d", T, E, topk);
   if (H < 128 || F < 128 || H % 128 || F % 128)
     return fail(Q4Q8_ERR_INVALID_ARG, "moe_decode: H=%d and F=%d must be positive multiples of 128", H, F);
-  if (H > (1 << 20) || F > (1 << 20) || !q4q8::moe_decode_fits(T, H, F))
+  if (any_t) {
+    const int64_t P = (int64_t)T * topk;
+    if (P > (1LL << 22) || H > (1 << 20) || F > (1 << 20) || (int64_t)T * H * 2 >= (1LL << 31) ||
+        P * F * 2 >= (1LL << 31) || P * H * 2 >= (1LL << 31))
+      return fail(Q4Q8_ERR_UNSUPPORTED, "moe_forward: sizes beyond limits (T*topk <= 2^22, T*H, T*topk*F and "
+                                        "T*topk*H below 2^30 elements)");
+  } else if (H > (1 << 20) || F > (1 << 20) || !q4q8::moe_decode_fits(T, H, F)) {
     return fail(Q4Q8_ERR_UNSUPPORTED,
                 "moe_decode: T=%d H=%d F=%d beyond the decode path (T <= 8 and T*(max(H,F)+8)*2 + 512 <= 52 KB; "
-                "use q4q8_moe_route + q4q8_moe_qgemm)",
+                "use q4q8_moe_forward, or q4q8_moe_route + q4q8_moe_qgemm)",
                 T, H, F);
+  }
   const size_t need = q4q8::moe_workspace_bytes(fmt, T, E, topk, H, F);
   if (use_scratch) {
     if (need > kScratchBytes)
@@ -509,6 +516,10 @@ int moe_decode_impl(int fmt, const void* Wg, const void* Wu, const void* Wd, int
   }
   clear_hip_error();
   const q4q8::MoeRouteOut ro = {logits, ids, gates, counts, offsets, sorted_pairs};
+  if (any_t)
+    return hip_status(q4q8::launch_moe_forward(fmt, xdt, Wg, Wu, Wd, E, H, F, X, T, topk, ro, out, h_out, ws,
+                                               (hipStream_t)stream),
+                      "moe_forward launch");
   return hip_status(q4q8::launch_moe_decode_call(fmt, xdt, Wg, Wu, Wd, E, H, F, X, T, topk, ro, out, h_out, ws,
                                                  (hipStream_t)stream),
                     "moe_decode launch");
@@ -524,6 +535,14 @@ int q4q8_moe_decode(int fmt, const void* Wg, const void* Wu, const void* Wd, int
                     size_t ws_bytes, void* stream) {
   return moe_decode_impl(fmt, Wg, Wu, Wd, E, H, F, logits, X, xdt, T, topk, ids, gates, counts, offsets,
                          sorted_pairs, out, h_out, ws, ws_bytes, stream, false);
+}
+
+int q4q8_moe_forward(int fmt, const void* Wg, const void* Wu, const void* Wd, int E, int H, int F,
+                     const float* logits, const void* X, int xdt, int T, int topk, int32_t* ids, float* gates,
+                     int32_t* counts, int32_t* offsets, int32_t* sorted_pairs, float* out, void* h_out, void* ws,
+                     size_t ws_bytes, void* stream) {
+  return moe_decode_impl(fmt, Wg, Wu, Wd, E, H, F, logits, X, xdt, T, topk, ids, gates, counts, offsets,
+                         sorted_pairs, out, h_out, ws, ws_bytes, stream, false, true);
 }
 
 int q4q8_moe_decode_noalloc(int fmt, const void* Wg, const void* Wu, const void* Wd, int E, int H, int F,

@@ -48,6 +48,36 @@ __global__ __launch_bounds__(256) void moe_topk_kernel(const float* __restrict__
   if (t < T) topk_token<NS>(logits, t, E, topk, threadIdx.x & 63, ids, gates);   // whole wave
 }
 
+// Top-k of token t and its row scaling (as the row-scaling pre-pass: the
+// row times 2^-xexp[t] as fp16, its largest magnitude in [4, 8)): the
+// routing and the activation pre-pass of the one-call MoE in one launch.
+// Workgroup of 8 waves for 4 tokens: wave w < 4 routes token 4 b + w, wave
+// 4 + w scales its row, so the two latency chains run side by side.  H is a
+// multiple of 8.
+template <int NS, int SRC>
+__global__ __launch_bounds__(512) void moe_prep_kernel(const float* __restrict__ logits, int T, int E, int topk,
+                                                       int32_t* __restrict__ ids, float* __restrict__ gates,
+                                                       const uint16_t* __restrict__ X, int H,
+                                                       uint16_t* __restrict__ x16, int32_t* __restrict__ xexp) {
+  const int w = threadIdx.x >> 6;
+  const int t = blockIdx.x * 4 + (w & 3);
+  if (t >= T) return;   // whole wave
+  const int lane = threadIdx.x & 63;
+  if (w < 4) {
+    topk_token<NS>(logits, t, E, topk, lane, ids, gates);
+    return;
+  }
+  const uint16_t* xr = X + (int64_t)t * H;
+  uint32_t m = 0;
+  for (int c8 = lane; c8 < H / 8; c8 += 64) m = max(m, max_mag_bits8(*(const u32x4_t*)(xr + c8 * 8)));
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, off));
+  const int ex = row_exponent<SRC>(m);
+  if (lane == 0) xexp[t] = ex;
+  for (int c8 = lane; c8 < H / 8; c8 += 64)
+    *(u32x4_t*)(x16 + (int64_t)t * H + c8 * 8) = f16x8_scaled<SRC>(*(const u32x4_t*)(xr + c8 * 8), -ex);
+}
+
 // ---------------------------------------------------------------------------
 // Sort: counts, offsets, sorted_pairs (stable counting sort, one workgroup)
 // ---------------------------------------------------------------------------
@@ -219,30 +249,138 @@ hipError_t launch_moe_route(const float* logits, int T, int E, int topk, int32_t
 enum { kGateUp = 0, kDown = 1 };
 constexpr int kStreamBM = 64;
 
+// Routing outputs the gate+up kernel forms itself (ROUTE): from the pairs'
+// experts (ids, pair order) each expert's workgroups find its rows; the
+// expert's first workgroup stores its count, offset and slice of the sorted
+// pairs, the same values the sort kernel gives.
+struct MoeRouteArgs {
+  const int32_t* ids;   // [Ptot]
+  int32_t* counts;      // [E]
+  int32_t* offsets;     // [E + 1]
+  int32_t* sorted;      // [Ptot]
+  int32_t E;
+};
+
 // WAVES waves per workgroup; KP columns per LDS phase (64 rows x KP fp16).
-template <int FMT, int MODE, int NT, int P, int WAVES, int KP>
+template <int FMT, int MODE, int NT, int P, int WAVES, int KP, bool ROUTE = false>
 __global__ __launch_bounds__(WAVES * 64) void moe_stream_kernel(
     const uint8_t* __restrict__ W0, const uint8_t* __restrict__ W1, int64_t wstride, int N, int K,
     const uint16_t* __restrict__ src, int src_rows, int T, int topk, int Ptot,
     const int32_t* __restrict__ offsets, const int32_t* __restrict__ sorted_pairs, const int32_t* __restrict__ xexp,
-    uint16_t* __restrict__ out16, uint16_t* __restrict__ h_out, int tiles_per_wave, int groups) {
+    uint16_t* __restrict__ out16, uint16_t* __restrict__ h_out, int tiles_per_wave, int groups, MoeRouteArgs ra) {
+  static_assert(!ROUTE || MODE == kGateUp, "the routed form is the gate+up pass");
   constexpr int NW = MODE == kGateUp ? 2 : 1;
   constexpr int MT = kStreamBM / 16, BM = kStreamBM;
   constexpr int REC = Fmt<FMT>::kRecBytes;
   constexpr int CODE = Fmt<FMT>::kCodeBytes;
   constexpr int NV = FMT == kQ4_0 ? 1 : 2;
   constexpr int THREADS = WAVES * 64;
-  constexpr int NH = BM * 16 / THREADS;   // row offsets per thread in one LDS chunk
   __shared__ __attribute__((aligned(1024))) uint16_t xs[BM * KP];
+  __shared__ int s_rowbase[BM];   // source row of each of the row tile's BM rows (-1: none)
 
   const int e = blockIdx.y;
-  // Clamped to the Ptot pairs, so malformed offsets cannot send the row
-  // stores past h / y (the decode path clamps the same way).
-  const int seg = min(max(offsets[e], 0), Ptot);
-  const int cnt = min(offsets[e + 1], Ptot) - seg;
-  if (cnt <= 0) return;   // uniform over the workgroup
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+
+  // ROUTE: block-wide exclusive scan of two per-thread counts (pairs of this
+  // expert, pairs of lower experts) over one round of THREADS x 8 pairs.
+  __shared__ int s_wsum[2][WAVES];
+  auto scan2 = [&](int v0, int v1, int& ex0, int& tot0, int& tot1) __attribute__((always_inline)) {
+    int i0 = v0, i1 = v1;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int o0 = __shfl_up(i0, off), o1 = __shfl_up(i1, off);
+      if (lane >= off) {
+        i0 += o0;
+        i1 += o1;
+      }
+    }
+    if (lane == 63) {
+      s_wsum[0][wave] = i0;
+      s_wsum[1][wave] = i1;
+    }
+    __syncthreads();
+    int before = 0;
+    tot0 = 0;
+    tot1 = 0;
+#pragma unroll
+    for (int w = 0; w < WAVES; ++w) {
+      before += w < wave ? s_wsum[0][w] : 0;
+      tot0 += s_wsum[0][w];
+      tot1 += s_wsum[1][w];
+    }
+    ex0 = before + i0 - v0;
+    __syncthreads();   // s_wsum is reused by the next round
+  };
+  // Thread tid's 8 pair experts of the round starting at r0 (-1 past Ptot):
+  // two 16-byte buffer loads (4-byte alignment suffices for buffer loads).
+  const __amdgpu_buffer_rsrc_t ids_res = uniform_rsrc(ra.ids, ROUTE ? Ptot * 4 : 0);
+  auto load_ids8 = [&](int r0, int (&id)[8]) __attribute__((always_inline)) {
+    const u32x4_t a0 = __builtin_amdgcn_raw_buffer_load_b128(ids_res, (uint32_t)(r0 + tid * 8) * 4, 0, 0);
+    const u32x4_t a1 = __builtin_amdgcn_raw_buffer_load_b128(ids_res, (uint32_t)(r0 + tid * 8 + 4) * 4, 0, 0);
+    const uint32_t v[8] = {a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
+#pragma unroll
+    for (int q = 0; q < 8; ++q) id[q] = r0 + tid * 8 + q < Ptot ? (int)v[q] : -1;
+  };
+
+  int seg, cnt;
+  bool rows0_done = false;   // ROUTE, one round: row tile 0 and the sorted pairs are stored already
+  if constexpr (ROUTE) {
+    seg = 0;
+    cnt = 0;
+    if (Ptot <= THREADS * 8) {
+      // One round: the scan gives the ranks, seg and cnt together.
+      int id[8];
+      load_ids8(0, id);
+      int cs = 0, cb = 0;
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        cs += id[q] == e ? 1 : 0;
+        cb += (id[q] >= 0 && id[q] < e) ? 1 : 0;
+      }
+      if (tid < BM) s_rowbase[tid] = -1;
+      int ex;
+      scan2(cs, cb, ex, cnt, seg);   // (its barriers order the s_rowbase reset before the fills)
+      int rank = ex;
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        if (id[q] == e) {
+          const int pr = tid * 8 + q;
+          if (rank < BM) s_rowbase[rank] = min(pr / topk, T - 1);
+          ra.sorted[seg + rank] = pr;
+          ++rank;
+        }
+      }
+      rows0_done = true;
+    }
+    // Otherwise pass 1: seg = pairs routed to lower experts, cnt = pairs
+    // routed to e (pass 2, the ranks, follows in the prologue).
+    for (int r0 = 0; !rows0_done && r0 < Ptot; r0 += THREADS * 8) {
+      int id[8];
+      load_ids8(r0, id);
+      int cs = 0, cb = 0;
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        cs += id[q] == e ? 1 : 0;
+        cb += (id[q] >= 0 && id[q] < e) ? 1 : 0;
+      }
+      int ex, ts, tb;
+      scan2(cs, cb, ex, ts, tb);
+      cnt += ts;
+      seg += tb;
+    }
+    if (blockIdx.x == 0 && tid == 0) {
+      ra.counts[e] = cnt;
+      ra.offsets[e] = seg;
+      if (e == ra.E - 1) ra.offsets[ra.E] = Ptot;
+    }
+  } else {
+    // Clamped to the Ptot pairs, so malformed offsets cannot send the row
+    // stores past h / y (the decode path clamps the same way).
+    seg = min(max(offsets[e], 0), Ptot);
+    cnt = min(offsets[e + 1], Ptot) - seg;
+  }
+  if (cnt <= 0) return;   // uniform over the workgroup
   const int r = lane & 15, g = lane >> 4;
   const int nchunks = K / kChunkK;
   const int tiles = N / kTileRows;
@@ -292,31 +430,67 @@ __global__ __launch_bounds__(WAVES * 64) void moe_stream_kernel(
   // thread fills slot THREADS p + tid of the phase: chunk slot / (BM 16),
   // then row / column group as in the tile engine.
   const __amdgpu_buffer_rsrc_t xres = uniform_rsrc(src, (int)((int64_t)src_rows * K * 2));
-  auto load_x = [&](int rt, int kph) __attribute__((always_inline)) {
-    const int col0 = kph * kpc;
-    const int ncols = min(kpc, K - col0);
-    const int nslots = BM * ncols / 8;
-    int rowoff[NH];
-#pragma unroll
-    for (int h = 0; h < NH; ++h) {   // slot % (BM 16) takes NH values per thread: rows (h THREADS + tid) / 16
-      const int row = (h * THREADS + tid) >> 4;
-      const int i = rt * BM + row;
+  // Source rows of row tile rt into s_rowbase; the caller orders it with a
+  // barrier before load_x reads it.
+  // (ROUTE: the rows of every row tile but the first are read back from the
+  // sorted pairs this workgroup stored in its prologue.)
+  const int32_t* sp_rows = ROUTE ? ra.sorted : sorted_pairs;
+  auto set_rows = [&](int rt) __attribute__((always_inline)) {
+    if (tid < BM) {
+      const int i = rt * BM + tid;
       int base = -1;
       if (i < cnt) {
         if constexpr (MODE == kGateUp)
-          base = min(sorted_pairs[seg + i] / topk, T - 1);
+          base = min(max(sp_rows[seg + i], 0) / topk, T - 1);
         else
           base = seg + i;
       }
-      rowoff[h] = base;
+      s_rowbase[tid] = base;
     }
+  };
+  // ROUTE prologue, pass 2: each of the expert's pairs gets its rank in pair
+  // order (the stable sort); ranks below BM give row tile 0's rows.  Every
+  // workgroup of the expert stores the same sorted pairs (equal values), so
+  // each can read its later row tiles back.
+  auto route_rows0 = [&]() __attribute__((always_inline)) {
+    if (tid < BM) s_rowbase[tid] = -1;
+    __syncthreads();
+    int run = 0;
+    for (int r0 = 0; r0 < Ptot; r0 += THREADS * 8) {
+      int id[8];
+      load_ids8(r0, id);
+      int cs = 0;
+#pragma unroll
+      for (int q = 0; q < 8; ++q) cs += id[q] == e ? 1 : 0;
+      int ex, ts, tb;
+      scan2(cs, 0, ex, ts, tb);
+      int rank = run + ex;
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        if (id[q] == e) {
+          const int pr = r0 + tid * 8 + q;
+          if (rank < BM) s_rowbase[rank] = min(pr / topk, T - 1);
+          ra.sorted[seg + rank] = pr;
+          ++rank;
+        }
+      }
+      run += ts;
+    }
+  };
+  auto load_x = [&](int kph) __attribute__((always_inline)) {
+    const int col0 = kph * kpc;
+    const int ncols = min(kpc, K - col0);
+    const int nslots = BM * ncols / 8;
+    // nslots is a multiple of 1024 (ncols of 128), so a wave's 64 slots are
+    // all in or all past the phase: the copy is skipped per wave, and no LDS
+    // write lands past xs whatever THREADS is.
     for (int p = 0; p * THREADS < nslots; ++p) {
       const int slot = p * THREADS + tid;
+      if (p * THREADS + wave * 64 >= nslots) break;   // wave-uniform
       const int cc = slot / (BM * 16), q = slot % (BM * 16);
       const int row = q >> 4, cg = (q & 15) ^ (row & 15);
-      const int base = rowoff[p % NH];
-      const uint32_t v =
-          (base >= 0 && slot < nslots) ? (uint32_t)(((int64_t)base * K + col0 + cc * kChunkK + cg * 8) * 2) : kOOB;
+      const int base = s_rowbase[row];
+      const uint32_t v = base >= 0 ? (uint32_t)(((int64_t)base * K + col0 + cc * kChunkK + cg * 8) * 2) : kOOB;
       uint16_t* dst = xs + (p * THREADS + wave * 64) * 8;   // wave-uniform
       __builtin_amdgcn_raw_ptr_buffer_load_lds(xres, (__attribute__((address_space(3))) void*)dst, 16, v, 0, 0, 0);
     }
@@ -382,7 +556,7 @@ __global__ __launch_bounds__(WAVES * 64) void moe_stream_kernel(
               // is formed at its true scale and rounded to bf16 (its storage
               // precision); the down product's fp16 copy carries 2^-2ex
               // (|h| <= |z_gate| |z_up|), undone by the combine.
-              const int ex = xexp[min(max(sorted_pairs[seg + row], 0), Ptot - 1) / topk];
+              const int ex = xexp[s_rowbase[i * 16 + r]];   // the row's token (row < cnt)
               const float4_t zg = acc[(0 * NT + t) * MT + i], zu = acc[(1 * NT + t) * MT + i];
               uint32_t hf[2], hb[2];
 #pragma unroll
@@ -419,7 +593,13 @@ __global__ __launch_bounds__(WAVES * 64) void moe_stream_kernel(
   // Prologue: the first phase of X, then P steps of weights in flight; the
   // barrier's fence waits for the X copies only (they were issued first).
   WStage ws[P];
-  load_x(0, 0);
+  if constexpr (ROUTE) {
+    if (!rows0_done) route_rows0();
+  } else {
+    set_rows(0);
+  }
+  __syncthreads();
+  load_x(0);
   static_for<0, P>([&](auto jc) __attribute__((always_inline)) { load_next(ws[decltype(jc)::value]); });
   __syncthreads();
   int cur_rt = 0, cur_kph = 0;
@@ -433,7 +613,11 @@ __global__ __launch_bounds__(WAVES * 64) void moe_stream_kernel(
         const int kph = c / cpp;
         if (kph != cur_kph || rt != cur_rt) {   // uniform: reload the LDS phase
           __syncthreads();
-          load_x(rt, kph);
+          if (rt != cur_rt) {
+            set_rows(rt);
+            __syncthreads();
+          }
+          load_x(kph);
           __syncthreads();
           cur_rt = rt;
           cur_kph = kph;
@@ -489,11 +673,43 @@ __global__ __launch_bounds__(256) void moe_combine_kernel(const uint16_t* __rest
 namespace {
 
 // Streaming-kernel configuration (measured on MI355X).
-constexpr int kMoeWaves = 8;     // waves per workgroup
+// Streaming-kernel configuration (measured on MI355X, T 512, E 128, top-8,
+// H 2048, F 768): 12 gate+up waves (3 a SIMD) with 2 Q4_0 tile pairs (1
+// for Q8_0, whose codes take twice the registers) and 16 down waves (4 a
+// SIMD) with 2 tiles, within the register budgets of those occupancies;
+// 8 waves with 3 / 4 tiles (2 a SIMD) measured 63.6 / 39.0 us (Q4_0) and
+// 108 / 56 us (Q8_0) against 61.4 / 37.0 and 98 / 55.
+#ifndef Q4Q8_MOE_WAVES_G
+#define Q4Q8_MOE_WAVES_G 12
+#endif
+#ifndef Q4Q8_MOE_WAVES_D
+#define Q4Q8_MOE_WAVES_D 16
+#endif
+#ifndef Q4Q8_MOE_NTG4
+#define Q4Q8_MOE_NTG4 2
+#endif
+#ifndef Q4Q8_MOE_NTG8
+#define Q4Q8_MOE_NTG8 1
+#endif
+#ifndef Q4Q8_MOE_PG4
+#define Q4Q8_MOE_PG4 2
+#endif
+#ifndef Q4Q8_MOE_PG8
+#define Q4Q8_MOE_PG8 3
+#endif
+#ifndef Q4Q8_MOE_NTD
+#define Q4Q8_MOE_NTD 2
+#endif
+#ifndef Q4Q8_MOE_PD4
+#define Q4Q8_MOE_PD4 4
+#endif
+#ifndef Q4Q8_MOE_PD8
+#define Q4Q8_MOE_PD8 3
+#endif
+constexpr int kMoeWavesG = Q4Q8_MOE_WAVES_G;   // waves per workgroup, gate+up
+constexpr int kMoeWavesD = Q4Q8_MOE_WAVES_D;   // waves per workgroup, down
 constexpr int kMoeKP = 1024;     // LDS phase columns (64 rows x kMoeKP fp16)
 constexpr int kMoeSlots = 1;     // workgroups per CU the split aims at
-constexpr int kMoeNTG4 = 3, kMoeNTG8 = 2, kMoePG = 2;   // gate+up
-constexpr int kMoeNTD = 4, kMoePD = 3;                  // down
 
 size_t round256(size_t b) { return (b + 255) / 256 * 256; }
 
@@ -518,10 +734,13 @@ MoeWs moe_ws_layout(void* ws, int T, int topk, int H, int F) {
   return w;
 }
 
+// ra: null, or the routed form (the gate+up kernel derives offsets and the
+// sorted pairs from ra->ids and stores them in ra's arrays, which the down
+// kernel then reads).
 template <int FMT>
 void launch_experts(const void* Wg, const void* Wu, const void* Wd, int E, int H, int F, const uint16_t* x16, int T,
                     int topk, const float* gates, const int32_t* offsets, const int32_t* sorted_pairs, float* out,
-                    void* h_out, const MoeWs& w, hipStream_t s) {
+                    void* h_out, const MoeWs& w, hipStream_t s, const MoeRouteArgs* ra = nullptr) {
   const int P = T * topk;
   const int64_t sg = (int64_t)(F / kTileRows) * (H / kChunkK) * Fmt<FMT>::kRecBytes;   // repacked [F, H]
   const int64_t sd = (int64_t)(H / kTileRows) * (F / kChunkK) * Fmt<FMT>::kRecBytes;   // repacked [H, F]
@@ -534,19 +753,29 @@ void launch_experts(const void* Wg, const void* Wu, const void* Wd, int E, int H
     groups = (tpw + nt - 1) / nt;
   };
   // gate+up: tile pairs per group (Q8_0 codes are twice as large), stages.
-  constexpr int NTG = FMT == kQ4_0 ? kMoeNTG4 : kMoeNTG8, PG = kMoePG;
-  constexpr int NTD = kMoeNTD, PD = kMoePD;   // down: tiles per group, stages
+  constexpr int NTG = FMT == kQ4_0 ? Q4Q8_MOE_NTG4 : Q4Q8_MOE_NTG8;
+  constexpr int PG = FMT == kQ4_0 ? Q4Q8_MOE_PG4 : Q4Q8_MOE_PG8;
+  constexpr int NTD = Q4Q8_MOE_NTD;                                    // down: tiles per group
+  constexpr int PD = FMT == kQ4_0 ? Q4Q8_MOE_PD4 : Q4Q8_MOE_PD8;      // down: stages
   int nwe, tpw, groups;
-  split(F / kTileRows, NTG, kMoeWaves, nwe, tpw, groups);
-  moe_stream_kernel<FMT, kGateUp, NTG, PG, kMoeWaves, kMoeKP><<<dim3((unsigned)nwe, (unsigned)E),
-                                                                 dim3(kMoeWaves * 64), 0, s>>>(
-      (const uint8_t*)Wg, (const uint8_t*)Wu, sg, F, H, x16, T, T, topk, P, offsets, sorted_pairs, w.xexp, w.h16,
-      (uint16_t*)h_out, tpw, groups);
-  split(H / kTileRows, NTD, kMoeWaves, nwe, tpw, groups);
-  moe_stream_kernel<FMT, kDown, NTD, PD, kMoeWaves, kMoeKP><<<dim3((unsigned)nwe, (unsigned)E),
-                                                              dim3(kMoeWaves * 64), 0, s>>>(
+  split(F / kTileRows, NTG, kMoeWavesG, nwe, tpw, groups);
+  const dim3 ggrid((unsigned)nwe, (unsigned)E), gblock(kMoeWavesG * 64);
+  if (ra) {
+    moe_stream_kernel<FMT, kGateUp, NTG, PG, kMoeWavesG, kMoeKP, true><<<ggrid, gblock, 0, s>>>(
+        (const uint8_t*)Wg, (const uint8_t*)Wu, sg, F, H, x16, T, T, topk, P, nullptr, nullptr, w.xexp, w.h16,
+        (uint16_t*)h_out, tpw, groups, *ra);
+    offsets = ra->offsets;
+    sorted_pairs = ra->sorted;
+  } else {
+    moe_stream_kernel<FMT, kGateUp, NTG, PG, kMoeWavesG, kMoeKP><<<ggrid, gblock, 0, s>>>(
+        (const uint8_t*)Wg, (const uint8_t*)Wu, sg, F, H, x16, T, T, topk, P, offsets, sorted_pairs, w.xexp, w.h16,
+        (uint16_t*)h_out, tpw, groups, MoeRouteArgs{});
+  }
+  split(H / kTileRows, NTD, kMoeWavesD, nwe, tpw, groups);
+  moe_stream_kernel<FMT, kDown, NTD, PD, kMoeWavesD, kMoeKP><<<dim3((unsigned)nwe, (unsigned)E),
+                                                               dim3(kMoeWavesD * 64), 0, s>>>(
       (const uint8_t*)Wd, nullptr, sd, H, F, w.h16, P, T, topk, P, offsets, sorted_pairs, w.xexp, w.y16, nullptr,
-      tpw, groups);
+      tpw, groups, MoeRouteArgs{});
   moe_combine_kernel<<<dim3((unsigned)((H / 8 + 255) / 256), (unsigned)T), dim3(256), 0, s>>>(w.y16, gates, w.xexp,
                                                                                               T, topk, H, out);
 }
@@ -584,6 +813,43 @@ hipError_t launch_moe_decode_call(int fmt, int xdt, const void* Wg, const void* 
   if (!launch_moe_decode_routed(fmt, xdt, Wg, Wu, Wd, E, H, F, X, T, topk, ro, h, w.y16, w.xexp, out, stream))
     moe_combine_kernel<<<dim3((unsigned)((H / 8 + 255) / 256), (unsigned)T), dim3(256), 0, stream>>>(
         w.y16, ro.gates, w.xexp, T, topk, H, out);
+  return hipGetLastError();
+}
+
+template <int NS>
+static void launch_prep(int xdt, const float* logits, int T, int E, int topk, int32_t* ids, float* gates,
+                        const void* X, int H, uint16_t* x16, int32_t* xexp, hipStream_t s) {
+  const dim3 grid((unsigned)((T + 3) / 4)), block(512);
+  if (xdt == kBF16)
+    moe_prep_kernel<NS, kBF16><<<grid, block, 0, s>>>(logits, T, E, topk, ids, gates, (const uint16_t*)X, H, x16,
+                                                      xexp);
+  else
+    moe_prep_kernel<NS, kF16><<<grid, block, 0, s>>>(logits, T, E, topk, ids, gates, (const uint16_t*)X, H, x16,
+                                                     xexp);
+}
+
+hipError_t launch_moe_forward(int fmt, int xdt, const void* Wg, const void* Wu, const void* Wd, int E, int H, int F,
+                              const void* X, int T, int topk, const MoeRouteOut& ro, float* out, void* h_out,
+                              void* ws, hipStream_t stream) {
+  if (moe_decode_fits(T, H, F))
+    return launch_moe_decode_call(fmt, xdt, Wg, Wu, Wd, E, H, F, X, T, topk, ro, out, h_out, ws, stream);
+  // Three launches before the combine: top-k and the row scaling of every
+  // token; gate+up, whose workgroups find their expert's rows from the ids
+  // (the stable sort, without a sort launch) and store counts, offsets and
+  // the sorted pairs; down.
+  const MoeWs w = moe_ws_layout(ws, T, topk, H, F);
+  if (E <= 64) launch_prep<1>(xdt, ro.logits, T, E, topk, ro.ids, ro.gates, X, H, w.x16, w.xexp, stream);
+  else if (E <= 128) launch_prep<2>(xdt, ro.logits, T, E, topk, ro.ids, ro.gates, X, H, w.x16, w.xexp, stream);
+  else if (E <= 256) launch_prep<4>(xdt, ro.logits, T, E, topk, ro.ids, ro.gates, X, H, w.x16, w.xexp, stream);
+  else if (E <= 512) launch_prep<8>(xdt, ro.logits, T, E, topk, ro.ids, ro.gates, X, H, w.x16, w.xexp, stream);
+  else launch_prep<16>(xdt, ro.logits, T, E, topk, ro.ids, ro.gates, X, H, w.x16, w.xexp, stream);
+  const MoeRouteArgs ra = {ro.ids, ro.counts, ro.offsets, ro.sorted_pairs, E};
+  if (fmt == kQ4_0)
+    launch_experts<kQ4_0>(Wg, Wu, Wd, E, H, F, w.x16, T, topk, ro.gates, nullptr, nullptr, out, h_out, w, stream,
+                          &ra);
+  else
+    launch_experts<kQ8_0>(Wg, Wu, Wd, E, H, F, w.x16, T, topk, ro.gates, nullptr, nullptr, out, h_out, w, stream,
+                          &ra);
   return hipGetLastError();
 }
 

@@ -106,6 +106,12 @@ hipError_t launch_moe_decode_call(int fmt, int xdt, const void* Wg, const void* 
                                   int F, const void* X, int T, int topk, const MoeRouteOut& ro, float* out,
                                   void* h_out, void* ws, hipStream_t s);
 
+// The one-call MoE layer: q4q8_moe_route + q4q8_moe_qgemm's results for any
+// T (the decode call for the few tokens it takes).
+hipError_t launch_moe_forward(int fmt, int xdt, const void* Wg, const void* Wu, const void* Wd, int E, int H, int F,
+                              const void* X, int T, int topk, const MoeRouteOut& ro, float* out, void* h_out,
+                              void* ws, hipStream_t s);
+
 hipError_t launch_moe_qgemm(int fmt, int xdt, const void* Wg, const void* Wu, const void* Wd, int E, int H, int F,
                             const void* X, int T, int topk, const float* gates, const int32_t* offsets,
                             const int32_t* sorted_pairs, float* out, void* h_out, void* ws, hipStream_t stream);

@@ -354,6 +354,24 @@ int q4q8_moe_decode(int fmt, const void* Wg, const void* Wu, const void* Wd,
                     float* out, void* h_out, void* ws, size_t ws_bytes,
                     void* stream);
 
+/* The whole MoE layer in one call for any T: q4q8_moe_route followed by
+ * q4q8_moe_qgemm, with the same results bit for bit (routing arrays, out,
+ * h_out).  Up to the decode path's limits (T <= 8 and T * (max(H, F) + 8)
+ * * 2 + 512 <= 52 KB) it is q4q8_moe_decode.  Above, three launches precede
+ * the combine: top-k plus the activation row scaling (one wave per token),
+ * then gate+up, whose workgroups find their expert's rows from the routed
+ * experts in pair order -- the stable sort, formed in the expert kernel
+ * instead of by a sort kernel (the expert's first workgroup stores its
+ * count, offset and slice of sorted_pairs) -- then down.
+ *   Arguments as q4q8_moe_decode; ws of q4q8_moe_workspace(fmt, T, E, topk,
+ *   H, F) bytes.  Limits as q4q8_moe_route and q4q8_moe_qgemm. */
+int q4q8_moe_forward(int fmt, const void* Wg, const void* Wu, const void* Wd,
+                     int E, int H, int F, const float* logits, const void* X,
+                     int xdt, int T, int topk, int32_t* ids, float* gates,
+                     int32_t* counts, int32_t* offsets, int32_t* sorted_pairs,
+                     float* out, void* h_out, void* ws, size_t ws_bytes,
+                     void* stream);
+
 /* q4q8_moe_decode without a workspace argument, for callers that cannot
  * allocate device memory (code under HIP graph capture, tight serving loops,
  * harnesses that forbid allocation).  The call allocates nothing and calls

@@ -306,3 +306,19 @@ def test_stream_read_validation(q):
         st = L.q4q8_stream_read_timed(_vp(a["buf"]) if a["buf"] else None, a["bytes"],
                                       _vp(a["digest"]) if a["digest"] else None, a["dbytes"], None, None, None)
         assert st == want, (over, st, q.last_error())
+
+
+def test_build_scratch_guard_parses_remarks():
+    """build.py refuses spills in the kernels whose waits are hand-counted;
+    its parser of the compiler's resource remarks finds scratch users."""
+    import importlib.util
+    spec = importlib.util.spec_from_file_location("q4q8_build", os.path.join(ROOT, "gemm_q4_q8_amd", "build.py"))
+    b = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(b)
+    text = ("x.hip:1:1: remark: Function Name: _ZN4q4q812qgemm_kernelILi1E [-Rpass-analysis=kernel-resource-usage]\n"
+            "x.hip:1:1: remark:     VGPRs: 250 [-Rpass-analysis=kernel-resource-usage]\n"
+            "x.hip:1:1: remark:     ScratchSize [bytes/lane]: 16 [-Rpass-analysis=kernel-resource-usage]\n"
+            "x.hip:2:1: remark: Function Name: _ZN4q4q88other_kernel [-Rpass-analysis=kernel-resource-usage]\n"
+            "x.hip:2:1: remark:     ScratchSize [bytes/lane]: 0 [-Rpass-analysis=kernel-resource-usage]\n")
+    assert b._scratch_users(text) == [("_ZN4q4q812qgemm_kernelILi1E [-Rpass-analysis=kernel-resource-usage]", 16)]
+    assert "qgemm_kernel" in b.NO_SCRATCH

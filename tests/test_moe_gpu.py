@@ -415,3 +415,82 @@ def test_moe_activation_range(q, T, xdt):
             one = _run_moe_decode(q, fmt, logits, x, wg, wu, wd, k, H, F)
             for key in ("h", "out"):
                 assert np.array_equal(one[key], two[key]), key
+
+
+def _run_forward(q, fmt, logits, x, wg, wu, wd, k, H, F):
+    """The one-call entry point (q4q8_moe_forward), every output read back."""
+    E = len(wg)
+    Wg, Wu, Wd = _stack(q, fmt, wg, F, H), _stack(q, fmt, wu, F, H), _stack(q, fmt, wd, H, F)
+    L = torch.from_numpy(logits).to(dev())
+    T = logits.shape[0]
+    h = torch.full((T * k, F), float("nan"), dtype=torch.bfloat16, device=dev())
+    route = (torch.full((T, k), -7, dtype=torch.int32, device=dev()), torch.full((T, k), -7.0, device=dev()),
+             torch.full((E,), -7, dtype=torch.int32, device=dev()), torch.full((E + 1,), -7, dtype=torch.int32, device=dev()),
+             torch.full((T * k,), -7, dtype=torch.int32, device=dev()))
+    out, (ids, gates, counts, offsets, sp) = q.moe_forward(fmt, Wg, Wu, Wd, E, H, F, L, act_tensor(x), k, route=route,
+                                                           h_out=h)
+    torch.cuda.synchronize()
+    return dict(ids=ids.cpu().numpy(), gates=gates.cpu().numpy(), counts=counts.cpu().numpy(),
+                offsets=offsets.cpu().numpy(), sp=sp.cpu().numpy(), h=values(h),
+                out=out.cpu().numpy().astype(np.float64))
+
+
+FORWARD_CASES = [
+    # fmt, xdt, T, E, k, H, F
+    (synth.Q4_0, synth.BF16, 40, 8, 2, 256, 128),
+    (synth.Q8_0, synth.F16, 12, 16, 4, 384, 256),     # just past the decode path
+    (synth.Q4_0, synth.F16, 200, 4, 2, 128, 256),     # ~100 rows per expert: two row tiles
+    (synth.Q4_0, synth.BF16, 1000, 16, 5, 128, 128),  # 5000 pairs: two rounds of the in-kernel sort
+    (synth.Q8_0, synth.BF16, 48, 4, 2, 1536, 1152),   # partial LDS phases
+    (synth.Q4_0, synth.BF16, 30, 64, 8, 256, 128),    # many empty experts
+    (synth.Q4_0, synth.BF16, 3, 16, 4, 256, 128),     # the decode path
+]
+
+
+@pytest.mark.parametrize("fmt,xdt,T,E,k,H,F", FORWARD_CASES)
+def test_moe_forward(q, fmt, xdt, T, E, k, H, F):
+    """q4q8_moe_forward (routing and the sort formed inside the expert
+    kernels) against the oracle, and bit for bit against q4q8_moe_route +
+    q4q8_moe_qgemm (routing arrays, h, out)."""
+    seed = 150 + T + E + k
+    logits = synth.router_logits(synth.rng_for(seed, 0), T, E)
+    x = synth.activation(synth.rng_for(seed, 1), (T, H), xdt)
+    wg = [synth.q_weight(synth.rng_for(seed, 1000 + e), fmt, F, H) for e in range(E)]
+    wu = [synth.q_weight(synth.rng_for(seed, 2000 + e), fmt, F, H) for e in range(E)]
+    wd = [synth.q_weight(synth.rng_for(seed, 3000 + e), fmt, H, F) for e in range(E)]
+    one = _run_forward(q, fmt, logits, x, wg, wu, wd, k, H, F)
+    two = _run_moe(q, fmt, logits, x, wg, wu, wd, k, H, F)
+    for key in ("ids", "gates", "offsets", "sp", "h", "out"):
+        assert np.array_equal(one[key], two[key]), key
+    assert np.array_equal(one["counts"], np.diff(two["offsets"]))
+    _check_moe(fmt, logits, x, wg, wu, wd, k, H, F, one, f"moe_forward fmt{fmt} T{T} E{E} k{k} H{H} F{F}")
+
+
+@pytest.mark.parametrize("fmt", [synth.Q4_0, synth.Q8_0])
+def test_moe_forward_full_size(q, fmt):
+    """The MoE workload through q4q8_moe_forward: bit for bit the two-call
+    path (whose full-size parity against the oracle's chain is tested above),
+    routing arrays against the oracle, NaN-free."""
+    cfg = synth.MOE
+    T, E, k, H, F = cfg["T"], cfg["E"], cfg["topk"], cfg["H"], cfg["F"]
+    logits, x, wg, wu, wd = synth.moe(fmt=fmt)
+    one = _run_forward(q, fmt, logits, x, wg, wu, wd, k, H, F)
+    two = _run_moe(q, fmt, logits, x, wg, wu, wd, k, H, F)
+    for key in ("ids", "gates", "offsets", "sp", "h", "out"):
+        assert np.array_equal(one[key], two[key]), key
+    rid, _ = oracle.moe_route(logits, k)
+    rc, ro, rsp = oracle.moe_sort(rid, E)
+    assert np.array_equal(one["ids"], rid) and np.array_equal(one["counts"], rc)
+    assert np.array_equal(one["offsets"], ro) and np.array_equal(one["sp"], rsp)
+    assert np.all(np.isfinite(one["out"]))
+
+
+def test_moe_forward_nan_logits(q):
+    E, k, H, F = 24, 4, 256, 128
+    wg = [synth.q_weight(synth.rng_for(75, 1000 + e), synth.Q4_0, F, H) for e in range(E)]
+    wu = [synth.q_weight(synth.rng_for(75, 2000 + e), synth.Q4_0, F, H) for e in range(E)]
+    wd = [synth.q_weight(synth.rng_for(75, 3000 + e), synth.Q4_0, H, F) for e in range(E)]
+    logits = _nan_logits(76, 40, E)
+    x = synth.activation(synth.rng_for(77, 40), (40, H), synth.BF16)
+    one = _run_forward(q, synth.Q4_0, logits, x, wg, wu, wd, k, H, F)
+    _check_moe(synth.Q4_0, logits, x, wg, wu, wd, k, H, F, one, "moe_forward NaN logits")
