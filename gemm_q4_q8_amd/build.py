@@ -81,6 +81,46 @@ def build(verbose: bool = True) -> str:
     return OUT
 
 
+# Host-side AddressSanitizer + UndefinedBehaviorSanitizer build, for CPU tests
+# of the host code (argument validation, the host repack): every -fsanitize=
+# applies to the host pass only; the device code is built as usual.
+SAN_DIR = os.path.join(BUILD, "san")
+SAN_OUT = os.path.join(SAN_DIR, "libq4q8_san.so")
+SAN_FLAGS = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+             "-Xarch_host", "-fno-omit-frame-pointer", "-g"]
+
+
+def asan_runtime() -> str:
+    """The clang AddressSanitizer runtime to preload into an uninstrumented python."""
+    hits = sorted(glob.glob(os.path.join(os.path.dirname(os.path.dirname(os.path.realpath(_hipcc()))),
+                                         "llvm", "lib", "clang", "*", "lib", "linux", "libclang_rt.asan-x86_64.so")))
+    if not hits:
+        raise RuntimeError("libclang_rt.asan-x86_64.so not found next to hipcc")
+    return hits[-1]
+
+
+def build_sanitized(verbose: bool = True) -> str:
+    os.makedirs(SAN_DIR, exist_ok=True)
+    srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
+
+    def one(src):
+        obj = os.path.join(SAN_DIR, os.path.basename(src) + ".o")
+        r = subprocess.run([_hipcc(), *CFLAGS, *SAN_FLAGS, "-c", src, "-o", obj], capture_output=True, text=True)
+        if r.returncode:
+            raise RuntimeError(f"hipcc (sanitized) failed on {src}:\n{r.stderr}")
+        return obj
+
+    with cf.ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
+        objs = list(ex.map(one, srcs))
+    r = subprocess.run([_hipcc(), "-shared", "-fPIC", f"--offload-arch={ARCH}", *SAN_FLAGS, "-shared-libsan", *objs,
+                        "-o", SAN_OUT], capture_output=True, text=True)
+    if r.returncode:
+        raise RuntimeError(f"link (sanitized) failed:\n{r.stderr}")
+    if verbose:
+        print(f"built {SAN_OUT}")
+    return SAN_OUT
+
+
 if __name__ == "__main__":
     build()
     sys.exit(0)

@@ -79,13 +79,15 @@ const char* q4q8_status_string(int s) {
 
 const char* q4q8_last_error(void) { return g_last_error; }
 
+// Sizes beyond the shape limits every product call enforces (N <= 2^30,
+// K <= 2^24) are bad arguments too: the byte counts would overflow.
 size_t q4q8_canonical_bytes(int fmt, int64_t N, int64_t K) {
-  if (!any_fmt_ok(fmt) || N < 1 || K < 32 || K % 32) return 0;
+  if (!any_fmt_ok(fmt) || N < 1 || K < 32 || K % 32 || N > (1LL << 30) || K > (1LL << 24)) return 0;
   return (size_t)(N * (K / 32) * canon_block(fmt));
 }
 
 size_t q4q8_repacked_bytes(int fmt, int64_t N, int64_t K) {
-  if (!any_fmt_ok(fmt) || N < 1 || K < 32 || K % 32) return 0;
+  if (!any_fmt_ok(fmt) || N < 1 || K < 32 || K % 32 || N > (1LL << 30) || K > (1LL << 24)) return 0;
   return (size_t)repacked(fmt, N, K);
 }
 

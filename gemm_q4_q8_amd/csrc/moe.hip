@@ -243,8 +243,9 @@ hipError_t launch_moe_route(const float* logits, int T, int E, int topk, int32_t
 //     around the LDS reloads;
 //   * at the end of each tile group the epilogue stores h = silu(g) * u
 //     (gate+up) or y at its pair row (down).
-// Every step issues the same weight loads (the ring runs past the end on
-// harmless re-reads), so the compiler's wait counts stay exact.
+// Every step issues the same weight loads (past the last step with an
+// out-of-range offset, which reads zero and moves no memory), so the
+// compiler's wait counts stay exact.
 // ---------------------------------------------------------------------------
 enum { kGateUp = 0, kDown = 1 };
 constexpr int kStreamBM = 64;
@@ -404,13 +405,17 @@ __global__ __launch_bounds__(WAVES * 64) void moe_stream_kernel(
   // Load cursor: (group lg, chunk lc); it advances one chunk per step and
   // wraps over groups (and, implicitly, row tiles: the weights do not depend
   // on the row tile).
-  int lg = 0, lc = 0;
+  // Steps past the last one (the ring's final P) issue the same loads with
+  // an out-of-range offset: they read zero and move no memory, and the
+  // compiler's wait counts stay exact.
+  int lg = 0, lc = 0, ln = 0;
   auto load_next = [&](WStage& s) __attribute__((always_inline)) {
+    const bool live = ln++ < total;
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
       const int lt = lg * NT + t;
       const int so = (lt * nchunks + lc) * REC;
-      const bool ok = lt < tv;
+      const bool ok = live && lt < tv;
 #pragma unroll
       for (int w = 0; w < NW; ++w) {
 #pragma unroll

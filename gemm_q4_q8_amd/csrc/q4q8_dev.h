@@ -234,8 +234,17 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t uniform_rsrc(const void* base,
   return __builtin_amdgcn_make_buffer_rsrc((void*)(((uint64_t)hi << 32) | lo), (short)0, n, 0x00020000);
 }
 
-// silu(z) = z / (1 + exp(-z)), fp32 (the SwiGLU gate activation).
-__device__ __forceinline__ float silu_f32(float z) { return z / (1.0f + expf(-z)); }
+// silu(z) = z sigmoid(z) = z / (1 + 2^(-z log2(e))), fp32 (the SwiGLU gate
+// activation), on the hardware's base-2 exponential and reciprocal (each
+// within about one ulp; the argument's own rounding adds a relative error
+// near 2^-24 |z|).  For finite z the result is within about 1e-5 relative of
+// the exact silu, far below h's bf16 rounding (2^-9).  Large negative z give
+// 2^(+big) = inf and a zero reciprocal, so silu -> -0; large positive z give
+// sigmoid 1.
+__device__ __forceinline__ float silu_f32(float z) {
+  const float e = __builtin_amdgcn_exp2f(-z * 1.44269504088896341f);
+  return z * __builtin_amdgcn_rcpf(1.0f + e);
+}
 
 __device__ __forceinline__ float half_bits_to_float(uint32_t bits16) {
   return (float)__builtin_bit_cast(_Float16, (uint16_t)bits16);

@@ -60,9 +60,10 @@ struct TileCfg {
   static constexpr int XLOADS = MT / 2;          // 16-byte copies per thread per chunk (BM * 16 / 512)
   static constexpr int WLOADS = 2 * NT * NW;     // weight loads per wave per chunk
   static constexpr int STAGE_HALFS = BM * kChunkK;
-  static constexpr int LDS_HALFS = S * STAGE_HALFS;
+  static constexpr int RED_HALFS = 8 * NW * (MT / 2) * NT * 512;   // the K-half reduction (1 KB per tile and wave)
+  static constexpr int LDS_HALFS = S * STAGE_HALFS > RED_HALFS ? S * STAGE_HALFS : RED_HALFS;
   static_assert(MT % 2 == 0 && S >= 3, "tile shape");
-  static_assert(8 * NW * (MT / 2) * NT * 1024 <= LDS_HALFS * 2, "K-half reduction must fit in the ring");
+  static_assert(LDS_HALFS * 2 <= 160 * 1024, "LDS per workgroup");
 };
 
 // Main loop.  wres[w]: weight matrix w restricted to this wave's tiles

@@ -101,12 +101,14 @@ const char* q4q8_last_error(void);
 /* Weight layout (load time)                                                */
 /* ------------------------------------------------------------------------ */
 
-/* Bytes of a canonical N x K matrix: N * (K/32) * (18 | 34).  0 on bad args. */
+/* Bytes of a canonical N x K matrix: N * (K/32) * (18 | 34).  0 on bad args
+ * (including N > 2^30 or K > 2^24, the product calls' shape limits). */
 size_t q4q8_canonical_bytes(int fmt, int64_t N, int64_t K);
 
 /* Bytes of the repacked N x K matrix.  Rows are padded to a multiple of 16
  * and K to a multiple of 128; when N % 16 == 0 and K % 128 == 0 this equals
- * the canonical size (no byte is added).  0 on bad args. */
+ * the canonical size (no byte is added).  0 on bad args (as for
+ * q4q8_canonical_bytes). */
 size_t q4q8_repacked_bytes(int fmt, int64_t N, int64_t K);
 
 /* Convert canonical blocks to the gfx950 layout every product call reads
