@@ -132,8 +132,11 @@ __global__ __launch_bounds__(512) void qgemm_kernel(const uint8_t* __restrict__ 
 // within 2^20 of its largest magnitude converts exactly (bf16 has 8
 // significant bits, fp16 keeps them down to 2^-17), the rest rounds to
 // nearest even with an absolute error below 2^-25 of the scaled row, and the
-// consumer multiplies its fp32 results by 2^e[m].  One workgroup per row:
-// a max pass, then a convert pass that re-reads the row (from L2).
+// consumer multiplies its fp32 results by 2^e[m].  One workgroup per row;
+// rows of up to kRowRegs x 2048 values stay in registers between the max
+// and the conversion, longer ones are read twice (the second time from L2).
+constexpr int kRowRegs = 4;
+
 template <int SRC>
 __global__ __launch_bounds__(256) void rowscale_f16_kernel(const uint16_t* __restrict__ src, int64_t lds_,
                                                            uint16_t* __restrict__ dst, int64_t ldd, int cols8,
@@ -141,10 +144,19 @@ __global__ __launch_bounds__(256) void rowscale_f16_kernel(const uint16_t* __res
   const int64_t row = blockIdx.x;
   const int tid = threadIdx.x;
   const uint16_t* s = src + row * lds_;
-  // Magnitude bits (sign cleared) order bf16 and fp16 values like their
-  // absolute values, with inf and NaN above every finite value.
+  const bool in_regs = cols8 <= kRowRegs * 256;   // uniform
+  u32x4_t v[kRowRegs];
   uint32_t m = 0;
-  for (int c8 = tid; c8 < cols8; c8 += 256) m = max(m, max_mag_bits8(*(const u32x4_t*)(s + c8 * 8)));
+  if (in_regs) {
+#pragma unroll
+    for (int u = 0; u < kRowRegs; ++u) {
+      const int c8 = tid + u * 256;
+      v[u] = c8 < cols8 ? *(const u32x4_t*)(s + c8 * 8) : u32x4_t{0u, 0u, 0u, 0u};
+      m = max(m, max_mag_bits8(v[u]));
+    }
+  } else {
+    for (int c8 = tid; c8 < cols8; c8 += 256) m = max(m, max_mag_bits8(*(const u32x4_t*)(s + c8 * 8)));
+  }
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, off));
   __shared__ uint32_t wmax[4];
@@ -153,9 +165,19 @@ __global__ __launch_bounds__(256) void rowscale_f16_kernel(const uint16_t* __res
   m = max(max(wmax[0], wmax[1]), max(wmax[2], wmax[3]));
   const int e = row_exponent<SRC>(m);
   if (tid == 0) rexp[row] = e;
-  for (int c8 = tid; c8 < cols8p; c8 += 256) {
-    const u32x4_t o = c8 < cols8 ? f16x8_scaled<SRC>(*(const u32x4_t*)(s + c8 * 8), -e) : u32x4_t{0u, 0u, 0u, 0u};
-    *(u32x4_t*)(dst + row * ldd + c8 * 8) = o;
+  if (in_regs) {
+#pragma unroll
+    for (int u = 0; u < kRowRegs; ++u) {
+      const int c8 = tid + u * 256;
+      if (c8 < cols8p)
+        *(u32x4_t*)(dst + row * ldd + c8 * 8) = c8 < cols8 ? f16x8_scaled<SRC>(v[u], -e) : u32x4_t{0u, 0u, 0u, 0u};
+    }
+    for (int c8 = tid + kRowRegs * 256; c8 < cols8p; c8 += 256) *(u32x4_t*)(dst + row * ldd + c8 * 8) = u32x4_t{0u, 0u, 0u, 0u};
+  } else {
+    for (int c8 = tid; c8 < cols8p; c8 += 256) {
+      const u32x4_t o = c8 < cols8 ? f16x8_scaled<SRC>(*(const u32x4_t*)(s + c8 * 8), -e) : u32x4_t{0u, 0u, 0u, 0u};
+      *(u32x4_t*)(dst + row * ldd + c8 * 8) = o;
+    }
   }
 }
 
