@@ -807,7 +807,10 @@ def main():
                 "algorithmic_bytes_per_launch": k_bytes, "mean_kernel_us": round(mean_k * 1e6, 3),
                 "kernel_us_min_median_max": [round(sd[0] * 1e6, 2), round(sd[len(sd) // 2] * 1e6, 2),
                                              round(sd[-1] * 1e6, 2)],
-                "launches_timed": len(durs), "kernel_source_hash": src_hash}
+                "launches_timed": len(durs), "kernel_source_hash": src_hash,
+                # the same launch replayed from a HIP graph, one per step, gaps included
+                "graph_step_us": round(ms_per_step * 1e3, 3),
+                "graph_step_frac": round(step_bytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
     log(f"step kernel mean {mean_k * 1e6:.2f} us (min {sd[0] * 1e6:.2f}, median {sd[len(sd) // 2] * 1e6:.2f}, "
         f"max {sd[-1] * 1e6:.2f}) -> {achieved:.1f} GB/s")
 
