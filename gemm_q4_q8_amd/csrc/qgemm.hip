@@ -6,8 +6,9 @@
 // Best-in-Class LLM Inference on Apple Silicon via Native Metal", technical
 // summary, "Methodologie", prefill optimisation and kernel specialisation;
 // the M5 follow-up review, "Method", routes the prefill GEMM to the matrix
-// units).  Here one workgroup computes a 128 x 192 block (64 x 64 for small
-// M) with the tile engine of qgemm_core.h.  BF16 activations are converted
+// units).  Here one workgroup computes a 128 x 192 block (narrower blocks
+// when M is too small to give every CU one) with the tile engine of
+// qgemm_core.h.  BF16 activations are converted
 // once to fp16 by a small pre-pass into the caller's workspace, each row
 // scaled by a power of two so its largest magnitude lands in [4, 8); the
 // epilogue multiplies the row's results back.  Workgroup ids are remapped so each XCD (ids
@@ -207,16 +208,25 @@ static void launch_tile(const void* W, int64_t N, int64_t K, const void* X, int6
            (const uint8_t*)W, (int)N, (int)K, (const uint16_t*)X, ldx, (int)M, rexp, Y, ldy, m_tiles, n_tiles);
 }
 
-// Tile shape: 128 rows x 192 columns (3 weight tiles per wave); 64 x 64 for
-// small M, where more workgroups matter more than operand reuse.
+// Tile shape: 128 rows x 192 columns (3 weight tiles per wave) when that
+// gives every CU a workgroup; below that, narrower tiles trade operand reuse
+// for workgroups (measured on MI355X, K 4096, N 12288, bf16 in and out, call
+// time including the pre-pass: M = 128: 51 us with 128 x 192 tiles, 31 us
+// with 128 x 64; M = 256: 54 us, 43 us with 128 x 128; 64 x 64 tiles and
+// deeper rings (5-8 stages) measured the same or slower).
 template <int FMT, int YDT>
 static void launch_shape(const void* W, int64_t N, int64_t K, const void* X, int64_t ldx, int64_t M,
                          const int32_t* rexp, void* Y, int64_t ldy, hipStream_t s, const LaunchEvents& ev) {
   constexpr int S = FMT == kQ4_0 ? Q4Q8_GEMM_STAGES_Q4 : FMT == kQ8_0 ? Q4Q8_GEMM_STAGES_Q8 : Q4Q8_GEMM_STAGES_F16;
-  if (M <= 64)
-    launch_tile<FMT, YDT, 4, 1, S>(W, N, K, X, ldx, M, rexp, Y, ldy, s, ev);
-  else
+  const int64_t wide = (M + 127) / 128 * ((N + 191) / 192);
+  if (wide >= 256)
     launch_tile<FMT, YDT, 8, 3, S>(W, N, K, X, ldx, M, rexp, Y, ldy, s, ev);
+  else if (M > 128)
+    launch_tile<FMT, YDT, 8, 2, S>(W, N, K, X, ldx, M, rexp, Y, ldy, s, ev);
+  else if (M > 64)
+    launch_tile<FMT, YDT, 8, 1, S>(W, N, K, X, ldx, M, rexp, Y, ldy, s, ev);
+  else
+    launch_tile<FMT, YDT, 4, 1, S>(W, N, K, X, ldx, M, rexp, Y, ldy, s, ev);
 }
 
 // BF16 activations: one row-scaled fp16 copy [M, Kp], Kp = K rounded up to

@@ -79,10 +79,12 @@ def test_qgemm_zero_weights(q):
     assert torch.all(y.abs() <= 1e-5)
 
 
-@pytest.mark.parametrize("fmt,M", [(synth.Q4_0, 512), (synth.Q4_0, 2048), (synth.Q8_0, 512), (synth.FP16, 512)])
+@pytest.mark.parametrize("fmt,M", [(synth.Q4_0, 128), (synth.Q4_0, 256), (synth.Q4_0, 512), (synth.Q4_0, 2048),
+                                   (synth.Q8_0, 256), (synth.Q8_0, 512), (synth.FP16, 512)])
 def test_qgemm_prefill_full_size_sampled(q, fmt, M):
-    """The prefill shapes (K 4096, N 12288) in the benchmark's launch shape
-    (Q8_0 and fp16 weights drawn as the benchmark draws them); 4096 sampled
+    """The prefill shapes (K 4096, N 12288; M 128 and 256 take the narrower
+    tiles) in the benchmark's launch shape (Q8_0 and fp16 weights drawn as
+    the benchmark draws them); 4096 sampled
     outputs plus every output of the first and last 16-row block against the
     oracle, and NaN/Inf-free everywhere."""
     w, x = synth.prefill(M)
