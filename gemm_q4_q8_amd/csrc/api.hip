@@ -7,6 +7,7 @@
 #include <mutex>
 
 #include "../../include/q4q8.h"
+#include "../../include/q4q8_measure.h"
 #include "q4q8_internal.h"
 
 namespace q4q8 {

@@ -31,7 +31,11 @@
  * Conventions for every call below.
  *   - Ownership: the caller allocates and frees everything (weights,
  *     activations, outputs, workspace).  The library allocates no memory and
- *     keeps no device state.
+ *     keeps no device state, except q4q8_moe_decode_noalloc's static scratch
+ *     array (one per GPU, described there).
+ *   - Measurement: dispatch-timed forms of some calls (q4q8_*_timed) and an
+ *     HBM read probe are exported too; they are declared in q4q8_measure.h,
+ *     apart from the product interface.
  *   - Streams: `stream` is a hipStream_t passed as void* (NULL = the null
  *     stream).  Calls enqueue work and return without synchronising; results
  *     are ready once the stream reaches that point.
@@ -169,14 +173,6 @@ typedef struct {
 int q4q8_qgemv_grouped(int fmt, const q4q8_gemv_desc* descs, int count,
                        int xdt, int M, void* stream);
 
-/* As q4q8_qgemv_grouped, and the dispatch itself records ev_start when the
- * kernel starts and ev_stop when it ends (hipEvent_t handles, either may be
- * NULL), so hipEventElapsedTime gives the kernel's own duration.  For
- * measurement; the result is identical. */
-int q4q8_qgemv_grouped_timed(int fmt, const q4q8_gemv_desc* descs, int count,
-                             int xdt, int M, void* stream,
-                             void* ev_start, void* ev_stop);
-
 /* ------------------------------------------------------------------------ */
 /* Decode FFN: fused gate/up GEMV with a SwiGLU epilogue, then down          */
 /* (technical summary, "Methodologie": kernel fusion of FFN blocks, which    */
@@ -198,14 +194,6 @@ int q4q8_qgemv_grouped_timed(int fmt, const q4q8_gemv_desc* descs, int count,
 int q4q8_qgemv_swiglu(int fmt, const void* Wg, const void* Wu, int64_t F,
                       int64_t K, const void* x, int xdt, int64_t ldx, int M,
                       void* h, int hdt, int64_t ldh, void* stream);
-
-/* As q4q8_qgemv_swiglu, with dispatch-recorded events (see
- * q4q8_qgemv_grouped_timed).  For measurement; the result is identical. */
-int q4q8_qgemv_swiglu_timed(int fmt, const void* Wg, const void* Wu,
-                            int64_t F, int64_t K, const void* x, int xdt,
-                            int64_t ldx, int M, void* h, int hdt,
-                            int64_t ldh, void* stream, void* ev_start,
-                            void* ev_stop);
 
 /* Workspace bytes of q4q8_ffn_decode: the h rows (2 bytes each), M * F * 2
  * rounded up to 256.  0 for M outside 1..8 or F not a positive multiple of 32. */
@@ -229,14 +217,6 @@ int q4q8_ffn_decode(int fmt, const void* Wg, const void* Wu, const void* Wd,
                     int64_t H, int64_t F, const void* x, int xdt,
                     int64_t ldx, int M, float* y, int64_t ldy, void* ws,
                     size_t ws_bytes, void* stream);
-
-/* As q4q8_ffn_decode, with ev_start recorded when the first kernel starts
- * and ev_stop when the second ends.  For measurement. */
-int q4q8_ffn_decode_timed(int fmt, const void* Wg, const void* Wu,
-                          const void* Wd, int64_t H, int64_t F,
-                          const void* x, int xdt, int64_t ldx, int M,
-                          float* y, int64_t ldy, void* ws, size_t ws_bytes,
-                          void* stream, void* ev_start, void* ev_stop);
 
 /* ------------------------------------------------------------------------ */
 /* Prefill: quantised GEMM                                                   */
@@ -268,16 +248,6 @@ int q4q8_qgemm(int fmt, const void* W, int64_t N, int64_t K,
                const void* X, int xdt, int64_t ldx, int64_t M,
                void* Y, int ydt, int64_t ldy, void* ws, size_t ws_bytes,
                void* stream);
-
-/* As q4q8_qgemm, with dispatch-recorded events (see
- * q4q8_qgemv_grouped_timed): ev_start when the first kernel of the call
- * starts, ev_stop when the last ends.  For measurement; the result is
- * identical. */
-int q4q8_qgemm_timed(int fmt, const void* W, int64_t N, int64_t K,
-                     const void* X, int xdt, int64_t ldx, int64_t M,
-                     void* Y, int ydt, int64_t ldy, void* ws,
-                     size_t ws_bytes, void* stream,
-                     void* ev_start, void* ev_stop);
 
 /* ------------------------------------------------------------------------ */
 /* Mixture of experts (review, "Method": MoE expert GEMM and fused expert    */
@@ -420,36 +390,6 @@ size_t q4q8_moe_decode_noalloc_max_scratch(void);
 int q4q8_attn_prefill(int dt, const void* Q, const void* K, const void* V,
                       void* O, int B, int S, int Hq, int Hkv, int D,
                       int causal, float scale, void* stream);
-
-/* As q4q8_attn_prefill, with dispatch-recorded events (see
- * q4q8_qgemv_grouped_timed).  For measurement; the result is identical. */
-int q4q8_attn_prefill_timed(int dt, const void* Q, const void* K,
-                            const void* V, void* O, int B, int S, int Hq,
-                            int Hkv, int D, int causal, float scale,
-                            void* stream, void* ev_start, void* ev_stop);
-
-/* ------------------------------------------------------------------------ */
-/* Measurement helper: the HBM read ceiling the decode GEMV is compared      */
-/* with (not a quantised product)                                           */
-/* ------------------------------------------------------------------------ */
-
-/* Bytes the digest of q4q8_stream_read_timed needs (one word per wave of its
- * fixed grid). */
-size_t q4q8_stream_read_digest_bytes(void);
-
-/* Reads bytes of device memory at buf once, with 16-byte non-temporal loads
- * (the GEMV's weight-load policy) over a grid that fills every CU, and writes
- * per-wave XOR digests of the 32-bit words read to digest, so that XOR-ing
- * every digest word gives the XOR of the buffer.  ev_start / ev_stop
- * (optional, as in q4q8_qgemv_grouped_timed) bracket the kernel; bytes / that
- * time is the streaming read rate.
- *   buf:    device, 16-byte aligned; bytes a multiple of 16 (>= 16).
- *   digest: device, >= q4q8_stream_read_digest_bytes() bytes, 4-byte aligned;
- *           overwritten.
- * Errors: Q4Q8_ERR_INVALID_ARG (null, size), Q4Q8_ERR_ALIGNMENT. */
-int q4q8_stream_read_timed(const void* buf, size_t bytes, uint32_t* digest,
-                           size_t digest_bytes, void* stream,
-                           void* ev_start, void* ev_stop);
 
 #ifdef __cplusplus
 }

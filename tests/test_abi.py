@@ -1,5 +1,6 @@
 """Host-side checks of the C ABI: symbols, validation, host repack (no GPU)."""
 import ctypes
+import glob
 import os
 import re
 
@@ -9,7 +10,7 @@ import pytest
 import synth
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADER = os.path.join(ROOT, "include", "q4q8.h")
+HEADERS = sorted(glob.glob(os.path.join(ROOT, "include", "*.h")))
 
 
 @pytest.fixture(scope="module")
@@ -20,7 +21,7 @@ def q():
 
 
 def _declared_functions():
-    text = open(HEADER).read()
+    text = "\n".join(open(h).read() for h in HEADERS)
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     return sorted(set(re.findall(r"\b(q4q8_[a-z0-9_]+)\s*\(", text)))
 
@@ -322,3 +323,32 @@ def test_build_scratch_guard_parses_remarks():
             "x.hip:2:1: remark:     ScratchSize [bytes/lane]: 0 [-Rpass-analysis=kernel-resource-usage]\n")
     assert b._scratch_users(text) == [("_ZN4q4q812qgemm_kernelILi1E [-Rpass-analysis=kernel-resource-usage]", 16)]
     assert "qgemm_kernel" in b.NO_SCRATCH
+
+
+def test_measurement_calls_live_in_their_own_header():
+    """The product header declares no measurement call; q4q8_measure.h holds
+    them (the library exports both sets)."""
+    prod = re.sub(r"/\*.*?\*/", "", open(os.path.join(ROOT, "include", "q4q8.h")).read(), flags=re.S)
+    meas = re.sub(r"/\*.*?\*/", "", open(os.path.join(ROOT, "include", "q4q8_measure.h")).read(), flags=re.S)
+    prod_names = set(re.findall(r"\b(q4q8_[a-z0-9_]+)\s*\(", prod))
+    meas_names = set(re.findall(r"\b(q4q8_[a-z0-9_]+)\s*\(", meas))
+    assert not [n for n in prod_names if n.endswith("_timed") or "stream_read" in n]
+    assert {"q4q8_qgemv_grouped_timed", "q4q8_qgemm_timed", "q4q8_stream_read_timed",
+            "q4q8_stream_read_digest_bytes"} <= meas_names
+
+
+@pytest.mark.parametrize("name", ["q4q8.h", "q4q8_measure.h"])
+def test_headers_compile_as_c_and_cxx(name, tmp_path):
+    """Each public header is self-contained C99 and C++ (extern "C")."""
+    import shutil
+    import subprocess
+    gcc = shutil.which("gcc")
+    if gcc is None:
+        pytest.skip("no gcc")
+    src = tmp_path / "use.c"
+    src.write_text(f'#include "{name}"\nint main(void) {{ return Q4Q8_OK; }}\n')
+    inc = os.path.join(ROOT, "include")
+    for lang, std in (("c", "-std=c99"), ("c++", "-std=c++17")):
+        r = subprocess.run([gcc, "-x", lang, std, "-Wall", "-Werror", "-fsyntax-only", "-I", inc, str(src)],
+                           capture_output=True, text=True)
+        assert r.returncode == 0, r.stderr
