@@ -155,13 +155,38 @@ class ClockSampler:
                 "samples": len(d)}
 
 
-def stream_ceiling(q, torch, ev: HipEvents):
+def stream_ceiling(q, torch, ev: HipEvents, launch_bytes: int):
     """Measured HBM ceiling on this machine.  Read: the library's read probe
     (q4q8_stream_read_timed: 16-byte non-temporal loads, the GEMV's policy)
     over 4 GiB, bytes / dispatch-event time.  Copy (context): a 1 GiB device
     copy, bytes read + written / time.  Both far larger than the 256 MB
-    Infinity Cache; best and median of 10 repetitions after 2 warm-ups."""
+    Infinity Cache; best and median of 10 repetitions after 2 warm-ups.
+    Read at the launch's size: the same probe over launch_bytes, eight
+    buffers in turn (870 MB, past the Infinity Cache), launched eagerly one
+    after another as the headline's timed launches are, mean of 64, on the
+    best of four grids (2048 .. 16384 workgroups): what one plain read of
+    that many bytes costs, ramp and tail included."""
     out = {}
+    n = launch_bytes // 16 * 16
+    bufs = [torch.empty(n, dtype=torch.uint8, device="cuda:0") for _ in range(8)]
+    digest = None
+    best = None
+    for wgs in (2048, 4096, 8192, 16384):
+        pairs = [(ev.create(), ev.create()) for _ in range(72)]
+        for i, e in enumerate(pairs):
+            digest = q.stream_read(bufs[i % 8], digest=digest, events=e, workgroups=wgs)
+        ts = [ev.elapsed_ms(*e) * 1e-3 for e in pairs[8:]]
+        for e in pairs:
+            ev.destroy(e[0])
+            ev.destroy(e[1])
+        mean = sum(ts) / len(ts)
+        if best is None or mean < best[0]:
+            best = (mean, wgs)
+    out["read_launch_bytes"] = n
+    out["read_launch_us_mean"] = round(best[0] * 1e6, 3)
+    out["read_launch_GB/s"] = round(n / best[0] / 1e9, 1)
+    out["read_launch_workgroups"] = best[1]
+    del bufs, digest
     buf = torch.empty(1 << 32, dtype=torch.uint8, device="cuda:0")
     digest = None
     ts = []
@@ -192,8 +217,9 @@ def stream_ceiling(q, torch, ev: HipEvents):
     del b, c
     torch.cuda.empty_cache()
     out["how"] = ("read: q4q8_stream_read_timed over 4 GiB (non-temporal 16-byte loads), "
-                  "bytes / dispatch-event time, best of 10; copy: torch copy_ of 1 GiB, (read + written) bytes / "
-                  "time, best of 10")
+                  "bytes / dispatch-event time, best of 10; read_launch: the same probe over the headline "
+                  "launch's bytes, 8 buffers in turn, mean of 64 eager launches, best of 4 grids; copy: torch copy_ of 1 GiB, "
+                  "(read + written) bytes / time, best of 10")
     return out
 
 
@@ -817,8 +843,9 @@ def main():
 
     ceiling = None
     if not args.no_ceiling:
-        ceiling = stream_ceiling(q, torch, ev)
+        ceiling = stream_ceiling(q, torch, ev, k_bytes)
         ceiling["headline_kernel_frac_of_read"] = round(achieved / ceiling["read_GB/s"], 4)
+        ceiling["headline_kernel_vs_read_launch"] = round(achieved / ceiling["read_launch_GB/s"], 4)
         roofline["measured_ceiling"] = ceiling
         log(f"measured stream ceiling {json.dumps(ceiling)}")
 

@@ -81,6 +81,7 @@ def _declare(lib):
         "q4q8_moe_decode_noalloc_max_scratch": (sz, []),
         "q4q8_stream_read_digest_bytes": (sz, []),
         "q4q8_stream_read_timed": (i32, [vp, sz, vp, sz, vp, vp, vp]),
+        "q4q8_stream_read_grid_timed": (i32, [vp, sz, i32, vp, sz, vp, vp, vp]),
     }
     for name, (res, args) in sig.items():
         f = getattr(lib, name)
@@ -440,17 +441,23 @@ def attn_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool
 # ----------------------------------------------------------------------------
 # Measurement helper
 # ----------------------------------------------------------------------------
-def stream_read(buf: torch.Tensor, digest: torch.Tensor = None, events=None) -> torch.Tensor:
+def stream_read(buf: torch.Tensor, digest: torch.Tensor = None, events=None, workgroups: int = None) -> torch.Tensor:
     """Read every byte of buf once on the GPU (the HBM read-ceiling probe);
     returns the per-wave XOR digests (int32).  events: optional (start, stop)
-    hipEvent_t handles recorded around the kernel."""
+    hipEvent_t handles recorded around the kernel.  workgroups: the probe's
+    grid (default: the library's, tuned for GiB-sized reads)."""
     _dev(buf, "buf")
     n = int(lib().q4q8_stream_read_digest_bytes())
     if digest is None:
         digest = torch.empty(n // 4, dtype=torch.int32, device=buf.device)
     ev = events or (None, None)
-    st = lib().q4q8_stream_read_timed(_ptr(buf), buf.numel() * buf.element_size(), _ptr(digest),
-                                      digest.numel() * digest.element_size(), _stream(buf),
-                                      ctypes.c_void_p(ev[0]), ctypes.c_void_p(ev[1]))
+    if workgroups is None:
+        st = lib().q4q8_stream_read_timed(_ptr(buf), buf.numel() * buf.element_size(), _ptr(digest),
+                                          digest.numel() * digest.element_size(), _stream(buf),
+                                          ctypes.c_void_p(ev[0]), ctypes.c_void_p(ev[1]))
+    else:
+        st = lib().q4q8_stream_read_grid_timed(_ptr(buf), buf.numel() * buf.element_size(), int(workgroups),
+                                               _ptr(digest), digest.numel() * digest.element_size(), _stream(buf),
+                                               ctypes.c_void_p(ev[0]), ctypes.c_void_p(ev[1]))
     _check(st, "stream_read")
     return digest

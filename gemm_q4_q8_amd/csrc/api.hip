@@ -13,7 +13,8 @@
 namespace q4q8 {
 // HBM read-ceiling probe (csrc/probe.hip), a measurement helper.
 size_t stream_read_digest_bytes();
-hipError_t launch_stream_read(const void* buf, size_t bytes, uint32_t* digest, hipStream_t s,
+int stream_read_max_workgroups();
+hipError_t launch_stream_read(const void* buf, size_t bytes, int workgroups, uint32_t* digest, hipStream_t s,
                               const LaunchEvents& ev);
 }  // namespace q4q8
 
@@ -367,10 +368,13 @@ int q4q8_qgemm_timed(int fmt, const void* W, int64_t N, int64_t K, const void* X
 
 size_t q4q8_stream_read_digest_bytes(void) { return q4q8::stream_read_digest_bytes(); }
 
-int q4q8_stream_read_timed(const void* buf, size_t bytes, uint32_t* digest, size_t digest_bytes, void* stream,
-                           void* ev_start, void* ev_stop) {
+int q4q8_stream_read_grid_timed(const void* buf, size_t bytes, int workgroups, uint32_t* digest,
+                                size_t digest_bytes, void* stream, void* ev_start, void* ev_stop) {
   if (!buf || !digest) return fail(Q4Q8_ERR_INVALID_ARG, "stream_read: null pointer");
   if (bytes < 16 || bytes % 16) return fail(Q4Q8_ERR_INVALID_ARG, "stream_read: bytes=%zu is not a positive multiple of 16", bytes);
+  if (workgroups < 1 || workgroups > q4q8::stream_read_max_workgroups())
+    return fail(Q4Q8_ERR_INVALID_ARG, "stream_read: workgroups=%d outside 1..%d", workgroups,
+                q4q8::stream_read_max_workgroups());
   if (digest_bytes < q4q8::stream_read_digest_bytes())
     return fail(Q4Q8_ERR_INVALID_ARG, "stream_read: digest needs %zu bytes, got %zu", q4q8::stream_read_digest_bytes(),
                 digest_bytes);
@@ -379,7 +383,14 @@ int q4q8_stream_read_timed(const void* buf, size_t bytes, uint32_t* digest, size
   q4q8::LaunchEvents ev;
   ev.start = (hipEvent_t)ev_start;
   ev.stop = (hipEvent_t)ev_stop;
-  return hip_status(q4q8::launch_stream_read(buf, bytes, digest, (hipStream_t)stream, ev), "stream_read");
+  clear_hip_error();
+  return hip_status(q4q8::launch_stream_read(buf, bytes, workgroups, digest, (hipStream_t)stream, ev), "stream_read");
+}
+
+int q4q8_stream_read_timed(const void* buf, size_t bytes, uint32_t* digest, size_t digest_bytes, void* stream,
+                           void* ev_start, void* ev_stop) {
+  return q4q8_stream_read_grid_timed(buf, bytes, q4q8::stream_read_max_workgroups(), digest, digest_bytes, stream,
+                                     ev_start, ev_stop);
 }
 
 int q4q8_moe_route(const float* logits, int T, int E, int topk, int32_t* ids, float* gates, int32_t* counts,

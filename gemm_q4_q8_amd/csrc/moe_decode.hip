@@ -297,6 +297,7 @@ __global__ __launch_bounds__(WAVES * 64) void moe_gemv_kernel(const MoeDecArgs a
 // y to fp16 as the unfused path stores it, and accumulates
 // out[t, n] = sum_j gates[t, j] y_j[n] over j = 0 .. topk-1 in the combine
 // kernel's order: the same values, one launch and no y round trip fewer.
+constexpr int kDcMaxTokens = 4;   // tokens up to which the fused form is used (measured below)
 struct MoeDcArgs {
   const uint8_t* W;          // down weights of expert 0
   int64_t mat_bytes;         // repacked bytes of one expert's [H, F] matrix
@@ -325,13 +326,27 @@ __global__ __launch_bounds__(WAVES * 64) void moe_down_combine_kernel(const MoeD
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int topk = a.topk, KQ = a.kq;
-  for (int i = tid; i <= a.E; i += WAVES * 64) s_off[i] = a.offsets[i];
+  // Both routing loads in one round trip: the offsets (two a thread) and
+  // this thread's sorted pair (the fused path takes at most kDcMaxTokens
+  // tokens, so every pair has a thread).
+  constexpr int THREADS = WAVES * 64;
+  static_assert(2 * THREADS > kDecMaxExperts && kDcMaxTokens * kDecMaxTopk <= THREADS, "one pass of loads");
+  int offv[2];
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const int i = tid + u * THREADS;
+    offv[u] = i <= a.E ? a.offsets[i] : 0;
+  }
+  const int spv = tid < a.npos ? a.sorted_pairs[tid] : -1;
   if (tid < kDecMaxTopk) s_pos[tid] = 0;   // stays in bounds for malformed routing
   __syncthreads();
+#pragma unroll
+  for (int u = 0; u < 2; ++u)
+    if (tid + u * THREADS <= a.E) s_off[tid + u * THREADS] = offv[u];
   // Inverse of the sort for this token's pairs t topk .. t topk + topk - 1.
-  for (int i = tid; i < a.npos; i += WAVES * 64) {
-    const int p = a.sorted_pairs[i] - t * topk;
-    if (p >= 0 && p < topk) s_pos[p] = i;
+  if (tid < a.npos) {
+    const int p = spv - t * topk;
+    if (p >= 0 && p < topk) s_pos[p] = tid;
   }
   __syncthreads();
   const int j = wave / KQ, kw = wave - j * KQ;
@@ -441,8 +456,7 @@ constexpr int kDcWaves = 16;
 // Past 4 tokens the unfused down (one pass over each expert's weights for all
 // of its tokens) plus the combine is faster (measured on MI355X, E 128 top-8
 // H 2048 F 768: fused 21.7/24.5/31.1/44.7 us per step at T = 1/2/4/8 against
-// 23.1/26.5/32.3/42.8 unfused).
-constexpr int kDcMaxTokens = 4;
+// 23.1/26.5/32.3/42.8 unfused): kDcMaxTokens.
 bool down_combine_fits(int topk, int F) {
   return topk >= 1 && topk <= kDecMaxTopk && (int64_t)topk * (F + 8) * 2 + kDecXSlack <= 52 * 1024;
 }

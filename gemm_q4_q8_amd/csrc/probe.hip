@@ -3,7 +3,8 @@
 // Reads a buffer once with 16-byte non-temporal loads (the policy the GEMV's
 // weight loads use), four loads in flight per thread, over a fixed grid of
 // many short workgroups (measured on MI355X: 512-thread workgroups, 64 per
-// CU, beat longer grid-stride loops over fewer of them); each wave folds
+// CU, beat longer grid-stride loops over fewer of them for GiB-sized reads;
+// a caller may pick a smaller grid for a short read); each wave folds
 // what it read into one XOR digest word so the loads cannot be dropped.
 // Bytes read / kernel time is the streaming read rate the quantised GEMV is
 // compared with.
@@ -20,7 +21,7 @@ constexpr int kProbeUnroll = 4;
 
 __global__ __launch_bounds__(kProbeThreads) void stream_read_kernel(const u32x4_t* __restrict__ p, int64_t n16,
                                                                     uint32_t* __restrict__ digest) {
-  const int64_t stride = (int64_t)kProbeBlocks * kProbeThreads;
+  const int64_t stride = (int64_t)gridDim.x * kProbeThreads;
   uint32_t acc = 0;
   int64_t i = (int64_t)blockIdx.x * kProbeThreads + threadIdx.x;
   for (; i + (kProbeUnroll - 1) * stride < n16; i += kProbeUnroll * stride) {
@@ -43,9 +44,12 @@ __global__ __launch_bounds__(kProbeThreads) void stream_read_kernel(const u32x4_
 
 size_t stream_read_digest_bytes() { return (size_t)kProbeBlocks * (kProbeThreads / 64) * sizeof(uint32_t); }
 
-hipError_t launch_stream_read(const void* buf, size_t bytes, uint32_t* digest, hipStream_t s,
+int stream_read_max_workgroups() { return kProbeBlocks; }
+
+// workgroups: 1 .. kProbeBlocks (the caller checks).
+hipError_t launch_stream_read(const void* buf, size_t bytes, int workgroups, uint32_t* digest, hipStream_t s,
                               const LaunchEvents& ev) {
-  launch(stream_read_kernel, dim3(kProbeBlocks), dim3(kProbeThreads), 0, s, ev, (const u32x4_t*)buf,
+  launch(stream_read_kernel, dim3((unsigned)workgroups), dim3(kProbeThreads), 0, s, ev, (const u32x4_t*)buf,
          (int64_t)(bytes / 16), digest);
   return hipGetLastError();
 }

@@ -83,6 +83,17 @@ int q4q8_stream_read_timed(const void* buf, size_t bytes, uint32_t* digest,
                            size_t digest_bytes, void* stream,
                            void* ev_start, void* ev_stop);
 
+/* As q4q8_stream_read_timed over a grid of `workgroups` 512-thread
+ * workgroups (1 .. 16384; q4q8_stream_read_timed takes 16384, the best
+ * grid for GiB-sized reads), so that a short read can be timed on the grid
+ * that suits its size.  Only the digest words of those workgroups (the
+ * first workgroups * 8) are written.
+ * Errors: as q4q8_stream_read_timed, and Q4Q8_ERR_INVALID_ARG for
+ * workgroups outside 1 .. 16384. */
+int q4q8_stream_read_grid_timed(const void* buf, size_t bytes, int workgroups,
+                                uint32_t* digest, size_t digest_bytes,
+                                void* stream, void* ev_start, void* ev_stop);
+
 #ifdef __cplusplus
 }
 #endif

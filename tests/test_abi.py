@@ -307,6 +307,10 @@ def test_stream_read_validation(q):
         st = L.q4q8_stream_read_timed(_vp(a["buf"]) if a["buf"] else None, a["bytes"],
                                       _vp(a["digest"]) if a["digest"] else None, a["dbytes"], None, None, None)
         assert st == want, (over, st, q.last_error())
+    for wgs in (0, -1, 16385):   # the grid form: workgroups outside 1 .. 16384
+        st = L.q4q8_stream_read_grid_timed(_vp(ok["buf"]), ok["bytes"], wgs, _vp(ok["digest"]), ok["dbytes"],
+                                           None, None, None)
+        assert st == -1, (wgs, st, q.last_error())
 
 
 def test_build_scratch_guard_parses_remarks():

@@ -30,3 +30,18 @@ def test_stream_read_digest(q, n16):
     digest2 = q.stream_read(buf, digest=digest)
     torch.cuda.synchronize()
     assert np.bitwise_xor.reduce(digest2.cpu().numpy().view(np.uint32)) == np.bitwise_xor.reduce(host)
+
+
+@pytest.mark.parametrize("wgs", [1, 2048, 8192])
+def test_stream_read_grid_digest(q, wgs):
+    """The grid form (a caller-chosen number of workgroups) also reads every
+    byte once: the XOR of the digest words of its wgs * 8 waves equals the
+    buffer's."""
+    n16 = 1000003
+    rng = np.random.default_rng(91 + wgs)
+    host = rng.integers(0, 2**32, size=4 * n16, dtype=np.uint32)
+    buf = torch.from_numpy(host.view(np.int32)).to(dev())
+    digest = q.stream_read(buf, workgroups=wgs)
+    torch.cuda.synchronize()
+    got = np.bitwise_xor.reduce(digest.cpu().numpy().view(np.uint32)[: wgs * 8])
+    assert got == np.bitwise_xor.reduce(host)
