@@ -88,7 +88,11 @@ __global__ __launch_bounds__(kAttnWaves * 64, 2) void attn_prefill_kernel(const 
   // Otherwise one query block each, and the dispatch order puts heavy blocks
   // first in the first half of the grid and light ones first in the second,
   // so workgroups b and b + half, which tend to share a CU, balance.
-  const int bid = blockIdx.x;
+  // Workgroup i runs on XCD i % 8: with the paired split each XCD takes a
+  // contiguous range of (batch, head) pairs, so a key/value head's K and V
+  // stay in one XCD's L2 (measured: S 2048 causal 80.6 -> 77.3 us).
+  int bid = blockIdx.x;
+  if (a.paired && gridDim.x % 8 == 0) bid = (bid % 8) * (gridDim.x / 8) + bid / 8;
   int pi, bh, nparts;
   if (a.paired) {
     pi = bid % a.per_bh;
@@ -138,14 +142,18 @@ __global__ __launch_bounds__(kAttnWaves * 64, 2) void attn_prefill_kernel(const 
   // V: global -> registers -> LDS transposed.  Thread t takes keys
   // 4 (t % 16) .. + 3 at d 8 (t / 16) .. + 7 and writes, for each d, the four
   // keys as one 8-byte word of V^T.
+  // V by buffer loads (past S: out of range, zero) rather than global loads
+  // under a branch (measured: S 2048 causal 77 -> 70 us).
   const int vk0 = 4 * (tid & 15), vd0 = 8 * (tid >> 4);
+  const __amdgpu_buffer_rsrc_t vres = uniform_rsrc(vb, (int)((int64_t)S * kvstride * 2));
   u32x4_t st[4];
   auto fetch_v = [&](int blk) {
     const int n0 = blk * kAttnBN;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int key = n0 + vk0 + i;
-      st[i] = key < S ? *(const u32x4_t*)(vb + (int64_t)key * kvstride + vd0) : u32x4_t{0, 0, 0, 0};
+      const uint32_t off = key < S ? (uint32_t)(((int64_t)key * kvstride + vd0) * 2) : 0x80000000u;
+      st[i] = __builtin_amdgcn_raw_buffer_load_b128(vres, off, 0, 0);
     }
   };
   auto stash_v = [&](int buf) {
