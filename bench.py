@@ -404,10 +404,10 @@ def extra_workloads(q, torch, synth, ev: HipEvents, quick: bool, only=None):
         lay = DecodeLayer(q, torch, synth, M, LAYER_COPIES)
         for mode in (["chain"] if M == 1 else ["one", "chain"]):
             lay.mode = mode
-            dt = time_graph_steps(torch, lay, 200, 16)
+            dt = time_graph_steps(torch, lay, 2000, 200)   # settled step time, as for the headline
             rec = {"workload": f"8B layer decode step M={M}, " + (
                 "one grouped launch" if mode == "one" else "dependency order (4 launches)"),
-                "GB/s": round(lay.step_bytes() * 200 / dt / 1e9, 1), "us_per_step": round(dt / 200 * 1e6, 2)}
+                "GB/s": round(lay.step_bytes() * 2000 / dt / 1e9, 1), "us_per_step": round(dt / 2000 * 1e6, 2)}
             if mode == "chain":
                 mean_k, _ = time_dominant_kernel(q, lay, ev, 32, "gate_up")
                 rec["gate_up_kernel_us"] = round(mean_k * 1e6, 2)
@@ -514,11 +514,11 @@ def attn_workloads(q, torch, synth, ev: HipEvents, quick: bool):
         qa, ka, va = synth.attention_inputs(c["B"], S, c["Hq"], c["Hkv"], c["D"], c["dt"], c["seed"])
         t = [torch.from_numpy(a.bits.view("int16")).view(torch.bfloat16).to(dev) for a in (qa, ka, va)]
         o = torch.empty_like(t[0])
-        reps = 24
-        pairs = [(ev.create(), ev.create()) for _ in range(reps + 4)]
+        reps, warm = 200, 40   # back to back: the settled time
+        pairs = [(ev.create(), ev.create()) for _ in range(reps + warm)]
         for pr in pairs:
             q.attn_prefill(*t, causal=True, out=o, events=pr)
-        d = sorted(ev.elapsed_ms(a, b) * 1e-3 for a, b in pairs[4:])
+        d = sorted(ev.elapsed_ms(a, b) * 1e-3 for a, b in pairs[warm:])
         for a, b in pairs:
             ev.destroy(a)
             ev.destroy(b)
@@ -591,10 +591,10 @@ def ffn_workloads(q, torch, synth, ev: HipEvents, quick: bool):
         with torch.cuda.graph(g):
             for i in range(LAYER_COPIES):
                 step(i)
-        for _ in range(4):
+        for _ in range(25):
             g.replay()
         torch.cuda.synchronize()
-        reps = 25
+        reps = 250   # 2000 steps: the settled step time
         t0 = time.perf_counter()
         for _ in range(reps):
             g.replay()
@@ -638,11 +638,14 @@ def prefill_workloads(q, torch, synth, ev: HipEvents, quick: bool):
         X = torch.from_numpy(x.bits.view("int16")).view(torch.bfloat16).to(dev)
         Y = torch.empty((M, w.N), dtype=torch.bfloat16, device=dev)
         wsp = torch.empty(q.qgemm_workspace(synth.BF16, M, w.K), dtype=torch.uint8, device=dev)
-        reps = 24
-        pairs = [(ev.create(), ev.create()) for _ in range(reps + 4)]
-        for i in range(reps + 4):
+        reps, warm = 200, 40   # back to back: the settled time
+        pairs = [(ev.create(), ev.create()) for _ in range(reps + warm)]
+        for i in range(reps + warm):
             q.qgemm(fmt, Ws[i % 4], w.N, w.K, X, out=Y, ws=wsp, events=pairs[i])
-        d = sorted(ev.elapsed_ms(a, b) * 1e-3 for a, b in pairs[4:])
+        d = sorted(ev.elapsed_ms(a, b) * 1e-3 for a, b in pairs[warm:])
+        for a, b in pairs:
+            ev.destroy(a)
+            ev.destroy(b)
         mean = sum(d) / len(d)
         fl = 2.0 * M * w.N * w.K
         # The MFMA peak assumes 2.4 GHz: sample the clock over ~0.25 s of back-to-back calls.
@@ -699,7 +702,7 @@ def moe_workload(q, torch, synth, fmt: int = 1):
     roof = max(wbytes / (HBM_PEAK_GBS * 1e9), fl / (F16_MFMA_PEAK_TFLOPS * 1e12))
     res = []
     for name, step in (("one call, moe_forward", step_one), ("moe_route + moe_qgemm", step_two)):
-        dt = _time_launches(torch, step, 30)
+        dt = _time_launches(torch, step, 300, warmup=30)   # ~40 ms: the settled step time
         res.append({"workload": f"{synth.FORMAT_NAME[fmt]} moe T={T} E={E} top{k} H={H} F={F} (bf16 tokens; {name})",
                     "step_us": round(dt * 1e6, 2),
                     "TFLOP/s": round(fl / dt / 1e12, 1),
@@ -764,10 +767,10 @@ def moe_decode_workloads(q, torch, synth, quick: bool):
             with torch.cuda.graph(g):
                 for i in range(sets):
                     step(i)
-            for _ in range(3):
+            for _ in range(12):
                 g.replay()
             torch.cuda.synchronize()
-            reps = 20
+            reps = 125   # 2000 steps: the settled step time
             t0 = time.perf_counter()
             for _ in range(reps):
                 g.replay()
@@ -785,8 +788,11 @@ def moe_decode_workloads(q, torch, synth, quick: bool):
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=800)
-    ap.add_argument("--warmup", type=int, default=80)
+    # 4000 steps after 400 warm-up ones take ~0.1 s of GPU time; the step time
+    # settles after a few thousand steps (measured on MI355X: 22.1-22.7 us a
+    # step over the first 800 after 80, 20.7 us over 4000 after 400).
+    ap.add_argument("--steps", type=int, default=4000)
+    ap.add_argument("--warmup", type=int, default=400)
     ap.add_argument("--kernel-reps", type=int, default=64)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-extra", action="store_true", help="skip the other workloads")
