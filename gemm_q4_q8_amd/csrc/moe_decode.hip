@@ -96,13 +96,30 @@ __global__ __launch_bounds__(WAVES * 64) void moe_gemv_kernel(const MoeDecArgs a
   __shared__ int32_t s_pair[kMoeDecodeMaxTokens];
   __shared__ uint32_t s_rmax[kMoeDecodeMaxTokens];   // gate/up: magnitude bits of each row's largest |x|
   __shared__ int32_t s_ex[kMoeDecodeMaxTokens];      // each row's exponent
-  if (tid < kMoeDecodeMaxTokens) s_rmax[tid] = 0;    // ordered by the routing's barriers below
+  if (tid < kMoeDecodeMaxTokens) s_rmax[tid] = 0;    // ordered by a barrier before the first atomicMax
   int e, r0, M;
   if constexpr (ROUTED) {
     __shared__ int32_t s_ids[kMoeDecodeMaxTokens * kDecMaxTopk];
     __shared__ float s_gates[kMoeDecodeMaxTokens * kDecMaxTopk];
     __shared__ int32_t s_sorted[kMoeDecodeMaxTokens * kDecMaxTopk];
     const int npos = a.npos;
+    // Every token's row (T <= 4), staged raw while the routing runs: row t
+    // at xs + t (K + 8), its largest magnitude into s_rmax[t].  The expert's
+    // rows are then a subset, read through their token index.
+    __syncthreads();   // s_rmax cleared before any atomicMax
+    {
+      const int per_row = a.K / 8 + 1;
+      const int pieces = a.T * per_row + kDecXSlack / 16;
+      for (int i = tid; i < pieces; i += WAVES * 64) {
+        const int t = i / per_row, k8 = i - t * per_row;
+        u32x4_t v = u32x4_t{0, 0, 0, 0};
+        if (t < a.T && k8 < a.K / 8) {
+          v = *(const u32x4_t*)(a.X + (int64_t)t * a.ldx + k8 * 8);
+          atomicMax(&s_rmax[t], max_mag_bits8(v));
+        }
+        *(u32x4_t*)(xs + i * 8) = v;
+      }
+    }
     if ((tid >> 6) < a.T) topk_token<ROUTED ? RNS : 1>(a.logits, tid >> 6, a.E, a.topk, tid & 63, s_ids, s_gates);
     __syncthreads();
     if (tid < npos) {   // rank of pair tid in the stable order by (expert, pair id)
@@ -194,7 +211,22 @@ __global__ __launch_bounds__(WAVES * 64) void moe_gemv_kernel(const MoeDecArgs a
 #pragma unroll
   for (int p = 0; p < P; ++p) gemv_load<FMT>(st[p], wres, ks + p * KSH, lane, r);
   const int per_row = K / 8 + 1;
-  const int pieces = M * per_row + kDecXSlack / 16;
+  // ROUTED: every token's row is in LDS already (row t = token t); its
+  // exponent, then the scaled fp16 copy in place.
+  const int pieces = ROUTED ? 0 : M * per_row + kDecXSlack / 16;
+  if constexpr (ROUTED) {
+    if (tid < kMoeDecodeMaxTokens) {
+      const int ex = row_exponent<SRC>(s_rmax[tid]);
+      s_ex[tid] = ex;
+      if (blockIdx.x == 0 && tid < a.T) a.xexp[tid] = ex;   // the down kernel's and combine's copy
+    }
+    __syncthreads();
+    for (int i = tid; i < a.T * per_row; i += WAVES * 64) {   // the pieces this thread staged
+      const int t = i / per_row;
+      if (i - t * per_row < K / 8) *(u32x4_t*)(xs + i * 8) = f16x8_scaled<SRC>(*(const u32x4_t*)(xs + i * 8),
+                                                                              -s_ex[t]);
+    }
+  }
   for (int i = tid; i < pieces; i += WAVES * 64) {
     const int mm = i / per_row, k8 = i - mm * per_row;
     u32x4_t v = u32x4_t{0, 0, 0, 0};
@@ -209,7 +241,7 @@ __global__ __launch_bounds__(WAVES * 64) void moe_gemv_kernel(const MoeDecArgs a
     }
     *(u32x4_t*)(xs + i * 8) = v;
   }
-  if constexpr (MODE == kDecGateUp) {
+  if constexpr (MODE == kDecGateUp && !ROUTED) {
     __syncthreads();
     if (tid < kMoeDecodeMaxTokens) {
       const int ex = row_exponent<SRC>(s_rmax[tid]);
@@ -224,7 +256,9 @@ __global__ __launch_bounds__(WAVES * 64) void moe_gemv_kernel(const MoeDecArgs a
     }
   }
   __syncthreads();
-  const uint16_t* xrow = xs + (mvalid ? m : 0) * (K + 8) + 8 * g;
+  // The lane's activation row in LDS: row m, or (ROUTED) its token's row.
+  const int xr = ROUTED ? (mvalid ? s_pair[m] / a.topk : 0) : (mvalid ? m : 0);
+  const uint16_t* xrow = xs + xr * (K + 8) + 8 * g;
 
   float acc[NI];
 #pragma unroll
@@ -265,7 +299,8 @@ __global__ __launch_bounds__(WAVES * 64) void moe_gemv_kernel(const MoeDecArgs a
       if (MODE == kDecGateUp) {   // z = 2^ex acc: h at its true scale
         float u = red[wave + KSH][i][lane];
         for (int w = 1; w < KSH; ++w) u += red[wave + KSH + w][i][lane];
-        const int ex = s_ex[min(4 * i + g, kMoeDecodeMaxTokens - 1)];
+        const int mo = min(4 * i + g, kMoeDecodeMaxTokens - 1);
+        const int ex = ROUTED ? s_ex[s_pair[min(mo, M - 1)] / a.topk] : s_ex[mo];   // exponents by token (ROUTED) or row
         v = silu_f32(__builtin_ldexpf(v, ex)) * __builtin_ldexpf(u, ex);
       }
       acc[i] = v;
