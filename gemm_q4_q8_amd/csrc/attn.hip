@@ -23,7 +23,9 @@
 //     for lane group g; V is stored transposed in LDS ([d][key]) so that the
 //     A operand reads those keys as two 8-byte runs;
 //   * O^T accumulates in fp32 (lane (r, g) holds O[query r][d 16 t + 4 g + v])
-//     and is rescaled by exp2(m_old - m_new) when the max moves.
+//     and is rescaled by exp2(m_old - m_new) when the reference max moves
+//     (only by more than a fixed headroom, so rarely); the row sums come
+//     from one more MFMA per key step against a V^T tile of ones.
 // Causal masking skips key blocks past the query block's last query and
 // masks the diagonal blocks per element (in a separate instance of the block
 // step); each workgroup takes a light and a heavy query block in turn.
@@ -39,7 +41,9 @@ constexpr int kAttnWaves = 4;
 // 16-query tiles per wave: QT (2, or 1 when the grid would leave CUs
 // without a second workgroup); 16 QT kAttnWaves queries per workgroup.
 constexpr int kAttnBN = 64;                  // keys per block
-constexpr int kVStride = kAttnBN + 12;       // V^T rows in LDS (halfs; +8 measured slower)
+// Headroom of the softmax's reference max (log2 units): P values stay at or
+// below 2^8, well inside the fp16 and bf16 operand ranges.
+constexpr float kAttnSlack = 8.0f;
 
 struct AttnArgs {
   const uint16_t* q;
@@ -68,18 +72,35 @@ __device__ __forceinline__ uint32_t pack_rn(float lo, float hi) {
   }
 }
 
+// Transposed LDS read of four 16-bit values (ds_read_b64_tr_b16).
+__device__ __forceinline__ u32x2_t read_tr16(const uint16_t* p) {
+  typedef short short4_t __attribute__((ext_vector_type(4)));
+  return __builtin_bit_cast(
+      u32x2_t, __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) short4_t*)(p)));
+}
+
+// max(a, b) and max(a, b, c) that return NaN if any operand is NaN
+// (v_maximum_f32 / v_maximum3_f32; fmaxf would first canonicalise every
+// operand that comes out of an MFMA).
+__device__ __forceinline__ float maxf(float a, float b) { return __builtin_elementwise_maximum(a, b); }
+__device__ __forceinline__ float max3f(float a, float b, float c) {
+  return __builtin_elementwise_maximum(__builtin_elementwise_maximum(a, b), c);
+}
+
 template <int DT, int QT>
 __global__ __launch_bounds__(kAttnWaves * 64, 2) void attn_prefill_kernel(const AttnArgs a) {
   typedef typename Op<DT>::vec vec;
+  constexpr uint32_t kOnes2 = DT == kBF16 ? 0x3F803F80u : 0x3C003C00u;   // (1, 1) in the operand type
   constexpr int kAttnQT = QT;
   constexpr int kAttnBM = 16 * QT * kAttnWaves;   // queries per workgroup
-  // Two buffers of K and V^T: block j + 1 is written while block j is read.
-  // K: 16-byte column group cg of key k at slot 16 k + (cg ^ (k % 16)),
-  // written by the buffer loads' LDS path (1 KB contiguous per wave
-  // instruction, so no row padding: the XOR keeps the fragment reads on
-  // distinct banks).  V^T: [d][key], rows kVStride halfs apart.
+  // Two buffers of K and V: block j + 1 is written while block j is read,
+  // both by the buffer loads' LDS path (1 KB contiguous per wave instruction,
+  // so rows cannot be padded; XOR swizzles of the 16-byte column groups keep
+  // the fragment reads on distinct banks).  K: column group cg of key k at
+  // slot 16 k + (cg ^ (k % 16)).  V: column group cg of key k at slot
+  // 16 k + (cg ^ 2 (k % 8)), read transposed (ds_read_b64_tr_b16).
   __shared__ __attribute__((aligned(1024))) uint16_t ks_buf[2][kAttnBN * kAttnD];
-  __shared__ __attribute__((aligned(16))) uint16_t vts_buf[2][kAttnD * kVStride];
+  __shared__ __attribute__((aligned(1024))) uint16_t vs_buf[2][kAttnBN * kAttnD];
 
   // Work split.  Paired (causal, enough work for two workgroups per CU):
   // workgroup i of a (batch, head) takes query blocks i and mblocks - 1 - i
@@ -124,60 +145,75 @@ __global__ __launch_bounds__(kAttnWaves * 64, 2) void attn_prefill_kernel(const 
   int m0 = 0, wq0 = 0, nblocks = 0;
   vec qf[kAttnQT][kAttnD / 32];
 
-  // K: global -> LDS by the buffer loads' LDS path, 4 copies of 16 bytes per
-  // lane; copy p of wave w fills slots 64 (4 p + w) .. + 63.
-  const __amdgpu_buffer_rsrc_t kres = uniform_rsrc(kb, (int)((int64_t)S * kvstride * 2));
-  auto copy_k = [&](int blk, int buf) {
+  // K and V of key block blk are read through a buffer resource that starts
+  // at the block's first key and ends at key S - 1, so keys past S read zero
+  // by the resource's range check and the per-lane offsets stay fixed.
+  auto block_rsrc = [&](const uint16_t* base, int blk) __attribute__((always_inline)) {
     const int n0 = blk * kAttnBN;
+    return uniform_rsrc(base + (int64_t)n0 * kvstride, (int)((int64_t)(S - n0) * kvstride * 2));
+  };
+  // K: global -> LDS by the buffer loads' LDS path, 4 copies of 16 bytes per
+  // lane; copy p of wave w fills slots 64 (4 p + w) .. + 63, i.e. key
+  // 16 p + 4 w + g of the block, column group r ^ (key % 16).
+  uint32_t koff[4];
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    const int key = 16 * p + 4 * wave + g, cg = r ^ (key & 15);
+    koff[p] = (uint32_t)((key * kvstride + cg * 8) * 2);
+  }
+  auto copy_k = [&](int blk, int buf) {
+    const __amdgpu_buffer_rsrc_t kres = block_rsrc(kb, blk);
 #pragma unroll
     for (int p = 0; p < 4; ++p) {
-      const int slot = (4 * p + wave) * 64 + lane;
-      const int key = slot >> 4, cg = (slot & 15) ^ (key & 15);
-      const uint32_t off = n0 + key < S ? (uint32_t)(((int64_t)(n0 + key) * kvstride + cg * 8) * 2) : 0x80000000u;
       uint16_t* dst = ks_buf[buf] + (4 * p + wave) * 64 * 8;   // wave-uniform
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(kres, (__attribute__((address_space(3))) void*)dst, 16, off, 0, 0,
-                                               0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(kres, (__attribute__((address_space(3))) void*)dst, 16, koff[p], 0,
+                                               0, 0);
     }
   };
-  // V: global -> registers -> LDS transposed.  Thread t takes keys
-  // 4 (t % 16) .. + 3 at d 8 (t / 16) .. + 7 and writes, for each d, the four
-  // keys as one 8-byte word of V^T.
-  // V by buffer loads (past S: out of range, zero) rather than global loads
-  // under a branch (measured: S 2048 causal 77 -> 70 us).
-  const int vk0 = 4 * (tid & 15), vd0 = 8 * (tid >> 4);
-  const __amdgpu_buffer_rsrc_t vres = uniform_rsrc(vb, (int)((int64_t)S * kvstride * 2));
-  u32x4_t st[4];
-  auto fetch_v = [&](int blk) {
-    const int n0 = blk * kAttnBN;
+  // V: the same copies as K with V's swizzle: slot 16 key + r holds column
+  // group r ^ 2 (key % 8) of key 16 p + 4 w + g.
+  uint32_t voff[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int key = n0 + vk0 + i;
-      const uint32_t off = key < S ? (uint32_t)(((int64_t)key * kvstride + vd0) * 2) : 0x80000000u;
-      st[i] = __builtin_amdgcn_raw_buffer_load_b128(vres, off, 0, 0);
-    }
-  };
-  auto stash_v = [&](int buf) {
-    uint16_t* vt = vts_buf[buf];
+  for (int p = 0; p < 4; ++p) {
+    const int key = 16 * p + 4 * wave + g, cg = r ^ (2 * (key & 7));
+    voff[p] = (uint32_t)((key * kvstride + cg * 8) * 2);
+  }
+  auto copy_v = [&](int blk, int buf) {
+    const __amdgpu_buffer_rsrc_t vres = block_rsrc(vb, blk);
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      // Half j of the four keys' words: low halves (j even) or high halves.
-      const int w = j >> 1;
-      const uint32_t sel = (j & 1) ? 0x07060302u : 0x05040100u;
-      *(u32x2_t*)(vt + (vd0 + j) * kVStride + vk0) =
-          u32x2_t{__builtin_amdgcn_perm(st[1][w], st[0][w], sel), __builtin_amdgcn_perm(st[3][w], st[2][w], sel)};
+    for (int p = 0; p < 4; ++p) {
+      uint16_t* dst = vs_buf[buf] + (4 * p + wave) * 64 * 8;   // wave-uniform
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(vres, (__attribute__((address_space(3))) void*)dst, 16, voff[p], 0,
+                                               0, 0);
     }
   };
 
   float4_t acc_o[kAttnQT][kAttnD / 16];
-  float m_run[kAttnQT], l_run[kAttnQT];
+  // Row sums of P by the matrix cores: O^T's extra tile with V^T all ones
+  // (every register of lane (r, g) then holds the sum for query r, taken over
+  // the rounded P that the product uses).
+  float4_t acc_l[kAttnQT];
+  float m_run[kAttnQT];
+  const vec ones = __builtin_bit_cast(vec, u32x4_t{kOnes2, kOnes2, kOnes2, kOnes2});
 
   // Per-lane LDS offsets (halfs): K fragment of key tile t, d step s at
-  // 2048 t + kofs[s]; V^T fragment of d tile t, key step s at
-  // 1216 t + 32 s + vofs (the rest folds into instruction offsets).
+  // 2048 t + kofs[s]; V fragment of d tile t, keys 32 s + 16 h + .. at
+  // 4096 s + 2048 h + vofs[t] (the rest folds into instruction offsets).
   int kofs[kAttnD / 32];
 #pragma unroll
   for (int s = 0; s < kAttnD / 32; ++s) kofs[s] = 128 * r + 8 * ((4 * s + g) ^ r);
-  const int vofs = r * kVStride + 4 * g;
+  // The transposed read: in each 16-lane group, lane 4 i + q names four
+  // adjacent halfs of row i of a 4 x 16 block, and lane j receives column j,
+  // rows 0..3.  Lane (r, g) names key 4 g + i (i = r / 4), d 16 t + 4 q
+  // (q = r % 4), so it receives V[4 g + 0..3][16 t + r]: the A operand's keys
+  // 4 g .. 4 g + 3 of V^T (and, 16 keys on, 16 + 4 g ..), in the key order
+  // the P^T operand uses.
+  int vofs[kAttnD / 16];
+#pragma unroll
+  for (int t = 0; t < kAttnD / 16; ++t) {
+    const int key = 4 * g + (r >> 2), q = r & 3;
+    vofs[t] = key * kAttnD + (((2 * t + (q >> 1)) ^ (2 * (key & 7))) * 8) + (q & 1) * 4;
+  }
 
   // One key block, read from LDS buffer blk % 2.  MASK: the block reaches
   // past S or the diagonal for some query of the workgroup (a separate
@@ -187,10 +223,10 @@ __global__ __launch_bounds__(kAttnWaves * 64, 2) void attn_prefill_kernel(const 
     const int BUF = blk & 1;
     if (blk + 1 < nblocks) {   // in flight during this block's math
       copy_k(blk + 1, BUF ^ 1);
-      fetch_v(blk + 1);
+      copy_v(blk + 1, BUF ^ 1);
     }
     const uint16_t* ks = ks_buf[BUF];
-    const uint16_t* vts = vts_buf[BUF];
+    const uint16_t* vsb = vs_buf[BUF];
 
     // S^T for 64 keys x the wave's two 16-query tiles; each K fragment
     // serves both tiles.
@@ -220,35 +256,43 @@ __global__ __launch_bounds__(kAttnWaves * 64, 2) void attn_prefill_kernel(const 
           for (int v = 0; v < 4; ++v) sc[u][t][v] = 16 * t + v <= lim ? sc[u][t][v] : -INFINITY;
       }
       // Block max for the lane's query on the raw scores (scale > 0
-      // commutes with max).
-      float mx = -INFINITY;
-#pragma unroll
-      for (int t = 0; t < kAttnBN / 16; ++t)
-        mx = fmaxf(fmaxf(mx, fmaxf(sc[u][t][0], sc[u][t][1])), fmaxf(sc[u][t][2], sc[u][t][3]));
-      mx = fmaxf(mx, __shfl_xor(mx, 16));
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const float m_new = fmaxf(m_run[u], mx * a.scale_log2);
+      // commutes with max).  The NaN-propagating maximum takes three operands
+      // per instruction with no canonicalising moves in front (a NaN score
+      // makes its row NaN either way).
+      float mx = max3f(sc[u][0][0], sc[u][0][1], sc[u][0][2]);
+      mx = max3f(mx, sc[u][0][3], sc[u][1][0]);
+      mx = max3f(mx, sc[u][1][1], sc[u][1][2]);
+      mx = max3f(mx, sc[u][1][3], sc[u][2][0]);
+      mx = max3f(mx, sc[u][2][1], sc[u][2][2]);
+      mx = max3f(mx, sc[u][2][3], sc[u][3][0]);
+      mx = max3f(mx, sc[u][3][1], sc[u][3][2]);
+      mx = maxf(mx, sc[u][3][3]);
+      mx = maxf(mx, __shfl_xor(mx, 16));
+      mx = maxf(mx, __shfl_xor(mx, 32));
+      // The reference max m moves only when the block's max exceeds it by
+      // more than kAttnSlack (log2 units), so p <= 2^kAttnSlack and most
+      // blocks skip the rescale of O; O and the row sum share m, so the
+      // quotient is unchanged.
+      const float m_cand = maxf(m_run[u], mx * a.scale_log2);
+      const bool move = m_cand > m_run[u] + kAttnSlack;   // m = -inf: any finite max moves it
+      const float m_new = move ? m_cand : m_run[u];
       const float m_use = m_new == -INFINITY ? 0.0f : m_new;   // a row with nothing visible yet
-      const float alpha = __builtin_amdgcn_exp2f(m_run[u] - m_use);
+      const float alpha = move ? __builtin_amdgcn_exp2f(m_run[u] - m_use) : 1.0f;
       m_run[u] = m_new;
       // p = 2^(s * scale * log2 e - m): one FMA and one v_exp per score.
-      float lsum = 0.0f;
       uint32_t pb[kAttnBN / 16][2];
 #pragma unroll
       for (int t = 0; t < kAttnBN / 16; ++t) {
         float p[4];
 #pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          p[v] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[u][t][v], a.scale_log2, -m_use));
-          lsum += p[v];
-        }
+        for (int v = 0; v < 4; ++v) p[v] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[u][t][v], a.scale_log2, -m_use));
         pb[t][0] = pack_rn<DT>(p[0], p[1]);
         pb[t][1] = pack_rn<DT>(p[2], p[3]);
       }
-      l_run[u] = l_run[u] * alpha + lsum;
-      if (__any(alpha != 1.0f)) {   // the max moved for some query of the tile
+      if (__any(move)) {   // the reference max moved for some query of the tile
 #pragma unroll
         for (int t = 0; t < kAttnD / 16; ++t) acc_o[u][t] *= alpha;
+        acc_l[u] *= alpha;
       }
 #pragma unroll
       for (int s = 0; s < kAttnBN / 32; ++s)
@@ -261,17 +305,16 @@ __global__ __launch_bounds__(kAttnWaves * 64, 2) void attn_prefill_kernel(const 
     for (int s = 0; s < kAttnBN / 32; ++s) {
 #pragma unroll
       for (int t = 0; t < kAttnD / 16; ++t) {
-        const uint16_t* vrow = vts + 16 * kVStride * t + 32 * s + vofs;
-        const u32x2_t lo = *(const u32x2_t*)vrow;
-        const u32x2_t hi = *(const u32x2_t*)(vrow + 16);
+        const u32x2_t lo = read_tr16(vsb + 4096 * s + vofs[t]);
+        const u32x2_t hi = read_tr16(vsb + 4096 * s + 2048 + vofs[t]);
         const vec vf = __builtin_bit_cast(vec, u32x4_t{lo[0], lo[1], hi[0], hi[1]});
 #pragma unroll
         for (int u = 0; u < kAttnQT; ++u) acc_o[u][t] = Op<DT>::mfma(vf, pf[u][s], acc_o[u][t]);
       }
+#pragma unroll
+      for (int u = 0; u < kAttnQT; ++u) acc_l[u] = Op<DT>::mfma(ones, pf[u][s], acc_l[u]);
     }
-    // The other buffer was last read before the previous barrier.
-    if (blk + 1 < nblocks) stash_v(BUF ^ 1);
-    __syncthreads();   // also waits for the K copies of the next block
+    __syncthreads();   // also waits for the K and V copies of the next block
   };
 
   typedef std::integral_constant<bool, false> Full;
@@ -298,15 +341,14 @@ __global__ __launch_bounds__(kAttnWaves * 64, 2) void attn_prefill_kernel(const 
 #pragma unroll
     for (int u = 0; u < kAttnQT; ++u) {
       m_run[u] = -INFINITY;
-      l_run[u] = 0.0f;
+      acc_l[u] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
       for (int t = 0; t < kAttnD / 16; ++t) acc_o[u][t] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
     }
     // Blocks before nfull need no mask for any query of the workgroup.
     const int nfull = min(S / kAttnBN, a.causal ? m0 / kAttnBN : nblocks);
     copy_k(0, 0);   // both buffers are free: the previous part ended on a barrier
-    fetch_v(0);
-    stash_v(0);
+    copy_v(0, 0);
     __syncthreads();   // its fence also waits for the LDS copies
     int blk = 0;
     for (; blk < nfull; ++blk) block(blk, Full());
@@ -315,10 +357,7 @@ __global__ __launch_bounds__(kAttnWaves * 64, 2) void attn_prefill_kernel(const 
     // Normalise and store: lane (r, g) writes O[q][16 t + 4 g .. + 3].
 #pragma unroll
     for (int u = 0; u < kAttnQT; ++u) {
-      float l = l_run[u];
-      l += __shfl_xor(l, 16);
-      l += __shfl_xor(l, 32);
-      const float inv = 1.0f / l;
+      const float inv = 1.0f / acc_l[u][0];
       const int qi = wq0 + 16 * u + r;
       if (qi < S) {
 #pragma unroll
