@@ -4,13 +4,15 @@
 // Metal", technical summary, "Methodologie", prefill optimisation; the M5
 // review, "Method", routes this prefill attention to the matrix units).
 //
-// Per workgroup: 4 waves x 2 tiles of 16 queries of one (batch, query head);
-// K and V of the matching key/value head (GQA: head h reads kv head
+// Per workgroup: 4 waves x 2 (or 1) tiles of 16 queries of one (batch, query
+// head); K and V of the matching key/value head (GQA: head h reads kv head
 // h / (Hq / Hkv)) pass through two LDS buffers in blocks of 64 keys: the next
-// block's loads are in flight while the current one is used (K straight to
-// LDS by the buffer loads' LDS path, V through registers for the transpose),
-// one barrier per block.  Each LDS fragment feeds both query tiles of a
-// wave, and the two tiles' independent softmax and MFMA chains interleave.
+// block's loads are in flight while the current one is used (both straight
+// to LDS by the buffer loads' LDS path, V read back transposed), one barrier
+// per block.  Each LDS fragment feeds both query tiles of a wave, and the two
+// tiles' independent softmax and MFMA chains interleave.  Mid-size causal
+// grids run two such groups of 4 waves per workgroup over the two halves of
+// every query block's key range, merged at the end.
 // Per wave, tile and key block, with v_mfma_f32_16x16x32 on bf16 (or fp16)
 // operands:
 //   * S^T = K Q^T  (A = K rows from LDS, B = the wave's Q^T held in
@@ -20,15 +22,16 @@
 //   * P^T = exp2(S^T * scale * log2 e - m) rounded to the operand type is
 //     already the B operand of O^T = V^T P^T when the 32 keys of an MFMA
 //     step are taken in the order (4 g .. 4 g + 3, 16 + 4 g .. 16 + 4 g + 3)
-//     for lane group g; V is stored transposed in LDS ([d][key]) so that the
-//     A operand reads those keys as two 8-byte runs;
+//     for lane group g; V stays [key][d] in LDS and the transposed LDS read
+//     gives the A operand those keys as two runs of four;
 //   * O^T accumulates in fp32 (lane (r, g) holds O[query r][d 16 t + 4 g + v])
 //     and is rescaled by exp2(m_old - m_new) when the reference max moves
 //     (only by more than a fixed headroom, so rarely); the row sums come
 //     from one more MFMA per key step against a V^T tile of ones.
 // Causal masking skips key blocks past the query block's last query and
 // masks the diagonal blocks per element (in a separate instance of the block
-// step); each workgroup takes a light and a heavy query block in turn.
+// step); in paired grids each workgroup takes a light and a heavy query
+// block in turn.
 #include "q4q8_dev.h"
 #include "q4q8_internal.h"
 
@@ -87,20 +90,26 @@ __device__ __forceinline__ float max3f(float a, float b, float c) {
   return __builtin_elementwise_maximum(__builtin_elementwise_maximum(a, b), c);
 }
 
-template <int DT, int QT>
-__global__ __launch_bounds__(kAttnWaves * 64, 2) void attn_prefill_kernel(const AttnArgs a) {
+// KS groups of kAttnWaves waves per workgroup.  KS = 2 splits every query
+// block's key range between the groups (group 0 the first half of the key
+// blocks, group 1 the rest, both over the same queries, each with its own K/V
+// buffers), and group 1 merges group 0's partial O, max and sum through LDS at
+// the end: a causal grid of 128-query blocks then fills every CU once with two
+// waves a SIMD while each wave keeps two query tiles.
+template <int DT, int QT, int KS>
+__global__ __launch_bounds__(kAttnWaves * 64 * KS, KS == 1 ? 2 : 1) void attn_prefill_kernel(const AttnArgs a) {
   typedef typename Op<DT>::vec vec;
   constexpr uint32_t kOnes2 = DT == kBF16 ? 0x3F803F80u : 0x3C003C00u;   // (1, 1) in the operand type
   constexpr int kAttnQT = QT;
   constexpr int kAttnBM = 16 * QT * kAttnWaves;   // queries per workgroup
-  // Two buffers of K and V: block j + 1 is written while block j is read,
-  // both by the buffer loads' LDS path (1 KB contiguous per wave instruction,
-  // so rows cannot be padded; XOR swizzles of the 16-byte column groups keep
-  // the fragment reads on distinct banks).  K: column group cg of key k at
-  // slot 16 k + (cg ^ (k % 16)).  V: column group cg of key k at slot
+  // Two buffers of K and V per group: block j + 1 is written while block j is
+  // read, both by the buffer loads' LDS path (1 KB contiguous per wave
+  // instruction, so rows cannot be padded; XOR swizzles of the 16-byte column
+  // groups keep the fragment reads on distinct banks).  K: column group cg of
+  // key k at slot 16 k + (cg ^ (k % 16)).  V: column group cg of key k at slot
   // 16 k + (cg ^ 2 (k % 8)), read transposed (ds_read_b64_tr_b16).
-  __shared__ __attribute__((aligned(1024))) uint16_t ks_buf[2][kAttnBN * kAttnD];
-  __shared__ __attribute__((aligned(1024))) uint16_t vs_buf[2][kAttnBN * kAttnD];
+  // kv_lds[group][0: K, 1: V][buffer].
+  __shared__ __attribute__((aligned(1024))) uint16_t kv_lds[KS][2][2][kAttnBN * kAttnD];
 
   // Work split.  Paired (causal, enough work for two workgroups per CU):
   // workgroup i of a (batch, head) takes query blocks i and mblocks - 1 - i
@@ -139,6 +148,7 @@ __global__ __launch_bounds__(kAttnWaves * 64, 2) void attn_prefill_kernel(const 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int grp = wave / kAttnWaves, wv = wave % kAttnWaves;   // key group, wave in the group
   const int r = lane & 15, g = lane >> 4;
   // Per query block (set by the part loop below): its first query m0, the
   // wave's first query wq0, the key blocks it needs.
@@ -153,19 +163,19 @@ __global__ __launch_bounds__(kAttnWaves * 64, 2) void attn_prefill_kernel(const 
     return uniform_rsrc(base + (int64_t)n0 * kvstride, (int)((int64_t)(S - n0) * kvstride * 2));
   };
   // K: global -> LDS by the buffer loads' LDS path, 4 copies of 16 bytes per
-  // lane; copy p of wave w fills slots 64 (4 p + w) .. + 63, i.e. key
-  // 16 p + 4 w + g of the block, column group r ^ (key % 16).
+  // lane; copy p of wave w (of the group) fills slots 64 (4 p + w) .. + 63,
+  // i.e. key 16 p + 4 w + g of the block, column group r ^ (key % 16).
   uint32_t koff[4];
 #pragma unroll
   for (int p = 0; p < 4; ++p) {
-    const int key = 16 * p + 4 * wave + g, cg = r ^ (key & 15);
+    const int key = 16 * p + 4 * wv + g, cg = r ^ (key & 15);
     koff[p] = (uint32_t)((key * kvstride + cg * 8) * 2);
   }
   auto copy_k = [&](int blk, int buf) {
     const __amdgpu_buffer_rsrc_t kres = block_rsrc(kb, blk);
 #pragma unroll
     for (int p = 0; p < 4; ++p) {
-      uint16_t* dst = ks_buf[buf] + (4 * p + wave) * 64 * 8;   // wave-uniform
+      uint16_t* dst = kv_lds[grp][0][buf] + (4 * p + wv) * 64 * 8;   // wave-uniform
       __builtin_amdgcn_raw_ptr_buffer_load_lds(kres, (__attribute__((address_space(3))) void*)dst, 16, koff[p], 0,
                                                0, 0);
     }
@@ -175,14 +185,14 @@ __global__ __launch_bounds__(kAttnWaves * 64, 2) void attn_prefill_kernel(const 
   uint32_t voff[4];
 #pragma unroll
   for (int p = 0; p < 4; ++p) {
-    const int key = 16 * p + 4 * wave + g, cg = r ^ (2 * (key & 7));
+    const int key = 16 * p + 4 * wv + g, cg = r ^ (2 * (key & 7));
     voff[p] = (uint32_t)((key * kvstride + cg * 8) * 2);
   }
   auto copy_v = [&](int blk, int buf) {
     const __amdgpu_buffer_rsrc_t vres = block_rsrc(vb, blk);
 #pragma unroll
     for (int p = 0; p < 4; ++p) {
-      uint16_t* dst = vs_buf[buf] + (4 * p + wave) * 64 * 8;   // wave-uniform
+      uint16_t* dst = kv_lds[grp][1][buf] + (4 * p + wv) * 64 * 8;   // wave-uniform
       __builtin_amdgcn_raw_ptr_buffer_load_lds(vres, (__attribute__((address_space(3))) void*)dst, 16, voff[p], 0,
                                                0, 0);
     }
@@ -218,15 +228,16 @@ __global__ __launch_bounds__(kAttnWaves * 64, 2) void attn_prefill_kernel(const 
   // One key block, read from LDS buffer blk % 2.  MASK: the block reaches
   // past S or the diagonal for some query of the workgroup (a separate
   // instance, so full blocks carry no mask arithmetic).
-  auto block = [&](int blk, auto maskc) __attribute__((always_inline)) {
+  // bend: the end of this group's key blocks.
+  auto block = [&](int blk, int bend, auto maskc) __attribute__((always_inline)) {
     constexpr bool MASK = decltype(maskc)::value;
     const int BUF = blk & 1;
-    if (blk + 1 < nblocks) {   // in flight during this block's math
+    if (blk + 1 < bend) {   // in flight during this block's math
       copy_k(blk + 1, BUF ^ 1);
       copy_v(blk + 1, BUF ^ 1);
     }
-    const uint16_t* ks = ks_buf[BUF];
-    const uint16_t* vsb = vs_buf[BUF];
+    const uint16_t* ks = kv_lds[grp][0][BUF];
+    const uint16_t* vsb = kv_lds[grp][1][BUF];
 
     // S^T for 64 keys x the wave's two 16-query tiles; each K fragment
     // serves both tiles.
@@ -322,7 +333,7 @@ __global__ __launch_bounds__(kAttnWaves * 64, 2) void attn_prefill_kernel(const 
   for (int part = 0; part < nparts; ++part) {
     const int mb = part == 0 ? pi : a.mblocks - 1 - pi;
     m0 = mb * kAttnBM;
-    wq0 = m0 + wave * 16 * kAttnQT;
+    wq0 = m0 + wv * 16 * kAttnQT;
     // Key blocks: all of them, or up to the last query of the block (causal).
     const int kend = a.causal ? min(S, m0 + kAttnBM) : S;
     nblocks = (kend + kAttnBN - 1) / kAttnBN;
@@ -347,27 +358,72 @@ __global__ __launch_bounds__(kAttnWaves * 64, 2) void attn_prefill_kernel(const 
     }
     // Blocks before nfull need no mask for any query of the workgroup.
     const int nfull = min(S / kAttnBN, a.causal ? m0 / kAttnBN : nblocks);
-    copy_k(0, 0);   // both buffers are free: the previous part ended on a barrier
-    copy_v(0, 0);
+    // This group's key blocks [b0, b1); both groups take nsteps steps (one
+    // barrier each), group 0 idling through its last one when it has fewer.
+    const int ksplit = KS == 2 ? nblocks / 2 : nblocks;
+    const int b0 = grp == 0 ? 0 : ksplit, b1 = grp == 0 ? ksplit : nblocks;
+    const int nsteps = KS == 2 ? nblocks - ksplit : nblocks;
+    if (b0 < b1) {   // both buffers are free: the previous part ended on a barrier
+      copy_k(b0, b0 & 1);
+      copy_v(b0, b0 & 1);
+    }
     __syncthreads();   // its fence also waits for the LDS copies
-    int blk = 0;
-    for (; blk < nfull; ++blk) block(blk, Full());
-    for (; blk < nblocks; ++blk) block(blk, Masked());
+    int blk = b0;
+    for (; blk < min(b1, nfull); ++blk) block(blk, b1, Full());
+    for (; blk < b1; ++blk) block(blk, b1, Masked());
+    for (int i = b1 - b0; i < nsteps; ++i) __syncthreads();   // one barrier per step of the other group
+
+    bool store = true;
+    if constexpr (KS == 2) {
+      // Group 0 hands its partial O (relative to its reference max), max and
+      // sum to group 1 through the LDS (its own K/V buffers for O, group 1's
+      // for the max and sum; every block read ended on the last barrier).
+      float4_t* po = (float4_t*)&kv_lds[0][0][0][0];
+      float2_t* pml = (float2_t*)&kv_lds[1][0][0][0];
+      if (grp == 0) {
+#pragma unroll
+        for (int u = 0; u < kAttnQT; ++u) {
+#pragma unroll
+          for (int t = 0; t < kAttnD / 16; ++t) po[((wv * kAttnQT + u) * (kAttnD / 16) + t) * 64 + lane] = acc_o[u][t];
+          pml[(wv * kAttnQT + u) * 64 + lane] = float2_t{m_run[u], acc_l[u][0]};
+        }
+      }
+      __syncthreads();
+      if (grp == 1) {
+#pragma unroll
+        for (int u = 0; u < kAttnQT; ++u) {
+          const float2_t ml = pml[(wv * kAttnQT + u) * 64 + lane];
+          const float m = maxf(ml[0], m_run[u]);
+          // exp2(-inf) = 0 drops a group that saw no key of the row; a row
+          // that saw none at all (past S) is not stored.
+          const float f0 = m == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(ml[0] - m);
+          const float f1 = m == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m_run[u] - m);
+          acc_l[u][0] = acc_l[u][0] * f1 + ml[1] * f0;
+#pragma unroll
+          for (int t = 0; t < kAttnD / 16; ++t)
+            acc_o[u][t] = acc_o[u][t] * f1 + po[((wv * kAttnQT + u) * (kAttnD / 16) + t) * 64 + lane] * f0;
+        }
+      }
+      store = grp == 1;
+    }
 
     // Normalise and store: lane (r, g) writes O[q][16 t + 4 g .. + 3].
+    if (store) {
 #pragma unroll
-    for (int u = 0; u < kAttnQT; ++u) {
-      const float inv = 1.0f / acc_l[u][0];
-      const int qi = wq0 + 16 * u + r;
-      if (qi < S) {
+      for (int u = 0; u < kAttnQT; ++u) {
+        const float inv = 1.0f / acc_l[u][0];
+        const int qi = wq0 + 16 * u + r;
+        if (qi < S) {
 #pragma unroll
-        for (int t = 0; t < kAttnD / 16; ++t) {
-          const float4_t o = acc_o[u][t] * inv;
-          *(u32x2_t*)(ob + (int64_t)qi * qstride + 16 * t + 4 * g) =
-              u32x2_t{pack_rn<DT>(o[0], o[1]), pack_rn<DT>(o[2], o[3])};
+          for (int t = 0; t < kAttnD / 16; ++t) {
+            const float4_t o = acc_o[u][t] * inv;
+            *(u32x2_t*)(ob + (int64_t)qi * qstride + 16 * t + 4 * g) =
+                u32x2_t{pack_rn<DT>(o[0], o[1]), pack_rn<DT>(o[2], o[3])};
+          }
         }
       }
     }
+    if constexpr (KS == 2) __syncthreads();   // the merge's LDS reads end before the next part's copies
   }
 }
 
@@ -390,6 +446,21 @@ hipError_t launch_attn_prefill(int dt, const void* q, const void* k, const void*
   // S 512 22.9 -> 17.1 us; S 2048 causal 85 -> 79 us, non-causal 107 us kept
   // on two tiles, which one tile would take to 137 us).
   const int64_t wg128 = (int64_t)((S + 127) / 128) * Hq * B;
+  a.scale_log2 = scale * 1.4426950408889634f;
+  // Causal grids whose paired 128-query blocks give every CU one 8-wave
+  // workgroup, but not two 4-wave ones, split their key ranges between two
+  // wave groups (KS = 2; measured, S 2048, 32 heads: 51.5 -> 45.5 us against
+  // one tile a wave in paired 64-query workgroups, medians of five runs).
+  const int64_t pairs128 = (int64_t)((S + 255) / 256) * Hq * B;
+  if (causal && pairs128 >= 256 && pairs128 < 512) {
+    a.mblocks = (S + 127) / 128;
+    a.paired = 1;
+    a.per_bh = (a.mblocks + 1) / 2;
+    const dim3 grid((unsigned)(a.per_bh * Hq * B)), block(2 * kAttnWaves * 64);
+    if (dt == kBF16) launch(attn_prefill_kernel<kBF16, 2, 2>, grid, block, 0, s, ev, a);
+    else launch(attn_prefill_kernel<kF16, 2, 2>, grid, block, 0, s, ev, a);
+    return hipGetLastError();
+  }
   const int qt = wg128 >= (causal ? 1024 : 512) ? 2 : 1;
   const int bm = 16 * qt * kAttnWaves;
   a.mblocks = (S + bm - 1) / bm;
@@ -398,14 +469,13 @@ hipError_t launch_attn_prefill(int dt, const void* q, const void* k, const void*
   // would leave half the CU slots empty).
   a.paired = causal && (int64_t)((a.mblocks + 1) / 2) * Hq * B >= 512;
   a.per_bh = a.paired ? (a.mblocks + 1) / 2 : a.mblocks;
-  a.scale_log2 = scale * 1.4426950408889634f;
   const dim3 grid((unsigned)(a.per_bh * Hq * B)), block(kAttnWaves * 64);
   if (qt == 2) {
-    if (dt == kBF16) launch(attn_prefill_kernel<kBF16, 2>, grid, block, 0, s, ev, a);
-    else launch(attn_prefill_kernel<kF16, 2>, grid, block, 0, s, ev, a);
+    if (dt == kBF16) launch(attn_prefill_kernel<kBF16, 2, 1>, grid, block, 0, s, ev, a);
+    else launch(attn_prefill_kernel<kF16, 2, 1>, grid, block, 0, s, ev, a);
   } else {
-    if (dt == kBF16) launch(attn_prefill_kernel<kBF16, 1>, grid, block, 0, s, ev, a);
-    else launch(attn_prefill_kernel<kF16, 1>, grid, block, 0, s, ev, a);
+    if (dt == kBF16) launch(attn_prefill_kernel<kBF16, 1, 1>, grid, block, 0, s, ev, a);
+    else launch(attn_prefill_kernel<kF16, 1, 1>, grid, block, 0, s, ev, a);
   }
   return hipGetLastError();
 }

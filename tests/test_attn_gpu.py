@@ -73,6 +73,18 @@ def test_attn_paired_query_blocks(q, B, S):
     _check(got[:, rows], ref, bound, f"attn paired B{B} S{S}")
 
 
+@pytest.mark.parametrize("B,S,Hq,Hkv,dt", [(4, 300, 32, 8, synth.BF16), (4, 520, 32, 4, synth.F16)])
+def test_attn_key_split_full(q, B, S, Hq, Hkv, dt):
+    """Causal grids large enough for the two-group form (each query block's
+    key range split between two wave groups and merged): every output, ragged
+    S (the last query block partly past S), paired blocks with a middle block
+    alone (300: three 128-query blocks)."""
+    qa, ka, va = synth.attention_inputs(B, S, Hq, Hkv, 128, dt, 170 + S)
+    got = _run(q, qa, ka, va, True)
+    ref, bound = oracle.attention(qa.values, ka.values, va.values, causal=True)
+    _check(got, ref, bound, f"attn key split B{B} S{S} Hq{Hq} Hkv{Hkv} dt{dt}")
+
+
 def test_attn_large_scores(q):
     """Scores far from 0 (inputs x 6): the running max must move often."""
     B, S, Hq, Hkv = 1, 384, 2, 1
