@@ -461,6 +461,18 @@ hipError_t launch_attn_prefill(int dt, const void* q, const void* k, const void*
     else launch(attn_prefill_kernel<kF16, 2, 2>, grid, block, 0, s, ev, a);
     return hipGetLastError();
   }
+  // Small causal grids (64-query blocks give at most one workgroup per CU):
+  // one tile a wave, two wave groups over each block's key range.
+  const int64_t wg64 = (int64_t)((S + 63) / 64) * Hq * B;
+  if (causal && wg64 <= 256) {
+    a.mblocks = (S + 63) / 64;
+    a.paired = 0;
+    a.per_bh = a.mblocks;
+    const dim3 grid((unsigned)(a.per_bh * Hq * B)), block(2 * kAttnWaves * 64);
+    if (dt == kBF16) launch(attn_prefill_kernel<kBF16, 1, 2>, grid, block, 0, s, ev, a);
+    else launch(attn_prefill_kernel<kF16, 1, 2>, grid, block, 0, s, ev, a);
+    return hipGetLastError();
+  }
   const int qt = wg128 >= (causal ? 1024 : 512) ? 2 : 1;
   const int bm = 16 * qt * kAttnWaves;
   a.mblocks = (S + bm - 1) / bm;
