@@ -278,6 +278,10 @@ __global__ __launch_bounds__(WAVES * 64) void moe_stream_kernel(
   constexpr int THREADS = WAVES * 64;
   __shared__ __attribute__((aligned(1024))) uint16_t xs[BM * KP];
   __shared__ int s_rowbase[BM];   // source row of each of the row tile's BM rows (-1: none)
+  // Per row of the row tile, what its epilogue needs: the token's exponent
+  // (gate+up) or the pair id (down).  Staged with the rows, so the epilogue
+  // issues no global load (whose wait would also drain the weight ring).
+  __shared__ int s_rowaux[BM];
 
   const int e = blockIdx.y;
   const int tid = threadIdx.x, lane = tid & 63;
@@ -443,14 +447,18 @@ __global__ __launch_bounds__(WAVES * 64) void moe_stream_kernel(
   auto set_rows = [&](int rt) __attribute__((always_inline)) {
     if (tid < BM) {
       const int i = rt * BM + tid;
-      int base = -1;
+      int base = -1, aux = 0;
       if (i < cnt) {
-        if constexpr (MODE == kGateUp)
+        if constexpr (MODE == kGateUp) {
           base = min(max(sp_rows[seg + i], 0) / topk, T - 1);
-        else
+          aux = xexp[base];
+        } else {
           base = seg + i;
+          aux = min(max(sorted_pairs[seg + i], 0), Ptot - 1);
+        }
       }
       s_rowbase[tid] = base;
+      s_rowaux[tid] = aux;
     }
   };
   // ROUTE prologue, pass 2: each of the expert's pairs gets its rank in pair
@@ -561,7 +569,7 @@ __global__ __launch_bounds__(WAVES * 64) void moe_stream_kernel(
               // is formed at its true scale and rounded to bf16 (its storage
               // precision); the down product's fp16 copy carries 2^-2ex
               // (|h| <= |z_gate| |z_up|), undone by the combine.
-              const int ex = xexp[s_rowbase[i * 16 + r]];   // the row's token (row < cnt)
+              const int ex = s_rowaux[i * 16 + r];   // the row's token's exponent (row < cnt)
               const float4_t zg = acc[(0 * NT + t) * MT + i], zu = acc[(1 * NT + t) * MT + i];
               uint32_t hf[2], hb[2];
 #pragma unroll
@@ -579,7 +587,7 @@ __global__ __launch_bounds__(WAVES * 64) void moe_stream_kernel(
               *(u32x2_t*)(out16 + idx) = u32x2_t{hf[0], hf[1]};
               if (h_out) *(u32x2_t*)(h_out + idx) = u32x2_t{hb[0], hb[1]};
             } else {
-              const int64_t pair = min(max(sorted_pairs[seg + row], 0), Ptot - 1);
+              const int64_t pair = s_rowaux[i * 16 + r];
               const float4_t v = acc[t * MT + i];
               const uint32_t lo = (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)v[0]) |
                                   ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)v[1]) << 16);
@@ -596,7 +604,8 @@ __global__ __launch_bounds__(WAVES * 64) void moe_stream_kernel(
   };
 
   // Prologue: the first phase of X, then P steps of weights in flight; the
-  // barrier's fence waits for the X copies only (they were issued first).
+  // barrier waits for the X copies only (they were issued first: the ring's
+  // loads may still be in flight).
   WStage ws[P];
   if constexpr (ROUTE) {
     if (!rows0_done) route_rows0();
@@ -604,9 +613,15 @@ __global__ __launch_bounds__(WAVES * 64) void moe_stream_kernel(
     set_rows(0);
   }
   __syncthreads();
+  if constexpr (ROUTE) {   // row tile 0's exponents (its rows were ranked above)
+    if (tid < BM) s_rowaux[tid] = s_rowbase[tid] >= 0 ? xexp[s_rowbase[tid]] : 0;
+  }
   load_x(0);
   static_for<0, P>([&](auto jc) __attribute__((always_inline)) { load_next(ws[decltype(jc)::value]); });
-  __syncthreads();
+  constexpr int kRingLoads = P * NT * NW * (NV + 1);   // vector loads per load_next, P of them
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("s_waitcnt vmcnt(%0)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::"n"(kRingLoads) : "memory");
+  __builtin_amdgcn_sched_barrier(0);
   int cur_rt = 0, cur_kph = 0;
 
   // Compute cursor: row tile rt, group gi, chunk c.
@@ -617,7 +632,11 @@ __global__ __launch_bounds__(WAVES * 64) void moe_stream_kernel(
       if (s0 + J < total) {
         const int kph = c / cpp;
         if (kph != cur_kph || rt != cur_rt) {   // uniform: reload the LDS phase
-          __syncthreads();
+          // Every wave is done reading the phase (and its rows): LDS reads
+          // only, the weight ring stays in flight.
+          __builtin_amdgcn_sched_barrier(0);
+          asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+          __builtin_amdgcn_sched_barrier(0);
           if (rt != cur_rt) {
             set_rows(rt);
             __syncthreads();
