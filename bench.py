@@ -504,27 +504,30 @@ def q8_3b_workloads(q, torch, synth, ev: HipEvents, quick: bool):
 
 
 def attn_workloads(q, torch, synth, ev: HipEvents, quick: bool):
-    """Prefill attention, 8B-shaped heads (Hq 32, Hkv 8, D 128), causal, bf16,
-    S = 512 and 2048.  Flops = 4 D Hq B (S (S + 1) / 2) (QK^T and PV over the
-    visible pairs); time from dispatch events."""
+    """Prefill attention, 8B-shaped heads (Hq 32, Hkv 8, D 128), bf16: causal
+    S = 512, 2048 and 4096, non-causal S = 2048.  Flops = 4 D Hq B x the
+    visible (query, key) pairs (S (S + 1) / 2 causal, S^2 otherwise): QK^T and
+    PV; time from dispatch events."""
     out = []
     dev = torch.device("cuda:0")
     c = synth.ATTN
-    for S in ([2048] if quick else [512, 2048]):
+    cases = [(2048, True)] if quick else [(512, True), (2048, True), (4096, True), (2048, False)]
+    for S, causal in cases:
         qa, ka, va = synth.attention_inputs(c["B"], S, c["Hq"], c["Hkv"], c["D"], c["dt"], c["seed"])
         t = [torch.from_numpy(a.bits.view("int16")).view(torch.bfloat16).to(dev) for a in (qa, ka, va)]
         o = torch.empty_like(t[0])
         reps, warm = 200, 40   # back to back: the settled time
         pairs = [(ev.create(), ev.create()) for _ in range(reps + warm)]
         for pr in pairs:
-            q.attn_prefill(*t, causal=True, out=o, events=pr)
+            q.attn_prefill(*t, causal=causal, out=o, events=pr)
         d = sorted(ev.elapsed_ms(a, b) * 1e-3 for a, b in pairs[warm:])
         for a, b in pairs:
             ev.destroy(a)
             ev.destroy(b)
         mean = sum(d) / len(d)
-        fl = 4.0 * c["D"] * c["Hq"] * c["B"] * S * (S + 1) / 2
-        out.append({"workload": f"prefill attention S={S} Hq={c['Hq']} Hkv={c['Hkv']} D={c['D']} causal bf16",
+        fl = 4.0 * c["D"] * c["Hq"] * c["B"] * (S * (S + 1) / 2 if causal else S * S)
+        kind = "causal" if causal else "non-causal"
+        out.append({"workload": f"prefill attention S={S} Hq={c['Hq']} Hkv={c['Hkv']} D={c['D']} {kind} bf16",
                     "kernel_us_mean": round(mean * 1e6, 2), "kernel_us_min": round(d[0] * 1e6, 2),
                     "TFLOP/s": round(fl / mean / 1e12, 1),
                     "mfma_frac": round(fl / mean / 1e12 / F16_MFMA_PEAK_TFLOPS, 4)})
