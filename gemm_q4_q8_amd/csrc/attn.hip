@@ -439,12 +439,9 @@ hipError_t launch_attn_prefill(int dt, const void* q, const void* k, const void*
   a.Hq = Hq;
   a.Hkv = Hkv;
   a.causal = causal;
-  // Two 16-query tiles per wave (every K / V^T fragment serves both), or one
-  // when 128-query workgroups would not give every CU two of them (short
-  // sequences: S 512, 32 heads is 128 workgroups) -- four for causal grids,
-  // whose uneven blocks balance better in smaller pieces (measured, 32 heads:
-  // S 512 22.9 -> 17.1 us; S 2048 causal 85 -> 79 us, non-causal 107 us kept
-  // on two tiles, which one tile would take to 137 us).
+  // Grid choice, in order: the two key-split forms for causal grids that
+  // would otherwise leave CUs with one 4-wave workgroup or none, then the
+  // one-group form (KS = 1).
   const int64_t wg128 = (int64_t)((S + 127) / 128) * Hq * B;
   a.scale_log2 = scale * 1.4426950408889634f;
   // Causal grids whose paired 128-query blocks give every CU one 8-wave
@@ -473,6 +470,11 @@ hipError_t launch_attn_prefill(int dt, const void* q, const void* k, const void*
     else launch(attn_prefill_kernel<kF16, 1, 2>, grid, block, 0, s, ev, a);
     return hipGetLastError();
   }
+  // One group: two 16-query tiles per wave (every K / V^T fragment serves
+  // both), or one when 128-query workgroups would not give every CU two of
+  // them -- four for causal grids, whose uneven blocks balance better in
+  // smaller pieces (measured, 32 heads: S 512 22.9 -> 17.1 us; non-causal
+  // S 2048 107 us kept on two tiles, which one tile would take to 137 us).
   const int qt = wg128 >= (causal ? 1024 : 512) ? 2 : 1;
   const int bm = 16 * qt * kAttnWaves;
   a.mblocks = (S + bm - 1) / bm;
