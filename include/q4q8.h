@@ -385,7 +385,7 @@ size_t q4q8_moe_decode_noalloc_max_scratch(void);
  *   D:    head dimension, 128.  Hq a multiple of Hkv.  scale > 0 (usually
  *         1/sqrt(D)).
  * Scores and the softmax statistics are fp32; the probabilities enter the
- * P.V product rounded to dt; O is rounded once to dt.
+ * P.V product and the row sums rounded to dt; O is rounded once to dt.
  * Errors: Q4Q8_ERR_UNSUPPORTED for other D or dtypes. */
 int q4q8_attn_prefill(int dt, const void* Q, const void* K, const void* V,
                       void* O, int B, int S, int Hq, int Hkv, int D,

@@ -1,10 +1,11 @@
 """GPU parity of prefill attention against the CPU oracle.
 
 Acceptance per output: |o - o_ref| <= 2^-7 * sum_j p_j |v_j| + 2^-8 |o_ref| +
-1e-5.  The probabilities enter the P.V product rounded to the operand type
-(relative 2^-8 for bf16) while the normalising sum uses them unrounded, and
-O itself is rounded once to the storage type: both are covered with a factor
-2 margin; the fp32 scores' own rounding is far below.
+1e-5.  The probabilities enter the P.V product and the normalising sum
+rounded to the operand type (relative 2^-9 for bf16, so O is a weighted mean
+with weights off by at most that much each), and O itself is rounded once to
+the storage type: both are covered with a margin; the fp32 scores' own
+rounding is far below.
 """
 import numpy as np
 import pytest
