@@ -71,6 +71,7 @@ struct MoeDecArgs {
 };
 
 constexpr int kDecXSlack = 512;
+constexpr int kDecXP = 3;        // activation pieces per thread loaded before the first store (routed form)
 constexpr int kDecMaxExperts = 1024;
 constexpr int kDecMaxTopk = 16;            // the route's top-k limit
 
@@ -107,10 +108,33 @@ __global__ __launch_bounds__(WAVES * 64) void moe_gemv_kernel(const MoeDecArgs a
     // at xs + t (K + 8), its largest magnitude into s_rmax[t].  The expert's
     // rows are then a subset, read through their token index.
     __syncthreads();   // s_rmax cleared before any atomicMax
+    // The routing waves' logits are loaded first, so their latency overlaps
+    // the row staging below.
+    float lg[ROUTED ? RNS : 1];
+    if ((tid >> 6) < a.T) topk_load<ROUTED ? RNS : 1>(a.logits, tid >> 6, a.E, tid & 63, lg);
     {
       const int per_row = a.K / 8 + 1;
       const int pieces = a.T * per_row + kDecXSlack / 16;
-      for (int i = tid; i < pieces; i += WAVES * 64) {
+      // The first kDecXP pieces of every thread are loaded before any is
+      // stored (straight-line code: one wait covers them and the logits).
+      u32x4_t xv[kDecXP];
+#pragma unroll
+      for (int u = 0; u < kDecXP; ++u) {
+        const int i = tid + u * WAVES * 64;
+        const int t = i / per_row, k8 = i - t * per_row;
+        xv[u] = (i < pieces && t < a.T && k8 < a.K / 8) ? *(const u32x4_t*)(a.X + (int64_t)t * a.ldx + k8 * 8)
+                                                        : u32x4_t{0, 0, 0, 0};
+      }
+#pragma unroll
+      for (int u = 0; u < kDecXP; ++u) {
+        const int i = tid + u * WAVES * 64;
+        const int t = i / per_row;
+        if (i < pieces) {
+          if (t < a.T) atomicMax(&s_rmax[t], max_mag_bits8(xv[u]));
+          *(u32x4_t*)(xs + i * 8) = xv[u];
+        }
+      }
+      for (int i = tid + kDecXP * WAVES * 64; i < pieces; i += WAVES * 64) {
         const int t = i / per_row, k8 = i - t * per_row;
         u32x4_t v = u32x4_t{0, 0, 0, 0};
         if (t < a.T && k8 < a.K / 8) {
@@ -120,7 +144,7 @@ __global__ __launch_bounds__(WAVES * 64) void moe_gemv_kernel(const MoeDecArgs a
         *(u32x4_t*)(xs + i * 8) = v;
       }
     }
-    if ((tid >> 6) < a.T) topk_token<ROUTED ? RNS : 1>(a.logits, tid >> 6, a.E, a.topk, tid & 63, s_ids, s_gates);
+    if ((tid >> 6) < a.T) topk_select<ROUTED ? RNS : 1>(lg, tid >> 6, a.E, a.topk, tid & 63, s_ids, s_gates);
     __syncthreads();
     if (tid < npos) {   // rank of pair tid in the stable order by (expert, pair id)
       const int ep = s_ids[tid];

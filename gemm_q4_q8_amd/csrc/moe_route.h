@@ -28,19 +28,27 @@ __device__ __forceinline__ void route_dpp_step(float& bv, int& bi) {
   bi = better ? oi : bi;
 }
 
-// Top-k of token t by one wave.  NS: 64-expert slots per lane (E <= 64 NS).
-// Branch-free: out-of-range and taken experts compare as never better.
+// Token t's logits for the top-k below: lane holds experts lane + 64 i
+// (raw; the selection reads NaN as -inf).  A separate step so that a caller
+// can issue these loads before other memory work and select afterwards.
 template <int NS>
-__device__ __forceinline__ void topk_token(const float* __restrict__ logits, int t, int E, int topk, int lane,
-                                           int32_t* __restrict__ ids, float* __restrict__ gates) {
-  // Lane holds experts lane + 64 i.  NaN ranks as -inf.
+__device__ __forceinline__ void topk_load(const float* __restrict__ logits, int t, int E, int lane, float (&v)[NS]) {
   const __amdgpu_buffer_rsrc_t rs = uniform_rsrc(logits + (int64_t)t * E, E * 4);
+#pragma unroll
+  for (int i = 0; i < NS; ++i)
+    v[i] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, (lane + 64 * i) * 4, 0, 0));
+}
+
+// Top-k of token t by one wave from its loaded logits.  NS: 64-expert slots
+// per lane (E <= 64 NS).  Branch-free: out-of-range and taken experts compare
+// as never better.
+template <int NS>
+__device__ __forceinline__ void topk_select(const float (&raw)[NS], int t, int E, int topk, int lane,
+                                            int32_t* __restrict__ ids, float* __restrict__ gates) {
+  // NaN ranks as -inf.
   float v[NS];
 #pragma unroll
-  for (int i = 0; i < NS; ++i) {
-    const float x = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, (lane + 64 * i) * 4, 0, 0));
-    v[i] = (lane + 64 * i < E && x == x) ? x : -INFINITY;
-  }
+  for (int i = 0; i < NS; ++i) v[i] = (lane + 64 * i < E && raw[i] == raw[i]) ? raw[i] : -INFINITY;
   uint32_t live = 0;   // bit i: expert lane + 64 i exists and is not taken yet
 #pragma unroll
   for (int i = 0; i < NS; ++i) live |= (lane + 64 * i < E ? 1u : 0u) << i;
@@ -86,6 +94,14 @@ __device__ __forceinline__ void topk_token(const float* __restrict__ logits, int
     if (lane == 0) ids[(int64_t)t * topk + j] = bi;
   }
   if (lane < topk) gates[(int64_t)t * topk + lane] = my_exp / sum;
+}
+
+template <int NS>
+__device__ __forceinline__ void topk_token(const float* __restrict__ logits, int t, int E, int topk, int lane,
+                                           int32_t* __restrict__ ids, float* __restrict__ gates) {
+  float v[NS];
+  topk_load<NS>(logits, t, E, lane, v);
+  topk_select<NS>(v, t, E, topk, lane, ids, gates);
 }
 
 }  // namespace q4q8
