@@ -10,15 +10,16 @@
 // block's loads are in flight while the current one is used (both straight
 // to LDS by the buffer loads' LDS path, V read back transposed), one barrier
 // per block.  Each LDS fragment feeds both query tiles of a wave, and the two
-// tiles' independent softmax and MFMA chains interleave.  Mid-size causal
-// grids run two such groups of 4 waves per workgroup over the two halves of
-// every query block's key range, merged at the end.
+// tiles' independent softmax and MFMA chains interleave.  Causal grids too
+// small to give every CU two 4-wave workgroups run two such groups of 4 waves
+// per workgroup over the two halves of every query block's key range, merged
+// at the end.
 // Per wave, tile and key block, with v_mfma_f32_16x16x32 on bf16 (or fp16)
 // operands:
 //   * S^T = K Q^T  (A = K rows from LDS, B = the wave's Q^T held in
 //     registers).  Lane (r, g) ends up with the scores of query r against
 //     keys 16 t + 4 g + v, i.e. every lane's values belong to one query, so
-//     the running max and sum need only the 4 lanes r, r+16, r+32, r+48;
+//     the running max needs only the 4 lanes r, r+16, r+32, r+48;
 //   * P^T = exp2(S^T * scale * log2 e - m) rounded to the operand type is
 //     already the B operand of O^T = V^T P^T when the 32 keys of an MFMA
 //     step are taken in the order (4 g .. 4 g + 3, 16 + 4 g .. 16 + 4 g + 3)
