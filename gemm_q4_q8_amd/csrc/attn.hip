@@ -13,7 +13,10 @@
 // tiles' independent softmax and MFMA chains interleave.  Causal grids too
 // small to give every CU two 4-wave workgroups run two such groups of 4 waves
 // per workgroup over the two halves of every query block's key range, merged
-// at the end.
+// at the end; with two tiles a wave and paired query blocks, the first group
+// runs the light block whole and then the heavy block's first key blocks,
+// the second group the rest of the heavy one, and only the heavy block is
+// merged (the K / V copies run on across the switch, its Q waits in LDS).
 // Per wave, tile and key block, with v_mfma_f32_16x16x32 on bf16 (or fp16)
 // operands:
 //   * S^T = K Q^T  (A = K rows from LDS, B = the wave's Q^T held in
@@ -111,6 +114,11 @@ __global__ __launch_bounds__(kAttnWaves * 64 * KS, KS == 1 ? 2 : 1) void attn_pr
   // 16 k + (cg ^ 2 (k % 8)), read transposed (ds_read_b64_tr_b16).
   // kv_lds[group][0: K, 1: V][buffer].
   __shared__ __attribute__((aligned(1024))) uint16_t kv_lds[KS][2][2][kAttnBN * kAttnD];
+  // The paired two-group form (KS = 2, two tiles a wave) keeps the heavy
+  // query block's Q here: 16-byte column group cg of query row q (of the
+  // block) at slot 16 q + (cg ^ (q % 16)).
+  constexpr bool kSeg = KS == 2 && QT == 2;
+  __shared__ __attribute__((aligned(1024))) uint16_t q_lds[kSeg ? kAttnBM * kAttnD : 8];
 
   // Work split.  Paired (causal, enough work for two workgroups per CU):
   // workgroup i of a (batch, head) takes query blocks i and mblocks - 1 - i
@@ -161,7 +169,7 @@ __global__ __launch_bounds__(kAttnWaves * 64 * KS, KS == 1 ? 2 : 1) void attn_pr
   // by the resource's range check and the per-lane offsets stay fixed.
   auto block_rsrc = [&](const uint16_t* base, int blk) __attribute__((always_inline)) {
     const int n0 = blk * kAttnBN;
-    return uniform_rsrc(base + (int64_t)n0 * kvstride, (int)((int64_t)(S - n0) * kvstride * 2));
+    return uniform_rsrc(base + (int64_t)n0 * kvstride, (int)((int64_t)min(S - n0, kAttnBN) * kvstride * 2));
   };
   // K: global -> LDS by the buffer loads' LDS path, 4 copies of 16 bytes per
   // lane; copy p of wave w (of the group) fills slots 64 (4 p + w) .. + 63,
@@ -230,12 +238,13 @@ __global__ __launch_bounds__(kAttnWaves * 64 * KS, KS == 1 ? 2 : 1) void attn_pr
   // past S or the diagonal for some query of the workgroup (a separate
   // instance, so full blocks carry no mask arithmetic).
   // bend: the end of this group's key blocks.
-  auto block = [&](int blk, int bend, auto maskc) __attribute__((always_inline)) {
+  // BUF: the LDS buffers holding block blk; nxt: the key block the group
+  // takes next (copied into the other buffers during this one), or -1.
+  auto block = [&](int blk, int BUF, int nxt, auto maskc) __attribute__((always_inline)) {
     constexpr bool MASK = decltype(maskc)::value;
-    const int BUF = blk & 1;
-    if (blk + 1 < bend) {   // in flight during this block's math
-      copy_k(blk + 1, BUF ^ 1);
-      copy_v(blk + 1, BUF ^ 1);
+    if (nxt >= 0) {   // in flight during this block's math
+      copy_k(nxt, BUF ^ 1);
+      copy_v(nxt, BUF ^ 1);
     }
     const uint16_t* ks = kv_lds[grp][0][BUF];
     const uint16_t* vsb = kv_lds[grp][1][BUF];
@@ -331,6 +340,148 @@ __global__ __launch_bounds__(kAttnWaves * 64 * KS, KS == 1 ? 2 : 1) void attn_pr
 
   typedef std::integral_constant<bool, false> Full;
   typedef std::integral_constant<bool, true> Masked;
+  if constexpr (kSeg) {
+    // Paired blocks L = pi (light; absent when it is the middle block) and
+    // H = mblocks - 1 - pi (heavy) of one (batch, head).  Group 0 takes all
+    // of L's key blocks, then H's first pH; group 1 the rest of H's, so both
+    // carry about the same number; only H's two partial results are merged.
+    // The K / V copies run on across group 0's switch from L to H (the same
+    // head's keys), and H's Q comes from LDS, so the switch costs no load
+    // latency.
+    const int mbH = a.mblocks - 1 - pi;
+    const bool hasL = nparts == 2;
+    const int m0L = pi * kAttnBM, m0H = mbH * kAttnBM;
+    const int nL = hasL ? (min(S, m0L + kAttnBM) + kAttnBN - 1) / kAttnBN : 0;
+    const int nH = (min(S, m0H + kAttnBM) + kAttnBN - 1) / kAttnBN;
+    const int nfullL = min(S / kAttnBN, m0L / kAttnBN), nfullH = min(S / kAttnBN, m0H / kAttnBN);
+    const int pH = max(0, (nH - nL) / 2);
+    const int mysteps = grp == 0 ? nL + pH : nH - pH;
+    const int nsteps = max(nL + pH, nH - pH);
+    auto kb_of = [&](int i) __attribute__((always_inline)) { return grp == 0 ? (i < nL ? i : i - nL) : pH + i; };
+
+    // H's Q into LDS (rows past S read zero), copy p of wave w at slots
+    // 64 (8 p + w) .. + 63.
+    {
+      const __amdgpu_buffer_rsrc_t qres =
+          uniform_rsrc(qb + (int64_t)m0H * qstride, (int)((int64_t)min(S - m0H, kAttnBM) * qstride * 2));
+#pragma unroll
+      for (int p = 0; p < 4; ++p) {
+        const int slot = (8 * p + wave) * 64 + lane;
+        const int qrow = slot >> 4, cg = (slot & 15) ^ (qrow & 15);
+        uint16_t* dst = q_lds + (8 * p + wave) * 64 * 8;   // wave-uniform
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(qres, (__attribute__((address_space(3))) void*)dst, 16,
+                                                 (uint32_t)((qrow * qstride + cg * 8) * 2), 0, 0, 0);
+      }
+    }
+    auto q_from_lds = [&]() __attribute__((always_inline)) {
+#pragma unroll
+      for (int u = 0; u < kAttnQT; ++u) {
+        const int qrow = wv * 16 * kAttnQT + 16 * u + r;
+#pragma unroll
+        for (int s2 = 0; s2 < kAttnD / 32; ++s2)
+          qf[u][s2] = *(const vec*)(q_lds + (qrow * 16 + ((4 * s2 + g) ^ (qrow & 15))) * 8);
+      }
+    };
+    auto reset = [&]() __attribute__((always_inline)) {
+#pragma unroll
+      for (int u = 0; u < kAttnQT; ++u) {
+        m_run[u] = -INFINITY;
+        acc_l[u] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int t = 0; t < kAttnD / 16; ++t) acc_o[u][t] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
+      }
+    };
+    // Normalise and store the wave's tiles of the query block at m0.
+    auto store_o = [&]() __attribute__((always_inline)) {
+#pragma unroll
+      for (int u = 0; u < kAttnQT; ++u) {
+        const float inv = 1.0f / acc_l[u][0];
+        const int qi = wq0 + 16 * u + r;
+        if (qi < S) {
+#pragma unroll
+          for (int t = 0; t < kAttnD / 16; ++t) {
+            const float4_t o = acc_o[u][t] * inv;
+            *(u32x2_t*)(ob + (int64_t)qi * qstride + 16 * t + 4 * g) =
+                u32x2_t{pack_rn<DT>(o[0], o[1]), pack_rn<DT>(o[2], o[3])};
+          }
+        }
+      }
+    };
+    const bool startL = grp == 0 && hasL;
+    m0 = startL ? m0L : m0H;
+    wq0 = m0 + wv * 16 * kAttnQT;
+    if (startL) {   // L's Q from global memory (the barrier below waits for it)
+#pragma unroll
+      for (int u = 0; u < kAttnQT; ++u) {
+        const int qi = wq0 + 16 * u + r;
+#pragma unroll
+        for (int s2 = 0; s2 < kAttnD / 32; ++s2) {
+          u32x4_t t = u32x4_t{0, 0, 0, 0};
+          if (qi < S) t = *(const u32x4_t*)(qb + (int64_t)qi * qstride + 32 * s2 + 8 * g);
+          qf[u][s2] = __builtin_bit_cast(vec, t);
+        }
+      }
+    }
+    reset();
+    if (mysteps > 0) {
+      copy_k(kb_of(0), 0);
+      copy_v(kb_of(0), 0);
+    }
+    __syncthreads();   // its fence also waits for the LDS copies (Q of H included)
+    if (!startL) q_from_lds();
+    // Two segments a group: group 0 runs L's blocks, then H's first pH;
+    // group 1 runs H's from pH on (its second segment is empty).  Each
+    // segment is a loop over blocks without a mask, then one over masked.
+    int i = 0;   // step count: the K/V buffer parity
+#pragma unroll 1
+    for (int seg = 0; seg < 2; ++seg) {
+      const bool segL = grp == 0 && seg == 0;
+      const int kb0 = grp == 0 ? 0 : (seg == 0 ? pH : nH);
+      const int kb1 = grp == 0 ? (seg == 0 ? nL : pH) : nH;
+      const int nfull = segL ? nfullL : nfullH;
+      const int nxt_after = segL && pH > 0 ? 0 : -1;
+      const int f1 = min(max(nfull, kb0), kb1);
+      for (int j = kb0; j < f1; ++j, ++i) block(j, i & 1, j + 1 < kb1 ? j + 1 : nxt_after, Full());
+      for (int j = f1; j < kb1; ++j, ++i) block(j, i & 1, j + 1 < kb1 ? j + 1 : nxt_after, Masked());
+      if (segL && hasL) {   // L done: store it, continue with H
+        store_o();
+        reset();
+        q_from_lds();
+        m0 = m0H;
+        wq0 = m0 + wv * 16 * kAttnQT;
+      }
+    }
+    for (; i < nsteps; ++i) __syncthreads();   // one barrier per step of the other group
+    // Group 0 hands its partial O of H (relative to its reference max), max
+    // and sum to group 1 through the LDS (group 0's K/V buffers for O, group
+    // 1's for the max and sum; every block read ended on the last barrier).
+    float4_t* po = (float4_t*)&kv_lds[0][0][0][0];
+    float2_t* pml = (float2_t*)&kv_lds[1][0][0][0];
+    if (grp == 0) {
+#pragma unroll
+      for (int u = 0; u < kAttnQT; ++u) {
+#pragma unroll
+        for (int t = 0; t < kAttnD / 16; ++t) po[((wv * kAttnQT + u) * (kAttnD / 16) + t) * 64 + lane] = acc_o[u][t];
+        pml[(wv * kAttnQT + u) * 64 + lane] = float2_t{m_run[u], acc_l[u][0]};
+      }
+    }
+    __syncthreads();
+    if (grp == 1) {
+#pragma unroll
+      for (int u = 0; u < kAttnQT; ++u) {
+        const float2_t ml = pml[(wv * kAttnQT + u) * 64 + lane];
+        const float m = maxf(ml[0], m_run[u]);
+        const float f0 = m == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(ml[0] - m);
+        const float f1 = m == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m_run[u] - m);
+        acc_l[u][0] = acc_l[u][0] * f1 + ml[1] * f0;
+#pragma unroll
+        for (int t = 0; t < kAttnD / 16; ++t)
+          acc_o[u][t] = acc_o[u][t] * f1 + po[((wv * kAttnQT + u) * (kAttnD / 16) + t) * 64 + lane] * f0;
+      }
+      store_o();
+    }
+    return;
+  }
   for (int part = 0; part < nparts; ++part) {
     const int mb = part == 0 ? pi : a.mblocks - 1 - pi;
     m0 = mb * kAttnBM;
@@ -370,8 +521,8 @@ __global__ __launch_bounds__(kAttnWaves * 64 * KS, KS == 1 ? 2 : 1) void attn_pr
     }
     __syncthreads();   // its fence also waits for the LDS copies
     int blk = b0;
-    for (; blk < min(b1, nfull); ++blk) block(blk, b1, Full());
-    for (; blk < b1; ++blk) block(blk, b1, Masked());
+    for (; blk < min(b1, nfull); ++blk) block(blk, blk & 1, blk + 1 < b1 ? blk + 1 : -1, Full());
+    for (; blk < b1; ++blk) block(blk, blk & 1, blk + 1 < b1 ? blk + 1 : -1, Masked());
     for (int i = b1 - b0; i < nsteps; ++i) __syncthreads();   // one barrier per step of the other group
 
     bool store = true;
