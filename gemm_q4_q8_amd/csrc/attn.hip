@@ -94,6 +94,17 @@ __device__ __forceinline__ float max3f(float a, float b, float c) {
   return __builtin_elementwise_maximum(__builtin_elementwise_maximum(a, b), c);
 }
 
+// max over lanes l, l ^ 16, l ^ 32 and l ^ 48 (the four lanes that hold one
+// query's scores) by the cross-lane swap instructions, which stay in the
+// VALU: v_permlane16_swap of a value with itself gives rows (0, 0, 2, 2) and
+// (1, 1, 3, 3) of 16 lanes, v_permlane32_swap halves (0, 0) and (1, 1).
+__device__ __forceinline__ float max_lanes4(float m) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(m), __float_as_uint(m), false, false);
+  m = maxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(m), __float_as_uint(m), false, false);
+  return maxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+
 // KS groups of kAttnWaves waves per workgroup.  KS = 2 splits every query
 // block's key range between the groups (group 0 the first half of the key
 // blocks, group 1 the rest, both over the same queries, each with its own K/V
@@ -288,8 +299,7 @@ __global__ __launch_bounds__(kAttnWaves * 64 * KS, KS == 1 ? 2 : 1) void attn_pr
       mx = max3f(mx, sc[u][2][3], sc[u][3][0]);
       mx = max3f(mx, sc[u][3][1], sc[u][3][2]);
       mx = maxf(mx, sc[u][3][3]);
-      mx = maxf(mx, __shfl_xor(mx, 16));
-      mx = maxf(mx, __shfl_xor(mx, 32));
+      mx = max_lanes4(mx);
       // The reference max m moves only when the block's max exceeds it by
       // more than kAttnSlack (log2 units), so p <= 2^kAttnSlack and most
       // blocks skip the rescale of O; O and the row sum share m, so the
