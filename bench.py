@@ -527,10 +527,17 @@ def attn_workloads(q, torch, synth, ev: HipEvents, quick: bool):
         mean = sum(d) / len(d)
         fl = 4.0 * c["D"] * c["Hq"] * c["B"] * (S * (S + 1) / 2 if causal else S * S)
         kind = "causal" if causal else "non-causal"
+        # The MFMA peak assumes 2.4 GHz: sample the clock over ~0.25 s of back-to-back calls.
+        with ClockSampler(ev.hip) as clk:
+            for _ in range(max(1, int(0.25 / max(mean, 1e-6)))):
+                q.attn_prefill(*t, causal=causal, out=o)
+            torch.cuda.synchronize()
         out.append({"workload": f"prefill attention S={S} Hq={c['Hq']} Hkv={c['Hkv']} D={c['D']} {kind} bf16",
-                    "kernel_us_mean": round(mean * 1e6, 2), "kernel_us_min": round(d[0] * 1e6, 2),
+                    "kernel_us_mean": round(mean * 1e6, 2), "kernel_us_median": round(d[len(d) // 2] * 1e6, 2),
+                    "kernel_us_min": round(d[0] * 1e6, 2),
                     "TFLOP/s": round(fl / mean / 1e12, 1),
-                    "mfma_frac": round(fl / mean / 1e12 / F16_MFMA_PEAK_TFLOPS, 4)})
+                    "mfma_frac": round(fl / mean / 1e12 / F16_MFMA_PEAK_TFLOPS, 4),
+                    "sclk_during_calls": clk.summary()})
     return out
 
 
