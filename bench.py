@@ -13,10 +13,13 @@ down: four launches, since attention, norms and SwiGLU would sit between
 them) is reported under "workloads".  Consecutive steps use different copies
 of the layer's weights (8 copies, 868 MB, more than the 256 MB Infinity
 Cache), as consecutive layers of a model would, so the weights stream from
-HBM.  Launches are captured in HIP graphs.
+HBM.  The K timed steps are one HIP graph of K launches, as a model's decode
+graph holds one launch per layer.
 
-value = algorithmic bytes of K steps / wall time of K steps (GB/s), inputs
-resident in HBM.  Algorithmic bytes per step = repacked weight bytes (0.5625
+value = algorithmic bytes of K steps / GPU time of K steps (GB/s), inputs
+resident in HBM: events on the stream bracket exactly the K graph-replayed
+steps, which are all queued (behind a bounded ~300 us spin kernel) before
+the first one starts, with a synchronize on both sides.  Algorithmic bytes per step = repacked weight bytes (0.5625
 B per weight, exactly the canonical Q4_0 bytes) + activations read (fp16) +
 outputs written (fp32).
 
@@ -94,6 +97,29 @@ class HipEvents:
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
+
+
+# After ~50 ms idle the GPU runs the headline step ~10 % slower for its first
+# ~10 ms of load (measured on MI355X, 200-step windows: 22.1, 22.0, 20.6,
+# 20.2, then 19.9 us a step).  Every timed measurement below is preceded by
+# this much of its own work, untimed.
+SETTLE_MS = 30.0
+
+
+def settle(torch, fn, ms: float = SETTLE_MS) -> int:
+    """Run fn(i) back to back, untimed, for at least `ms` milliseconds of wall
+    time (synchronising after doubling batches); returns the calls made."""
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    i, n = 0, 4
+    while True:
+        for _ in range(n):
+            fn(i)
+            i += 1
+        torch.cuda.synchronize()
+        if (time.perf_counter() - t0) * 1e3 >= ms:
+            return i
+        n *= 2
 
 
 class ClockSampler:
@@ -279,8 +305,33 @@ class DecodeLayer:
             self.q.qgemv_grouped(1, probs, self.M, descs=descs, events=ev)
 
 
+def _gate_cycles(torch, gate_us: float = 300.0) -> int:
+    """Cycles of torch's bounded spin kernel (torch.cuda._sleep) that hold a
+    stream for about gate_us microseconds, from one timed calibration run."""
+    n = 1 << 20
+    torch.cuda._sleep(n)                 # first launch loads the kernel
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    torch.cuda._sleep(n)
+    e1.record()
+    torch.cuda.synchronize()
+    us = max(e0.elapsed_time(e1) * 1e3, 1.0)
+    return max(1, min(int(n * gate_us / us), 1 << 28))
+
+
 def time_graph_steps(torch, layer: DecodeLayer, steps: int, warmup: int):
-    """Capture one graph over all weight copies (one step each) and replay."""
+    """Time `steps` decode steps replayed from one HIP graph.
+
+    Returns (GPU seconds of the `steps` timed steps, host seconds around
+    them).  The W warm-up steps and the K timed steps are each captured as
+    one graph (consecutive steps on consecutive weight copies, as the layers
+    of a model's decode graph), so the timed span holds one graph launch.
+    That span sits between two events on the stream that runs it; before the
+    first event the stream is held by a bounded spin kernel (~300 us) while
+    the host submits the graph, so the host's launch latency stays outside
+    it; the host clock around spin + steps is returned beside it.  Before the
+    warm-up steps an 8-step graph is replayed, untimed, for SETTLE_MS."""
     L = len(layer.copies)
     s = torch.cuda.Stream()
     s.wait_stream(torch.cuda.current_stream())
@@ -289,36 +340,41 @@ def time_graph_steps(torch, layer: DecodeLayer, steps: int, warmup: int):
             layer.step(c)
     torch.cuda.current_stream().wait_stream(s)
     torch.cuda.synchronize()
-    g_all = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(g_all):
-        for c in range(L):
-            layer.step(c)
-    g_one = []
-    for c in range(L):
+
+    def capture(n, start):
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g):
-            layer.step(c)
-        g_one.append(g)
-    torch.cuda.synchronize()
+            for i in range(n):
+                layer.step((start + i) % L)
+        return g
 
-    def run(n):
-        for _ in range(n // L):
-            g_all.replay()
-        for c in range(n % L):
-            g_one[c].replay()
-
-    run(warmup)
+    g_all = capture(L, 0)
+    g_warm = capture(warmup, 0) if warmup > 0 else None
+    g_timed = capture(steps, warmup % L)
     torch.cuda.synchronize()
+    gate = _gate_cycles(torch)
+
+    settle(torch, lambda i: g_all.replay())
+    if g_warm is not None:
+        g_warm.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
-    run(steps)
+    torch.cuda._sleep(gate)
+    e0.record()
+    g_timed.replay()
+    e1.record()
     torch.cuda.synchronize()
-    return time.perf_counter() - t0
+    host = time.perf_counter() - t0
+    del g_all, g_warm, g_timed
+    return e0.elapsed_time(e1) * 1e-3, host
 
 
 def time_dominant_kernel(q, layer: DecodeLayer, ev: HipEvents, reps: int, group: str):
     """Mean duration (s) of one launch group, from dispatch-recorded events."""
     pairs = [(ev.create(), ev.create()) for _ in range(reps)]
     L = len(layer.copies)
+    settle(layer.torch, lambda i: layer.step(i % L))
     for i in range(reps):
         layer.step(i % L, timed_group=group, events=pairs[i])
     durs = [ev.elapsed_ms(a, b) * 1e-3 for a, b in pairs]
@@ -377,6 +433,7 @@ def cpu_baseline(synth, budget_s: float = 25.0):
 # Other workloads
 # ----------------------------------------------------------------------------
 def _time_launches(torch, fn, reps: int, warmup: int = 3):
+    settle(torch, fn)
     for i in range(warmup):
         fn(i)
     torch.cuda.synchronize()
@@ -404,7 +461,7 @@ def extra_workloads(q, torch, synth, ev: HipEvents, quick: bool, only=None):
         lay = DecodeLayer(q, torch, synth, M, LAYER_COPIES)
         for mode in (["chain"] if M == 1 else ["one", "chain"]):
             lay.mode = mode
-            dt = time_graph_steps(torch, lay, 2000, 200)   # settled step time, as for the headline
+            dt, _ = time_graph_steps(torch, lay, 2000, 200)   # settled step time, as for the headline
             rec = {"workload": f"8B layer decode step M={M}, " + (
                 "one grouped launch" if mode == "one" else "dependency order (4 launches)"),
                 "GB/s": round(lay.step_bytes() * 2000 / dt / 1e9, 1), "us_per_step": round(dt / 2000 * 1e6, 2)}
@@ -447,6 +504,7 @@ def gemv2048_workload(q, torch, synth, ev: HipEvents):
     probs = [[(Wi, 2048, 2048, xt, y)] for Wi in Ws]
     descs = [q.gemv_descs(p) for p in probs]
     pairs = [(ev.create(), ev.create()) for _ in range(64)]
+    settle(torch, lambda i: q.qgemv_grouped(1, probs[i % 128], 1, descs=descs[i % 128]))
     for i in range(64):
         q.qgemv_grouped(1, probs[i], 1, descs=descs[i], events=pairs[i])
     kd = sum(ev.elapsed_ms(a, b) for a, b in pairs) / 64 * 1e-3
@@ -475,6 +533,7 @@ def q8_3b_workloads(q, torch, synth, ev: HipEvents, quick: bool):
             probs = [[(c, w.N, w.K, xt, yq)] for c in copies]
             descs = [q.gemv_descs(p) for p in probs]
             pairs = [(ev.create(), ev.create()) for _ in range(32)]
+            settle(torch, lambda i: q.qgemv_grouped(2, probs[i % len(probs)], M, descs=descs[i % len(probs)]))
             for i in range(32):
                 q.qgemv_grouped(2, probs[i % len(probs)], M, descs=descs[i % len(probs)], events=pairs[i])
             kd = sum(ev.elapsed_ms(a, b) for a, b in pairs) / 32 * 1e-3
@@ -493,6 +552,7 @@ def q8_3b_workloads(q, torch, synth, ev: HipEvents, quick: bool):
         probs = [[(c[n], ws[n].N, ws[n].K, xts[n], yq[n]) for n in names] for c in copies]
         descs = [q.gemv_descs(p) for p in probs]
         pairs = [(ev.create(), ev.create()) for _ in range(32)]
+        settle(torch, lambda i: q.qgemv_grouped(2, probs[i % 5], M, descs=descs[i % 5]))
         for i in range(32):
             q.qgemv_grouped(2, probs[i % 5], M, descs=descs[i % 5], events=pairs[i])
         kd = sum(ev.elapsed_ms(a, b) for a, b in pairs[4:]) / 28 * 1e-3
@@ -518,6 +578,7 @@ def attn_workloads(q, torch, synth, ev: HipEvents, quick: bool):
         o = torch.empty_like(t[0])
         reps, warm = 200, 40   # back to back: the settled time
         pairs = [(ev.create(), ev.create()) for _ in range(reps + warm)]
+        settle(torch, lambda i: q.attn_prefill(*t, causal=causal, out=o))
         for pr in pairs:
             q.attn_prefill(*t, causal=causal, out=o, events=pr)
         d = sorted(ev.elapsed_ms(a, b) * 1e-3 for a, b in pairs[warm:])
@@ -555,6 +616,7 @@ def fp16_layer_workload(q, torch, synth, ev: HipEvents):
     probs = [[(c[i], N, K, xs[K], ys[i]) for i, (_, N, K) in enumerate(mats)] for c in copies]
     descs = [q.gemv_descs(p) for p in probs]
     pairs = [(ev.create(), ev.create()) for _ in range(36)]
+    settle(torch, lambda i: q.qgemv_grouped(synth.FP16, probs[i % 2], 1, descs=descs[i % 2]))
     for i, pr in enumerate(pairs):
         q.qgemv_grouped(synth.FP16, probs[i % 2], 1, descs=descs[i % 2], events=pr)
     kd = sum(ev.elapsed_ms(a, b) for a, b in pairs[4:]) / 32 * 1e-3
@@ -601,6 +663,7 @@ def ffn_workloads(q, torch, synth, ev: HipEvents, quick: bool):
         with torch.cuda.graph(g):
             for i in range(LAYER_COPIES):
                 step(i)
+        settle(torch, lambda i: g.replay())
         for _ in range(25):
             g.replay()
         torch.cuda.synchronize()
@@ -611,6 +674,7 @@ def ffn_workloads(q, torch, synth, ev: HipEvents, quick: bool):
         torch.cuda.synchronize()
         dt = (time.perf_counter() - t0) / (reps * LAYER_COPIES)
         pairs = [(ev.create(), ev.create()) for _ in range(36)]
+        settle(torch, lambda i: g.replay())
         for i, pr in enumerate(pairs):
             c = copies[i % LAYER_COPIES]
             q.ffn_decode(1, c["wg"], c["wu"], c["wd"], H, F, x, out=y, ws=wsp, events=pr)
@@ -650,6 +714,7 @@ def prefill_workloads(q, torch, synth, ev: HipEvents, quick: bool):
         wsp = torch.empty(q.qgemm_workspace(synth.BF16, M, w.K), dtype=torch.uint8, device=dev)
         reps, warm = 200, 40   # back to back: the settled time
         pairs = [(ev.create(), ev.create()) for _ in range(reps + warm)]
+        settle(torch, lambda i: q.qgemm(fmt, Ws[i % 4], w.N, w.K, X, out=Y, ws=wsp))
         for i in range(reps + warm):
             q.qgemm(fmt, Ws[i % 4], w.N, w.K, X, out=Y, ws=wsp, events=pairs[i])
         d = sorted(ev.elapsed_ms(a, b) * 1e-3 for a, b in pairs[warm:])
@@ -777,6 +842,7 @@ def moe_decode_workloads(q, torch, synth, quick: bool):
             with torch.cuda.graph(g):
                 for i in range(sets):
                     step(i)
+            settle(torch, lambda i: g.replay())
             for _ in range(12):
                 g.replay()
             torch.cuda.synchronize()
@@ -798,9 +864,9 @@ def moe_decode_workloads(q, torch, synth, quick: bool):
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    # 4000 steps after 400 warm-up ones take ~0.1 s of GPU time; the step time
-    # settles after a few thousand steps (measured on MI355X: 22.1-22.7 us a
-    # step over the first 800 after 80, 20.7 us over 4000 after 400).
+    # 4000 steps after 400 warm-up ones take ~0.1 s of GPU time (the
+    # driver's own runs use other K / W; every run first settles the GPU for
+    # SETTLE_MS with untimed replays of the step).
     ap.add_argument("--steps", type=int, default=4000)
     ap.add_argument("--warmup", type=int, default=400)
     ap.add_argument("--kernel-reps", type=int, default=64)
@@ -832,18 +898,32 @@ def main():
     log("building the 8B-shaped layer (8 weight copies)...")
     layer = DecodeLayer(q, torch, synth, 1, LAYER_COPIES)
     step_bytes = layer.step_bytes()
+    # The measured read ceiling and the step's launch timed alone (eager,
+    # dispatch-recorded events) come first; each timed part is preceded by
+    # SETTLE_MS of its own work, untimed.
+    ceiling = None
+    if not args.no_ceiling:
+        ceiling = stream_ceiling(q, torch, ev, step_bytes)
+    k_bytes = step_bytes
+    mean_k, durs = time_dominant_kernel(q, layer, ev, args.kernel_reps, "all")
+    achieved = k_bytes / mean_k / 1e9
+    sd = sorted(durs)
+    log(f"step kernel mean {mean_k * 1e6:.2f} us (min {sd[0] * 1e6:.2f}, median {sd[len(sd) // 2] * 1e6:.2f}, "
+        f"max {sd[-1] * 1e6:.2f}) -> {achieved:.1f} GB/s")
+    if ceiling is not None:
+        ceiling["headline_kernel_frac_of_read"] = round(achieved / ceiling["read_GB/s"], 4)
+        ceiling["headline_kernel_vs_read_launch"] = round(achieved / ceiling["read_launch_GB/s"], 4)
+        log(f"measured stream ceiling {json.dumps(ceiling)}")
+
     log(f"step bytes {step_bytes}; timing {args.steps} steps after {args.warmup} warm-up steps")
-    dt = time_graph_steps(torch, layer, args.steps, args.warmup)
+    dt, host_dt = time_graph_steps(torch, layer, args.steps, args.warmup)
     value = step_bytes * args.steps / dt / 1e9
     ms_per_step = dt / args.steps * 1e3
-    log(f"value {value:.1f} GB/s, {ms_per_step * 1e3:.2f} us/step")
+    log(f"value {value:.1f} GB/s, {ms_per_step * 1e3:.2f} us/step (host clock around gate + steps: "
+        f"{host_dt * 1e3:.3f} ms)")
 
-    mean_k, durs = time_dominant_kernel(q, layer, ev, args.kernel_reps, "all")
-    k_bytes = step_bytes
-    achieved = k_bytes / mean_k / 1e9
     src_hash = _kernel_source_hash()
     traffic = _profile_traffic(src_hash)
-    sd = sorted(durs)
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
                 "kernel": "qgemv grouped launch of the 8B layer's seven Q4_0 projections, M=1",
@@ -854,16 +934,8 @@ def main():
                 # the same launch replayed from a HIP graph, one per step, gaps included
                 "graph_step_us": round(ms_per_step * 1e3, 3),
                 "graph_step_frac": round(step_bytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
-    log(f"step kernel mean {mean_k * 1e6:.2f} us (min {sd[0] * 1e6:.2f}, median {sd[len(sd) // 2] * 1e6:.2f}, "
-        f"max {sd[-1] * 1e6:.2f}) -> {achieved:.1f} GB/s")
-
-    ceiling = None
-    if not args.no_ceiling:
-        ceiling = stream_ceiling(q, torch, ev, k_bytes)
-        ceiling["headline_kernel_frac_of_read"] = round(achieved / ceiling["read_GB/s"], 4)
-        ceiling["headline_kernel_vs_read_launch"] = round(achieved / ceiling["read_launch_GB/s"], 4)
+    if ceiling is not None:
         roofline["measured_ceiling"] = ceiling
-        log(f"measured stream ceiling {json.dumps(ceiling)}")
 
     if args.calibrate_copy:
         a = torch.empty(1 << 28, dtype=torch.uint8, device="cuda:0")
@@ -896,6 +968,12 @@ def main():
                                "down; hidden 4096, ffn 12288), Q4_0 weights, M=1 fp16 activations (four "
                                "independent inputs), one grouped launch",
                    "M": 1, "weight_copies": LAYER_COPIES, "launches_per_step": 1, "step_bytes": step_bytes,
+                   "timing": "the W warm-up steps and the K timed steps each captured as one HIP graph "
+                             "(one launch per step, consecutive steps on consecutive weight copies); GPU "
+                             "events around the timed graph, queued behind a bounded spin kernel; before "
+                             f"the W steps an 8-step graph is replayed untimed for {SETTLE_MS:g} ms so the GPU "
+                             "leaves its idle clock state",
+                   "host_ms_gate_and_steps": round(host_dt * 1e3, 4),
                    "hbm_frac": round(value / HBM_PEAK_GBS, 4)},
         "roofline": roofline,
         "cpu_baseline": cpu,

@@ -29,6 +29,13 @@
 #ifndef Q4Q8_GEMM_STAGES_F16
 #define Q4Q8_GEMM_STAGES_F16 4
 #endif
+// The wide tile: 16 MT rows x 64 NT columns.
+#ifndef Q4Q8_GEMM_WIDE_MT
+#define Q4Q8_GEMM_WIDE_MT 8
+#endif
+#ifndef Q4Q8_GEMM_WIDE_NT
+#define Q4Q8_GEMM_WIDE_NT 3
+#endif
 
 namespace q4q8 {
 
@@ -218,9 +225,10 @@ template <int FMT, int YDT>
 static void launch_shape(const void* W, int64_t N, int64_t K, const void* X, int64_t ldx, int64_t M,
                          const int32_t* rexp, void* Y, int64_t ldy, hipStream_t s, const LaunchEvents& ev) {
   constexpr int S = FMT == kQ4_0 ? Q4Q8_GEMM_STAGES_Q4 : FMT == kQ8_0 ? Q4Q8_GEMM_STAGES_Q8 : Q4Q8_GEMM_STAGES_F16;
-  const int64_t wide = (M + 127) / 128 * ((N + 191) / 192);
+  constexpr int WMT = Q4Q8_GEMM_WIDE_MT, WNT = Q4Q8_GEMM_WIDE_NT;
+  const int64_t wide = (M + 16 * WMT - 1) / (16 * WMT) * ((N + 64 * WNT - 1) / (64 * WNT));
   if (wide >= 256)
-    launch_tile<FMT, YDT, 8, 3, S>(W, N, K, X, ldx, M, rexp, Y, ldy, s, ev);
+    launch_tile<FMT, YDT, WMT, WNT, S>(W, N, K, X, ldx, M, rexp, Y, ldy, s, ev);
   else if (M > 128)
     launch_tile<FMT, YDT, 8, 2, S>(W, N, K, X, ldx, M, rexp, Y, ldy, s, ev);
   else if (M > 64)
