@@ -374,7 +374,8 @@ def time_dominant_kernel(q, layer: DecodeLayer, ev: HipEvents, reps: int, group:
     """Mean duration (s) of one launch group, from dispatch-recorded events."""
     pairs = [(ev.create(), ev.create()) for _ in range(reps)]
     L = len(layer.copies)
-    settle(layer.torch, lambda i: layer.step(i % L))
+    n = settle(layer.torch, lambda i: layer.step(i % L))
+    log(f"{group}: {n} untimed launches, then {reps} timed")
     for i in range(reps):
         layer.step(i % L, timed_group=group, events=pairs[i])
     durs = [ev.elapsed_ms(a, b) * 1e-3 for a, b in pairs]

@@ -18,10 +18,13 @@
 #include "q4q8_internal.h"
 #include "qgemm_core.h"
 
-// Pipeline depth per format: Q8_0 weight stages take 15 registers a lane
-// each, so its ring is one stage shorter to stay within 256 registers.
+// Pipeline depth per format.  Q8_0 weight stages take 15 registers a lane
+// each, so its ring is one stage shorter to stay within 256 registers; Q4_0
+// with two or three weight tiles a wave measured 1.5-2 % faster with 3
+// stages than with 4 (MI355X, K 4096, N 12288: M 256 37.2 -> 36.4 us, M 512
+// 56.2 -> 55.5 us, M 2048 201.9 -> 198.4 us a call).
 #ifndef Q4Q8_GEMM_STAGES_Q4
-#define Q4Q8_GEMM_STAGES_Q4 4
+#define Q4Q8_GEMM_STAGES_Q4 3
 #endif
 #ifndef Q4Q8_GEMM_STAGES_Q8
 #define Q4Q8_GEMM_STAGES_Q8 3
@@ -225,6 +228,9 @@ template <int FMT, int YDT>
 static void launch_shape(const void* W, int64_t N, int64_t K, const void* X, int64_t ldx, int64_t M,
                          const int32_t* rexp, void* Y, int64_t ldy, hipStream_t s, const LaunchEvents& ev) {
   constexpr int S = FMT == kQ4_0 ? Q4Q8_GEMM_STAGES_Q4 : FMT == kQ8_0 ? Q4Q8_GEMM_STAGES_Q8 : Q4Q8_GEMM_STAGES_F16;
+  // One weight tile a wave issues a third of the loads per chunk: a deeper
+  // ring pays there (Q4_0, M 128: 27.0 us with 3 stages, 25.7 with 4).
+  constexpr int S1 = FMT == kQ4_0 ? 4 : S;
   constexpr int WMT = Q4Q8_GEMM_WIDE_MT, WNT = Q4Q8_GEMM_WIDE_NT;
   const int64_t wide = (M + 16 * WMT - 1) / (16 * WMT) * ((N + 64 * WNT - 1) / (64 * WNT));
   if (wide >= 256)
@@ -232,9 +238,9 @@ static void launch_shape(const void* W, int64_t N, int64_t K, const void* X, int
   else if (M > 128)
     launch_tile<FMT, YDT, 8, 2, S>(W, N, K, X, ldx, M, rexp, Y, ldy, s, ev);
   else if (M > 64)
-    launch_tile<FMT, YDT, 8, 1, S>(W, N, K, X, ldx, M, rexp, Y, ldy, s, ev);
+    launch_tile<FMT, YDT, 8, 1, S1>(W, N, K, X, ldx, M, rexp, Y, ldy, s, ev);
   else
-    launch_tile<FMT, YDT, 4, 1, S>(W, N, K, X, ldx, M, rexp, Y, ldy, s, ev);
+    launch_tile<FMT, YDT, 4, 1, S1>(W, N, K, X, ldx, M, rexp, Y, ldy, s, ev);
 }
 
 // BF16 activations: one row-scaled fp16 copy [M, Kp], Kp = K rounded up to
