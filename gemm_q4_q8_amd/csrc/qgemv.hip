@@ -320,11 +320,25 @@ hipError_t launch_qgemv(int fmt, int xdt, GemvArgs args, int max_chunks, int max
   // x goes to LDS for every problem whose rows fit there; the LDS is sized
   // for the longest of those, and a problem with a longer K reads x from
   // global memory (M = 8 with K = 12288 next to K = 4096 problems).
-  int xk = 0;
-  for (int i = 0; i < args.count; ++i) {
-    const int k = args.p[i].K;
-    if ((int64_t)args.M * (k + 8) * 2 + kXSlack <= kLdsCap && k > xk) xk = k;
+  // A launch of problems with different K and at most 3 activation rows
+  // stages only the problems whose rows take <= 40 KB: the deeper ones (the
+  // 12288-deep down projection, 49-74 KB of rows at M = 2-3) read x from
+  // global memory, so the LDS no longer caps the workgroups a CU holds
+  // (measured on MI355X, 8B layer in one launch, graph-replayed steps: M = 2
+  // 22.5 -> 21.9 us, M = 3 22.7 -> 22.5 us; at M = 1 all rows fit anyway, at
+  // M = 4 the global reads of four rows cost more: 25.0 -> 28.9 us).
+  int64_t target = kLdsCap;
+  if (args.M <= 3) {
+    bool mk = false;
+    for (int i = 1; i < args.count; ++i) mk |= args.p[i].K != args.p[0].K;
+    if (mk) target = 40 * 1024;
   }
+  int xk = 0;
+  for (int pass = 0; pass < 2 && xk == 0; ++pass)   // no problem under the target: the usual LDS cap
+    for (int i = 0; i < args.count; ++i) {
+      const int k = args.p[i].K;
+      if ((int64_t)args.M * (k + 8) * 2 + kXSlack <= (pass ? kLdsCap : target) && k > xk) xk = k;
+    }
   args.xk = xk;
   GemvShape c = pick_shape(args.total_tiles, max_chunks, args.M, xk > 0 ? xk : max_k);
   if (c.xmode == kXLds && xk < max_k) c.xmode = kXMixed;
