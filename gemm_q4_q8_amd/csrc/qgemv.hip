@@ -320,18 +320,21 @@ hipError_t launch_qgemv(int fmt, int xdt, GemvArgs args, int max_chunks, int max
   // x goes to LDS for every problem whose rows fit there; the LDS is sized
   // for the longest of those, and a problem with a longer K reads x from
   // global memory (M = 8 with K = 12288 next to K = 4096 problems).
-  // A launch of problems with different K and at most 3 activation rows
-  // stages only the problems whose rows take <= 40 KB: the deeper ones (the
-  // 12288-deep down projection, 49-74 KB of rows at M = 2-3) read x from
+  // A launch of problems with different K stages only the problems whose
+  // rows take <= 40 KB (at most 3 activation rows) or <= 76 KB (5 or more
+  // rows, so that two workgroups share a CU); the deeper ones read x from
   // global memory, so the LDS no longer caps the workgroups a CU holds
-  // (measured on MI355X, 8B layer in one launch, graph-replayed steps: M = 2
-  // 22.5 -> 21.9 us, M = 3 22.7 -> 22.5 us; at M = 1 all rows fit anyway, at
-  // M = 4 the global reads of four rows cost more: 25.0 -> 28.9 us).
+  // (measured on MI355X, one grouped launch: 8B layer M = 2 22.5 -> 21.9 us,
+  // M = 3 22.7 -> 22.5 us; Q8_0 3B matrices M = 8 19.9 -> 16.8 us, the
+  // 8192-deep down projection's 131 KB of rows had held one workgroup a CU.
+  // At M = 1 all rows fit anyway; at M = 4 the global reads of four rows cost
+  // more: 25.0 -> 28.9 us).
   int64_t target = kLdsCap;
-  if (args.M <= 3) {
+  {
     bool mk = false;
     for (int i = 1; i < args.count; ++i) mk |= args.p[i].K != args.p[0].K;
-    if (mk) target = 40 * 1024;
+    if (mk && args.M <= 3) target = 40 * 1024;
+    if (mk && args.M >= 5) target = 76 * 1024;   // two workgroups a CU
   }
   int xk = 0;
   for (int pass = 0; pass < 2 && xk == 0; ++pass)   // no problem under the target: the usual LDS cap

@@ -192,7 +192,7 @@ def test_qgemv_oversized_x(q, fmt, xdt, M, N, K):
     _grouped_check(q, fmt, [w], [x], M, f"oversized x fmt{fmt} M{M} K{K}")
 
 
-@pytest.mark.parametrize("M", [1, 2, 3, 8])
+@pytest.mark.parametrize("M", [1, 2, 3, 5, 8])
 def test_qgemv_layer_8b_one_launch(q, M):
     """The 8B-shaped layer's seven projections in one grouped launch (the
     benchmark's headline launch shape), every output."""
@@ -202,7 +202,7 @@ def test_qgemv_layer_8b_one_launch(q, M):
                    f"8B layer one launch M{M}")
 
 
-@pytest.mark.parametrize("M", [1, 8])
+@pytest.mark.parametrize("M", [1, 2, 5, 8])
 def test_qgemv_q8_3b_one_launch(q, M):
     ws, xs = synth.q8_3b(M)
     names = list(ws)
