@@ -1,9 +1,10 @@
 """Seeded random shapes through every product family against the oracle:
 decode GEMV (Q4_0 / Q8_0 / fp16 weights, fp16 / bf16 x, M = 1..8), grouped
 GEMV launches of 2-8 problems with different K, prefill GEMM (every format and
-output dtype, ragged M and N), and the MoE layer through the one-call prefill
+output dtype, ragged M and N), the MoE layer through the one-call prefill
 entry point and the one-call decode entry point (routing ids and the sorted
-pairs bit-exact, h and out within their bounds).  Shapes are drawn from a
+pairs bit-exact, h and out within their bounds), and prefill attention
+(batch, sequence length, head counts with GQA, causal or not, bf16 / fp16).  Shapes are drawn from a
 fixed seed, so every run checks the same cases."""
 import numpy as np
 import pytest
@@ -28,7 +29,8 @@ def q():
 
 
 def _cases(kind, n):
-    rng = np.random.default_rng(synth.rng_for(970, {"gemv": 0, "grouped": 1, "gemm": 2, "moe": 3, "dec": 4}[kind])
+    rng = np.random.default_rng(synth.rng_for(970, {"gemv": 0, "grouped": 1, "gemm": 2, "moe": 3, "dec": 4,
+                                                     "attn": 5}[kind])
                                 .integers(1 << 62))
     return [int(s) for s in rng.integers(1 << 30, size=n)]
 
@@ -109,3 +111,22 @@ def test_random_moe_decode(q, seed):
     got = tm._run_moe_decode(q, fmt, logits, x, wg, wu, wd, k, H, F)
     tm._check_moe(fmt, logits, x, wg, wu, wd, k, H, F, got,
                   f"moe_decode fmt{fmt} T{logits.shape[0]} E{len(wg)} k{k} H{H} F{F}")
+
+
+@pytest.mark.parametrize("seed", _cases("attn", 16))
+def test_random_attention(q, seed):
+    r = np.random.default_rng(seed)
+    B, S = int(r.integers(1, 3)), int(r.integers(1, 1100))
+    Hkv = int(r.choice([1, 2, 4, 8]))
+    Hq = Hkv * int(r.choice([1, 2, 4]))
+    causal, dt = bool(r.integers(0, 2)), int(r.choice([1, 2]))
+    qa, ka, va = synth.attention_inputs(B, S, Hq, Hkv, 128, dt, seed)
+    o = q.attn_prefill(act_tensor(qa), act_tensor(ka), act_tensor(va), causal=causal)
+    torch.cuda.synchronize()
+    got = values(o)
+    ref, bound = oracle.attention(qa.values, ka.values, va.values, causal=causal)
+    tol = 2.0 ** -7 * bound + 2.0 ** -8 * np.abs(ref) + 1e-5   # the attention tests' acceptance rule
+    err = np.abs(got - ref)
+    assert np.all(np.isfinite(got)) and np.all(err <= tol), \
+        f"attn B{B} S{S} Hq{Hq} Hkv{Hkv} causal{causal} dt{dt}: err/tol {(err / tol).max():.3g}"
+
